@@ -1,0 +1,54 @@
+"""KV compression: softmax-weighted pooling of m consecutive tokens into one entry.
+
+Test infrastructure: see the package docstring.
+
+[P5] section "두 가지 압축 전략: CSA 및 HCA": CSA merges 4 consecutive tokens
+into one KV entry by softmax-weighted pooling; HCA merges 128 tokens into one.
+[P3] section "쉽게 이해하기": the merge is learned (each token's contribution is
+learned), not a plain mean.
+
+Readings taken where the pages are silent:
+  * one scalar pooling logit z per token; softmax over the m tokens of a block;
+  * blocks are aligned and non-overlapping: block j = tokens [j*m, j*m+m);
+  * the pooled vector is rotated (partial RoPE) AFTER pooling, at position
+    p_j = pos0 + j*m + entry_pos_offset (offset 0: the block's first token);
+  * storage: bf16 by RNE, or e4m3fn with one fp32 scale per entry,
+    s = max|e|/448 (s = 1 when the entry is all zero), code = RNE_sat(e/s).
+"""
+import numpy as np
+
+from . import formats, rope
+
+
+def pool(x, z, m):
+    """x [n_tok, D] fp64, z [n_tok] fp64 -> pooled [n_tok/m, D] fp64 (no RoPE)."""
+    n_tok, D = x.shape
+    assert n_tok % m == 0
+    xb = x.reshape(n_tok // m, m, D)
+    zb = z.reshape(n_tok // m, m)
+    zmax = zb.max(axis=1, keepdims=True)
+    w = np.exp(zb - zmax)
+    alpha = w / w.sum(axis=1, keepdims=True)
+    return np.einsum("jm,jmd->jd", alpha, xb)
+
+
+def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=0):
+    """One sequence.
+
+    x_bits [n_tok, D] bf16 bits; z [n_tok] fp32; pos0 = position of x[0].
+    Returns (exact fp64 rotated entries [n, D], stored, scale) where stored is
+    bf16 bits [n, D] (scale None) or e4m3 codes [n, D] with fp32 scales [n].
+    """
+    x = formats.bf16_to_f64(x_bits)
+    zz = np.asarray(z, dtype=np.float64)
+    e = pool(x, zz, m)
+    n = e.shape[0]
+    p = pos0 + np.arange(n, dtype=np.int64) * m + entry_pos_offset
+    e = rope.apply(e, p, d_rope, rope_base)
+    if out_dtype == "bf16":
+        return e, formats.f64_to_bf16(e), None
+    assert out_dtype == "fp8"
+    amax = np.abs(e).max(axis=1)
+    s = np.where(amax == 0, 1.0, amax / formats.E4M3_MAX).astype(np.float32)
+    codes = formats.f64_to_e4m3(e / s.astype(np.float64)[:, None])
+    return e, codes, s

@@ -1,0 +1,75 @@
+"""Decode loop of one CSA layer and one HCA layer with ring buffers and re-compression.
+
+Test infrastructure: see the package docstring.
+
+[P3] section "주요 인사이트": CSA layers and HCA layers are interleaved 1:1.
+[P3] section "쉽게 이해하기" and [P4]: each keeps a window of the latest 128
+tokens. [P5] section "두 가지 압축 전략: CSA 및 HCA": CSA pools 4 tokens per
+entry and selects top-k with the FP4 indexer; HCA pools 128 tokens per entry
+and attends to all entries.
+
+Readings taken where the pages are silent:
+  * decode step at position t: the new raw token (bf16) and its pooling logit
+    go into ring slot t mod W; when (t+1) is a multiple of m, the block of
+    positions [t-m+1, t] (contiguous ring slots, since m divides W) is
+    compressed into entry (t+1)/m - 1 at position t-m+1; then the layer
+    attends with its query at t;
+  * the indexer key of each CSA entry is an input (already present in the key
+    buffer); only its visibility (j < n_entries) changes during the loop.
+"""
+import numpy as np
+
+from . import attention, compress, indexer, topk as topk_mod
+
+
+class Layer:
+    """State of one layer for a batch of sequences (arrays are modified in place)."""
+
+    def __init__(self, kind, m, W, d_rope, d_v, rope_base, scale, ckv, ckv_scale, dtype,
+                 n_entries, ring_x, ring_z, k=None, ik=None, ik_scale=None):
+        assert kind in ("csa", "hca")
+        self.kind, self.m, self.W = kind, m, W
+        self.d_rope, self.d_v, self.rope_base, self.scale = d_rope, d_v, rope_base, scale
+        self.ckv, self.ckv_scale, self.dtype = ckv, ckv_scale, dtype
+        self.n_entries = np.array(n_entries, dtype=np.int64)
+        self.ring_x, self.ring_z = ring_x, ring_z
+        self.k, self.ik, self.ik_scale = k, ik, ik_scale
+
+    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None):
+        """Positions t [B]; x_new [B, D] bf16; z_new [B]; q [B, H, D] bf16; iq [B, H_I, D_I/2].
+
+        Returns (o fp64 [B, H, d_v], lse [B, H], idx int32 [B, k] or None).
+        """
+        B = len(t)
+        outs, lses, idxs = [], [], []
+        for b in range(B):
+            tb = int(t[b])
+            self.ring_x[b, tb % self.W] = x_new[b]
+            self.ring_z[b, tb % self.W] = z_new[b]
+            if (tb + 1) % self.m == 0:
+                j = (tb + 1) // self.m - 1
+                assert j == self.n_entries[b], "entry count out of step with position"
+                p0 = tb - self.m + 1
+                slots = np.arange(p0, tb + 1) % self.W
+                _, stored, s = compress.compress(self.ring_x[b, slots], self.ring_z[b, slots], p0,
+                                                 self.m, self.d_rope, self.rope_base, self.dtype)
+                self.ckv[b, j] = stored[0]
+                if s is not None:
+                    self.ckv_scale[b, j] = s[0]
+                self.n_entries[b] = j + 1
+            n = int(self.n_entries[b])
+            assert n == (tb + 1) // self.m
+            sel = None
+            if self.kind == "csa":
+                sc = indexer.scores(iq[b][None], iq_scale[b][None], self.ik[b, :n], self.ik_scale[b, :n],
+                                    np.array([n]))
+                sel, _ = topk_mod.topk(sc, self.k)
+                sel = sel[0]
+                idxs.append(sel)
+            ent = attention.Entries(self.ckv[b], None if self.ckv_scale is None else self.ckv_scale[b],
+                                    self.dtype)
+            o, lse = attention.decode_one(q[b], tb, ent, n, sel, self.ring_x[b], self.W,
+                                          self.d_rope, self.d_v, self.rope_base, self.scale)
+            outs.append(o)
+            lses.append(lse)
+        return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)

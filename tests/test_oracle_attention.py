@@ -1,0 +1,203 @@
+"""Pins of oracle.attention and oracle.hybrid: textbook attention, closed forms, brute force."""
+import math
+
+import numpy as np
+import torch
+
+from oracle import attention, compress, formats, hybrid, indexer, rope, topk
+
+
+def _bf16(rng, shape, std=1.0):
+    return formats.f64_to_bf16(rng.standard_normal(shape) * std)
+
+
+def sdpa(q, k, v, scale, bias=None):
+    """Textbook attention from torch (fp64, CPU): softmax(q k^T * scale + bias) v."""
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(a)).double()[None, None] for a in (q, k, v))
+    mask = None if bias is None else torch.from_numpy(bias).double()[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return o[0, 0].numpy()
+
+
+def test_block_of_one_full_selection_no_window_is_plain_attention():
+    """m=1, uniform logits, k=N, W=0, no RoPE: CSA reduces to textbook softmax attention."""
+    rng = np.random.default_rng(0)
+    L, H, D = 40, 4, 16
+    x = _bf16(rng, (L, D), 0.7)
+    _, stored, _ = compress.compress(x, np.zeros(L, np.float32), 0, 1, 0, 10000.0, "bf16")
+    assert np.array_equal(stored, x)
+    ent = attention.Entries(stored, None, "bf16")
+    q = _bf16(rng, (H, D), 0.7)
+    t = L - 1
+    iq = rng.integers(0, 256, (1, 2, 16), dtype=np.uint8)
+    ik = rng.integers(0, 256, (L, 16), dtype=np.uint8)
+    sc = indexer.scores(iq, np.full((1, 2, 1), 127, np.uint8), ik, np.full((L, 1), 127, np.uint8), np.array([L]))
+    sel = topk.topk(sc, L)[0][0]
+    o, lse = attention.decode_one(q, t, ent, L, sel, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.3)
+    xf = formats.bf16_to_f64(x)
+    want = sdpa(formats.bf16_to_f64(q), xf, xf, 0.3)
+    assert np.allclose(o, want, rtol=1e-12, atol=1e-14)
+    logits = 0.3 * formats.bf16_to_f64(q) @ xf.T
+    assert np.allclose(lse, np.log(np.exp(logits).sum(axis=1)), atol=1e-12)
+
+
+def test_topk_of_all_entries_equals_dense_hca_path():
+    rng = np.random.default_rng(1)
+    N, H, D, dv, W = 30, 3, 24, 16, 8
+    ckv = rng.integers(0, 0x7E, (N, D), dtype=np.uint8)
+    sc = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    ent = attention.Entries(ckv, sc, "fp8")
+    ring = _bf16(rng, (W, D), 0.3)
+    q = _bf16(rng, (H, D), 0.3)
+    t = 4 * N + 2
+    perm = rng.permutation(N)
+    a = attention.decode_one(q, t, ent, N, perm, ring, W, 8, dv, 10000.0, 0.2)
+    b = attention.decode_one(q, t, ent, N, None, ring, W, 8, dv, 10000.0, 0.2)
+    assert np.allclose(a[0], b[0], rtol=1e-12, atol=1e-15) and np.allclose(a[1], b[1], atol=1e-12)
+
+
+def test_window_duplicates_add_ln2_to_their_logits():
+    """m=1, k=N, W>0, no RoPE: the last W tokens appear twice -> +ln 2 on their logits."""
+    rng = np.random.default_rng(2)
+    L, H, D, W = 50, 2, 8, 6
+    x = _bf16(rng, (L, D))
+    ent = attention.Entries(x, None, "bf16")
+    ring = np.zeros((W, D), np.uint16)
+    t = L - 1
+    for p in range(L - W, L):
+        ring[p % W] = x[p]
+    q = _bf16(rng, (H, D))
+    o, lse = attention.decode_one(q, t, ent, L, np.arange(L), ring, W, 0, D, 1.0, 0.5)
+    bias = np.zeros((H, L))
+    bias[:, L - W:] = math.log(2.0)
+    xf = formats.bf16_to_f64(x)
+    assert np.allclose(o, sdpa(formats.bf16_to_f64(q), xf, xf, 0.5, bias), rtol=1e-12, atol=1e-14)
+
+
+def test_no_entries_is_sliding_window_attention_and_union_is_lse_merge():
+    rng = np.random.default_rng(3)
+    H, D, dv, W, dr = 4, 16, 12, 8, 8
+    t = 5                                      # fewer than W tokens so far, no entries
+    ring = _bf16(rng, (W, D))
+    q = _bf16(rng, (H, D))
+    ent = attention.Entries(rng.integers(0, 0x7E, (4, D), dtype=np.uint8), np.ones(4, np.float32) / 64, "fp8")
+    o, lse = attention.decode_one(q, t, ent, 0, None, ring, W, dr, dv, 10000.0, 0.25)
+    pos = np.arange(0, t + 1)
+    kw = rope.apply(formats.bf16_to_f64(ring[pos % W]), pos, dr, 10000.0)
+    qr = rope.apply(formats.bf16_to_f64(q), np.full(H, t), dr, 10000.0)
+    assert np.allclose(o, sdpa(qr, kw, kw[:, :dv], 0.25), rtol=1e-12, atol=1e-14)
+    # union of entries and window = LSE-merge of the two partial attentions
+    t2 = 23
+    ring2 = _bf16(rng, (W, D))
+    ou, lu = attention.decode_one(q, t2, ent, 4, None, ring2, W, dr, dv, 10000.0, 0.25)
+    oe, le = attention.decode_one(q, t2, ent, 4, None, ring2, 0, dr, dv, 10000.0, 0.25)
+    pos2 = np.arange(t2 - W + 1, t2 + 1)
+    qr2 = rope.apply(formats.bf16_to_f64(q), np.full(H, t2), dr, 10000.0)
+    kw2 = rope.apply(formats.bf16_to_f64(ring2[pos2 % W]), pos2, dr, 10000.0)
+    ow, lw = attention.attend(qr2, kw2, kw2[:, :dv], 0.25)
+    mx = np.maximum(le, lw)
+    lm = mx + np.log(np.exp(le - mx) + np.exp(lw - mx))
+    om = (np.exp(le - lm)[:, None] * oe + np.exp(lw - lm)[:, None] * ow)
+    assert np.allclose(ou, om, rtol=1e-12, atol=1e-14) and np.allclose(lu, lm, atol=1e-12)
+
+
+def test_decode_matches_loop_brute_force():
+    rng = np.random.default_rng(4)
+    N, H, D, dv, W, dr, base, scale = 6, 2, 8, 6, 4, 4, 100.0, 0.4
+    ckv = _bf16(rng, (N, D))
+    ring = _bf16(rng, (W, D))
+    q = _bf16(rng, (H, D))
+    t, sel = 29, [4, -1, 1, 5]
+    o, lse = attention.decode_one(q, t, attention.Entries(ckv, None, "bf16"), 7, sel, ring, W, dr, dv, base, scale)
+
+    def rot(v, p):
+        v = list(v)
+        for i in range(dr // 2):
+            a = p * base ** (-2.0 * i / dr)
+            x0, x1 = v[D - dr + 2 * i], v[D - dr + 2 * i + 1]
+            v[D - dr + 2 * i], v[D - dr + 2 * i + 1] = x0 * math.cos(a) - x1 * math.sin(a), x0 * math.sin(a) + x1 * math.cos(a)
+        return v
+    keys = [list(formats.bf16_to_f64(ckv[j])) for j in (4, 1, 5)]
+    keys += [rot(formats.bf16_to_f64(ring[p % W]), p) for p in range(t - W + 1, t + 1)]
+    for h in range(H):
+        qh = rot(formats.bf16_to_f64(q[h]), t)
+        lg = [scale * sum(a * b for a, b in zip(qh, kk)) for kk in keys]
+        mx = max(lg)
+        ws = [math.exp(v - mx) for v in lg]
+        den = sum(ws)
+        for d in range(dv):
+            assert abs(o[h, d] - sum(w * kk[d] for w, kk in zip(ws, keys)) / den) < 1e-12
+        assert abs(lse[h] - (mx + math.log(den))) < 1e-12
+
+
+def test_shifting_every_position_leaves_the_output_unchanged():
+    rng = np.random.default_rng(5)
+    m, nblk, H, D, dv, W, dr = 4, 8, 2, 16, 8, 8, 8
+    x = _bf16(rng, (m * nblk, D))
+    z = rng.standard_normal(m * nblk).astype(np.float32)
+    q = _bf16(rng, (H, D))
+    outs = []
+    for shift in (0, 4 * 1000):
+        e, _, _ = compress.compress(x, z, shift, m, dr, 10000.0, "bf16")
+        # use the exact fp64 entries so only position arithmetic is tested
+        class Exact:
+            D = e.shape[1]
+
+            def rows(self, sel, e=e):
+                return e[np.asarray(sel, dtype=np.int64)] if len(sel) else np.zeros((0, self.D))
+        t = shift + m * nblk - 1
+        ring = np.zeros((W, D), np.uint16)
+        for p in range(t - W + 1, t + 1):
+            ring[p % W] = x[p - shift]
+        outs.append(attention.decode_one(q, t, Exact(), nblk, None, ring, W, dr, dv, 10000.0, 0.3)[0])
+    assert np.allclose(outs[0], outs[1], rtol=1e-9, atol=1e-12)
+
+
+def test_hybrid_loop_equals_one_shot_recomputation():
+    """The ring buffer and periodic re-compression agree with compressing the full token history."""
+    rng = np.random.default_rng(6)
+    B, H, D, dv, dr, W, L, steps = 2, 2, 16, 8, 8, 16, 64, 40
+    HI, DI, k = 2, 32, 8
+    tokens = _bf16(rng, (B, L + steps, D), 0.5)
+    logits = rng.standard_normal((B, L + steps)).astype(np.float32)
+    layers = {}
+    for kind, m in (("csa", 4), ("hca", 16)):
+        n0 = L // m
+        cap = (L + steps) // m
+        ckv = np.zeros((B, cap, D), np.uint8)
+        scl = np.ones((B, cap), np.float32)
+        for b in range(B):   # initial entries: compression of the history (so one-shot can rebuild them)
+            _, c, s = compress.compress(tokens[b, :L], logits[b, :L], 0, m, dr, 10000.0, "fp8")
+            ckv[b, :n0], scl[b, :n0] = c, s
+        ring_x = np.zeros((B, W, D), np.uint16)
+        ring_z = np.zeros((B, W), np.float32)
+        for p in range(L - W, L):
+            ring_x[:, p % W] = tokens[:, p]
+            ring_z[:, p % W] = logits[:, p]
+        ik = rng.integers(0, 256, (B, cap, DI // 2), dtype=np.uint8)
+        iks = rng.integers(126, 128, (B, cap, DI // 32), dtype=np.uint8)
+        layers[kind] = hybrid.Layer(kind, m, W, dr, dv, 10000.0, 0.3, ckv, scl, "fp8", np.full(B, n0),
+                                    ring_x, ring_z, k=k, ik=ik, ik_scale=iks)
+    for s in range(steps):
+        t = np.full(B, L + s)
+        q = _bf16(rng, (B, H, D), 0.5)
+        iq = rng.integers(0, 256, (B, HI, DI // 2), dtype=np.uint8)
+        iqs = np.full((B, HI, 1), 127, np.uint8)
+        for kind, lay in layers.items():
+            o, lse, idx = lay.step(t, tokens[:, L + s], logits[:, L + s], q, iq, iqs)
+            m = lay.m
+            n = (L + s + 1) // m
+            for b in range(B):   # one-shot: compress the whole history, attend from scratch
+                _, c, sc = compress.compress(tokens[b, :n * m], logits[b, :n * m], 0, m, dr, 10000.0, "fp8")
+                assert np.array_equal(lay.ckv[b, :n], c) and np.array_equal(lay.ckv_scale[b, :n], sc)
+                ent = attention.Entries(c, sc, "fp8")
+                sel = None
+                if kind == "csa":
+                    scs = indexer.scores(iq[b][None], iqs[b][None], lay.ik[b, :n], lay.ik_scale[b, :n], np.array([n]))
+                    sel = topk.topk(scs, k)[0][0]
+                    assert np.array_equal(sel, idx[b])
+                full_ring = np.zeros((W, D), np.uint16)
+                for p in range(L + s - W + 1, L + s + 1):
+                    full_ring[p % W] = tokens[b, p]
+                o1, l1 = attention.decode_one(q[b], L + s, ent, n, sel, full_ring, W, dr, dv, 10000.0, 0.3)
+                assert np.allclose(o[b], o1, rtol=0, atol=0) and np.allclose(lse[b], l1, rtol=0, atol=0)

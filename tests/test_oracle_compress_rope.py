@@ -1,0 +1,151 @@
+"""Pins of oracle.rope and oracle.compress: closed forms, invariants, brute force."""
+import math
+import os
+
+import numpy as np
+
+from oracle import compress, formats, rope
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(rng, shape, std=1.0):
+    return formats.f64_to_bf16(rng.standard_normal(shape) * std)
+
+
+# ------------------------------------------------------------------ RoPE
+def test_rope_matches_complex_rotation():
+    rng = np.random.default_rng(0)
+    D, dr, base = 12, 8, 10000.0
+    u = rng.standard_normal((5, D))
+    pos = np.array([0, 1, 7, 1000, 2 ** 20 + 3])
+    got = rope.apply(u, pos, dr, base)
+    # textbook complex form: (u_2i + i u_2i+1) * exp(i p base^(-2i/dr)) on the last dr dims
+    z = u[:, D - dr::2] + 1j * u[:, D - dr + 1::2]
+    theta = np.array([base ** (-(2.0 * i) / dr) for i in range(dr // 2)])
+    zr = z * np.exp(1j * pos[:, None] * theta[None, :])
+    assert np.allclose(got[:, :D - dr], u[:, :D - dr], rtol=0, atol=0)
+    assert np.allclose(got[:, D - dr::2], zr.real, rtol=0, atol=1e-12)
+    assert np.allclose(got[:, D - dr + 1::2], zr.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_position_zero_and_no_rope_are_identity():
+    u = np.random.default_rng(1).standard_normal((3, 16))
+    assert np.array_equal(rope.apply(u, np.zeros(3, np.int64), 8, 10000.0), u)
+    assert np.array_equal(rope.apply(u, np.arange(3) * 99, 0, 10000.0), u)
+
+
+def test_rope_preserves_pair_norms():
+    u = np.random.default_rng(2).standard_normal((4, 64))
+    r = rope.apply(u, np.array([3, 50, 9999, 123456]), 64, 10000.0)
+    assert np.allclose(np.hypot(r[:, 0::2], r[:, 1::2]), np.hypot(u[:, 0::2], u[:, 1::2]), atol=1e-13)
+
+
+def test_rope_dot_depends_only_on_position_difference():
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal(32), rng.standard_normal(32)
+    for a, b, d in [(5, 2, 1000), (100, 0, 77777), (2 ** 20, 2 ** 20 - 128, 12345)]:
+        d0 = rope.apply(q, np.array(a), 32, 10000.0) @ rope.apply(k, np.array(b), 32, 10000.0)
+        d1 = rope.apply(q, np.array(a + d), 32, 10000.0) @ rope.apply(k, np.array(b + d), 32, 10000.0)
+        # fp64 angles of size ~2^20 carry ~1e-10 absolute error
+        assert abs(d0 - d1) < 1e-9 * (1 + abs(d0))
+
+
+# ------------------------------------------------------------------ pooling
+def test_identical_tokens_pool_to_that_token_rotated():
+    rng = np.random.default_rng(4)
+    m, D, dr = 4, 16, 8
+    tok = _bf16(rng, (3, D))
+    x = np.repeat(tok, m, axis=0)
+    z = rng.standard_normal(3 * m).astype(np.float32)
+    e, _, _ = compress.compress(x, z, 40, m, dr, 10000.0, "bf16")
+    want = rope.apply(formats.bf16_to_f64(tok), 40 + np.arange(3) * m, dr, 10000.0)
+    assert np.allclose(e, want, rtol=0, atol=1e-14)
+
+
+def test_uniform_logits_give_the_mean_and_logit_shift_is_invisible():
+    rng = np.random.default_rng(5)
+    m, D = 128, 24
+    x = _bf16(rng, (2 * m, D))
+    e, _, _ = compress.compress(x, np.zeros(2 * m, np.float32), 0, m, 0, 10000.0, "bf16")
+    want = formats.bf16_to_f64(x).reshape(2, m, D).mean(axis=1)
+    assert np.allclose(e, want, rtol=0, atol=1e-15)
+    z = (np.round(rng.standard_normal(2 * m) * 1024) / 1024).astype(np.float32)  # exact after +shift
+    e1, _, _ = compress.compress(x, z, 0, m, 0, 10000.0, "bf16")
+    zs = (z.astype(np.float64) + np.repeat([3.0, -7.5], m)).astype(np.float32)
+    e2, _, _ = compress.compress(x, zs, 0, m, 0, 10000.0, "bf16")
+    assert np.allclose(e1, e2, rtol=0, atol=1e-14)
+
+
+def test_pooled_entry_lies_in_the_convex_hull_per_dim():
+    rng = np.random.default_rng(6)
+    m, D = 4, 32
+    x = _bf16(rng, (64 * m, D))
+    z = (rng.standard_normal(64 * m) * 3).astype(np.float32)
+    e, _, _ = compress.compress(x, z, 0, m, 0, 10000.0, "bf16")
+    xb = formats.bf16_to_f64(x).reshape(64, m, D)
+    assert np.all(e <= xb.max(axis=1) + 1e-15) and np.all(e >= xb.min(axis=1) - 1e-15)
+
+
+def test_block_of_one_is_the_rotated_token():
+    rng = np.random.default_rng(7)
+    x = _bf16(rng, (9, 16))
+    e, _, _ = compress.compress(x, rng.standard_normal(9).astype(np.float32), 100, 1, 8, 10000.0, "bf16")
+    assert np.allclose(e, rope.apply(formats.bf16_to_f64(x), 100 + np.arange(9), 8, 10000.0), atol=1e-15)
+
+
+def test_compress_matches_loop_brute_force():
+    rng = np.random.default_rng(8)
+    m, D, dr, base, pos0 = 4, 8, 4, 500.0, 17
+    x = _bf16(rng, (3 * m, D))
+    z = rng.standard_normal(3 * m).astype(np.float32)
+    e, stored, _ = compress.compress(x, z, pos0, m, dr, base, "bf16")
+    xf = formats.bf16_to_f64(x)
+    for j in range(3):
+        zz = [float(z[j * m + i]) for i in range(m)]
+        den = sum(math.exp(v) for v in zz)
+        pooled = [sum(math.exp(zz[i]) / den * xf[j * m + i, d] for i in range(m)) for d in range(D)]
+        p = pos0 + j * m
+        for i in range(dr // 2):
+            ang = p * base ** (-2.0 * i / dr)
+            a, b = pooled[D - dr + 2 * i], pooled[D - dr + 2 * i + 1]
+            pooled[D - dr + 2 * i] = a * math.cos(ang) - b * math.sin(ang)
+            pooled[D - dr + 2 * i + 1] = a * math.sin(ang) + b * math.cos(ang)
+        assert np.allclose(e[j], pooled, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(stored, formats.f64_to_bf16(e))
+
+
+def test_fp8_storage_scale_and_rounding_bound():
+    rng = np.random.default_rng(9)
+    m, D = 128, 64
+    x = _bf16(rng, (4 * m, D), 1 / 8)
+    z = rng.standard_normal(4 * m).astype(np.float32)
+    e, codes, s = compress.compress(x, z, 2 ** 20, m, 16, 10000.0, "fp8")
+    assert s.dtype == np.float32
+    amax = np.abs(e).max(axis=1)
+    assert np.allclose(s, amax / 448.0, rtol=1e-7, atol=0)
+    dec = formats.e4m3_to_f64(codes)
+    assert np.all(np.abs(dec).max(axis=1) == 448.0)        # the largest element maps to the top code
+    # RNE: error at most half a step of the e4m3 grid around each value (step 2^(e-3), subnormal 2^-9)
+    v = e / s.astype(np.float64)[:, None]
+    ex = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+    assert np.all(np.abs(dec - v) <= 2.0 ** (ex - 3) / 2 + 1e-12)
+
+
+def test_zero_entry_gets_unit_scale():
+    x = np.zeros((4, 8), np.uint16)
+    _, codes, s = compress.compress(x, np.zeros(4, np.float32), 0, 4, 0, 10000.0, "fp8")
+    assert s[0] == 1.0 and np.all(codes == 0)
+
+
+def test_page_entry_counts():
+    consts = {}
+    for line in open(os.path.join(GOLD, "page_constants.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, val = line.split()[:2]
+            consts[name] = int(val)
+    assert 4096 // consts["csa_block"] == 1024
+    assert 65536 // consts["csa_block"] == 16384
+    n_hca = 2 ** 20 // consts["hca_block"]
+    assert n_hca == 8192 and abs(n_hca - consts["hca_entries_1m_approx"]) / 8000 < 0.03
+    assert consts["hca_block"] // consts["csa_block"] == consts["hca_vs_csa_memory"]

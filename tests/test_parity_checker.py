@@ -1,0 +1,80 @@
+"""The parity checks must reject planted mistakes (planted in oracle outputs, on the CPU)."""
+import numpy as np
+import pytest
+
+from oracle import attention, formats, indexer, topk
+from tests import parity
+
+
+@pytest.fixture(scope="module")
+def oracle_case():
+    rng = np.random.default_rng(0)
+    iq = rng.integers(0, 256, (1, 4, 32), dtype=np.uint8)
+    ik = rng.integers(0, 256, (1024, 32), dtype=np.uint8)
+    sc = indexer.scores(iq, np.full((1, 4, 2), 127, np.uint8), ik, np.full((1024, 2), 127, np.uint8), np.array([1024]))
+    idx, s = topk.topk(sc, 128)
+    H, D = 16, 64
+    ckv = formats.f64_to_bf16(rng.standard_normal((1024, D)) / 8)
+    ring = formats.f64_to_bf16(rng.standard_normal((128, D)) / 8)
+    q = formats.f64_to_bf16(rng.standard_normal((H, D)))
+    o, _ = attention.decode_one(q, 4095, attention.Entries(ckv, None, "bf16"), 1024, idx[0], ring, 128, 32, D,
+                                10000.0, 1 / 8)
+    return idx, s, o
+
+
+def test_checker_accepts_the_oracle_itself(oracle_case):
+    idx, _, o = oracle_case
+    parity.topk_exact(idx, idx)
+    parity.attn_close(formats.f64_to_bf16(o), o)
+
+
+def test_checker_rejects_one_swapped_index(oracle_case):
+    idx, _, _ = oracle_case
+    bad = idx.copy()
+    bad[0, [3, 4]] = bad[0, [4, 3]]
+    with pytest.raises(parity.ParityError):
+        parity.topk_exact(bad, idx)
+
+
+def test_checker_rejects_a_flipped_tie_order(oracle_case):
+    idx, s, _ = oracle_case
+    ties = [i for i in range(127) if s[0, i] == s[0, i + 1]]
+    assert ties, "fixture should contain tied scores"
+    bad = idx.copy()
+    i = ties[0]
+    bad[0, [i, i + 1]] = bad[0, [i + 1, i]]
+    with pytest.raises(parity.ParityError):
+        parity.topk_exact(bad, idx)
+
+
+def test_checker_rejects_a_replaced_entry(oracle_case):
+    idx, _, _ = oracle_case
+    bad = idx.copy()
+    bad[0, -1] = next(j for j in range(1024) if j not in set(idx[0].tolist()))
+    with pytest.raises(parity.ParityError):
+        parity.topk_exact(bad, idx)
+
+
+def test_checker_rejects_output_off_by_6e3_relative(oracle_case):
+    _, _, o = oracle_case
+    rng = np.random.default_rng(1)
+    noise = rng.standard_normal(o.shape)
+    noise *= 6e-3 * np.linalg.norm(o) / np.linalg.norm(noise)
+    with pytest.raises(parity.ParityError):
+        parity.attn_close(formats.f64_to_bf16(o + noise), o)
+
+
+def test_compress_checks_reject_two_ulp_and_widespread_one_ulp():
+    w = formats.f64_to_bf16(np.linspace(-3, 3, 5000))
+    g = w.copy()
+    g[7] = np.uint16(int(g[7]) + 2)
+    with pytest.raises(parity.ParityError):
+        parity.compress_bf16_close(g, w)
+    g = w.copy()
+    g[:100] = (g[:100].astype(np.int64) + 1).astype(np.uint16)
+    with pytest.raises(parity.ParityError):
+        parity.compress_bf16_close(g, w)
+    c = np.arange(100, dtype=np.uint8)
+    s = np.ones(4, np.float32)
+    with pytest.raises(parity.ParityError):
+        parity.compress_fp8_close(c, s * (1 + 1e-5), c, s)
