@@ -1,0 +1,91 @@
+// Device helpers shared by the gfx950 kernels: storage conversions, wave-level
+// reductions, RoPE angles. Wavefront size is 64 on CDNA4.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cskv {
+
+constexpr int kWave = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: data read once).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// 8 bf16 in a uint4 -> 8 floats
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------- fp8 e4m3fn (OCP)
+// gfx950's v_cvt_*fp8* instructions use the OCP e4m3fn encoding.
+__device__ __forceinline__ float fp8_to_f32(uint32_t word, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(word, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(word, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(word, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(word, 3);
+  }
+}
+// four fp32 -> four e4m3fn codes (RNE), packed little-endian
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- RoPE
+// Angle p * base^(-2i/d_rope), formed in fp64 and reduced to [-pi, pi] before
+// the fp32 rotation (positions reach 2^20, where an fp32 angle would be off by
+// up to ~0.06 rad).
+__device__ __forceinline__ void rope_cs(double inv_freq, int64_t pos, float* c, float* s) {
+  double a = (double)pos * inv_freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  a = a - two_pi * rint(a / two_pi);
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+__device__ __forceinline__ double rope_inv_freq(float base, int pair, int d_rope) {
+  return pow((double)base, -2.0 * (double)pair / (double)d_rope);
+}
+
+}  // namespace cskv

@@ -1,0 +1,227 @@
+// KV compression (softmax pooling of m-token blocks + partial RoPE + storage
+// rounding) and the decode-time ring append.
+//
+// Method: page "DeepSeek-V4가 이차적 어텐션 비용 없이 백만 토큰 컨텍스트를 달성하는
+// 방법", section "두 가지 압축 전략: CSA 및 HCA" (4 tokens per CSA entry, 128 per
+// HCA entry, softmax-weighted pooling, partial RoPE); page "딥시크 V4 분석:
+// CSA·HCA 어텐션으로 100만 토큰 컨텍스트를 저비용에 구현한 방법", section "쉽게
+// 이해하기" (per-token learned contribution; 128-token window).
+//
+// Design (HBM-bound stream): one wavefront per output entry. Lane l owns the
+// 16-byte chunks l and l+64 of the D-dim row, so each token row is read by one
+// coalesced 1 KiB wave load (+ a short tail when D > 512). The m pooling
+// weights are wave-uniform scalars; tokens are read 8 at a time to keep
+// several loads in flight per lane. The fp8 scale needs the entry's max |e|,
+// which is a wave reduction with no LDS and no barrier.
+#include "common.cuh"
+#include "host_util.h"
+
+namespace cskv {
+
+constexpr int kCompressWaves = 4;  // waves per workgroup
+constexpr int kUnroll = 8;
+
+template <bool FP8>
+__global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
+    const uint16_t* __restrict__ x, int64_t x_seq_stride, const float* __restrict__ z,
+    int64_t z_seq_stride, const int64_t* __restrict__ pos0, int B, int n_ent, int D, int d_rope,
+    int m, int entry_pos_offset, float rope_base, void* __restrict__ out,
+    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
+  if (w >= B * n_ent) return;
+  const int b = w / n_ent;
+  const int j = w - b * n_ent;
+  const uint16_t* xb = x + (int64_t)b * x_seq_stride + (int64_t)j * m * D;
+  const float* zb = z + (int64_t)b * z_seq_stride + (int64_t)j * m;
+
+  // softmax over the block's m logits
+  float zmax = -INFINITY;
+  for (int i = lane; i < m; i += kWave) zmax = fmaxf(zmax, zb[i]);
+  zmax = wave_max(zmax);
+  float zsum = 0.f;
+  for (int i = lane; i < m; i += kWave) zsum += expf(zb[i] - zmax);
+  zsum = wave_sum(zsum);
+  const float inv = 1.0f / zsum;
+
+  const int cpr = D >> 3;  // 16-byte chunks per row
+  const bool has0 = lane < cpr;
+  const bool has1 = lane + kWave < cpr;
+  float acc0[8], acc1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
+
+  int i = 0;
+  for (; i + kUnroll <= m; i += kUnroll) {
+    uint4 v0[kUnroll], v1[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint4* row = reinterpret_cast<const uint4*>(xb + (int64_t)(i + u) * D);
+      v0[u] = has0 ? ld_stream16(row + lane) : make_uint4(0, 0, 0, 0);
+      v1[u] = has1 ? ld_stream16(row + lane + kWave) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float a = expf(zb[i + u] - zmax) * inv;
+      float f[8];
+      unpack8(v0[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc0[e] = fmaf(a, f[e], acc0[e]);
+      unpack8(v1[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc1[e] = fmaf(a, f[e], acc1[e]);
+    }
+  }
+  for (; i < m; ++i) {
+    const uint4* row = reinterpret_cast<const uint4*>(xb + (int64_t)i * D);
+    const float a = expf(zb[i] - zmax) * inv;
+    float f[8];
+    if (has0) {
+      unpack8(row[lane], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc0[e] = fmaf(a, f[e], acc0[e]);
+    }
+    if (has1) {
+      unpack8(row[lane + kWave], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc1[e] = fmaf(a, f[e], acc1[e]);
+    }
+  }
+
+  // partial RoPE on the last d_rope dims, at the entry's position
+  const int64_t p = pos0[b] + (int64_t)j * m + entry_pos_offset;
+  const int rope0 = D - d_rope;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = lane + h * kWave;
+    float* acc = h ? acc1 : acc0;
+    if (c < cpr && 8 * c >= rope0) {
+      const int pair0 = (8 * c - rope0) >> 1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float cs, sn;
+        rope_cs(rope_inv_freq(rope_base, pair0 + q, d_rope), p, &cs, &sn);
+        const float u0 = acc[2 * q], u1 = acc[2 * q + 1];
+        acc[2 * q] = u0 * cs - u1 * sn;
+        acc[2 * q + 1] = u0 * sn + u1 * cs;
+      }
+    }
+  }
+
+  const int64_t slot = (int64_t)b * out_seq_stride + (out_entry0 ? out_entry0[b] : 0) + j;
+  if (!FP8) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + slot * D;
+    if (has0) *reinterpret_cast<uint4*>(o + 8 * lane) = pack8(acc0);
+    if (has1) *reinterpret_cast<uint4*>(o + 8 * (lane + kWave)) = pack8(acc1);
+  } else {
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(acc0[e]), fabsf(acc1[e])));
+    amax = wave_max(amax);
+    float s = amax / 448.0f;
+    if (amax == 0.f) s = 1.0f;
+    uint8_t* o = reinterpret_cast<uint8_t*>(out) + slot * D;
+    if (has0) {
+      uint2 wv;
+      wv.x = f32x4_to_fp8(acc0[0] / s, acc0[1] / s, acc0[2] / s, acc0[3] / s);
+      wv.y = f32x4_to_fp8(acc0[4] / s, acc0[5] / s, acc0[6] / s, acc0[7] / s);
+      *reinterpret_cast<uint2*>(o + 8 * lane) = wv;
+    }
+    if (has1) {
+      uint2 wv;
+      wv.x = f32x4_to_fp8(acc1[0] / s, acc1[1] / s, acc1[2] / s, acc1[3] / s);
+      wv.y = f32x4_to_fp8(acc1[4] / s, acc1[5] / s, acc1[6] / s, acc1[7] / s);
+      *reinterpret_cast<uint2*>(o + 8 * (lane + kWave)) = wv;
+    }
+    if (lane == 0) out_scale[slot] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __restrict__ x_new,
+                                                          const float* __restrict__ z_new,
+                                                          const int64_t* __restrict__ pos,
+                                                          uint16_t* __restrict__ ring_x,
+                                                          float* __restrict__ ring_z, int D, int W) {
+  const int b = blockIdx.x;
+  const int64_t slot = (int64_t)b * W + (pos[b] % W);
+  const int cpr = D >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x_new + (int64_t)b * D);
+  uint4* dst = reinterpret_cast<uint4*>(ring_x + slot * D);
+  for (int c = threadIdx.x; c < cpr; c += blockDim.x) dst[c] = src[c];
+  if (threadIdx.x == 0 && z_new) ring_z[slot] = z_new[b];
+}
+
+static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stride, const float* z,
+                         int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
+                         int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
+                         void* out, float* out_scale, int64_t out_seq_stride,
+                         const int32_t* out_entry0, void* stream) {
+  CSKV_REQUIRE(B >= 1 && n_tok >= 0, CSKV_EINVAL, "%s: B=%d n_tok=%d", name, B, n_tok);
+  CSKV_REQUIRE(m >= 1 && m <= 1024, CSKV_EINVAL, "%s: m=%d outside [1, 1024]", name, m);
+  CSKV_REQUIRE(n_tok % m == 0, CSKV_EINVAL, "%s: n_tok=%d is not a multiple of m=%d", name, n_tok, m);
+  CSKV_REQUIRE(D % 8 == 0 && D >= 8, CSKV_EINVAL, "%s: D=%d must be a positive multiple of 8", name, D);
+  CSKV_REQUIRE(D <= 1024, CSKV_ENOTSUP, "%s: D=%d > 1024", name, D);
+  CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL,
+               "%s: d_rope=%d must be a multiple of 8 in [0, D]", name, d_rope);
+  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_dtype == CSKV_FP8_E4M3, CSKV_EINVAL,
+               "%s: unknown out_dtype %d", name, out_dtype);
+  if (n_tok == 0) return CSKV_OK;
+  CSKV_REQUIRE(x && z && pos0 && out, CSKV_EINVAL, "%s: null pointer", name);
+  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_scale, CSKV_EINVAL, "%s: fp8 output needs out_scale", name);
+  CSKV_REQUIRE(aligned16(x) && aligned16(out), CSKV_EINVAL, "%s: x/out must be 16-byte aligned", name);
+  CSKV_REQUIRE(x_seq_stride % 8 == 0 && x_seq_stride >= (int64_t)n_tok * D, CSKV_EINVAL,
+               "%s: x_seq_stride=%lld", name, (long long)x_seq_stride);
+  CSKV_REQUIRE(z_seq_stride >= n_tok, CSKV_EINVAL, "%s: z_seq_stride=%lld", name, (long long)z_seq_stride);
+  const int n_ent = n_tok / m;
+  CSKV_REQUIRE(out_seq_stride >= n_ent, CSKV_EINVAL, "%s: out_seq_stride=%lld", name, (long long)out_seq_stride);
+  CSKV_REQUIRE((int64_t)B * n_ent < (1ll << 31), CSKV_ENOTSUP, "%s: too many entries", name);
+  const int waves = B * n_ent;
+  dim3 grid((waves + kCompressWaves - 1) / kCompressWaves), block(kCompressWaves * kWave);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (out_dtype == CSKV_BF16)
+    compress_kernel<false><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
+                                                  d_rope, m, entry_pos_offset, rope_base, out, out_scale,
+                                                  out_seq_stride, out_entry0);
+  else
+    compress_kernel<true><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
+                                                 d_rope, m, entry_pos_offset, rope_base, out, out_scale,
+                                                 out_seq_stride, out_entry0);
+  CSKV_LAUNCH_CHECK(name);
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+extern "C" CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, const float* z,
+                            int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
+                            int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
+                            void* out, float* out_scale, int64_t out_seq_stride,
+                            const int32_t* out_entry0, void* stream) {
+  return cskv::compress_impl("csa_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
+                             d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,
+                             out_seq_stride, out_entry0, stream);
+}
+
+extern "C" CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z,
+                            int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
+                            int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
+                            void* out, float* out_scale, int64_t out_seq_stride,
+                            const int32_t* out_entry0, void* stream) {
+  return cskv::compress_impl("hca_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
+                             d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,
+                             out_seq_stride, out_entry0, stream);
+}
+
+extern "C" CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_new, const int64_t* pos,
+                                uint16_t* ring_x, float* ring_z, int B, int D, int W, void* stream) {
+  CSKV_REQUIRE(B >= 1 && W >= 1, CSKV_EINVAL, "cskv_ring_append: B=%d W=%d", B, W);
+  CSKV_REQUIRE(D % 8 == 0 && D >= 8, CSKV_EINVAL, "cskv_ring_append: D=%d", D);
+  CSKV_REQUIRE(x_new && pos && ring_x, CSKV_EINVAL, "cskv_ring_append: null pointer");
+  CSKV_REQUIRE(!z_new || ring_z, CSKV_EINVAL, "cskv_ring_append: z_new needs ring_z");
+  CSKV_REQUIRE(cskv::aligned16(x_new) && cskv::aligned16(ring_x), CSKV_EINVAL,
+               "cskv_ring_append: x_new/ring_x must be 16-byte aligned");
+  cskv::ring_append_kernel<<<B, 128, 0, reinterpret_cast<hipStream_t>(stream)>>>(x_new, z_new, pos, ring_x,
+                                                                                 ring_z, D, W);
+  CSKV_LAUNCH_CHECK("cskv_ring_append");
+  return CSKV_OK;
+}

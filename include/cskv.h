@@ -1,0 +1,192 @@
+/*
+ * cskv.h - C ABI of the MI355X (gfx950) hybrid compressed attention library.
+ *
+ * The method (DeepSeek-V4 hybrid attention) is described on the page
+ * "DeepSeek-V4가 이차적 어텐션 비용 없이 백만 토큰 컨텍스트를 달성하는 방법",
+ * section "두 가지 압축 전략: CSA 및 HCA": Compressed Sparse Attention (CSA)
+ * softmax-pools every 4 consecutive tokens into one KV entry, an FP4
+ * "lightning indexer" scores the entries and keeps the top-k (about 128), and
+ * attention runs over those plus a sliding window; Heavily Compressed
+ * Attention (HCA) pools 128 tokens per entry and attends to all entries; both
+ * use MQA (one shared KV head) with partial RoPE. The page "딥시크 V4 분석:
+ * CSA·HCA 어텐션으로 100만 토큰 컨텍스트를 저비용에 구현한 방법", section
+ * "쉽게 이해하기", gives the 128-token window branch.
+ *
+ * Conventions shared by every call
+ *  - Tensor arguments are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or keeps a pointer after a call returns.
+ *  - Every call is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and never synchronises. Errors found while validating arguments are
+ *    returned before anything is enqueued; a failed launch returns CSKV_EHIP.
+ *  - Layouts are dense row-major unless a stride argument says otherwise.
+ *    bf16 values are passed as uint16_t bit patterns. fp8 is OCP e4m3fn.
+ *    MXFP4 is OCP MX FP4: e2m1 codes packed two per byte, element 2i in the
+ *    low nibble of byte i, with one E8M0 scale byte (2^(E-127)) per 32 elements.
+ *  - All base pointers must be 16-byte aligned.
+ *  - The library holds no mutable global state; calls are thread-safe.
+ *    Calls that write the same buffers must be ordered by the caller.
+ *  - cskv_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef CSKV_H_
+#define CSKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSKV_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define CSKV_API __attribute__((visibility("default")))
+#else
+#define CSKV_API
+#endif
+
+/* Return codes. */
+#define CSKV_OK 0
+#define CSKV_EINVAL (-1)    /* null pointer, bad dimension, misalignment */
+#define CSKV_ENOTSUP (-2)   /* a shape outside what the kernels support */
+#define CSKV_EWORKSPACE (-3) /* workspace missing or too small */
+#define CSKV_EHIP (-4)      /* a HIP launch failed */
+
+/* Storage dtypes of compressed entries. */
+#define CSKV_BF16 0
+#define CSKV_FP8_E4M3 1
+
+CSKV_API int cskv_abi_version(void);
+CSKV_API const char* cskv_strerror(int code);
+CSKV_API const char* cskv_last_error(void);
+
+/*
+ * csa_compress / hca_compress - softmax-weighted pooling of m consecutive
+ * tokens into one KV entry, then partial RoPE, then storage rounding.
+ * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
+ * HCA": 4 tokens per CSA entry, 128 per HCA entry; page "딥시크 V4 분석 ...",
+ * section "쉽게 이해하기": the pooling weights are learned per token.)
+ *
+ * For each sequence b and block j in [0, n_tok/m):
+ *   a_i  = softmax_i(z[b, j*m + i]),  i = 0..m-1
+ *   e    = sum_i a_i * x[b, j*m + i, :]                  (fp32 accumulation)
+ *   e    = RoPE(e) on dims [D-d_rope, D) at p = pos0[b] + j*m + entry_pos_offset,
+ *          pairs (2i, 2i+1) of that slice, theta_i = rope_base^(-2i/d_rope)
+ *   out[b, out_entry0[b] + j, :] = bf16_rne(e)                       (CSKV_BF16)
+ *     or  s = max|e| / 448 (1 if e == 0); codes = e4m3_rne_sat(e / s),
+ *         out_scale[b, out_entry0[b] + j] = s                        (CSKV_FP8_E4M3)
+ *
+ * x        [B, x_seq_stride] bf16; row r of sequence b at x + b*x_seq_stride + r*D
+ *          (a ring slice works: rows are contiguous within a sequence)
+ * z        [B, z_seq_stride] fp32 pooling logits, z + b*z_seq_stride + r
+ * pos0     [B] int64, position of row 0 of each sequence
+ * out      bf16 [B, out_seq_stride, D] or fp8 codes [B, out_seq_stride, D]
+ * out_scale fp32 [B, out_seq_stride] (fp8 only; ignored for bf16)
+ * out_entry0 [B] int32 first entry slot written per sequence, or NULL (= 0)
+ * Requirements: B >= 1, n_tok >= 0 and n_tok % m == 0, 1 <= m <= 1024,
+ * D % 8 == 0 and 8 <= D <= 1024, d_rope % 8 == 0 and d_rope <= D,
+ * x_seq_stride % 8 == 0. hca_compress is the same operation (named for
+ * its use with m = 128).
+ */
+CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
+                 const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
+                 int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
+                 int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
+CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
+                 const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
+                 int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
+                 int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
+
+/*
+ * csa_index_topk - lightning-indexer scores and top-k selection.
+ * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
+ * HCA": an FP4 indexer scores the compressed entries against the query and
+ * the top-k, typically about 128, go on to attention. The score form is the
+ * DSA lightning indexer's.)
+ *
+ *   s(b,t,j) = sum_h w[b,t,h] * max(0, sum_d q[b,t,h,d] * k[b,j,d]),  j < n_valid[b,t]
+ * with q, k decoded from MXFP4. The scores are exact in fp32 as long as, per
+ * score, the E8M0 exponent spread of the query plus that of the key plus that
+ * of w stays within 2^24 / (H_I * D_I * 36) (8 for H_I*D_I = 1024). Entries
+ * are ordered by (score descending, index ascending; -0 == +0) and the first
+ * min(k, n_valid) are written; the rest of the row is -1 (score -inf).
+ *
+ * iq [B, T, H_I, D_I/2], iq_scale [B, T, H_I, D_I/32]
+ * head_w [B, T, H_I] fp32, or NULL for all ones
+ * ik [B, N_cap, D_I/2], ik_scale [B, N_cap, D_I/32]
+ * n_valid [B, T] int32 in [0, N_cap]
+ * out_idx [B, T, k] int32; out_score [B, T, k] fp32 or NULL
+ * ws: device workspace of at least csa_index_topk_workspace_size(...) bytes
+ * Requirements: D_I % 32 == 0, 32 <= D_I <= 512, 1 <= H_I <= 16, 1 <= k <= 1024.
+ */
+CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scale, const float* head_w,
+                   const uint8_t* ik, const uint8_t* ik_scale, const int32_t* n_valid, int B, int T,
+                   int N_cap, int H_I, int D_I, int k, int32_t* out_idx, float* out_score, void* ws,
+                   size_t ws_bytes, void* stream);
+CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, int D_I, int k);
+
+/*
+ * hybrid_attn_decode - one decode query per sequence: shared-KV MQA attention
+ * over compressed entries plus the sliding window, one joint softmax per head.
+ * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
+ * HCA": CSA attends to its top-k entries with a window branch alongside, HCA
+ * attends to all of its entries; MQA shares one KV head; partial RoPE.)
+ *
+ * For sequence b with query position t = q_pos[b]:
+ *   keys = entries {topk_idx[b, i] >= 0} (CSA) or {0..n_entries[b]-1} (topk_idx == NULL, HCA)
+ *          plus window tokens at positions [max(0, t-W+1), t], read raw from
+ *          ring slot (position mod W) and rotated at their own position
+ *   q_rot = RoPE(q[b, h], t); logit = softmax_scale * q_rot . key
+ *   out[b, h, :] = bf16_rne(sum softmax(logit) * key[:d_v]); out_lse[b, h] = ln(sum exp(logit))
+ * Entries are stored rotated: bf16 [B, N_cap, D], or fp8 codes [B, N_cap, D]
+ * with fp32 scales ckv_scale [B, N_cap] (value = code * scale).
+ *
+ * q [B, H, D] bf16 (unrotated); q_pos [B] int64; n_entries [B] int32 <= N_cap
+ * topk_idx [B, k] int32 (each -1 or in [0, n_entries[b])) or NULL
+ * win [B, W, D] bf16 ring of raw tokens; out [B, H, d_v] bf16; out_lse [B, H] fp32 or NULL
+ * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
+ * d_rope % 8 == 0, d_rope <= D, 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32.
+ */
+CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                       const float* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
+                       const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H,
+                       int D, int d_rope, int d_v, float rope_base, float softmax_scale,
+                       uint16_t* out, float* out_lse, void* ws, size_t ws_bytes, void* stream);
+CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense);
+
+/*
+ * hybrid_attn_prefill - the same attention for every row of one prompt.
+ * Row r is position t = pos0 + r. It sees entries j < min(N, floor((t+1)/m))
+ * (CSA: those listed in topk_idx[r]; HCA: all of them when topk_idx == NULL)
+ * and the raw tokens x at positions [max(pos0, t-W+1), t], rotated at their
+ * own positions.
+ *
+ * q [T, H, D] bf16; ckv / ckv_scale as in decode with N entries;
+ * topk_idx [T, k] or NULL; x [T, D] bf16 raw tokens of the prompt;
+ * out [T, H, d_v] bf16; out_lse [T, H] fp32 or NULL.
+ * Requirements as in decode, plus m >= 1.
+ */
+CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,
+                        const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
+                        int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v, int m,
+                        float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
+                        void* ws, size_t ws_bytes, void* stream);
+CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense);
+
+/*
+ * cskv_ring_append - decode state update: write each sequence's new raw token
+ * and pooling logit into its window ring at slot pos[b] mod W. (The window
+ * keeps the latest W tokens: page "딥시크 V4 분석 ...", section "쉽게 이해하기".)
+ *
+ * x_new [B, D] bf16; z_new [B] fp32 or NULL; pos [B] int64;
+ * ring_x [B, W, D] bf16; ring_z [B, W] fp32 or NULL (with z_new).
+ * Requirements: D % 8 == 0, W >= 1.
+ */
+CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_new, const int64_t* pos,
+                     uint16_t* ring_x, float* ring_z, int B, int D, int W, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSKV_H_ */

@@ -52,3 +52,18 @@ def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=
     s = np.where(amax == 0, 1.0, amax / formats.E4M3_MAX).astype(np.float32)
     codes = formats.f64_to_e4m3(e / s.astype(np.float64)[:, None])
     return e, codes, s
+
+
+def magnitude(x_bits, z, m, d_rope):
+    """sum_i a_i |x_i| per pooled element (rotated dims: the pair's two sums added).
+
+    The scale of the rounding error of any finite-precision evaluation of the
+    pooled entry; parity bounds are stated in multiples of it.
+    """
+    mag = pool(np.abs(formats.bf16_to_f64(x_bits)), np.asarray(z, dtype=np.float64), m)
+    if d_rope:
+        D = mag.shape[1]
+        pair = mag[:, D - d_rope::2] + mag[:, D - d_rope + 1::2]
+        mag[:, D - d_rope::2] = pair
+        mag[:, D - d_rope + 1::2] = pair
+    return mag

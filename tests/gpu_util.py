@@ -1,0 +1,31 @@
+"""Helpers for the GPU parity tests: device tensors from host arrays, poisoned outputs, logging."""
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def up(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def down(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def poisoned(shape, dtype):
+    """Output buffer filled with 0xFF bytes so unwritten elements show up (NaN for floats, -1 for ints)."""
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(0xFF)
+    return t

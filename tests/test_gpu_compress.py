@@ -1,0 +1,122 @@
+"""GPU parity of csa_compress / hca_compress / cskv_ring_append against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_kv_03_amd import configs, native, synth
+from oracle import compress as ocomp
+from tests import parity
+from tests.gpu_util import DEV, down, poisoned, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+def run_compress(x_bits, z, pos0, m, d_rope, dtype, entry_pos_offset=0, entry0=None, cap_extra=0,
+                 x_stride=None, fn=native.csa_compress):
+    """x_bits [B, n_tok, D] (device int16) -> device outputs."""
+    B, n_tok, D = x_bits.shape[0], x_bits.shape[1], x_bits.shape[2]
+    n = n_tok // m
+    cap = n + cap_extra
+    out_dt = native.CSKV_BF16 if dtype == "bf16" else native.CSKV_FP8_E4M3
+    out = poisoned((B, cap, D), torch.int16 if dtype == "bf16" else torch.uint8)
+    osc = poisoned((B, cap), torch.float32) if dtype == "fp8" else None
+    e0 = None if entry0 is None else up(np.asarray(entry0, np.int32))
+    fn(x_bits, x_stride or n_tok * D, z, z.shape[1], up(np.asarray(pos0, np.int64)), B, n_tok, D, d_rope, m,
+       entry_pos_offset, 10000.0, out_dt, out, osc, cap, e0)
+    return out, osc
+
+
+@pytest.mark.parametrize("m,D,d_rope,dtype", [
+    (4, 128, 64, "bf16"), (4, 576, 64, "bf16"), (1, 24, 8, "bf16"), (128, 576, 64, "fp8"),
+    (4, 576, 64, "fp8"), (128, 1024, 0, "bf16"), (5, 520, 520, "fp8"), (13, 64, 16, "bf16"),
+])
+def test_compress_small_matches_oracle(m, D, d_rope, dtype):
+    say("compress small", m, D, d_rope, dtype)
+    B, nblk = 3, 37                                  # ragged: 37 entries -> 10 workgroups of 4 waves
+    n_tok = nblk * m
+    x = synth.normal_bf16_bits((B, n_tok, D), 0.5, 11, DEV)
+    z = synth.normal((B, n_tok), 2.0, 12, DEV)
+    pos0 = [0, 2 ** 20 - 64 * m, 77]
+    out, osc = run_compress(x, z, pos0, m, d_rope, dtype)
+    xh, zh, oh = down(x).view(np.uint16), down(z), down(out)
+    for b in range(B):
+        e, _, _ = ocomp.compress(xh[b], zh[b], pos0[b], m, d_rope, 10000.0, dtype)
+        mag = ocomp.magnitude(xh[b], zh[b], m, d_rope)
+        if dtype == "bf16":
+            parity.compress_bf16_close(oh[b].view(np.uint16), e, mag, m, f"b={b}")
+        else:
+            parity.compress_fp8_close(oh[b], down(osc)[b], e, mag, m, f"b={b}")
+
+
+def test_compress_offsets_entry_slots_and_ring_stride():
+    """out_entry0, entry_pos_offset and a strided ring-like input all land where the ABI says."""
+    say("compress offsets")
+    B, m, D, W = 2, 4, 576, 128
+    ring = synth.normal_bf16_bits((B, W, D), 0.1, 21, DEV)
+    zr = synth.normal((B, W), 1.0, 22, DEV)
+    slot0 = 60                                         # compress ring slots 60..63
+    x_view = ring[:, slot0:slot0 + m]
+    cap = 10
+    out = poisoned((B, cap, D), torch.int16)
+    e0 = up(np.array([3, 7], np.int32))
+    pos0 = np.array([1000 + slot0, 5000 + slot0], np.int64)
+    native.hca_compress(x_view, W * D, zr[:, slot0:], W, up(pos0), B, m, D, 64, m, 2, 10000.0, native.CSKV_BF16,
+                        out, None, cap, e0)
+    oh = down(out).view(np.uint16)
+    rh, zh = down(ring).view(np.uint16), down(zr)
+    for b, slot in ((0, 3), (1, 7)):
+        e, _, _ = ocomp.compress(rh[b, slot0:slot0 + m], zh[b, slot0:slot0 + m], pos0[b], m, 64, 10000.0,
+                                 "bf16", entry_pos_offset=2)
+        mag = ocomp.magnitude(rh[b, slot0:slot0 + m], zh[b, slot0:slot0 + m], m, 64)
+        parity.compress_bf16_close(oh[b, slot:slot + 1], e, mag, m)
+        others = [i for i in range(cap) if i != slot]
+        assert np.all(oh[b, others] == 0xFFFF), "wrote outside its slot"
+
+
+def test_compress_c1_full():
+    w = configs.C1
+    say("compress", w.name)
+    x = synth.normal_bf16_bits((w.B, w.L, w.D), w.sigma, synth.seed_of(0, w.wid, 0), DEV)
+    z = synth.normal((w.B, w.L), 1.0, synth.seed_of(0, w.wid, 1), DEV)
+    out, _ = run_compress(x, z, [0], w.m, w.d_rope, "bf16")
+    xh, zh = down(x)[0].view(np.uint16), down(z)[0]
+    e, _, _ = ocomp.compress(xh, zh, 0, w.m, w.d_rope, w.rope_base, "bf16")
+    parity.compress_bf16_close(down(out)[0].view(np.uint16), e, ocomp.magnitude(xh, zh, w.m, w.d_rope), w.m)
+
+
+def test_compress_c3_full_size_sampled():
+    """HCA m=128 over 16 x 2^20 tokens (19.3 GB raw); check sampled entries one by one."""
+    w = configs.C3
+    say("compress", w.name, "full size")
+    x = synth.normal_bf16_bits((w.B, w.L, w.D), w.sigma, synth.seed_of(0, w.wid, 0), DEV)
+    z = synth.normal((w.B, w.L), 1.0, synth.seed_of(0, w.wid, 1), DEV)
+    n = w.L // w.m
+    out, osc = run_compress(x, z, [0] * w.B, w.m, w.d_rope, "fp8", fn=native.hca_compress)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    picks = [(b, j) for b in range(w.B) for j in sorted(set(rng.integers(0, n, 4).tolist()) | {0, n - 1})]
+    oc, os_ = out.cpu(), osc.cpu()
+    assert torch.isfinite(os_).all(), "unwritten scale"
+    for b, j in picks:
+        xs = x[b, j * w.m:(j + 1) * w.m].cpu().numpy().view(np.uint16)
+        zs = z[b, j * w.m:(j + 1) * w.m].cpu().numpy()
+        e, _, _ = ocomp.compress(xs, zs, j * w.m, w.m, w.d_rope, w.rope_base, "fp8")
+        mag = ocomp.magnitude(xs, zs, w.m, w.d_rope)
+        parity.compress_fp8_close(oc[b, j].numpy()[None], os_[b, j].numpy()[None], e, mag, w.m, f"entry {b},{j}")
+    del x, out
+
+
+def test_ring_append_writes_slot_pos_mod_w():
+    say("ring append")
+    B, D, W = 3, 576, 128
+    ring = poisoned((B, W, D), torch.int16)
+    rz = poisoned((B, W), torch.float32)
+    xn = synth.normal_bf16_bits((B, D), 1.0, 31, DEV)
+    zn = synth.normal((B,), 1.0, 32, DEV)
+    pos = np.array([0, 127, 2 ** 20 + 5], np.int64)
+    native.cskv_ring_append(xn, zn, up(pos), ring, rz, B, D, W)
+    rh, zh = down(ring), down(rz)
+    for b in range(B):
+        assert np.array_equal(rh[b, pos[b] % W], down(xn)[b]) and zh[b, pos[b] % W] == down(zn)[b]
+        others = [i for i in range(W) if i != pos[b] % W]
+        assert np.all(rh[b, others].view(np.uint16) == 0xFFFF)

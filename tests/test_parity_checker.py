@@ -64,17 +64,24 @@ def test_checker_rejects_output_off_by_6e3_relative(oracle_case):
         parity.attn_close(formats.f64_to_bf16(o + noise), o)
 
 
-def test_compress_checks_reject_two_ulp_and_widespread_one_ulp():
-    w = formats.f64_to_bf16(np.linspace(-3, 3, 5000))
-    g = w.copy()
-    g[7] = np.uint16(int(g[7]) + 2)
+def test_compress_checks_reject_errors_beyond_the_fp32_bound():
+    from oracle import compress as ocomp
+    rng = np.random.default_rng(2)
+    m, D = 4, 64
+    x = formats.f64_to_bf16(rng.standard_normal((8 * m, D)))
+    z = rng.standard_normal(8 * m).astype(np.float32)
+    e, stored, _ = ocomp.compress(x, z, 0, m, 16, 10000.0, "bf16")
+    mag = ocomp.magnitude(x, z, m, 16)
+    parity.compress_bf16_close(stored, e, mag, m)
+    bad = stored.copy()
+    bad[3, 5] = np.uint16(int(bad[3, 5]) + 2)                  # two ulp away
     with pytest.raises(parity.ParityError):
-        parity.compress_bf16_close(g, w)
-    g = w.copy()
-    g[:100] = (g[:100].astype(np.int64) + 1).astype(np.uint16)
+        parity.compress_bf16_close(bad, e, mag, m)
+    _, codes, s = ocomp.compress(x, z, 0, m, 16, 10000.0, "fp8")
+    parity.compress_fp8_close(codes, s, e, mag, m)
     with pytest.raises(parity.ParityError):
-        parity.compress_bf16_close(g, w)
-    c = np.arange(100, dtype=np.uint8)
-    s = np.ones(4, np.float32)
+        parity.compress_fp8_close(codes, s * (1 + 1e-4), e, mag, m)
+    badc = codes.copy()
+    badc[2, 7] = np.uint8(int(badc[2, 7]) + 1 if badc[2, 7] & 0x7F < 0x7E else int(badc[2, 7]) - 1)
     with pytest.raises(parity.ParityError):
-        parity.compress_fp8_close(c, s * (1 + 1e-5), c, s)
+        parity.compress_fp8_close(badc, s, e, mag, m)
