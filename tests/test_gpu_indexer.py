@@ -1,0 +1,101 @@
+"""GPU parity of csa_index_topk: bit-exact indices (order included) and exact scores."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_kv_03_amd import configs, native, synth
+from oracle import indexer as oidx
+from oracle import topk as otopk
+from tests import parity
+from tests.gpu_util import DEV, down, poisoned, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+def run_index(iq, iqs, ik, iks, n_valid, k, head_w=None):
+    B, T, H_I, half = iq.shape
+    N_cap = ik.shape[1]
+    D_I = half * 2
+    ws_n = native.csa_index_topk_workspace_size(B, T, N_cap, H_I, D_I, k)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=DEV)
+    oi = poisoned((B, T, k), torch.int32)
+    os_ = poisoned((B, T, k), torch.float32)
+    native.csa_index_topk(iq, iqs, head_w, ik, iks, n_valid, B, T, N_cap, H_I, D_I, k, oi, os_, ws)
+    return oi, os_
+
+
+def check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, head_w=None, rows=None):
+    iqh, iqsh, ikh, iksh, nvh = down(iq), down(iqs), down(ik), down(iks), down(nv)
+    hwh = None if head_w is None else down(head_w)
+    oih, osh = down(oi), down(os_)
+    B, T = nvh.shape
+    for b in range(B):
+        ts = range(T) if rows is None else rows
+        for t in ts:
+            sc = oidx.scores(iqh[b, t][None], iqsh[b, t][None], ikh[b], iksh[b], nvh[b, t][None],
+                             None if hwh is None else hwh[b, t][None])
+            idx, s = otopk.topk(sc, k)
+            parity.topk_exact(oih[b, t], idx[0], f"top-k b={b} t={t}")
+            assert np.array_equal(osh[b, t], s[0]), f"scores differ b={b} t={t}"
+
+
+@pytest.mark.parametrize("H_I,D_I,k,N_cap", [(8, 128, 128, 5000), (4, 64, 128, 1024), (3, 32, 16, 333),
+                                             (16, 256, 300, 9000), (8, 512, 1, 2100), (5, 160, 1024, 20000)])
+def test_index_topk_small(H_I, D_I, k, N_cap):
+    say("index small", H_I, D_I, k, N_cap)
+    B, T = 2, 3
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 101 + D_I, DEV)
+    ik, iks = synth.mxfp4_normal((B, N_cap, D_I), 102 + D_I, DEV)
+    nv = up(np.array([[N_cap, N_cap // 3, 0], [17, min(k, N_cap), N_cap - 1]], np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_)
+
+
+def test_index_topk_head_weights_and_negative_scores():
+    say("index head weights")
+    B, T, H_I, D_I, N, k = 1, 2, 8, 128, 3000, 64
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 111, DEV)
+    ik, iks = synth.mxfp4_normal((B, N, D_I), 112, DEV)
+    hw = up(np.array([[[1, -2, 0.5, -1, 4, 0.25, -0.5, 2]] * T], np.float32))
+    nv = up(np.array([[N, 2000]], np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k, hw)
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, head_w=hw)
+
+
+def test_index_topk_ties_go_to_the_lower_index():
+    """Keys drawn from 5 distinct patterns: scores collide massively; order must follow the index."""
+    say("index ties")
+    B, T, H_I, D_I, N, k = 2, 2, 8, 128, 7000, 256
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 121, DEV)
+    base, bsc = synth.mxfp4_normal((5, D_I), 122, DEV)
+    pick = torch.from_numpy(np.random.default_rng(0).integers(0, 5, (B, N))).to(DEV)
+    ik, iks = base[pick].contiguous(), bsc[pick].contiguous()
+    ik[1].zero_()                                   # sequence 1: every score is 0
+    nv = up(np.array([[N, 300], [N, 5]], np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_)
+    assert down(oi)[1, 0].tolist()[:10] == list(range(10))
+
+
+@pytest.mark.parametrize("wname", ["c1_csa_tiny", "c2_csa_b32_64k"])
+def test_index_topk_workload(wname):
+    w = configs.ALL[wname]
+    say("index", w.name)
+    n = w.L // w.m
+    iq, iqs = synth.mxfp4_normal((w.B, 1, w.H_I, w.D_I), synth.seed_of(0, w.wid, 10), DEV)
+    ik, iks = synth.mxfp4_normal((w.B, n, w.D_I), synth.seed_of(0, w.wid, 11), DEV)
+    nv = up(np.full((w.B, 1), n, np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, w.k)
+    check_against_oracle(iq, iqs, ik, iks, nv, w.k, oi, os_)
+
+
+def test_index_topk_hybrid_1m_shape():
+    """The CSA layer of the 1M hybrid pair: 8 queries over 262144 entries each (one decode step)."""
+    w = configs.C5
+    say("index", w.name)
+    n = w.L // w.m
+    iq, iqs = synth.mxfp4_normal((w.B, 1, w.H_I, w.D_I), synth.seed_of(0, w.wid, 10), DEV)
+    ik, iks = synth.mxfp4_normal((w.B, n + 64, w.D_I), synth.seed_of(0, w.wid, 11), DEV)
+    nv = up(np.full((w.B, 1), n, np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, w.k)
+    check_against_oracle(iq, iqs, ik, iks, nv, w.k, oi, os_)
