@@ -1,0 +1,535 @@
+// Shared-KV MQA attention over compressed entries plus the sliding window
+// (hybrid_attn_decode, hybrid_attn_prefill).
+//
+// Method: page "DeepSeek-V4가 이차적 어텐션 비용 없이 백만 토큰 컨텍스트를 달성하는
+// 방법", section "두 가지 압축 전략: CSA 및 HCA": CSA runs softmax attention over
+// its top-k compressed entries with a sliding-window branch alongside; HCA runs
+// dense attention over all of its entries; both use MQA (one KV head shared by
+// all query heads) with partial RoPE. Page "딥시크 V4 분석: CSA·HCA 어텐션으로
+// 100만 토큰 컨텍스트를 저비용에 구현한 방법", section "쉽게 이해하기": the window
+// holds the latest 128 tokens. Entries and window tokens share one softmax.
+//
+// Design. One query (a decode sequence, or one prefill row) has H heads and a
+// key set of compressed entries (a top-k list or a dense range) followed by
+// window tokens. A workgroup takes NW waves x 16 heads and one contiguous
+// split of that key set, staged 32 keys at a time into LDS as bf16 rows (fp8
+// codes widen exactly; the per-entry scale is folded into the logit and into
+// P; window tokens are rotated at their own position while staged). Per wave:
+//   S^T-free QK: v_mfma_f32_16x16x32_bf16 with Q (rotated, in registers) as A
+//               and K rows read with ds_read_b128 as B  -> S[16 heads][32 keys]
+//   online softmax in the log2 domain on the accumulator lanes
+//   P -> LDS as [key][head] with 8-byte writes; PV with P read back by the
+//   gfx950 transposed read ds_read_b64_tr_b16 as A and V (the first d_v dims
+//   of the same K rows) read by ds_read_b64_tr_b16 as B.
+// Splits write unnormalised partial outputs with (max, sum) in fp32; a combine
+// kernel merges them (log-sum-exp merge). One split writes the output directly.
+#include "common.cuh"
+#include "host_util.h"
+
+namespace cskv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTK = 32;            // keys per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+  const uint16_t* q;        // [nq, H, D]
+  const int64_t* q_pos;     // [nq] (decode) or nullptr (prefill: pos0 + row)
+  int64_t pos0;
+  const void* ckv;          // [B_kv, N_cap, D] bf16 bits or fp8 codes
+  const float* ckv_scale;   // [B_kv, N_cap] (fp8)
+  int fp8;
+  int N_cap;
+  int64_t ckv_seq;          // entries between sequences (0: all queries share one cache)
+  const int32_t* n_entries; // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))
+  int m;
+  const int32_t* topk;      // [nq, k] or nullptr (dense)
+  int k;
+  const uint16_t* win;      // decode: ring [nq, W, D]; prefill: x [T, D]
+  int ring;                 // 1: slot = pos mod W, per-query ring; 0: row = pos - pos0 of x
+  int W;
+  int nq, H, D, d_rope, d_v;
+  float rope_base, scale_log2;  // softmax_scale * log2(e)
+  int n_splits, keys_per_split;
+  uint16_t* out;            // [nq, H, d_v]
+  float* out_lse;           // [nq, H]
+  float* part_o;            // [nq, n_splits, H, d_v]
+  float* part_ml;           // [nq, n_splits, H, 2]
+};
+
+// Per query: entry-key count, window start position and count.
+struct KeySpace {
+  int64_t t;
+  int n_c;       // compressed keys (top-k slots or dense entries)
+  int64_t w0;    // first window position
+  int n_w;       // window tokens
+};
+
+__device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
+  KeySpace ks;
+  ks.t = a.q_pos ? a.q_pos[qi] : a.pos0 + qi;
+  if (a.topk) {
+    ks.n_c = a.k;
+  } else if (a.n_entries) {
+    ks.n_c = a.n_entries[qi];
+  } else {
+    int64_t v = (ks.t + 1) / a.m;
+    ks.n_c = (int)(v < a.N_cap ? v : a.N_cap);
+  }
+  const int64_t lo = a.ring ? 0 : a.pos0;
+  int64_t w0 = ks.t - a.W + 1;
+  if (w0 < lo) w0 = lo;
+  ks.w0 = w0;
+  ks.n_w = a.W > 0 ? (int)(ks.t - w0 + 1) : 0;
+  return ks;
+}
+
+template <int KD, int NV, int NW>
+struct AttnSmem {
+  uint16_t kt[kTK][KD * 32 + 8];  // key rows (bf16), padded
+  float kscale[kTK];              // per-key logit multiplier (log2 domain), -inf = masked
+  float kvscale[kTK];             // per-key value multiplier (fp8 entry scale, else 1)
+  uint16_t pt[NW][kTK][16 + 4];   // P^T per wave: [key][head]
+  double inv_freq[KD * 16];       // RoPE frequencies (d_rope/2 <= D/2)
+};
+
+// Rotate 8 consecutive bf16 dims (4 RoPE pairs starting at pair0) to position pos. The angle is
+// formed and reduced modulo 2*pi in fp64 (positions reach 2^20), then rotated in fp32.
+// Out of line so that callers' unrolled register arrays keep constant indices.
+__device__ __noinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_freq, int pair0) {
+  float f[8];
+  unpack8(v, f);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    double ang = (double)pos * inv_freq[pair0 + p];
+    ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    const float u0 = f[2 * p], u1 = f[2 * p + 1];
+    f[2 * p] = u0 * cs - u1 * sn;
+    f[2 * p + 1] = u0 * sn + u1 * cs;
+  }
+  return pack8(f);
+}
+
+// Stage keys [key0, key0+kTK) of query qi into LDS.
+template <int KD, int NV, int NW>
+__device__ __forceinline__ void stage_tile(const AttnArgs& a, int qi, const KeySpace& ks, int key0, int key_end,
+                                           AttnSmem<KD, NV, NW>& sm) {
+  constexpr int D = KD * 32;
+  constexpr int CPR = D / 8;  // 16-byte bf16 chunks per row
+  constexpr int NT = NW * kWave;
+  const int rope0 = D - a.d_rope;
+  const int b_kv = a.ckv_seq ? qi : 0;
+  for (int c = threadIdx.x; c < kTK * CPR; c += NT) {
+    const int r = c / CPR, ch = c - r * CPR;
+    const int key = key0 + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    float ls = -INFINITY, vs = 0.f;
+    if (key < key_end) {
+      if (key < ks.n_c) {
+        int idx = key;
+        if (a.topk) idx = a.topk[(int64_t)qi * a.k + key];
+        if (idx >= 0) {
+          const int64_t row = (int64_t)b_kv * a.ckv_seq + idx;
+          if (!a.fp8) {
+            v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ckv) + row * D + ch * 8);
+            ls = a.scale_log2;
+            vs = 1.f;
+          } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.ckv) + row * D + ch * 8);
+            // exact e4m3 -> bf16 widening, two values per instruction
+            v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+            v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+            v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+            v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+            const float s = a.ckv_scale[row];
+            ls = a.scale_log2 * s;
+            vs = s;
+          }
+        }
+      } else {
+        const int64_t pos = ks.w0 + (key - ks.n_c);
+        const int64_t row = a.ring ? ((int64_t)qi * a.W + pos % a.W) : (pos - a.pos0);
+        v = *reinterpret_cast<const uint4*>(a.win + row * D + ch * 8);
+        if (8 * ch >= rope0) v = rope8(v, pos, sm.inv_freq, (8 * ch - rope0) >> 1);
+        ls = a.scale_log2;
+        vs = 1.f;
+      }
+    }
+    *reinterpret_cast<uint4*>(&sm.kt[r][ch * 8]) = v;
+    if (ch == 0) {
+      sm.kscale[r] = ls;
+      sm.kvscale[r] = vs;
+    }
+  }
+}
+
+template <int KD, int NV, int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
+  constexpr int D = KD * 32;
+  __shared__ AttnSmem<KD, NV, NW> sm;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int qi = blockIdx.x;
+  const int head_groups = (a.H + 16 * NW - 1) / (16 * NW);
+  const int split = blockIdx.y / head_groups;
+  const int hg = blockIdx.y - split * head_groups;
+  const int h0 = hg * 16 * NW + wave * 16;  // this wave's first head
+
+  for (int i = threadIdx.x; i < a.d_rope / 2; i += NW * kWave)
+    sm.inv_freq[i] = pow((double)a.rope_base, -2.0 * (double)i / (double)a.d_rope);
+
+  const KeySpace ks = key_space(a, qi);
+  const int n_keys = ks.n_c + ks.n_w;
+  const int key_begin = split * a.keys_per_split;
+  const int key_end = min(n_keys, key_begin + a.keys_per_split);
+
+  // Q rows of this wave (A operand): lane holds head h0+col, dims 32s + 8g .. +7, rotated at t
+  uint4 qa[KD];
+  {
+    const int h = h0 + col;
+    const int rope0 = D - a.d_rope;
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      qa[s] = make_uint4(0, 0, 0, 0);
+      if (h < a.H) qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g);
+    }
+    __syncthreads();  // inv_freq ready
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      if (d0 >= rope0) qa[s] = rope8(qa[s], ks.t, sm.inv_freq, (d0 - rope0) >> 1);
+    }
+  }
+
+  f32x4 o[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+
+  for (int key0 = key_begin; key0 < key_end; key0 += kTK) {
+    __syncthreads();
+    stage_tile<KD, NV, NW>(a, qi, ks, key0, key_end, sm);
+    __syncthreads();
+
+    // S[head 4g+r][key col (+16)] = q_rot . k
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(&sm.kt[col][32 * s + 8 * g]);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(&sm.kt[16 + col][32 * s + 8 * g]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, qa[s]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k0), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k1), s1, 0, 0, 0);
+    }
+    const float c0 = sm.kscale[col], c1 = sm.kscale[16 + col];
+    const float v0 = sm.kvscale[col], v1 = sm.kvscale[16 + col];
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = c0 == -INFINITY ? -INFINITY : s0[r] * c0;
+      const float x1 = c1 == -INFINITY ? -INFINITY : s1[r] * c1;
+      float mx = fmaxf(x0, x1);
+#pragma unroll
+      for (int o2 = 8; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
+      const float mnew = fmaxf(mrow[r], mx);
+      const float base = mnew == -INFINITY ? 0.f : mnew;
+      const float p0 = exp2f(x0 - base), p1 = exp2f(x1 - base);
+      float ps = p0 + p1;
+#pragma unroll
+      for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
+      alpha[r] = exp2f(mrow[r] - base);
+      lrow[r] = lrow[r] * alpha[r] + ps;
+      mrow[r] = mnew;
+      s0[r] = p0 * v0;  // value-side scale folded into P
+      s1[r] = p1 * v1;
+    }
+    // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
+    {
+      uint2 w0, w1;
+      w0.x = pack_bf16x2(s0[0], s0[1]);
+      w0.y = pack_bf16x2(s0[2], s0[3]);
+      w1.x = pack_bf16x2(s1[0], s1[1]);
+      w1.y = pack_bf16x2(s1[2], s1[3]);
+      *reinterpret_cast<uint2*>(&sm.pt[wave][col][4 * g]) = w0;
+      *reinterpret_cast<uint2*>(&sm.pt[wave][16 + col][4 * g]) = w1;
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P^T writes done (wave-local data)
+    __builtin_amdgcn_wave_barrier();
+    // A = P[head col][keys 8g..8g+7] via two transposed reads of the [key][head] block
+    bf16x8 pa;
+    {
+      const int kr = 8 * g + (col >> 2), hc = 4 * (col & 3);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr][hc]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr + 4][hc]));
+      pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // O[head 4g+r][dim 16n+col] += P V, V = key rows' first d_v dims
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int kr = 8 * g + (col >> 2), dc = 16 * n + 4 * (col & 3);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr][dc]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr + 4][dc]));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[n], 0, 0, 0);
+    }
+  }
+
+  // write: direct (one split) or partial
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = h0 + 4 * g + r;
+    if (h >= a.H) continue;
+    if (a.n_splits == 1) {
+      const float inv = lrow[r] > 0.f ? 1.f / lrow[r] : 0.f;
+      uint16_t* dst = a.out + ((int64_t)qi * a.H + h) * a.d_v;
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        if (16 * n < a.d_v) dst[16 * n + col] = (uint16_t)f32_to_bf16_rne(o[n][r] * inv);
+      if (a.out_lse && col == 0)
+        a.out_lse[(int64_t)qi * a.H + h] = lrow[r] > 0.f ? (mrow[r] + log2f(lrow[r])) * kLn2 : -INFINITY;
+    } else {
+      const int64_t pidx = ((int64_t)qi * a.n_splits + split) * a.H + h;
+      float* dst = a.part_o + pidx * a.d_v;
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        if (16 * n < a.d_v) dst[16 * n + col] = o[n][r];
+      if (col == 0) {
+        a.part_ml[pidx * 2 + 0] = mrow[r];
+        a.part_ml[pidx * 2 + 1] = lrow[r];
+      }
+    }
+  }
+}
+
+// One workgroup per (query, head): log-sum-exp merge of the split partials.
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  const int qi = blockIdx.x, h = blockIdx.y;
+  const int64_t base = (int64_t)qi * a.n_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.H + h) * 2]);
+  const float Mb = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const int64_t p = ((base + s) * a.H + h) * 2;
+    L += a.part_ml[p + 1] * exp2f(a.part_ml[p] - Mb);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int d = threadIdx.x; d < a.d_v; d += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) {
+      const int64_t p = (base + s) * a.H + h;
+      const float w = exp2f(a.part_ml[p * 2] - Mb);
+      acc += w * a.part_o[p * a.d_v + d];
+    }
+    a.out[((int64_t)qi * a.H + h) * a.d_v + d] = (uint16_t)f32_to_bf16_rne(acc * inv);
+  }
+  if (threadIdx.x == 0 && a.out_lse)
+    a.out_lse[(int64_t)qi * a.H + h] = L > 0.f ? (Mb + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------- host side
+struct AttnPlan {
+  int nw, n_splits, keys_per_split;
+  size_t ws;
+};
+
+static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
+  AttnPlan p;
+  p.nw = H >= 64 ? 4 : (H + 15) / 16;
+  const int head_groups = (H + 16 * p.nw - 1) / (16 * p.nw);
+  const int64_t base = (int64_t)nq * head_groups;
+  // aim for ~512 workgroups, at least 2 tiles (64 keys) per split
+  int splits = (int)((512 + base - 1) / base);
+  const int max_splits = (max_keys + 2 * kTK - 1) / (2 * kTK);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int per = (max_keys + splits - 1) / splits;
+  per = (per + kTK - 1) / kTK * kTK;
+  if (per < kTK) per = kTK;
+  splits = (max_keys + per - 1) / per;
+  if (splits < 1) splits = 1;
+  p.n_splits = splits;
+  p.keys_per_split = per;
+  p.ws = splits > 1 ? (size_t)nq * splits * H * (d_v + 2) * sizeof(float) : 0;
+  return p;
+}
+
+typedef void (*AttnKernel)(AttnArgs);
+
+template <int KD, int NV>
+static AttnKernel pick_nw(int nw) {
+  switch (nw) {
+    case 1: return attn_kernel<KD, NV, 1>;
+    case 2: return attn_kernel<KD, NV, 2>;
+    case 3: return attn_kernel<KD, NV, 3>;
+    default: return attn_kernel<KD, NV, 4>;
+  }
+}
+
+// Compiled (D, d_v) pairs.
+static AttnKernel pick_kernel(int D, int d_v, int nw) {
+  if (D == 576 && d_v == 512) return pick_nw<18, 32>(nw);
+  if (D == 128 && d_v == 128) return pick_nw<4, 8>(nw);
+  if (D == 64 && d_v == 32) return pick_nw<2, 2>(nw);
+  if (D == 256 && d_v == 128) return pick_nw<8, 8>(nw);
+  return nullptr;
+}
+
+static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype) {
+  CSKV_REQUIRE(H >= 1 && H <= 128, CSKV_EINVAL, "%s: H=%d outside [1, 128]", name, H);
+  CSKV_REQUIRE(D % 32 == 0 && D >= 32, CSKV_EINVAL, "%s: D=%d must be a positive multiple of 32", name, D);
+  CSKV_REQUIRE(d_v % 16 == 0 && d_v >= 16 && d_v <= D, CSKV_EINVAL, "%s: d_v=%d", name, d_v);
+  CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL, "%s: d_rope=%d", name, d_rope);
+  CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
+  CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3, CSKV_EINVAL, "%s: ckv_dtype=%d", name, ckv_dtype);
+  CSKV_REQUIRE(pick_kernel(D, d_v, 1) != nullptr, CSKV_ENOTSUP,
+               "%s: (D, d_v) = (%d, %d) not compiled (576/512, 128/128, 256/128, 64/32)", name, D, d_v);
+  return CSKV_OK;
+}
+
+static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws, size_t ws_bytes, hipStream_t s) {
+  CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "%s: workspace %zu < %zu bytes", name,
+               ws_bytes, p.ws);
+  a.n_splits = p.n_splits;
+  a.keys_per_split = p.keys_per_split;
+  if (p.n_splits > 1) {
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = a.part_o + (size_t)a.nq * p.n_splits * a.H * a.d_v;
+  }
+  const int head_groups = (a.H + 16 * p.nw - 1) / (16 * p.nw);
+  AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw);
+  hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(p.nw * kWave), 0, s, a);
+  CSKV_LAUNCH_CHECK(name);
+  if (p.n_splits > 1) {
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.nq, a.H), dim3(128), 0, s, a);
+    CSKV_LAUNCH_CHECK(name);
+  }
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+using namespace cskv;
+
+extern "C" CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense) {
+  if (B < 1 || H < 1 || d_v < 1) return 0;
+  const int max_keys = (dense ? N_cap : k) + (W > 0 ? W : 0);
+  return plan_attn(B, H, d_v, max_keys > 0 ? max_keys : 1).ws;
+}
+
+extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                                           const float* ckv_scale, int ckv_dtype, int N_cap,
+                                           const int32_t* n_entries, const int32_t* topk_idx, int k,
+                                           const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
+                                           float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  const char* name = "hybrid_attn_decode";
+  CSKV_REQUIRE(B >= 1 && N_cap >= 0, CSKV_EINVAL, "%s: B=%d N_cap=%d", name, B, N_cap);
+  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype);
+  if (rc) return rc;
+  CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
+  CSKV_REQUIRE(q && q_pos && out && n_entries, CSKV_EINVAL, "%s: null pointer", name);
+  CSKV_REQUIRE(W == 0 || win, CSKV_EINVAL, "%s: null window", name);
+  CSKV_REQUIRE(N_cap == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
+  CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(win), CSKV_EINVAL, "%s: q/ckv/win must be 16-byte aligned",
+               name);
+  const int max_keys = (topk_idx ? k : N_cap) + W;
+  AttnPlan p = plan_attn(B, H, d_v, max_keys > 0 ? max_keys : 1);
+  AttnArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.pos0 = 0;
+  a.ckv = ckv;
+  a.ckv_scale = ckv_scale;
+  a.fp8 = ckv_dtype == CSKV_FP8_E4M3;
+  a.N_cap = N_cap;
+  a.ckv_seq = N_cap;
+  a.n_entries = n_entries;
+  a.m = 1;
+  a.topk = topk_idx;
+  a.k = k;
+  a.win = win;
+  a.ring = 1;
+  a.W = W;
+  a.nq = B;
+  a.H = H;
+  a.D = D;
+  a.d_rope = d_rope;
+  a.d_v = d_v;
+  a.rope_base = rope_base;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = out;
+  a.out_lse = out_lse;
+  return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense) {
+  return hybrid_attn_decode_workspace_size(T, H, d_v, N, k, W, dense);
+}
+
+extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,
+                                            const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
+                                            int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v,
+                                            int m, float rope_base, float softmax_scale, uint16_t* out,
+                                            float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* name = "hybrid_attn_prefill";
+  CSKV_REQUIRE(T >= 0 && N >= 0 && pos0 >= 0 && m >= 1, CSKV_EINVAL, "%s: T=%d N=%d pos0=%lld m=%d", name, T, N,
+               (long long)pos0, m);
+  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype);
+  if (rc) return rc;
+  if (T == 0) return CSKV_OK;
+  CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
+  CSKV_REQUIRE(q && out && (W == 0 || x), CSKV_EINVAL, "%s: null pointer", name);
+  CSKV_REQUIRE(N == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
+  CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(x), CSKV_EINVAL, "%s: q/ckv/x must be 16-byte aligned",
+               name);
+  const int max_keys = (topk_idx ? k : N) + W;
+  AttnPlan p = plan_attn(T, H, d_v, max_keys > 0 ? max_keys : 1);
+  AttnArgs a{};
+  a.q = q;
+  a.q_pos = nullptr;
+  a.pos0 = pos0;
+  a.ckv = ckv;
+  a.ckv_scale = ckv_scale;
+  a.fp8 = ckv_dtype == CSKV_FP8_E4M3;
+  a.N_cap = N;
+  a.ckv_seq = 0;
+  a.n_entries = nullptr;
+  a.m = m;
+  a.topk = topk_idx;
+  a.k = k;
+  a.win = x;
+  a.ring = 0;
+  a.W = W;
+  a.nq = T;
+  a.H = H;
+  a.D = D;
+  a.d_rope = d_rope;
+  a.d_v = d_v;
+  a.rope_base = rope_base;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = out;
+  a.out_lse = out_lse;
+  return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
