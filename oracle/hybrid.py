@@ -35,10 +35,11 @@ class Layer:
         self.ring_x, self.ring_z = ring_x, ring_z
         self.k, self.ik, self.ik_scale = k, ik, ik_scale
 
-    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None):
+    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True):
         """Positions t [B]; x_new [B, D] bf16; z_new [B]; q [B, H, D] bf16; iq [B, H_I, D_I/2].
 
-        Returns (o fp64 [B, H, d_v], lse [B, H], idx int32 [B, k] or None).
+        Returns (o fp64 [B, H, d_v], lse [B, H], idx int32 [B, k] or None); with
+        outputs=False only the state update (window, re-compression) runs.
         """
         B = len(t)
         outs, lses, idxs = [], [], []
@@ -59,6 +60,8 @@ class Layer:
                 self.n_entries[b] = j + 1
             n = int(self.n_entries[b])
             assert n == (tb + 1) // self.m
+            if not outputs:
+                continue
             sel = None
             if self.kind == "csa":
                 sc = indexer.scores(iq[b][None], iq_scale[b][None], self.ik[b, :n], self.ik_scale[b, :n],
@@ -72,4 +75,6 @@ class Layer:
                                           self.d_rope, self.d_v, self.rope_base, self.scale)
             outs.append(o)
             lses.append(lse)
+        if not outputs:
+            return None, None, None
         return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)
