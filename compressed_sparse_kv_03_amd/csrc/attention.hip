@@ -23,6 +23,8 @@
 //   of the same K rows) read by ds_read_b64_tr_b16 as B.
 // Splits write unnormalised partial outputs with (max, sum) in fp32; a combine
 // kernel merges them (log-sum-exp merge). One split writes the output directly.
+#include <type_traits>
+
 #include "common.cuh"
 #include "host_util.h"
 
@@ -88,6 +90,8 @@ __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
   return ks;
 }
 
+constexpr int kMaxSplitIdx = 1024;  // top-k slots staged per split (CSA)
+
 template <int KD, int NV, int NW>
 struct AttnSmem {
   uint16_t kt[kTK][KD * 32 + 8];  // key rows (bf16), padded
@@ -95,6 +99,7 @@ struct AttnSmem {
   float kvscale[kTK];             // per-key value multiplier (fp8 entry scale, else 1)
   uint16_t pt[NW][kTK][16 + 4];   // P^T per wave: [key][head]
   double inv_freq[KD * 16];       // RoPE frequencies (d_rope/2 <= D/2)
+  int sidx[kMaxSplitIdx];         // this split's top-k slots (CSA)
 };
 
 // Rotate 8 consecutive bf16 dims (4 RoPE pairs starting at pair0) to position pos. The angle is
@@ -116,60 +121,239 @@ __device__ __noinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_freq
   return pack8(f);
 }
 
-// Stage keys [key0, key0+kTK) of query qi into LDS.
-template <int KD, int NV, int NW>
-__device__ __forceinline__ void stage_tile(const AttnArgs& a, int qi, const KeySpace& ks, int key0, int key_end,
-                                           AttnSmem<KD, NV, NW>& sm) {
+// One tile's raw bytes in registers: every thread's chunks are loaded with independent
+// loads (issued back to back, consumed one tile later), so a tile costs one memory latency.
+// Entry tiles of an fp8 cache hold 8 bytes per 16-byte bf16 chunk; bf16 rows hold 16.
+template <int KD, int NW, bool NARROW>
+struct TileRegs {
+  static constexpr int CPR = KD * 4;                      // 16-byte bf16 chunks per row
+  static constexpr int NT = NW * kWave;
+  static constexpr int ITERS = (kTK * CPR + NT - 1) / NT;
+  typename std::conditional<NARROW, uint2, uint4>::type v[ITERS];
+  float sc;
+};
+
+// Entry tiles: keys [key0, key_end) all below n_c.
+template <int KD, int NV, int NW, bool FP8>
+__device__ __forceinline__ void entry_load(const AttnArgs& a, int qi, int key0, int key_end, int key_begin,
+                                           const AttnSmem<KD, NV, NW>& sm, TileRegs<KD, NW, FP8>& R) {
+  using TR = TileRegs<KD, NW, FP8>;
   constexpr int D = KD * 32;
-  constexpr int CPR = D / 8;  // 16-byte bf16 chunks per row
-  constexpr int NT = NW * kWave;
-  const int rope0 = D - a.d_rope;
-  const int b_kv = a.ckv_seq ? qi : 0;
-  for (int c = threadIdx.x; c < kTK * CPR; c += NT) {
-    const int r = c / CPR, ch = c - r * CPR;
+  const int64_t seq = (int64_t)(a.ckv_seq ? qi : 0) * a.ckv_seq;
+#pragma unroll
+  for (int j = 0; j < TR::ITERS; ++j) {
+    const int c = threadIdx.x + j * TR::NT;
+    const int r = c / TR::CPR, ch = c - r * TR::CPR;
     const int key = key0 + r;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    float ls = -INFINITY, vs = 0.f;
-    if (key < key_end) {
-      if (key < ks.n_c) {
-        int idx = key;
-        if (a.topk) idx = a.topk[(int64_t)qi * a.k + key];
-        if (idx >= 0) {
-          const int64_t row = (int64_t)b_kv * a.ckv_seq + idx;
-          if (!a.fp8) {
-            v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ckv) + row * D + ch * 8);
-            ls = a.scale_log2;
-            vs = 1.f;
-          } else {
-            const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.ckv) + row * D + ch * 8);
-            // exact e4m3 -> bf16 widening, two values per instruction
-            v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
-            v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
-            v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
-            v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
-            const float s = a.ckv_scale[row];
-            ls = a.scale_log2 * s;
-            vs = s;
-          }
-        }
-      } else {
-        const int64_t pos = ks.w0 + (key - ks.n_c);
-        const int64_t row = a.ring ? ((int64_t)qi * a.W + pos % a.W) : (pos - a.pos0);
-        v = *reinterpret_cast<const uint4*>(a.win + row * D + ch * 8);
-        if (8 * ch >= rope0) v = rope8(v, pos, sm.inv_freq, (8 * ch - rope0) >> 1);
-        ls = a.scale_log2;
-        vs = 1.f;
-      }
+    const int idx = (c < kTK * TR::CPR && key < key_end) ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
+    if constexpr (FP8) {
+      R.v[j] = make_uint2(0, 0);
+      if (idx >= 0)
+        R.v[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.ckv) + (seq + idx) * D + ch * 8);
+    } else {
+      R.v[j] = make_uint4(0, 0, 0, 0);
+      if (idx >= 0)
+        R.v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ckv) + (seq + idx) * D + ch * 8);
+    }
+  }
+  R.sc = 0.f;
+  if (threadIdx.x < kTK) {
+    const int key = key0 + threadIdx.x;
+    const int idx = key < key_end ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
+    if (idx >= 0) R.sc = FP8 ? a.ckv_scale[seq + idx] : 1.f;
+    if (idx < 0) R.sc = -1.f;  // masked
+  }
+}
+
+template <int KD, int NV, int NW, bool FP8>
+__device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD, NV, NW>& sm,
+                                            const TileRegs<KD, NW, FP8>& R) {
+  using TR = TileRegs<KD, NW, FP8>;
+#pragma unroll
+  for (int j = 0; j < TR::ITERS; ++j) {
+    const int c = threadIdx.x + j * TR::NT;
+    const int r = c / TR::CPR, ch = c - r * TR::CPR;
+    if (c >= kTK * TR::CPR) continue;
+    uint4 v;
+    if constexpr (FP8) {
+      // exact e4m3 -> bf16 widening, two values per instruction
+      const uint32_t w0 = R.v[j].x, w1 = R.v[j].y;
+      v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+      v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+      v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+      v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    } else {
+      v = R.v[j];
     }
     *reinterpret_cast<uint4*>(&sm.kt[r][ch * 8]) = v;
-    if (ch == 0) {
-      sm.kscale[r] = ls;
-      sm.kvscale[r] = vs;
+  }
+  if (threadIdx.x < kTK) {
+    const float sc = R.sc;
+    sm.kscale[threadIdx.x] = sc < 0.f ? -INFINITY : a.scale_log2 * sc;
+    sm.kvscale[threadIdx.x] = sc < 0.f ? 0.f : sc;
+  }
+}
+
+// Window tiles: keys [key0, key_end) all at or above n_c (raw bf16 tokens, rotated when stored).
+template <int KD, int NV, int NW>
+__device__ __forceinline__ void window_load(const AttnArgs& a, int qi, const KeySpace& ks, int key0, int key_end,
+                                            TileRegs<KD, NW, false>& R) {
+  using TR = TileRegs<KD, NW, false>;
+  constexpr int D = KD * 32;
+#pragma unroll
+  for (int j = 0; j < TR::ITERS; ++j) {
+    const int c = threadIdx.x + j * TR::NT;
+    const int r = c / TR::CPR, ch = c - r * TR::CPR;
+    const int key = key0 + r;
+    R.v[j] = make_uint4(0, 0, 0, 0);
+    if (c < kTK * TR::CPR && key < key_end) {
+      const int64_t pos = ks.w0 + (key - ks.n_c);
+      const int64_t row = a.ring ? ((int64_t)qi * a.W + pos % a.W) : (pos - a.pos0);
+      R.v[j] = *reinterpret_cast<const uint4*>(a.win + row * D + ch * 8);
+    }
+  }
+  R.sc = 0.f;
+}
+
+template <int KD, int NV, int NW>
+__device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, int key_end,
+                                             AttnSmem<KD, NV, NW>& sm, const TileRegs<KD, NW, false>& R) {
+  using TR = TileRegs<KD, NW, false>;
+  constexpr int D = KD * 32;
+  const int rope0 = D - a.d_rope;
+#pragma unroll
+  for (int j = 0; j < TR::ITERS; ++j) {
+    const int c = threadIdx.x + j * TR::NT;
+    const int r = c / TR::CPR, ch = c - r * TR::CPR;
+    if (c >= kTK * TR::CPR) continue;
+    const int key = key0 + r;
+    uint4 v = R.v[j];
+    if (key < key_end && 8 * ch >= rope0) v = rope8(v, ks.w0 + (key - ks.n_c), sm.inv_freq, (8 * ch - rope0) >> 1);
+    *reinterpret_cast<uint4*>(&sm.kt[r][ch * 8]) = v;
+  }
+  if (threadIdx.x < kTK) {
+    const bool ok = key0 + (int)threadIdx.x < key_end;
+    sm.kscale[threadIdx.x] = ok ? a.scale_log2 : -INFINITY;
+    sm.kvscale[threadIdx.x] = ok ? 1.f : 0.f;
+  }
+}
+
+// Per-wave attention state.
+template <int KD, int NV>
+struct WaveState {
+  uint4 qa[KD];
+  f32x4 o[NV];
+  float m[4], l[4];
+};
+
+// One staged tile: S = Q K^T on bf16 MFMA, online softmax, O += P V.
+template <int KD, int NV, int NW>
+__device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, NW>& sm, WaveState<KD, NV>& st) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  // S[head 4g+r][key col (+16)] = q_rot . k; K operands read in batches ahead of the MFMAs
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  constexpr int BQ = 6;
+#pragma unroll
+  for (int s = 0; s < KD; s += BQ) {
+    uint4 k0[BQ], k1[BQ];
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+      if (s + u < KD) {
+        k0[u] = *reinterpret_cast<const uint4*>(&sm.kt[col][32 * (s + u) + 8 * g]);
+        k1[u] = *reinterpret_cast<const uint4*>(&sm.kt[16 + col][32 * (s + u) + 8 * g]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+      if (s + u < KD) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, st.qa[s + u]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k0[u]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k1[u]), s1, 0, 0, 0);
+      }
+    }
+  }
+  const float c0 = sm.kscale[col], c1 = sm.kscale[16 + col];
+  const float v0 = sm.kvscale[col], v1 = sm.kvscale[16 + col];
+  float alpha[4];
+  bool moved = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float x0 = c0 == -INFINITY ? -INFINITY : s0[r] * c0;
+    const float x1 = c1 == -INFINITY ? -INFINITY : s1[r] * c1;
+    float mx = fmaxf(x0, x1);
+#pragma unroll
+    for (int o2 = 8; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
+    const float mnew = fmaxf(st.m[r], mx);
+    const float base = mnew == -INFINITY ? 0.f : mnew;
+    const float p0 = exp2f(x0 - base), p1 = exp2f(x1 - base);
+    float ps = p0 + p1;
+#pragma unroll
+    for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
+    alpha[r] = exp2f(st.m[r] - base);
+    moved |= mnew != st.m[r];
+    st.l[r] = st.l[r] * alpha[r] + ps;
+    st.m[r] = mnew;
+    s0[r] = p0 * v0;  // value-side scale folded into P
+    s1[r] = p1 * v1;
+  }
+  // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
+  {
+    uint2 w0, w1;
+    w0.x = pack_bf16x2(s0[0], s0[1]);
+    w0.y = pack_bf16x2(s0[2], s0[3]);
+    w1.x = pack_bf16x2(s1[0], s1[1]);
+    w1.y = pack_bf16x2(s1[2], s1[3]);
+    *reinterpret_cast<uint2*>(&sm.pt[wave][col][4 * g]) = w0;
+    *reinterpret_cast<uint2*>(&sm.pt[wave][16 + col][4 * g]) = w1;
+  }
+  // rescale O only when some row's running max moved in this wave
+  if (__ballot(moved)) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.o[n][r] *= alpha[r];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P^T writes done (wave-local data)
+  __builtin_amdgcn_wave_barrier();
+  // A = P[head col][keys 8g..8g+7] via two transposed reads of the [key][head] block
+  bf16x8 pa;
+  {
+    const int kr = 8 * g + (col >> 2), hc = 4 * (col & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr][hc]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr + 4][hc]));
+    pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // O[head 4g+r][dim 16n+col] += P V, V = key rows' first d_v dims, read in batches
+  constexpr int BV = 8;
+  const int kr = 8 * g + (col >> 2);
+#pragma unroll
+  for (int n = 0; n < NV; n += BV) {
+    i16x4 lo[BV], hi[BV];
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+      if (n + u < NV) {
+        const int dc = 16 * (n + u) + 4 * (col & 3);
+        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(&sm.kt[kr][dc]));
+        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr + 4][dc]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+      if (n + u < NV) {
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[u], hi[u], 0, 1, 2, 3, 4, 5, 6, 7));
+        st.o[n + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, st.o[n + u], 0, 0, 0);
+      }
     }
   }
 }
 
-template <int KD, int NV, int NW>
+template <int KD, int NV, int NW, bool FP8>
 __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
   constexpr int D = KD * 32;
   __shared__ AttnSmem<KD, NV, NW> sm;
@@ -189,109 +373,59 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
   const int n_keys = ks.n_c + ks.n_w;
   const int key_begin = split * a.keys_per_split;
   const int key_end = min(n_keys, key_begin + a.keys_per_split);
+  const int e_end = min(key_end, ks.n_c);  // entry keys [key_begin, e_end), window keys after
+  if (a.topk) {
+    const int n_sel = e_end - key_begin;
+    for (int i = threadIdx.x; i < n_sel; i += NW * kWave) sm.sidx[i] = a.topk[(int64_t)qi * a.k + key_begin + i];
+  }
 
-  // Q rows of this wave (A operand): lane holds head h0+col, dims 32s + 8g .. +7, rotated at t
-  uint4 qa[KD];
+  WaveState<KD, NV> st;
   {
     const int h = h0 + col;
     const int rope0 = D - a.d_rope;
 #pragma unroll
     for (int s = 0; s < KD; ++s) {
-      qa[s] = make_uint4(0, 0, 0, 0);
-      if (h < a.H) qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g);
+      st.qa[s] = make_uint4(0, 0, 0, 0);
+      if (h < a.H) st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g);
     }
-    __syncthreads();  // inv_freq ready
+    __syncthreads();  // inv_freq and sidx ready
 #pragma unroll
     for (int s = 0; s < KD; ++s) {
       const int d0 = 32 * s + 8 * g;
-      if (d0 >= rope0) qa[s] = rope8(qa[s], ks.t, sm.inv_freq, (d0 - rope0) >> 1);
+      if (d0 >= rope0) st.qa[s] = rope8(st.qa[s], ks.t, sm.inv_freq, (d0 - rope0) >> 1);
     }
   }
-
-  f32x4 o[NV];
 #pragma unroll
-  for (int n = 0; n < NV; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
+  for (int n = 0; n < NV; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.f;
+    st.m[r] = -INFINITY;
+    st.l[r] = 0.f;
   }
 
-  for (int key0 = key_begin; key0 < key_end; key0 += kTK) {
-    __syncthreads();
-    stage_tile<KD, NV, NW>(a, qi, ks, key0, key_end, sm);
-    __syncthreads();
-
-    // S[head 4g+r][key col (+16)] = q_rot . k
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KD; ++s) {
-      const uint4 k0 = *reinterpret_cast<const uint4*>(&sm.kt[col][32 * s + 8 * g]);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(&sm.kt[16 + col][32 * s + 8 * g]);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, qa[s]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k0), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k1), s1, 0, 0, 0);
+  // phase 1: compressed entries
+  if (key_begin < e_end) {
+    TileRegs<KD, NW, FP8> R;
+    entry_load<KD, NV, NW, FP8>(a, qi, key_begin, e_end, key_begin, sm, R);
+    for (int key0 = key_begin; key0 < e_end; key0 += kTK) {
+      __syncthreads();
+      entry_store<KD, NV, NW, FP8>(a, sm, R);
+      __syncthreads();
+      if (key0 + kTK < e_end) entry_load<KD, NV, NW, FP8>(a, qi, key0 + kTK, e_end, key_begin, sm, R);
+      tile_compute<KD, NV, NW>(sm, st);
     }
-    const float c0 = sm.kscale[col], c1 = sm.kscale[16 + col];
-    const float v0 = sm.kvscale[col], v1 = sm.kvscale[16 + col];
-    float alpha[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x0 = c0 == -INFINITY ? -INFINITY : s0[r] * c0;
-      const float x1 = c1 == -INFINITY ? -INFINITY : s1[r] * c1;
-      float mx = fmaxf(x0, x1);
-#pragma unroll
-      for (int o2 = 8; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
-      const float mnew = fmaxf(mrow[r], mx);
-      const float base = mnew == -INFINITY ? 0.f : mnew;
-      const float p0 = exp2f(x0 - base), p1 = exp2f(x1 - base);
-      float ps = p0 + p1;
-#pragma unroll
-      for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
-      alpha[r] = exp2f(mrow[r] - base);
-      lrow[r] = lrow[r] * alpha[r] + ps;
-      mrow[r] = mnew;
-      s0[r] = p0 * v0;  // value-side scale folded into P
-      s1[r] = p1 * v1;
-    }
-    // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
-    {
-      uint2 w0, w1;
-      w0.x = pack_bf16x2(s0[0], s0[1]);
-      w0.y = pack_bf16x2(s0[2], s0[3]);
-      w1.x = pack_bf16x2(s1[0], s1[1]);
-      w1.y = pack_bf16x2(s1[2], s1[3]);
-      *reinterpret_cast<uint2*>(&sm.pt[wave][col][4 * g]) = w0;
-      *reinterpret_cast<uint2*>(&sm.pt[wave][16 + col][4 * g]) = w1;
-    }
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P^T writes done (wave-local data)
-    __builtin_amdgcn_wave_barrier();
-    // A = P[head col][keys 8g..8g+7] via two transposed reads of the [key][head] block
-    bf16x8 pa;
-    {
-      const int kr = 8 * g + (col >> 2), hc = 4 * (col & 3);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr][hc]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr + 4][hc]));
-      pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    // O[head 4g+r][dim 16n+col] += P V, V = key rows' first d_v dims
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const int kr = 8 * g + (col >> 2), dc = 16 * n + 4 * (col & 3);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr][dc]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr + 4][dc]));
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[n], 0, 0, 0);
+  }
+  // phase 2: window tokens
+  const int w_begin = max(key_begin, ks.n_c);
+  if (w_begin < key_end) {
+    TileRegs<KD, NW, false> R;
+    window_load<KD, NV, NW>(a, qi, ks, w_begin, key_end, R);
+    for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
+      __syncthreads();
+      window_store<KD, NV, NW>(a, ks, key0, key_end, sm, R);
+      __syncthreads();
+      if (key0 + kTK < key_end) window_load<KD, NV, NW>(a, qi, ks, key0 + kTK, key_end, R);
+      tile_compute<KD, NV, NW>(sm, st);
     }
   }
 
@@ -301,48 +435,89 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
     const int h = h0 + 4 * g + r;
     if (h >= a.H) continue;
     if (a.n_splits == 1) {
-      const float inv = lrow[r] > 0.f ? 1.f / lrow[r] : 0.f;
+      const float inv = st.l[r] > 0.f ? 1.f / st.l[r] : 0.f;
       uint16_t* dst = a.out + ((int64_t)qi * a.H + h) * a.d_v;
 #pragma unroll
       for (int n = 0; n < NV; ++n)
-        if (16 * n < a.d_v) dst[16 * n + col] = (uint16_t)f32_to_bf16_rne(o[n][r] * inv);
+        if (16 * n < a.d_v) dst[16 * n + col] = (uint16_t)f32_to_bf16_rne(st.o[n][r] * inv);
       if (a.out_lse && col == 0)
-        a.out_lse[(int64_t)qi * a.H + h] = lrow[r] > 0.f ? (mrow[r] + log2f(lrow[r])) * kLn2 : -INFINITY;
+        a.out_lse[(int64_t)qi * a.H + h] = st.l[r] > 0.f ? (st.m[r] + log2f(st.l[r])) * kLn2 : -INFINITY;
     } else {
       const int64_t pidx = ((int64_t)qi * a.n_splits + split) * a.H + h;
       float* dst = a.part_o + pidx * a.d_v;
 #pragma unroll
       for (int n = 0; n < NV; ++n)
-        if (16 * n < a.d_v) dst[16 * n + col] = o[n][r];
+        if (16 * n < a.d_v) dst[16 * n + col] = st.o[n][r];
       if (col == 0) {
-        a.part_ml[pidx * 2 + 0] = mrow[r];
-        a.part_ml[pidx * 2 + 1] = lrow[r];
+        a.part_ml[pidx * 2 + 0] = st.m[r];
+        a.part_ml[pidx * 2 + 1] = st.l[r];
       }
     }
   }
 }
 
-// One workgroup per (query, head): log-sum-exp merge of the split partials.
+// One workgroup per (query, head): log-sum-exp merge of the split partials. Thread t owns
+// dims 4t..4t+3; every split's weight comes from LDS and the partial loads are independent.
+constexpr int kMaxSplits = 256;
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[2];
   const int qi = blockIdx.x, h = blockIdx.y;
-  const int64_t base = (int64_t)qi * a.n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.H + h) * 2]);
-  const float Mb = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const int64_t p = ((base + s) * a.H + h) * 2;
-    L += a.part_ml[p + 1] * exp2f(a.part_ml[p] - Mb);
+  const int S = a.n_splits;
+  const int64_t base = (int64_t)qi * S;
+  const int lane = threadIdx.x & (kWave - 1);
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const float m = a.part_ml[((base + s) * a.H + h) * 2];
+    wsh[s] = m;
+    mloc = fmaxf(mloc, m);
   }
+  mloc = wave_max(mloc);
+  if (lane == 0) red[threadIdx.x >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  const float Mb = M == -INFINITY ? 0.f : M;
+  float lloc = 0.f;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const float w = exp2f(wsh[s] - Mb);
+    wsh[s] = w;
+    lloc += w * a.part_ml[((base + s) * a.H + h) * 2 + 1];
+  }
+  lloc = wave_sum(lloc);
+  __syncthreads();
+  if (lane == 0) red[threadIdx.x >> 6] = lloc;
+  __syncthreads();
+  const float L = red[0] + red[1];
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = threadIdx.x; d < a.d_v; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const int64_t p = (base + s) * a.H + h;
-      const float w = exp2f(a.part_ml[p * 2] - Mb);
-      acc += w * a.part_o[p * a.d_v + d];
+  for (int d0 = 4 * threadIdx.x; d0 < a.d_v; d0 += 4 * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4*>(a.part_o + ((base + s + u) * a.H + h) * a.d_v + d0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = wsh[s + u];
+        acc.x += w * v[u].x;
+        acc.y += w * v[u].y;
+        acc.z += w * v[u].z;
+        acc.w += w * v[u].w;
+      }
     }
-    a.out[((int64_t)qi * a.H + h) * a.d_v + d] = (uint16_t)f32_to_bf16_rne(acc * inv);
+    for (; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((base + s) * a.H + h) * a.d_v + d0);
+      const float w = wsh[s];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+    uint2 packed;
+    packed.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    packed.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)qi * a.H + h) * a.d_v + d0) = packed;
   }
   if (threadIdx.x == 0 && a.out_lse)
     a.out_lse[(int64_t)qi * a.H + h] = L > 0.f ? (Mb + log2f(L)) * kLn2 : -INFINITY;
@@ -359,14 +534,19 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
   p.nw = H >= 64 ? 4 : (H + 15) / 16;
   const int head_groups = (H + 16 * p.nw - 1) / (16 * p.nw);
   const int64_t base = (int64_t)nq * head_groups;
-  // aim for ~512 workgroups, at least 2 tiles (64 keys) per split
+  // aim for ~512 workgroups with at least 2 tiles (64 keys) per split; a split holds at
+  // most kMaxSplitIdx keys, and there are at most kMaxSplits splits
   int splits = (int)((512 + base - 1) / base);
   const int max_splits = (max_keys + 2 * kTK - 1) / (2 * kTK);
   if (splits > max_splits) splits = max_splits;
+  const int min_splits = (max_keys + kMaxSplitIdx - 1) / kMaxSplitIdx;
+  if (splits < min_splits) splits = min_splits;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
   int per = (max_keys + splits - 1) / splits;
   per = (per + kTK - 1) / kTK * kTK;
   if (per < kTK) per = kTK;
+  if (per > kMaxSplitIdx) per = kMaxSplitIdx;
   splits = (max_keys + per - 1) / per;
   if (splits < 1) splits = 1;
   p.n_splits = splits;
@@ -377,23 +557,28 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
 
 typedef void (*AttnKernel)(AttnArgs);
 
-template <int KD, int NV>
+template <int KD, int NV, bool FP8>
 static AttnKernel pick_nw(int nw) {
   switch (nw) {
-    case 1: return attn_kernel<KD, NV, 1>;
-    case 2: return attn_kernel<KD, NV, 2>;
-    case 3: return attn_kernel<KD, NV, 3>;
-    default: return attn_kernel<KD, NV, 4>;
+    case 1: return attn_kernel<KD, NV, 1, FP8>;
+    case 2: return attn_kernel<KD, NV, 2, FP8>;
+    case 3: return attn_kernel<KD, NV, 3, FP8>;
+    default: return attn_kernel<KD, NV, 4, FP8>;
   }
 }
 
-// Compiled (D, d_v) pairs.
-static AttnKernel pick_kernel(int D, int d_v, int nw) {
-  if (D == 576 && d_v == 512) return pick_nw<18, 32>(nw);
-  if (D == 128 && d_v == 128) return pick_nw<4, 8>(nw);
-  if (D == 64 && d_v == 32) return pick_nw<2, 2>(nw);
-  if (D == 256 && d_v == 128) return pick_nw<8, 8>(nw);
+template <bool FP8>
+static AttnKernel pick_dims(int D, int d_v, int nw) {
+  if (D == 576 && d_v == 512) return pick_nw<18, 32, FP8>(nw);
+  if (D == 128 && d_v == 128) return pick_nw<4, 8, FP8>(nw);
+  if (D == 64 && d_v == 32) return pick_nw<2, 2, FP8>(nw);
+  if (D == 256 && d_v == 128) return pick_nw<8, 8, FP8>(nw);
   return nullptr;
+}
+
+// Compiled (D, d_v) pairs.
+static AttnKernel pick_kernel(int D, int d_v, int nw, bool fp8) {
+  return fp8 ? pick_dims<true>(D, d_v, nw) : pick_dims<false>(D, d_v, nw);
 }
 
 static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype) {
@@ -403,7 +588,8 @@ static int check_common(const char* name, int H, int D, int d_rope, int d_v, int
   CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL, "%s: d_rope=%d", name, d_rope);
   CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
   CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3, CSKV_EINVAL, "%s: ckv_dtype=%d", name, ckv_dtype);
-  CSKV_REQUIRE(pick_kernel(D, d_v, 1) != nullptr, CSKV_ENOTSUP,
+  CSKV_REQUIRE(d_v % 64 == 0 || d_v == 32, CSKV_ENOTSUP, "%s: d_v=%d", name, d_v);
+  CSKV_REQUIRE(pick_kernel(D, d_v, 1, false) != nullptr, CSKV_ENOTSUP,
                "%s: (D, d_v) = (%d, %d) not compiled (576/512, 128/128, 256/128, 64/32)", name, D, d_v);
   return CSKV_OK;
 }
@@ -418,7 +604,7 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
     a.part_ml = a.part_o + (size_t)a.nq * p.n_splits * a.H * a.d_v;
   }
   const int head_groups = (a.H + 16 * p.nw - 1) / (16 * p.nw);
-  AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw);
+  AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw, a.fp8 != 0);
   hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(p.nw * kWave), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {

@@ -209,9 +209,266 @@ __global__ __launch_bounds__(kIdxNT) void index_merge_kernel(IndexArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- decode path (few queries)
+//
+// Kernel Z zeroes each query's candidate counter and 12-bit histogram. Kernel A
+// gives each (query, chunk of entries) one workgroup: it scores the chunk into
+// LDS, finds the chunk's local top-k threshold with two LDS histograms (12 bits
+// of the ordered score, then the next 8 bits inside the threshold bin), claims
+// room for exactly the keys at or above it with one atomic on the query's
+// counter, writes them contiguously to the query's candidate list and adds
+// their 12-bit bin counts to the query's histogram. Kernel C, one workgroup per
+// query, finds the highest bin b' whose cumulative count from the top reaches k,
+// keeps the candidates in bins >= b' (a few hundred) and sorts them.
+// Exactness: every global top-k key is in its chunk's top-k, so it is a
+// candidate; the candidates in bins >= b' therefore include the whole global
+// top-k, and b' is the bin of the k-th best key (were it higher, k candidates
+// would beat that key).
+constexpr int kBins = 4096;     // 12-bit bins of the ordered score
+constexpr int kSubBins = 256;   // next 8 bits
+constexpr int kChunkA = 2048;   // entries per workgroup in kernel A
+constexpr int kCapF = 2048;     // candidates kernel C sorts directly
+
+struct DecodeArgs {
+  IndexArgs a;
+  uint64_t* cand;   // [Q][N_cap] candidate keys
+  uint32_t* hist;   // [Q][kBins] 12-bit bin counts of the candidates
+  uint32_t* cnt;    // [Q] candidates
+  int chunk, n_chunks;
+};
+
+__device__ __forceinline__ uint32_t key_bin(uint64_t key) { return (uint32_t)(key >> 52); }       // 12 bits
+__device__ __forceinline__ uint32_t key_bin20(uint64_t key) { return (uint32_t)(key >> 44); }     // 20 bits
+
+// Highest bin b (scanning from the top) whose cumulative count reaches kk; returns b and the
+// count strictly above it in *above. NB is a multiple of kIdxNT. kk >= 1 and total >= kk.
+template <int NB>
+__device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int* scratch) {
+  constexpr int PER = NB / kIdxNT;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+  // thread t owns bins [NB - PER*(t+1), NB - PER*t), i.e. the t-th slice from the top
+  const int top = NB - PER * t;
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i <= PER; ++i) s += hist[top - i];
+  int inc = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  int wbase = 0;
+  for (int i = 0; i < w; ++i) wbase += scratch[i];
+  const int incl = inc + wbase, excl = incl - s;
+  __syncthreads();
+  if (excl < kk && incl >= kk) {
+    int c = excl;
+    for (int i = 1; i <= PER; ++i) {
+      const int h = hist[top - i];
+      if (c + h >= kk) {
+        scratch[8] = top - i;
+        scratch[9] = c;
+        break;
+      }
+      c += h;
+    }
+  }
+  __syncthreads();
+  *above = scratch[9];
+  return scratch[8];
+}
+
+// Wave-aggregated append of the keys passing `p` to dst[*cnt ...] (LDS counter).
+__device__ __forceinline__ void append_lds(bool p, uint64_t key, uint64_t* dst, int* cnt, int cap) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t mask = __ballot(p);
+  if (mask == 0) return;
+  const int nw = __popcll(mask);
+  int base = 0;
+  if (lane == 0) base = atomicAdd(cnt, nw);
+  base = __shfl(base, 0, kWave);
+  const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+  if (p && base + off < cap) dst[base + off] = key;
+}
+
+__global__ __launch_bounds__(kIdxNT) void index_zero_kernel(DecodeArgs d) {
+  const int q = blockIdx.x;
+  uint32_t* h = d.hist + (int64_t)q * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kIdxNT) h[i] = 0;
+  if (threadIdx.x == 0) d.cnt[q] = 0;
+}
+
+struct ASmem {
+  uint64_t keys[kChunkA];
+  uint32_t hist[kBins];
+  uint32_t sub[kSubBins];
+  int scratch[16];
+  int cnt;
+  int base;
+};
+
+template <int KS>
+__global__ __launch_bounds__(kIdxNT) void index_score_kernel(DecodeArgs d) {
+  __shared__ ASmem sm;
+  const IndexArgs& a = d.a;
+  const int q = blockIdx.x;
+  const int b = q / a.T;
+  const int nv = min(a.n_valid[q], a.N_cap);
+  const int chunk = blockIdx.y;
+  const int c0 = chunk * d.chunk;
+  const int c1 = min(c0 + d.chunk, nv);
+  if (c0 >= c1) return;
+  const int n = c1 - c0;
+  for (int i = threadIdx.x; i < kBins; i += kIdxNT) sm.hist[i] = 0;
+  for (int i = threadIdx.x; i < kSubBins; i += kIdxNT) sm.sub[i] = 0;
+  if (threadIdx.x == 0) sm.cnt = 0;
+  uint4 qa[KS];
+  int qs[KS];
+  float hw[4];
+  load_query<KS>(a, q, qa, qs, hw);
+  __syncthreads();
+  score_range<KS>(a, b, c0, c1, qa, qs, hw, sm.keys);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kIdxNT) atomicAdd(&sm.hist[key_bin(sm.keys[i])], 1u);
+  __syncthreads();
+  const int kk = min(a.k, n);
+  int above;
+  const int bk = find_threshold_bin<kBins>(sm.hist, kk, &above, sm.scratch);
+  for (int i = threadIdx.x; i < n; i += kIdxNT) {
+    const uint32_t b20 = key_bin20(sm.keys[i]);
+    if ((int)(b20 >> 8) == bk) atomicAdd(&sm.sub[b20 & 255], 1u);
+  }
+  __syncthreads();
+  int above2;
+  const int sk = find_threshold_bin<kSubBins>(sm.sub, kk - above, &above2, sm.scratch);
+  const uint32_t thr20 = ((uint32_t)bk << 8) | (uint32_t)sk;
+  // keys at or above the threshold: the bins above bk, plus sub-bins >= sk of bin bk
+  const int n_keep = above + above2 + (int)sm.sub[sk];
+  if (threadIdx.x == 0) sm.base = (int)atomicAdd(&d.cnt[q], (uint32_t)n_keep);
+  for (int i = threadIdx.x; i < kBins; i += kIdxNT) sm.hist[i] = 0;
+  __syncthreads();
+  uint64_t* cand = d.cand + (int64_t)q * a.N_cap + sm.base;
+  const int n_round = (n + kIdxNT - 1) / kIdxNT * kIdxNT;
+  for (int i = threadIdx.x; i < n_round; i += kIdxNT) {
+    const uint64_t key = i < n ? sm.keys[i] : 0;
+    const bool p = i < n && key_bin20(key) >= thr20;
+    append_lds(p, key, cand, &sm.cnt, n_keep);
+    if (p) atomicAdd(&sm.hist[key_bin(key)], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = d.hist + (int64_t)q * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kIdxNT) {
+    const uint32_t c = sm.hist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+struct CSmem {
+  uint32_t hist[kBins];
+  uint64_t buf[kCapF];
+  uint64_t keys[1024 + kSub];  // slow path: running winners + one sub-chunk
+  SelectScratch sc;
+  int scratch[16];
+  int cnt;
+};
+
+__global__ __launch_bounds__(kIdxNT) void index_final_kernel(DecodeArgs d) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  CSmem& sm = *reinterpret_cast<CSmem*>(smem_raw);
+  const IndexArgs& a = d.a;
+  const int q = blockIdx.x;
+  const int nv = min(a.n_valid[q], a.N_cap);
+  const int kk = min(a.k, nv);
+  int32_t* oi = a.out_idx + (int64_t)q * a.k;
+  float* os = a.out_score ? a.out_score + (int64_t)q * a.k : nullptr;
+  if (kk > 0) {
+    const uint32_t* gh = d.hist + (int64_t)q * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kIdxNT) sm.hist[i] = gh[i];
+    __syncthreads();
+    int above;
+    const int bp = find_threshold_bin<kBins>(sm.hist, kk, &above, sm.scratch);
+    int cstar = 0;
+    for (int i = threadIdx.x; i < kBins; i += kIdxNT) cstar += i >= bp ? (int)sm.hist[i] : 0;
+    cstar = block_sum_int<kIdxNT>(cstar, sm.sc.red);
+    const int n_cand = (int)d.cnt[q];
+    const uint64_t* cq = d.cand + (int64_t)q * a.N_cap;
+    if (cstar <= kCapF) {
+      if (threadIdx.x == 0) sm.cnt = 0;
+      __syncthreads();
+      // 16 independent loads in flight per thread, then filter
+      constexpr int U = 16;
+      for (int i0 = 0; i0 < n_cand; i0 += U * kIdxNT) {
+        uint64_t kv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kIdxNT + threadIdx.x;
+          kv[u] = i < n_cand ? cq[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kIdxNT + threadIdx.x;
+          append_lds(i < n_cand && (int)key_bin(kv[u]) >= bp, kv[u], sm.buf, &sm.cnt, kCapF);
+        }
+      }
+      __syncthreads();
+      const int c = min(sm.cnt, kCapF);
+      int P = 1;
+      while (P < c) P <<= 1;
+      for (int i = c + threadIdx.x; i < P; i += kIdxNT) sm.buf[i] = 0;
+      __syncthreads();
+      bitonic_sort_desc<kIdxNT>(sm.buf, P);
+    } else {
+      // many keys tie into the threshold bin: exact running top-k over the filtered candidates
+      int kept = 0;
+      for (int s0 = 0; s0 < n_cand; s0 += kSub) {
+        const int s1 = min(s0 + kSub, n_cand);
+        if (threadIdx.x == 0) sm.cnt = 0;
+        __syncthreads();
+        const int n_round = (s1 - s0 + kIdxNT - 1) / kIdxNT * kIdxNT;
+        for (int i = threadIdx.x; i < n_round; i += kIdxNT) {
+          const int j = s0 + i;
+          const uint64_t key = j < s1 ? cq[j] : 0;
+          append_lds(j < s1 && (int)key_bin(key) >= bp, key, sm.keys + kept, &sm.cnt, kSub);
+        }
+        __syncthreads();
+        const int nn = kept + sm.cnt;
+        if (nn > 0) {
+          const int k2 = min(kk, nn);
+          select_topk<kIdxNT, kCapF>(sm.keys, nn, k2, sm.buf, &sm.sc);
+          for (int i = threadIdx.x; i < k2; i += kIdxNT) sm.keys[i] = sm.buf[i];
+          __syncthreads();
+          kept = k2;
+        }
+      }
+      for (int i = threadIdx.x; i < kept; i += kIdxNT) sm.buf[i] = sm.keys[i];
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < a.k; i += kIdxNT) {
+    if (i < kk) {
+      const uint64_t key = sm.buf[i];
+      oi[i] = (int32_t)(~(uint32_t)key);
+      if (os) os[i] = ordered_to_score((uint32_t)(key >> 32));
+    } else {
+      oi[i] = -1;
+      if (os) os[i] = -INFINITY;
+    }
+  }
+}
+
+static int decode_chunks(int N_cap) { return (N_cap + kChunkA - 1) / kChunkA; }
+
+static size_t decode_ws_bytes(int queries, int N_cap) {
+  return (size_t)queries * N_cap * sizeof(uint64_t) + (size_t)queries * (kBins + 1) * sizeof(uint32_t);
+}
+
 struct IndexPlan {
   int chunk, n_chunks, cap;
   size_t ws;
+  bool decode;
 };
 
 static IndexPlan plan_index(int B, int T, int N_cap, int k) {
@@ -236,7 +493,43 @@ static IndexPlan plan_index(int B, int T, int N_cap, int k) {
   p.n_chunks = n_chunks;
   p.cap = k <= 256 ? 512 : 2048;
   p.ws = (size_t)queries * n_chunks * k * sizeof(uint64_t);
+  // decode path: few queries (candidate lists of N_cap keys per query stay small)
+  p.decode = k <= 1024 && (size_t)queries * N_cap <= ((size_t)1 << 26);
+  if (p.decode) p.ws = decode_ws_bytes((int)queries, N_cap);
   return p;
+}
+
+template <int KS>
+static void launch_decode_score(const DecodeArgs& d, int queries, int n_chunks, hipStream_t s) {
+  hipLaunchKernelGGL((index_score_kernel<KS>), dim3(queries, n_chunks), dim3(kIdxNT), 0, s, d);
+}
+
+static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipStream_t s) {
+  DecodeArgs d;
+  d.a = a;
+  d.chunk = kChunkA;
+  d.n_chunks = decode_chunks(a.N_cap);
+  unsigned char* w = reinterpret_cast<unsigned char*>(ws);
+  d.cand = reinterpret_cast<uint64_t*>(w);
+  w += (size_t)queries * a.N_cap * sizeof(uint64_t);
+  d.hist = reinterpret_cast<uint32_t*>(w);
+  w += (size_t)queries * kBins * sizeof(uint32_t);
+  d.cnt = reinterpret_cast<uint32_t*>(w);
+  hipLaunchKernelGGL(index_zero_kernel, dim3(queries), dim3(kIdxNT), 0, s, d);
+  CSKV_LAUNCH_CHECK("csa_index_topk (zero)");
+  if (d.n_chunks > 0) {
+    if (ks == 1)
+      launch_decode_score<1>(d, queries, d.n_chunks, s);
+    else if (ks == 2)
+      launch_decode_score<2>(d, queries, d.n_chunks, s);
+    else
+      launch_decode_score<4>(d, queries, d.n_chunks, s);
+    CSKV_LAUNCH_CHECK("csa_index_topk (score)");
+  }
+  const size_t smem = sizeof(CSmem);
+  (void)hipFuncSetAttribute((const void*)index_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipLaunchKernelGGL(index_final_kernel, dim3(queries), dim3(kIdxNT), smem, s, d);
+  return CSKV_OK;
 }
 
 template <int CAP, int KS>
@@ -298,7 +591,8 @@ extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scal
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int queries = B * T;
   const int ks = (D_I + 127) / 128;
-  int rc = p.cap == 512 ? launch_index<512>(a, queries, ks, s) : launch_index<2048>(a, queries, ks, s);
+  int rc = p.decode ? launch_decode(a, queries, ks, ws, s)
+                    : (p.cap == 512 ? launch_index<512>(a, queries, ks, s) : launch_index<2048>(a, queries, ks, s));
   if (rc != CSKV_OK) return rc;
   CSKV_LAUNCH_CHECK("csa_index_topk (merge)");
   return CSKV_OK;

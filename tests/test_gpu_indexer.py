@@ -99,3 +99,17 @@ def test_index_topk_hybrid_1m_shape():
     nv = up(np.full((w.B, 1), n, np.int32))
     oi, os_ = run_index(iq, iqs, ik, iks, nv, w.k)
     check_against_oracle(iq, iqs, ik, iks, nv, w.k, oi, os_)
+
+
+def test_index_topk_many_queries_causal():
+    """A causal prompt (n_valid = floor((t+1)/4)) with enough queries to take the query-parallel path."""
+    say("index many queries causal")
+    T, H_I, D_I, k = 4200, 8, 128, 128
+    N = 16384
+    iq, iqs = synth.mxfp4_normal((1, T, H_I, D_I), 131, DEV)
+    ik, iks = synth.mxfp4_normal((1, N, D_I), 132, DEV)
+    t0 = 4 * N - T                                   # last row sees all N entries
+    nv = up(((np.arange(T) + t0 + 1) // 4).astype(np.int32)[None])
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    rows = sorted(set(np.random.default_rng(0).integers(0, T, 40).tolist()) | {0, T - 1})
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, rows=rows)
