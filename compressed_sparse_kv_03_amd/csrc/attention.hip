@@ -23,6 +23,7 @@
 //   of the same K rows) read by ds_read_b64_tr_b16 as B.
 // Splits write unnormalised partial outputs with (max, sum) in fp32; a combine
 // kernel merges them (log-sum-exp merge). One split writes the output directly.
+#include <math.h>
 #include <type_traits>
 
 #include "common.cuh"
@@ -35,6 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTK = 32;            // keys per LDS tile
+constexpr int kMaxRopePairs = 64;  // d_rope <= 128
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -61,6 +63,7 @@ struct AttnArgs {
   float* out_lse;           // [nq, H]
   float* part_o;            // [nq, n_splits, H, d_v]
   float* part_ml;           // [nq, n_splits, H, 2]
+  double inv_freq[kMaxRopePairs];  // RoPE frequencies base^(-2i/d_rope), formed on the host in fp64
 };
 
 // Per query: entry-key count, window start position and count.
@@ -91,29 +94,40 @@ __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
 }
 
 constexpr int kMaxSplitIdx = 1024;  // top-k slots staged per split (CSA)
+constexpr float kRescaleSlack = 8.f; // log2 units the running max may run ahead of the exponent base
 
-template <int KD, int NV, int NW>
+// LDS layout. Key rows have a pitch of D + 16 bf16 (an odd multiple of 8 dwords): the
+// QK operand reads (16 rows x 16 B per lane group) and the transposed PV reads (16 rows
+// x 8 B) then spread evenly over the 64 banks. P^T rows are 16 heads (8 dwords) wide.
+//
+// Work split. A workgroup has HG head groups of 16 heads and two waves per head group
+// (2*HG waves, two per SIMD when HG = 4). Wave (hg, hf) computes S for its head group
+// and keys [16hf, 16hf+16) of the 32-key tile; the two waves share the per-row maximum
+// through LDS so that both use the same exponent base, each writes its half of P^T, and
+// then each computes O += P V for the whole tile but only dims [hf*d_v/2, (hf+1)*d_v/2).
+template <int KD, int NV, int HG>
 struct AttnSmem {
-  uint16_t kt[kTK][KD * 32 + 8];  // key rows (bf16), padded
+  __align__(16) uint16_t kt[kTK][KD * 32 + 16];        // key rows (bf16)
+  __align__(16) uint16_t pt[HG][kTK][16];              // P^T per head group: [key][head]
+  __align__(16) uint16_t qr[HG * 16][kMaxRopePairs * 2 + 8];  // rotated query dims
+  float xmax[2][HG][16];                               // per-half row maxima of the tile
   float kscale[kTK];              // per-key logit multiplier (log2 domain), -inf = masked
   float kvscale[kTK];             // per-key value multiplier (fp8 entry scale, else 1)
-  uint16_t pt[NW][kTK][16 + 4];   // P^T per wave: [key][head]
-  double inv_freq[KD * 16];       // RoPE frequencies (d_rope/2 <= D/2)
+  double inv_freq[kMaxRopePairs];
   int sidx[kMaxSplitIdx];         // this split's top-k slots (CSA)
 };
 
 // Rotate 8 consecutive bf16 dims (4 RoPE pairs starting at pair0) to position pos. The angle is
 // formed and reduced modulo 2*pi in fp64 (positions reach 2^20), then rotated in fp32.
-// Out of line so that callers' unrolled register arrays keep constant indices.
-__device__ __noinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_freq, int pair0) {
+__device__ __forceinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_freq, int pair0) {
   float f[8];
   unpack8(v, f);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     double ang = (double)pos * inv_freq[pair0 + p];
     ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
+    const float af = (float)ang;  // |af| <= pi
+    const float sn = __sinf(af), cs = __cosf(af);
     const float u0 = f[2 * p], u1 = f[2 * p + 1];
     f[2 * p] = u0 * cs - u1 * sn;
     f[2 * p + 1] = u0 * sn + u1 * cs;
@@ -124,22 +138,22 @@ __device__ __noinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_freq
 // One tile's raw bytes in registers: every thread's chunks are loaded with independent
 // loads (issued back to back, consumed one tile later), so a tile costs one memory latency.
 // Entry tiles of an fp8 cache hold 8 bytes per 16-byte bf16 chunk; bf16 rows hold 16.
-template <int KD, int NW, bool NARROW>
+template <int KD, int HG, bool NARROW>
 struct TileRegs {
   static constexpr int CPR = KD * 4;                      // 16-byte bf16 chunks per row
-  static constexpr int NT = NW * kWave;
+  static constexpr int NT = 2 * HG * kWave;
   static constexpr int ITERS = (kTK * CPR + NT - 1) / NT;
   typename std::conditional<NARROW, uint2, uint4>::type v[ITERS];
   float sc;
 };
 
 // Entry tiles: keys [key0, key_end) all below n_c.
-template <int KD, int NV, int NW, bool FP8>
-__device__ __forceinline__ void entry_load(const AttnArgs& a, int qi, int key0, int key_end, int key_begin,
-                                           const AttnSmem<KD, NV, NW>& sm, TileRegs<KD, NW, FP8>& R) {
-  using TR = TileRegs<KD, NW, FP8>;
+template <int KD, int NV, int HG, bool FP8>
+__device__ __forceinline__ void entry_load(const AttnArgs& a, const void* cbase, const float* sbase, int key0,
+                                           int key_end, int key_begin, const AttnSmem<KD, NV, HG>& sm,
+                                           TileRegs<KD, HG, FP8>& R) {
+  using TR = TileRegs<KD, HG, FP8>;
   constexpr int D = KD * 32;
-  const int64_t seq = (int64_t)(a.ckv_seq ? qi : 0) * a.ckv_seq;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
     const int c = threadIdx.x + j * TR::NT;
@@ -149,26 +163,25 @@ __device__ __forceinline__ void entry_load(const AttnArgs& a, int qi, int key0, 
     if constexpr (FP8) {
       R.v[j] = make_uint2(0, 0);
       if (idx >= 0)
-        R.v[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.ckv) + (seq + idx) * D + ch * 8);
+        R.v[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(cbase) + (int64_t)idx * D + ch * 8);
     } else {
       R.v[j] = make_uint4(0, 0, 0, 0);
       if (idx >= 0)
-        R.v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.ckv) + (seq + idx) * D + ch * 8);
+        R.v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cbase) + (int64_t)idx * D + ch * 8);
     }
   }
-  R.sc = 0.f;
+  R.sc = -1.f;  // masked
   if (threadIdx.x < kTK) {
     const int key = key0 + threadIdx.x;
     const int idx = key < key_end ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
-    if (idx >= 0) R.sc = FP8 ? a.ckv_scale[seq + idx] : 1.f;
-    if (idx < 0) R.sc = -1.f;  // masked
+    if (idx >= 0) R.sc = FP8 ? sbase[idx] : 1.f;
   }
 }
 
-template <int KD, int NV, int NW, bool FP8>
-__device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD, NV, NW>& sm,
-                                            const TileRegs<KD, NW, FP8>& R) {
-  using TR = TileRegs<KD, NW, FP8>;
+template <int KD, int NV, int HG, bool FP8>
+__device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD, NV, HG>& sm,
+                                            const TileRegs<KD, HG, FP8>& R) {
+  using TR = TileRegs<KD, HG, FP8>;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
     const int c = threadIdx.x + j * TR::NT;
@@ -194,11 +207,11 @@ __device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD, NV, 
   }
 }
 
-// Window tiles: keys [key0, key_end) all at or above n_c (raw bf16 tokens, rotated when stored).
-template <int KD, int NV, int NW>
+// Window tiles: keys [key0, key_end) all at or above n_c (raw bf16 tokens, rotated in LDS).
+template <int KD, int NV, int HG>
 __device__ __forceinline__ void window_load(const AttnArgs& a, int qi, const KeySpace& ks, int key0, int key_end,
-                                            TileRegs<KD, NW, false>& R) {
-  using TR = TileRegs<KD, NW, false>;
+                                            TileRegs<KD, HG, false>& R) {
+  using TR = TileRegs<KD, HG, false>;
   constexpr int D = KD * 32;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
@@ -215,137 +228,152 @@ __device__ __forceinline__ void window_load(const AttnArgs& a, int qi, const Key
   R.sc = 0.f;
 }
 
-template <int KD, int NV, int NW>
+template <int KD, int NV, int HG>
 __device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, int key_end,
-                                             AttnSmem<KD, NV, NW>& sm, const TileRegs<KD, NW, false>& R) {
-  using TR = TileRegs<KD, NW, false>;
+                                             AttnSmem<KD, NV, HG>& sm, const TileRegs<KD, HG, false>& R) {
+  using TR = TileRegs<KD, HG, false>;
   constexpr int D = KD * 32;
-  const int rope0 = D - a.d_rope;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
     const int c = threadIdx.x + j * TR::NT;
     const int r = c / TR::CPR, ch = c - r * TR::CPR;
     if (c >= kTK * TR::CPR) continue;
-    const int key = key0 + r;
-    uint4 v = R.v[j];
-    if (key < key_end && 8 * ch >= rope0) v = rope8(v, ks.w0 + (key - ks.n_c), sm.inv_freq, (8 * ch - rope0) >> 1);
-    *reinterpret_cast<uint4*>(&sm.kt[r][ch * 8]) = v;
+    *reinterpret_cast<uint4*>(&sm.kt[r][ch * 8]) = R.v[j];
   }
   if (threadIdx.x < kTK) {
     const bool ok = key0 + (int)threadIdx.x < key_end;
     sm.kscale[threadIdx.x] = ok ? a.scale_log2 : -INFINITY;
     sm.kvscale[threadIdx.x] = ok ? 1.f : 0.f;
   }
+  __syncthreads();
+  // rotate the last d_rope dims in place: kTK rows x d_rope/8 chunks spread over the threads
+  const int rc = a.d_rope >> 3;
+  const int rope0 = D - a.d_rope;
+  for (int c = threadIdx.x; c < kTK * rc; c += TR::NT) {
+    const int r = c / rc, ch = c - r * rc;
+    const int key = key0 + r;
+    if (key < key_end) {
+      uint4* p = reinterpret_cast<uint4*>(&sm.kt[r][rope0 + 8 * ch]);
+      *p = rope8(*p, ks.w0 + (key - ks.n_c), sm.inv_freq, 4 * ch);
+    }
+  }
 }
 
-// Per-wave attention state.
-template <int KD, int NV>
+// Per-wave attention state. m is the exponent base of the running sums; it may lag the true
+// running max by up to kRescaleSlack (p <= 2^8), so O is rescaled only when a logit exceeds it
+// by more than that. l holds this wave's key half only; the halves are added at the end.
+template <int KD, int NVH>
 struct WaveState {
   uint4 qa[KD];
-  f32x4 o[NV];
+  f32x4 o[NVH];
   float m[4], l[4];
 };
 
-// One staged tile: S = Q K^T on bf16 MFMA, online softmax, O += P V.
-template <int KD, int NV, int NW>
-__device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, NW>& sm, WaveState<KD, NV>& st) {
+// Key row of k-slot block `half` (0: slots 0-3, 1: slots 4-7) of lane group g, lane col:
+// group g's 8 k-slots are rows 4g..4g+3 and 16+4g..16+4g+3.
+__device__ __forceinline__ int pv_row(int g, int col, int half) { return 16 * half + 4 * g + (col >> 2); }
+
+// One staged tile for wave (hg, hf). Ends with the workgroup barrier that makes P^T visible.
+template <int KD, int NV, int HG>
+__device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, HG>& sm, WaveState<KD, NV / 2>& st, int hg, int hf) {
+  constexpr int NVH = NV / 2;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
-  // S[head 4g+r][key col (+16)] = q_rot . k; K operands read in batches ahead of the MFMAs
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  const int krow = 16 * hf + col;
+  // S[head 4g+r][key krow] = q_rot . k; K operands read in batches ahead of the MFMAs
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
   constexpr int BQ = 6;
 #pragma unroll
   for (int s = 0; s < KD; s += BQ) {
-    uint4 k0[BQ], k1[BQ];
+    uint4 kv[BQ];
 #pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      if (s + u < KD) {
-        k0[u] = *reinterpret_cast<const uint4*>(&sm.kt[col][32 * (s + u) + 8 * g]);
-        k1[u] = *reinterpret_cast<const uint4*>(&sm.kt[16 + col][32 * (s + u) + 8 * g]);
-      }
-    }
+    for (int u = 0; u < BQ; ++u)
+      if (s + u < KD) kv[u] = *reinterpret_cast<const uint4*>(&sm.kt[krow][32 * (s + u) + 8 * g]);
 #pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      if (s + u < KD) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, st.qa[s + u]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k0[u]), s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, k1[u]), s1, 0, 0, 0);
-      }
-    }
+    for (int u = 0; u < BQ; ++u)
+      if (s + u < KD)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.qa[s + u]),
+                                                       __builtin_bit_cast(bf16x8, kv[u]), sacc, 0, 0, 0);
   }
-  const float c0 = sm.kscale[col], c1 = sm.kscale[16 + col];
-  const float v0 = sm.kvscale[col], v1 = sm.kvscale[16 + col];
-  float alpha[4];
-  bool moved = false;
+  const float ck = sm.kscale[krow], vk = sm.kvscale[krow];
+  float x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float x0 = c0 == -INFINITY ? -INFINITY : s0[r] * c0;
-    const float x1 = c1 == -INFINITY ? -INFINITY : s1[r] * c1;
-    float mx = fmaxf(x0, x1);
+    x[r] = ck == -INFINITY ? -INFINITY : sacc[r] * ck;
+    float m_ = x[r];
 #pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
-    const float mnew = fmaxf(st.m[r], mx);
-    const float base = mnew == -INFINITY ? 0.f : mnew;
-    const float p0 = exp2f(x0 - base), p1 = exp2f(x1 - base);
-    float ps = p0 + p1;
-#pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
-    alpha[r] = exp2f(st.m[r] - base);
-    moved |= mnew != st.m[r];
-    st.l[r] = st.l[r] * alpha[r] + ps;
-    st.m[r] = mnew;
-    s0[r] = p0 * v0;  // value-side scale folded into P
-    s1[r] = p1 * v1;
+    for (int o2 = 8; o2 > 0; o2 >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o2, kWave));
+    if (col == 0) sm.xmax[hf][hg][4 * g + r] = m_;
   }
-  // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
-  {
-    uint2 w0, w1;
-    w0.x = pack_bf16x2(s0[0], s0[1]);
-    w0.y = pack_bf16x2(s0[2], s0[3]);
-    w1.x = pack_bf16x2(s1[0], s1[1]);
-    w1.y = pack_bf16x2(s1[2], s1[3]);
-    *reinterpret_cast<uint2*>(&sm.pt[wave][col][4 * g]) = w0;
-    *reinterpret_cast<uint2*>(&sm.pt[wave][16 + col][4 * g]) = w1;
-  }
-  // rescale O only when some row's running max moved in this wave
-  if (__ballot(moved)) {
+  __syncthreads();
+  bool need = false;
+  float mx[4];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
+  for (int r = 0; r < 4; ++r) {
+    mx[r] = fmaxf(sm.xmax[0][hg][4 * g + r], sm.xmax[1][hg][4 * g + r]);
+    need |= mx[r] > st.m[r] + kRescaleSlack;
+  }
+  if (__ballot(need)) {  // rare after the first tile: move the exponent base up, rescale O and l
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mnew = mx[r] > st.m[r] + kRescaleSlack ? mx[r] : st.m[r];
+      alpha[r] = st.m[r] == -INFINITY ? 0.f : exp2f(st.m[r] - mnew);
+      st.l[r] *= alpha[r];
+      st.m[r] = mnew;
+    }
+#pragma unroll
+    for (int n = 0; n < NVH; ++n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) st.o[n][r] *= alpha[r];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P^T writes done (wave-local data)
-  __builtin_amdgcn_wave_barrier();
-  // A = P[head col][keys 8g..8g+7] via two transposed reads of the [key][head] block
+  float pv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float base = st.m[r] == -INFINITY ? 0.f : st.m[r];
+    const float p = exp2f(x[r] - base);
+    float ps = p;
+#pragma unroll
+    for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
+    st.l[r] += ps;
+    pv[r] = p * vk;  // value-side scale folded into P
+  }
+  // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
+  {
+    uint2 w;
+    w.x = pack_bf16x2(pv[0], pv[1]);
+    w.y = pack_bf16x2(pv[2], pv[3]);
+    *reinterpret_cast<uint2*>(&sm.pt[hg][krow][4 * g]) = w;
+  }
+  __syncthreads();
+  // A = P[head col][k-slots of group g] via two transposed reads of the [key][head] block
   bf16x8 pa;
   {
-    const int kr = 8 * g + (col >> 2), hc = 4 * (col & 3);
+    const int hc = 4 * (col & 3);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr][hc]));
+        (__attribute__((address_space(3))) i16x4*)(&sm.pt[hg][pv_row(g, col, 0)][hc]));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(&sm.pt[wave][kr + 4][hc]));
+        (__attribute__((address_space(3))) i16x4*)(&sm.pt[hg][pv_row(g, col, 1)][hc]));
     pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
-  // O[head 4g+r][dim 16n+col] += P V, V = key rows' first d_v dims, read in batches
+  // O[head 4g+r][dim 16(n + hf*NVH) + col] += P V over the whole tile, read in batches
   constexpr int BV = 8;
-  const int kr = 8 * g + (col >> 2);
+  const int r0 = pv_row(g, col, 0), r1 = pv_row(g, col, 1);
 #pragma unroll
-  for (int n = 0; n < NV; n += BV) {
+  for (int n = 0; n < NVH; n += BV) {
     i16x4 lo[BV], hi[BV];
 #pragma unroll
     for (int u = 0; u < BV; ++u) {
-      if (n + u < NV) {
-        const int dc = 16 * (n + u) + 4 * (col & 3);
-        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(&sm.kt[kr][dc]));
-        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(&sm.kt[kr + 4][dc]));
+      if (n + u < NVH) {
+        const int dc = 16 * (n + u + hf * NVH) + 4 * (col & 3);
+        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(&sm.kt[r0][dc]));
+        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(&sm.kt[r1][dc]));
       }
     }
 #pragma unroll
     for (int u = 0; u < BV; ++u) {
-      if (n + u < NV) {
+      if (n + u < NVH) {
         const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[u], hi[u], 0, 1, 2, 3, 4, 5, 6, 7));
         st.o[n + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, st.o[n + u], 0, 0, 0);
       }
@@ -353,21 +381,24 @@ __device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, NW>& sm, WaveState
   }
 }
 
-template <int KD, int NV, int NW, bool FP8>
-__global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
+template <int KD, int NV, int HG, bool FP8>
+__global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
   constexpr int D = KD * 32;
-  __shared__ AttnSmem<KD, NV, NW> sm;
+  constexpr int NT = 2 * HG * kWave;
+  constexpr int NVH = NV / 2;
+  __shared__ AttnSmem<KD, NV, HG> sm;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
+  const int hgw = wave % HG, hf = wave / HG;  // head group and key/dim half of this wave
   const int g = lane >> 4, col = lane & 15;
   const int qi = blockIdx.x;
-  const int head_groups = (a.H + 16 * NW - 1) / (16 * NW);
+  const int head_groups = (a.H + 16 * HG - 1) / (16 * HG);
   const int split = blockIdx.y / head_groups;
-  const int hg = blockIdx.y - split * head_groups;
-  const int h0 = hg * 16 * NW + wave * 16;  // this wave's first head
+  const int wg_hg = blockIdx.y - split * head_groups;
+  const int h0 = wg_hg * 16 * HG + hgw * 16;  // this wave's first head
+  const int rope0 = D - a.d_rope;
 
-  for (int i = threadIdx.x; i < a.d_rope / 2; i += NW * kWave)
-    sm.inv_freq[i] = pow((double)a.rope_base, -2.0 * (double)i / (double)a.d_rope);
+  for (int i = threadIdx.x; i < a.d_rope / 2; i += NT) sm.inv_freq[i] = a.inv_freq[i];
 
   const KeySpace ks = key_space(a, qi);
   const int n_keys = ks.n_c + ks.n_w;
@@ -376,27 +407,40 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
   const int e_end = min(key_end, ks.n_c);  // entry keys [key_begin, e_end), window keys after
   if (a.topk) {
     const int n_sel = e_end - key_begin;
-    for (int i = threadIdx.x; i < n_sel; i += NW * kWave) sm.sidx[i] = a.topk[(int64_t)qi * a.k + key_begin + i];
+    for (int i = threadIdx.x; i < n_sel; i += NT) sm.sidx[i] = a.topk[(int64_t)qi * a.k + key_begin + i];
   }
+  __syncthreads();  // inv_freq and sidx ready
+  // rotated query dims -> LDS (each thread rotates whole 8-dim chunks of the WG's heads)
+  {
+    const int rc = a.d_rope / 8;  // rotated chunks per head
+    for (int c = threadIdx.x; c < HG * 16 * rc; c += NT) {
+      const int hl = c / rc, ch = c - hl * rc;
+      const int h = wg_hg * 16 * HG + hl;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h < a.H) {
+        v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + rope0 + 8 * ch);
+        v = rope8(v, ks.t, sm.inv_freq, 4 * ch);
+      }
+      *reinterpret_cast<uint4*>(&sm.qr[hl][8 * ch]) = v;
+    }
+  }
+  __syncthreads();
 
-  WaveState<KD, NV> st;
+  WaveState<KD, NVH> st;
   {
     const int h = h0 + col;
-    const int rope0 = D - a.d_rope;
-#pragma unroll
-    for (int s = 0; s < KD; ++s) {
-      st.qa[s] = make_uint4(0, 0, 0, 0);
-      if (h < a.H) st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g);
-    }
-    __syncthreads();  // inv_freq and sidx ready
 #pragma unroll
     for (int s = 0; s < KD; ++s) {
       const int d0 = 32 * s + 8 * g;
-      if (d0 >= rope0) st.qa[s] = rope8(st.qa[s], ks.t, sm.inv_freq, (d0 - rope0) >> 1);
+      st.qa[s] = make_uint4(0, 0, 0, 0);
+      if (d0 >= rope0)
+        st.qa[s] = *reinterpret_cast<const uint4*>(&sm.qr[hgw * 16 + col][d0 - rope0]);
+      else if (h < a.H)
+        st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + d0);
     }
   }
 #pragma unroll
-  for (int n = 0; n < NV; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NVH; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     st.m[r] = -INFINITY;
@@ -405,52 +449,65 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs a) {
 
   // phase 1: compressed entries
   if (key_begin < e_end) {
-    TileRegs<KD, NW, FP8> R;
-    entry_load<KD, NV, NW, FP8>(a, qi, key_begin, e_end, key_begin, sm, R);
+    const int64_t seq = (int64_t)(a.ckv_seq ? qi : 0) * a.ckv_seq;
+    const void* cbase = FP8 ? (const void*)(reinterpret_cast<const uint8_t*>(a.ckv) + seq * D)
+                            : (const void*)(reinterpret_cast<const uint16_t*>(a.ckv) + seq * D);
+    const float* sbase = a.ckv_scale ? a.ckv_scale + seq : nullptr;
+    TileRegs<KD, HG, FP8> R;
+    entry_load<KD, NV, HG, FP8>(a, cbase, sbase, key_begin, e_end, key_begin, sm, R);
     for (int key0 = key_begin; key0 < e_end; key0 += kTK) {
       __syncthreads();
-      entry_store<KD, NV, NW, FP8>(a, sm, R);
+      entry_store<KD, NV, HG, FP8>(a, sm, R);
       __syncthreads();
-      if (key0 + kTK < e_end) entry_load<KD, NV, NW, FP8>(a, qi, key0 + kTK, e_end, key_begin, sm, R);
-      tile_compute<KD, NV, NW>(sm, st);
+      if (key0 + kTK < e_end) entry_load<KD, NV, HG, FP8>(a, cbase, sbase, key0 + kTK, e_end, key_begin, sm, R);
+      tile_compute<KD, NV, HG>(sm, st, hgw, hf);
     }
   }
   // phase 2: window tokens
   const int w_begin = max(key_begin, ks.n_c);
   if (w_begin < key_end) {
-    TileRegs<KD, NW, false> R;
-    window_load<KD, NV, NW>(a, qi, ks, w_begin, key_end, R);
+    TileRegs<KD, HG, false> R;
+    window_load<KD, NV, HG>(a, qi, ks, w_begin, key_end, R);
     for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
       __syncthreads();
-      window_store<KD, NV, NW>(a, ks, key0, key_end, sm, R);
+      window_store<KD, NV, HG>(a, ks, key0, key_end, sm, R);
       __syncthreads();
-      if (key0 + kTK < key_end) window_load<KD, NV, NW>(a, qi, ks, key0 + kTK, key_end, R);
-      tile_compute<KD, NV, NW>(sm, st);
+      if (key0 + kTK < key_end) window_load<KD, NV, HG>(a, qi, ks, key0 + kTK, key_end, R);
+      tile_compute<KD, NV, HG>(sm, st, hgw, hf);
     }
   }
 
-  // write: direct (one split) or partial
+  // combine the two key halves' sums: l = l_0 + l_1 (same exponent base m)
+  __syncthreads();
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.xmax[hf][hgw][4 * g + r] = st.l[r];
+  }
+  __syncthreads();
+  float lt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lt[r] = sm.xmax[0][hgw][4 * g + r] + sm.xmax[1][hgw][4 * g + r];
+
+  // write: direct (one split) or partial; this wave owns dims [hf*d_v/2, (hf+1)*d_v/2)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = h0 + 4 * g + r;
     if (h >= a.H) continue;
     if (a.n_splits == 1) {
-      const float inv = st.l[r] > 0.f ? 1.f / st.l[r] : 0.f;
-      uint16_t* dst = a.out + ((int64_t)qi * a.H + h) * a.d_v;
+      const float inv = lt[r] > 0.f ? 1.f / lt[r] : 0.f;
+      uint16_t* dst = a.out + ((int64_t)qi * a.H + h) * a.d_v + hf * 16 * NVH;
 #pragma unroll
-      for (int n = 0; n < NV; ++n)
-        if (16 * n < a.d_v) dst[16 * n + col] = (uint16_t)f32_to_bf16_rne(st.o[n][r] * inv);
-      if (a.out_lse && col == 0)
-        a.out_lse[(int64_t)qi * a.H + h] = st.l[r] > 0.f ? (st.m[r] + log2f(st.l[r])) * kLn2 : -INFINITY;
+      for (int n = 0; n < NVH; ++n) dst[16 * n + col] = (uint16_t)f32_to_bf16_rne(st.o[n][r] * inv);
+      if (a.out_lse && col == 0 && hf == 0)
+        a.out_lse[(int64_t)qi * a.H + h] = lt[r] > 0.f ? (st.m[r] + log2f(lt[r])) * kLn2 : -INFINITY;
     } else {
       const int64_t pidx = ((int64_t)qi * a.n_splits + split) * a.H + h;
-      float* dst = a.part_o + pidx * a.d_v;
+      float* dst = a.part_o + pidx * a.d_v + hf * 16 * NVH;
 #pragma unroll
-      for (int n = 0; n < NV; ++n)
-        if (16 * n < a.d_v) dst[16 * n + col] = st.o[n][r];
-      if (col == 0) {
+      for (int n = 0; n < NVH; ++n) dst[16 * n + col] = st.o[n][r];
+      if (col == 0 && hf == 0) {
         a.part_ml[pidx * 2 + 0] = st.m[r];
-        a.part_ml[pidx * 2 + 1] = st.l[r];
+        a.part_ml[pidx * 2 + 1] = lt[r];
       }
     }
   }
@@ -558,8 +615,8 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
 typedef void (*AttnKernel)(AttnArgs);
 
 template <int KD, int NV, bool FP8>
-static AttnKernel pick_nw(int nw) {
-  switch (nw) {
+static AttnKernel pick_nw(int hg) {
+  switch (hg) {
     case 1: return attn_kernel<KD, NV, 1, FP8>;
     case 2: return attn_kernel<KD, NV, 2, FP8>;
     case 3: return attn_kernel<KD, NV, 3, FP8>;
@@ -587,14 +644,16 @@ static int check_common(const char* name, int H, int D, int d_rope, int d_v, int
   CSKV_REQUIRE(d_v % 16 == 0 && d_v >= 16 && d_v <= D, CSKV_EINVAL, "%s: d_v=%d", name, d_v);
   CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL, "%s: d_rope=%d", name, d_rope);
   CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
+  CSKV_REQUIRE(d_rope <= 2 * kMaxRopePairs, CSKV_ENOTSUP, "%s: d_rope=%d > %d", name, d_rope, 2 * kMaxRopePairs);
   CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3, CSKV_EINVAL, "%s: ckv_dtype=%d", name, ckv_dtype);
-  CSKV_REQUIRE(d_v % 64 == 0 || d_v == 32, CSKV_ENOTSUP, "%s: d_v=%d", name, d_v);
+  CSKV_REQUIRE(d_v % 32 == 0, CSKV_ENOTSUP, "%s: d_v=%d must be a multiple of 32", name, d_v);
   CSKV_REQUIRE(pick_kernel(D, d_v, 1, false) != nullptr, CSKV_ENOTSUP,
                "%s: (D, d_v) = (%d, %d) not compiled (576/512, 128/128, 256/128, 64/32)", name, D, d_v);
   return CSKV_OK;
 }
 
 static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws, size_t ws_bytes, hipStream_t s) {
+  for (int i = 0; i < a.d_rope / 2; ++i) a.inv_freq[i] = pow((double)a.rope_base, -2.0 * (double)i / (double)a.d_rope);
   CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "%s: workspace %zu < %zu bytes", name,
                ws_bytes, p.ws);
   a.n_splits = p.n_splits;
@@ -605,7 +664,7 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   }
   const int head_groups = (a.H + 16 * p.nw - 1) / (16 * p.nw);
   AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw, a.fp8 != 0);
-  hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(p.nw * kWave), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(2 * p.nw * kWave), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {
     hipLaunchKernelGGL(attn_combine_kernel, dim3(a.nq, a.H), dim3(128), 0, s, a);

@@ -145,7 +145,7 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * topk_idx [B, k] int32 (each -1 or in [0, n_entries[b])) or NULL
  * win [B, W, D] bf16 ring of raw tokens; out [B, H, d_v] bf16; out_lse [B, H] fp32 or NULL
  * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
- * d_rope % 8 == 0, d_rope <= D, 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32.
+ * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32.
  */
 CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
                        const float* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
