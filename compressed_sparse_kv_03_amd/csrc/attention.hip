@@ -300,9 +300,7 @@ __device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, HG>& sm, WaveState
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     x[r] = ck == -INFINITY ? -INFINITY : sacc[r] * ck;
-    float m_ = x[r];
-#pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o2, kWave));
+    const float m_ = row16_max(x[r]);
     if (col == 0) sm.xmax[hf][hg][4 * g + r] = m_;
   }
   __syncthreads();
@@ -333,10 +331,7 @@ __device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, HG>& sm, WaveState
   for (int r = 0; r < 4; ++r) {
     const float base = st.m[r] == -INFINITY ? 0.f : st.m[r];
     const float p = exp2f(x[r] - base);
-    float ps = p;
-#pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, kWave);
-    st.l[r] += ps;
+    st.l[r] += row16_sum(p);
     pv[r] = p * vk;  // value-side scale folded into P
   }
   // P^T to LDS: [key][head], 4 consecutive heads per 8-byte write
@@ -588,13 +583,13 @@ struct AttnPlan {
 
 static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
   AttnPlan p;
-  p.nw = H >= 64 ? 4 : (H + 15) / 16;
+  p.nw = H >= 64 ? 4 : (H + 15) / 16;  // head groups of 16 per workgroup (two waves each)
   const int head_groups = (H + 16 * p.nw - 1) / (16 * p.nw);
   const int64_t base = (int64_t)nq * head_groups;
-  // aim for ~512 workgroups with at least 2 tiles (64 keys) per split; a split holds at
-  // most kMaxSplitIdx keys, and there are at most kMaxSplits splits
-  int splits = (int)((512 + base - 1) / base);
-  const int max_splits = (max_keys + 2 * kTK - 1) / (2 * kTK);
+  // one workgroup per CU (256) when the queries alone do not fill the GPU; a split holds at
+  // least one tile and at most kMaxSplitIdx keys, and there are at most kMaxSplits splits
+  int splits = (int)((256 + base - 1) / base);
+  const int max_splits = (max_keys + kTK - 1) / kTK;
   if (splits > max_splits) splits = max_splits;
   const int min_splits = (max_keys + kMaxSplitIdx - 1) / kMaxSplitIdx;
   if (splits < min_splits) splits = min_splits;

@@ -71,6 +71,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Reductions over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane gets the
+// result. quad_perm [1,0,3,2] and [2,3,0,1] combine within quads, row_ror 4 and 8 across them.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  const int x = __builtin_bit_cast(int, v);
+  switch (ctrl) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f(v, 0));
+  v = fmaxf(v, dpp_f(v, 1));
+  v = fmaxf(v, dpp_f(v, 2));
+  return fmaxf(v, dpp_f(v, 3));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f(v, 0);
+  v += dpp_f(v, 1);
+  v += dpp_f(v, 2);
+  return v + dpp_f(v, 3);
+}
+
 // ---------------------------------------------------------------- RoPE
 // Angle p * base^(-2i/d_rope), formed in fp64 and reduced to [-pi, pi] before
 // the fp32 rotation (positions reach 2^20, where an fp32 angle would be off by
