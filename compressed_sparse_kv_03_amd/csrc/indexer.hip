@@ -71,7 +71,7 @@ template <int KS>
 __device__ __forceinline__ void score_range(const IndexArgs& a, int b, int e_begin, int e_end,
                                             const uint4* qa, const int* qs, const float* hw,
                                             uint64_t* keys) {
-  constexpr int U = KS == 1 ? 8 : (KS == 2 ? 4 : 2);
+  constexpr int U = KS == 1 ? 16 : (KS == 2 ? 8 : 4);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int kb = lane >> 4, col = lane & 15;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kIdxNT) void index_merge_kernel(IndexArgs a) {
 // would beat that key).
 constexpr int kBins = 4096;     // 12-bit bins of the ordered score
 constexpr int kSubBins = 256;   // next 8 bits
-constexpr int kChunkA = 2048;   // entries per workgroup in kernel A
+constexpr int kChunkA = 4096;   // entries per workgroup in kernel A
 constexpr int kCapF = 2048;     // candidates kernel C sorts directly
 
 struct DecodeArgs {
@@ -241,10 +241,11 @@ __device__ __forceinline__ uint32_t key_bin(uint64_t key) { return (uint32_t)(ke
 __device__ __forceinline__ uint32_t key_bin20(uint64_t key) { return (uint32_t)(key >> 44); }     // 20 bits
 
 // Highest bin b (scanning from the top) whose cumulative count reaches kk; returns b and the
-// count strictly above it in *above. NB is a multiple of kIdxNT. kk >= 1 and total >= kk.
-template <int NB>
+// count strictly above it in *above. NB is a multiple of NT. kk >= 1 and total >= kk.
+// scratch holds at least 34 ints.
+template <int NB, int NT = kIdxNT>
 __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int* scratch) {
-  constexpr int PER = NB / kIdxNT;
+  constexpr int PER = NB / NT;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
   // thread t owns bins [NB - PER*(t+1), NB - PER*t), i.e. the t-th slice from the top
   const int top = NB - PER * t;
@@ -269,16 +270,16 @@ __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int*
     for (int i = 1; i <= PER; ++i) {
       const int h = hist[top - i];
       if (c + h >= kk) {
-        scratch[8] = top - i;
-        scratch[9] = c;
+        scratch[32] = top - i;
+        scratch[33] = c;
         break;
       }
       c += h;
     }
   }
   __syncthreads();
-  *above = scratch[9];
-  return scratch[8];
+  *above = scratch[33];
+  return scratch[32];
 }
 
 // Wave-aggregated append of the keys passing `p` to dst[*cnt ...] (LDS counter).
@@ -305,7 +306,7 @@ struct ASmem {
   uint64_t keys[kChunkA];
   uint32_t hist[kBins];
   uint32_t sub[kSubBins];
-  int scratch[16];
+  int scratch[34];
   int cnt;
   int base;
 };
@@ -366,16 +367,18 @@ __global__ __launch_bounds__(kIdxNT) void index_score_kernel(DecodeArgs d) {
   }
 }
 
+constexpr int kFinNT = 1024;   // threads of the final per-query kernel
+
 struct CSmem {
   uint32_t hist[kBins];
   uint64_t buf[kCapF];
   uint64_t keys[1024 + kSub];  // slow path: running winners + one sub-chunk
   SelectScratch sc;
-  int scratch[16];
+  int scratch[34];
   int cnt;
 };
 
-__global__ __launch_bounds__(kIdxNT) void index_final_kernel(DecodeArgs d) {
+__global__ __launch_bounds__(kFinNT) void index_final_kernel(DecodeArgs d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   CSmem& sm = *reinterpret_cast<CSmem*>(smem_raw);
   const IndexArgs& a = d.a;
@@ -384,78 +387,79 @@ __global__ __launch_bounds__(kIdxNT) void index_final_kernel(DecodeArgs d) {
   const int kk = min(a.k, nv);
   int32_t* oi = a.out_idx + (int64_t)q * a.k;
   float* os = a.out_score ? a.out_score + (int64_t)q * a.k : nullptr;
-  if (kk > 0) {
-    const uint32_t* gh = d.hist + (int64_t)q * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kIdxNT) sm.hist[i] = gh[i];
+  // slots >= kk are padding
+  for (int i = kk + threadIdx.x; i < a.k; i += kFinNT) {
+    oi[i] = -1;
+    if (os) os[i] = -INFINITY;
+  }
+  if (kk == 0) return;
+  const uint32_t* gh = d.hist + (int64_t)q * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kFinNT) sm.hist[i] = gh[i];
+  __syncthreads();
+  int above;
+  const int bp = find_threshold_bin<kBins, kFinNT>(sm.hist, kk, &above, sm.scratch);
+  int cstar = 0;
+  for (int i = threadIdx.x; i < kBins; i += kFinNT) cstar += i >= bp ? (int)sm.hist[i] : 0;
+  cstar = block_sum_int<kFinNT>(cstar, sm.sc.red);
+  const int n_cand = min((int)d.cnt[q], a.N_cap);
+  const uint64_t* cq = d.cand + (int64_t)q * a.N_cap;
+  if (cstar <= kCapF) {
+    if (threadIdx.x == 0) sm.cnt = 0;
     __syncthreads();
-    int above;
-    const int bp = find_threshold_bin<kBins>(sm.hist, kk, &above, sm.scratch);
-    int cstar = 0;
-    for (int i = threadIdx.x; i < kBins; i += kIdxNT) cstar += i >= bp ? (int)sm.hist[i] : 0;
-    cstar = block_sum_int<kIdxNT>(cstar, sm.sc.red);
-    const int n_cand = (int)d.cnt[q];
-    const uint64_t* cq = d.cand + (int64_t)q * a.N_cap;
-    if (cstar <= kCapF) {
-      if (threadIdx.x == 0) sm.cnt = 0;
-      __syncthreads();
-      // 16 independent loads in flight per thread, then filter
-      constexpr int U = 16;
-      for (int i0 = 0; i0 < n_cand; i0 += U * kIdxNT) {
-        uint64_t kv[U];
+    constexpr int U = 4;  // independent loads in flight per thread
+    for (int i0 = 0; i0 < n_cand; i0 += U * kFinNT) {
+      uint64_t kv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = i0 + u * kIdxNT + threadIdx.x;
-          kv[u] = i < n_cand ? cq[i] : 0;
-        }
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kFinNT + threadIdx.x;
+        kv[u] = i < n_cand ? cq[i] : 0;
+      }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = i0 + u * kIdxNT + threadIdx.x;
-          append_lds(i < n_cand && (int)key_bin(kv[u]) >= bp, kv[u], sm.buf, &sm.cnt, kCapF);
-        }
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kFinNT + threadIdx.x;
+        append_lds(i < n_cand && (int)key_bin(kv[u]) >= bp, kv[u], sm.buf, &sm.cnt, kCapF);
       }
-      __syncthreads();
-      const int c = min(sm.cnt, kCapF);
-      int P = 1;
-      while (P < c) P <<= 1;
-      for (int i = c + threadIdx.x; i < P; i += kIdxNT) sm.buf[i] = 0;
-      __syncthreads();
-      bitonic_sort_desc<kIdxNT>(sm.buf, P);
-    } else {
-      // many keys tie into the threshold bin: exact running top-k over the filtered candidates
-      int kept = 0;
-      for (int s0 = 0; s0 < n_cand; s0 += kSub) {
-        const int s1 = min(s0 + kSub, n_cand);
-        if (threadIdx.x == 0) sm.cnt = 0;
-        __syncthreads();
-        const int n_round = (s1 - s0 + kIdxNT - 1) / kIdxNT * kIdxNT;
-        for (int i = threadIdx.x; i < n_round; i += kIdxNT) {
-          const int j = s0 + i;
-          const uint64_t key = j < s1 ? cq[j] : 0;
-          append_lds(j < s1 && (int)key_bin(key) >= bp, key, sm.keys + kept, &sm.cnt, kSub);
-        }
-        __syncthreads();
-        const int nn = kept + sm.cnt;
-        if (nn > 0) {
-          const int k2 = min(kk, nn);
-          select_topk<kIdxNT, kCapF>(sm.keys, nn, k2, sm.buf, &sm.sc);
-          for (int i = threadIdx.x; i < k2; i += kIdxNT) sm.keys[i] = sm.buf[i];
-          __syncthreads();
-          kept = k2;
-        }
+    }
+    __syncthreads();
+    // rank selection: keys are distinct, so key i goes to slot #{keys greater than it}
+    const int c = min(sm.cnt, kCapF);
+    for (int i = threadIdx.x; i < c; i += kFinNT) {
+      const uint64_t key = sm.buf[i];
+      int rank = 0;
+      for (int j = 0; j < c; ++j) rank += sm.buf[j] > key;
+      if (rank < kk) {
+        oi[rank] = (int32_t)(~(uint32_t)key);
+        if (os) os[rank] = ordered_to_score((uint32_t)(key >> 32));
       }
-      for (int i = threadIdx.x; i < kept; i += kIdxNT) sm.buf[i] = sm.keys[i];
+    }
+    return;
+  }
+  // many keys tie into the threshold bin: exact running top-k over the filtered candidates
+  int kept = 0;
+  for (int s0 = 0; s0 < n_cand; s0 += kSub) {
+    const int s1 = min(s0 + kSub, n_cand);
+    if (threadIdx.x == 0) sm.cnt = 0;
+    __syncthreads();
+    const int n_round = (s1 - s0 + kFinNT - 1) / kFinNT * kFinNT;
+    for (int i = threadIdx.x; i < n_round; i += kFinNT) {
+      const int j = s0 + i;
+      const uint64_t key = j < s1 ? cq[j] : 0;
+      append_lds(j < s1 && (int)key_bin(key) >= bp, key, sm.keys + kept, &sm.cnt, kSub);
+    }
+    __syncthreads();
+    const int nn = kept + sm.cnt;
+    if (nn > 0) {
+      const int k2 = min(kk, nn);
+      select_topk<kFinNT, kCapF>(sm.keys, nn, k2, sm.buf, &sm.sc);
+      for (int i = threadIdx.x; i < k2; i += kFinNT) sm.keys[i] = sm.buf[i];
       __syncthreads();
+      kept = k2;
     }
   }
-  for (int i = threadIdx.x; i < a.k; i += kIdxNT) {
-    if (i < kk) {
-      const uint64_t key = sm.buf[i];
-      oi[i] = (int32_t)(~(uint32_t)key);
-      if (os) os[i] = ordered_to_score((uint32_t)(key >> 32));
-    } else {
-      oi[i] = -1;
-      if (os) os[i] = -INFINITY;
-    }
+  for (int i = threadIdx.x; i < kept; i += kFinNT) {
+    const uint64_t key = sm.keys[i];
+    oi[i] = (int32_t)(~(uint32_t)key);
+    if (os) os[i] = ordered_to_score((uint32_t)(key >> 32));
   }
 }
 
@@ -528,7 +532,7 @@ static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipS
   }
   const size_t smem = sizeof(CSmem);
   (void)hipFuncSetAttribute((const void*)index_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipLaunchKernelGGL(index_final_kernel, dim3(queries), dim3(kIdxNT), smem, s, d);
+  hipLaunchKernelGGL(index_final_kernel, dim3(queries), dim3(kFinNT), smem, s, d);
   return CSKV_OK;
 }
 
