@@ -113,3 +113,23 @@ def test_index_topk_many_queries_causal():
     oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
     rows = sorted(set(np.random.default_rng(0).integers(0, T, 40).tolist()) | {0, T - 1})
     check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, rows=rows)
+
+
+def test_index_topk_when_the_sample_overstates_the_top():
+    """Ten identical high-scoring keys sit on sampled entries (one at the start of each of the
+    first ten sampled runs): the sampled bound admits fewer than k keys, so the exact fallback
+    must produce the answer."""
+    say("index sampled-bound fallback")
+    B, H_I, D_I, k, N = 2, 8, 128, 128, 262144
+    iq, iqs = synth.mxfp4_normal((B, 1, H_I, D_I), 141, DEV)
+    ik, iks = synth.mxfp4_normal((B, N, D_I), 142, DEV)
+    stride = N // 128                                 # sampled runs of 16 start at g * N / 128
+    for b in range(B):
+        for i in range(10):
+            ik[b, i * stride] = iq[b, 0, 0]           # key = head-0 query codes: large positive dot
+            iks[b, i * stride] = iqs[b, 0, 0]
+    nv = up(np.full((B, 1), N, np.int32))
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_)
+    got = down(oi)[:, 0]
+    assert all(set(range(0, 10 * stride, stride)) <= set(got[b].tolist()) for b in range(B))
