@@ -76,7 +76,7 @@ __device__ __forceinline__ void score_range_to(const IndexArgs& a, int b, int e_
                                                uint8_t* wsc, Sink sink) {
   constexpr int U = UU ? UU : (KS == 1 ? 16 : (KS == 2 ? 8 : 4));
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
   const int kb = lane >> 4, col = lane & 15;
   const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
   const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
@@ -135,6 +135,96 @@ __device__ __forceinline__ void score_range_to(const IndexArgs& a, int b, int e_
       sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
     }
     __builtin_amdgcn_wave_barrier();  // slot reads done before the next batch overwrites it
+  }
+}
+
+// Streaming form of the scoring loop (decode kernel A): each wave owns groups of 16 entries
+// in batches of U groups and keeps two batches in flight (the next batch is requested before
+// the current one is scored). Every load is unconditional, from a clamped address (rows past
+// the range repeat its last row and are masked), so that the loads issue back to back and the
+// loop carries no branch. A lane's E8M0 scale byte comes from the aligned dword holding it
+// (the scale array is 4-byte aligned, so that dword lies inside the array's last dword at most).
+template <int KS, int U>
+struct KBatch {
+  uint4 kv[U][KS];
+  uint32_t sc[U][KS];
+};
+
+template <int KS, int U>
+__device__ __forceinline__ void kbatch_load(const uint8_t* ikb, const uint32_t* sc32, int64_t sc_off0, int kbytes,
+                                            int sbytes, int D_I, int e_begin, int e_end, int g, KBatch<KS, U>& B) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kb = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = min(e_begin + (g + u) * 16 + col, e_end - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool okk = (s * 128 + kb * 32) < D_I;
+      B.kv[u][s] = ld_stream16(ikb + (int64_t)e * kbytes + (okk ? s * 64 + kb * 16 : 0));
+      B.sc[u][s] = sc32[(sc_off0 + (int64_t)e * sbytes + (okk ? s * 4 + kb : 0)) >> 2];  // dword holding the byte
+    }
+  }
+}
+
+template <int KS, int U, typename Sink>
+__device__ __forceinline__ void kbatch_score(const KBatch<KS, U>& B, int64_t sc_off0, int sbytes, int D_I, int e_begin,
+                                             int e_end, int groups, int g, const uint4* qa, const int* qs,
+                                             const float* hw, Sink& sink) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kb = lane >> 4, col = lane & 15;
+  const int n = e_end - e_begin;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (g + u >= groups) break;
+    const int e = min(e_begin + (g + u) * 16 + col, e_end - 1);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool okk = (s * 128 + kb * 32) < D_I;
+      // lanes past D_I multiply by the zero query operand, so their (real, finite) codes need
+      // no masking; only the scale is replaced (an E8M0 byte of 255 would be NaN)
+      const int sh = 8 * (int)((sc_off0 + (int64_t)e * sbytes + s * 4 + kb) & 3);
+      const int byte = (int)((B.sc[u][s] >> sh) & 255u);
+      acc += mfma_fp4(qa[s], B.kv[u][s], qs[s], okk ? byte : 127);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
+    part += __shfl_xor(part, 16, kWave);
+    part += __shfl_xor(part, 32, kWave);
+    const int el = (g + u) * 16 + col;
+    sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
+  }
+}
+
+template <int KS, int NT, typename Sink>
+__device__ __forceinline__ void stream_range_to(const IndexArgs& a, int b, int e_begin, int e_end, const uint4* qa,
+                                                const int* qs, const float* hw, Sink sink) {
+  // batch size: 8 groups for one 128-wide step (6 in 1024-thread workgroups, whose waves have
+  // 128 registers), fewer for wider keys
+  constexpr int U = KS == 1 ? (NT > 512 ? 6 : 8) : (KS == 2 ? 3 : 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
+  const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
+  const uint32_t* sc32 = reinterpret_cast<const uint32_t*>(a.ik_scale);  // 4-byte aligned
+  const int64_t sc_off0 = (int64_t)b * a.N_cap * sbytes;                // this sequence's first scale byte
+  const int groups = (e_end - e_begin + 15) >> 4;
+  const int stride = (NT / kWave) * U;
+  // NB batches per outer step, fully unrolled: batch i+1 is requested before batch i is
+  // scored, and no batch is carried across the loop's back edge (which would force the
+  // compiler to wait for it there)
+  constexpr int NB = 6;
+  for (int g0 = wave * U; g0 < groups; g0 += stride * NB) {
+    KBatch<KS, U> X[NB];
+    kbatch_load<KS, U>(ikb, sc32, sc_off0, kbytes, sbytes, a.D_I, e_begin, e_end, g0, X[0]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int gi = g0 + i * stride;
+      if (gi >= groups) break;
+      if (i + 1 < NB) kbatch_load<KS, U>(ikb, sc32, sc_off0, kbytes, sbytes, a.D_I, e_begin, e_end, gi + stride, X[i + 1]);
+      kbatch_score<KS, U>(X[i], sc_off0, sbytes, a.D_I, e_begin, e_end, groups, gi, qa, qs, hw, sink);
+    }
   }
 }
 
@@ -245,39 +335,28 @@ __global__ __launch_bounds__(kIdxNT) void index_merge_kernel(IndexArgs a) {
 
 // ---------------------------------------------------------------- decode path (few queries)
 //
-// Kernel P (one workgroup per query) scores a deterministic sample of the visible
-// entries (S <= 2048: 128 runs of 16 consecutive entries spread evenly over them, or all
-// of them when there are no more than 2048) and turns the j-th best sample key,
-// j = ceil(8*k*S/n), into a lower bound L (the floor of its 20-bit score bin), so that
-// about 8k keys of the query are >= L. Kernel A streams every chunk of entries once
-// and keeps only the keys >= L: a chunk workgroup collects them in LDS and claims
-// room in the query's candidate list with one atomic. Kernel C checks that at least
-// k keys reached the list and that no chunk overflowed its buffer; then every key >= L
-// is a candidate and the k-th best key is >= L, so the top-k of the candidates is the
-// exact answer, found by rank selection. Otherwise (the sample overstated the top of
-// the distribution, or very many keys tie at L) C recomputes the query exactly with a
-// running top-k over all of its entries. The result is exact either way; only the
-// time differs.
-constexpr int kBins = 4096;       // 12-bit bins of the ordered score
-constexpr int kSubBins = 256;     // next 8 bits
-constexpr int kChunkA = 4096;     // entries per workgroup in kernel A
-constexpr int kSampleMax = 2048;  // sampled entries per query
-constexpr int kOver = 8;          // target candidates per query: kOver * k
-constexpr int kCandWG = 1024;     // candidates one chunk workgroup may hold
-constexpr int kCapF = 4096;       // candidates kernel C selects from directly
-constexpr int kFinNT = 1024;      // threads of kernel C
+// Kernel A (grid Q x C, 1024 threads, one workgroup per CU): streams chunk c of query q with
+// every wave keeping two batches of loads in flight, keeps all of the chunk's keys in LDS,
+// and writes the chunk's top keys to its 2k candidate slots (0 = empty): every key at or
+// above the floor of a histogram bin chosen so that at least min(k, chunk) and at most 2k
+// keys pass (radix-style refinement over [chunk min, chunk max], 11 bits per level). Kernel B
+// (one workgroup per query) runs the same selection over the C * 2k slots down to at most
+// kSelCap keys and ranks them. Exactness: an entry of the global top-k is beaten by fewer than
+// k keys overall, hence by fewer than k keys of its own chunk, so it is among its chunk's
+// passing keys; the top-k of the union of those is the global top-k. No step depends on the
+// data's distribution, and nothing is carried between calls.
+constexpr int kDecNT = 1024;     // threads of both decode kernels
+constexpr int kDecSub = 8448;    // entries a chunk workgroup holds in LDS at once
+constexpr int kSelBins = 2048;   // histogram bins per refinement level
+constexpr int kSelCap = 1024;    // kernel B: keys ranked directly
+constexpr int kStageMax = 8192;  // kernel B: candidate slots staged in LDS
+constexpr int kMaxSlots = 2048;  // 2k for k <= 1024
 
 struct DecodeArgs {
   IndexArgs a;
-  uint64_t* cand;    // [Q][N_cap] candidate keys
-  uint64_t* lbound;  // [Q] lower bound L
-  uint32_t* cnt;     // [Q] candidates
-  uint32_t* flag;    // [Q] nonzero: a chunk had more than kCandWG candidates
-  int chunk, n_chunks;
+  uint64_t* cand;  // [Q][C][slots] candidate keys, 0 = empty
+  int chunk, n_chunks, slots;
 };
-
-__device__ __forceinline__ uint32_t key_bin(uint64_t key) { return (uint32_t)(key >> 52); }       // 12 bits
-__device__ __forceinline__ uint32_t key_bin20(uint64_t key) { return (uint32_t)(key >> 44); }     // 20 bits
 
 // Highest bin b (scanning from the top) whose cumulative count reaches kk; returns b and the
 // count strictly above it in *above. NT is the block size (<= 1024); NB is a power of two.
@@ -328,185 +407,6 @@ __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int*
   return scratch[32];
 }
 
-// Wave-aggregated append of the keys passing `p` to dst[*cnt ...] (LDS counter); the
-// counter keeps counting past cap so that overflow can be detected.
-__device__ __forceinline__ void append_lds(bool p, uint64_t key, uint64_t* dst, int* cnt, int cap) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint64_t mask = __ballot(p);
-  if (mask == 0) return;
-  const int nw = __popcll(mask);
-  int base = 0;
-  if (lane == 0) base = atomicAdd(cnt, nw);
-  base = __shfl(base, 0, kWave);
-  const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-  if (p && base + off < cap) dst[base + off] = key;
-}
-
-constexpr int kSampNT = 1024;     // threads of kernel P
-
-struct PSmem {
-  uint64_t keys[kSampleMax];
-  uint32_t hist[kBins];
-  uint32_t sub[kSubBins];
-  int scratch[34];
-};
-
-// Entry of sample i: all entries when nv <= kSampleMax (S = nv); else run i/16 of 128
-// evenly spread runs of 16 consecutive entries (nv/128 >= 16, so the runs are disjoint).
-__device__ __forceinline__ int sample_entry(int i, int nv, int S) {
-  static_assert(kSampleMax == 128 * 16, "128 runs of 16 entries");
-  return S == nv ? i : (int)(((int64_t)(i >> 4) * nv) >> 7) + (i & 15);
-}
-
-// Score the sampled entries of query q into keys[0..S).
-// Every wave owns whole 16-sample groups and issues the loads of U groups before the
-// first MFMA, so that the gathers overlap.
-template <int KS>
-__device__ void score_samples(const IndexArgs& a, int q, int nv, int S, const uint4* qa, const int* qs,
-                              const float* hw, uint64_t* keys) {
-  constexpr int U = KS == 1 ? 8 : (KS == 2 ? 4 : 2);
-  constexpr int NW = kSampNT / kWave;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int kb = lane >> 4, col = lane & 15;
-  const int b = q / a.T;
-  const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
-  const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
-  const uint8_t* iksb = a.ik_scale + (int64_t)b * a.N_cap * sbytes;
-  const int groups = (S + 15) >> 4;
-  for (int g0 = wave * U; g0 < groups; g0 += NW * U) {
-    uint4 kv[U][KS];
-    int sc[U][KS];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = 16 * (g0 + u) + col;
-      const int e = i < S ? sample_entry(i, nv, S) : 0;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        kv[u][s] = make_uint4(0, 0, 0, 0);
-        sc[u][s] = 127;
-        if (i < S && (s * 128 + kb * 32) < a.D_I) {
-          kv[u][s] = *reinterpret_cast<const uint4*>(ikb + (int64_t)e * kbytes + s * 64 + kb * 16);
-          sc[u][s] = iksb[(int64_t)e * sbytes + s * 4 + kb];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = 16 * (g0 + u) + col;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc += mfma_fp4(qa[s], kv[u][s], qs[s], sc[u][s]);
-      float part = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      if (kb == 0 && i < S) keys[i] = make_key(part, (uint32_t)sample_entry(i, nv, S));
-    }
-  }
-}
-
-template <int KS>
-__global__ __launch_bounds__(kSampNT) void index_sample_kernel(DecodeArgs d) {
-  __shared__ PSmem sm;
-  const IndexArgs& a = d.a;
-  const int q = blockIdx.x;
-  const int nv = min(a.n_valid[q], a.N_cap);
-  const int kk = min(a.k, nv);
-  if (threadIdx.x == 0) {
-    d.cnt[q] = 0;
-    d.flag[q] = 0;
-    d.lbound[q] = 1;  // below every key
-  }
-  if (kk == 0) return;
-  const int S = min(nv, kSampleMax);
-  int64_t jj = ((int64_t)kOver * kk * S + nv - 1) / nv;
-  const int j = (int)(jj < 1 ? 1 : (jj > S ? S : jj));
-  if (j >= S) return;  // the bound would admit (almost) everything: keep L = 1
-  for (int i = threadIdx.x; i < kBins; i += kSampNT) sm.hist[i] = 0;
-  for (int i = threadIdx.x; i < kSubBins; i += kSampNT) sm.sub[i] = 0;
-  uint4 qa[KS];
-  int qs[KS];
-  float hw[4];
-  load_query<KS>(a, q, qa, qs, hw);
-  score_samples<KS>(a, q, nv, S, qa, qs, hw, sm.keys);
-  __syncthreads();
-  for (int i = threadIdx.x; i < S; i += kSampNT) atomicAdd(&sm.hist[key_bin(sm.keys[i])], 1u);
-  __syncthreads();
-  int above;
-  const int bk = find_threshold_bin<kBins, kSampNT>(sm.hist, j, &above, sm.scratch);
-  for (int i = threadIdx.x; i < S; i += kSampNT) {
-    const uint32_t b20 = key_bin20(sm.keys[i]);
-    if ((int)(b20 >> 8) == bk) atomicAdd(&sm.sub[b20 & 255], 1u);
-  }
-  __syncthreads();
-  int above2;
-  const int sk = find_threshold_bin<kSubBins, kSampNT>(sm.sub, j - above, &above2, sm.scratch);
-  if (threadIdx.x == 0) {
-    const uint64_t L = (uint64_t)(((uint32_t)bk << 8) | (uint32_t)sk) << 44;
-    d.lbound[q] = L == 0 ? 1 : L;
-  }
-}
-
-struct ASmem {
-  uint64_t buf[kCandWG];
-  __align__(16) uint8_t wsc[kIdxNT / kWave][1024];
-  int cnt;
-  int base;
-};
-
-template <int KS>
-__global__ __launch_bounds__(kIdxNT) void index_filter_kernel(DecodeArgs d) {
-  __shared__ ASmem sm;
-  const IndexArgs& a = d.a;
-  const int q = blockIdx.x;
-  const int b = q / a.T;
-  const int nv = min(a.n_valid[q], a.N_cap);
-  const int c0 = blockIdx.y * d.chunk;
-  const int c1 = min(c0 + d.chunk, nv);
-  if (c0 >= c1) return;
-  if (threadIdx.x == 0) sm.cnt = 0;
-  const uint64_t L = d.lbound[q];
-  uint4 qa[KS];
-  int qs[KS];
-  float hw[4];
-  load_query<KS>(a, q, qa, qs, hw);
-  __syncthreads();
-  uint64_t* buf = sm.buf;
-  int* cnt = &sm.cnt;
-  score_range_to<KS, kIdxNT>(a, b, c0, c1, qa, qs, hw, sm.wsc[threadIdx.x >> 6],
-                             [buf, cnt, L](bool p, int, uint64_t key) { append_lds(p && key >= L, key, buf, cnt, kCandWG); });
-  __syncthreads();
-  const int c = sm.cnt;
-  if (c == 0) return;
-  if (c > kCandWG) {
-    if (threadIdx.x == 0) atomicOr(&d.flag[q], 1u);
-    return;
-  }
-  if (threadIdx.x == 0) sm.base = (int)atomicAdd(&d.cnt[q], (uint32_t)c);
-  __syncthreads();
-  const int base = sm.base;
-  uint64_t* dst = d.cand + (int64_t)q * a.N_cap;
-  for (int i = threadIdx.x; i < c; i += kIdxNT)
-    if (base + i < a.N_cap) dst[base + i] = sm.buf[i];
-}
-
-struct CSmem {
-  uint64_t buf[kCapF];
-  uint64_t keys[1024 + kSub];  // exact paths: running winners + one sub-chunk
-  __align__(16) uint8_t wsc[kFinNT / kWave][1024];
-  uint32_t hist[kBins];
-  SelectScratch sc;
-  int scratch[34];
-  unsigned long long mx;
-  int cnt;
-};
-
-__device__ __forceinline__ void write_key(const IndexArgs& a, int32_t* oi, float* os, int slot, uint64_t key) {
-  oi[slot] = (int32_t)(~(uint32_t)key);
-  if (os) os[slot] = ordered_to_score((uint32_t)(key >> 32));
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -518,120 +418,273 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-template <int KS>
-__global__ __launch_bounds__(kFinNT) void index_final_kernel(DecodeArgs d) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  CSmem& sm = *reinterpret_cast<CSmem*>(smem_raw);
-  const IndexArgs& a = d.a;
-  const int q = blockIdx.x;
+struct SelShared {
+  uint32_t hist[kSelBins];
+  int scratch[34];
+  unsigned long long mx, mn;
+  int cnt;
+};
+
+// Max, min and count of the nonzero keys of keys[0..n) (block-wide, every thread gets them).
+template <int NT>
+__device__ void block_range(const uint64_t* keys, int n, SelShared& ss, uint64_t* hi, uint64_t* lo, int* cnt) {
   const int tid = threadIdx.x;
+  if (tid == 0) {
+    ss.mx = 0;
+    ss.mn = ~0ull;
+    ss.cnt = 0;
+  }
+  uint64_t mx = 0, mn = ~0ull;
+  int c = 0;
+  for (int i = tid; i < n; i += NT) {
+    const uint64_t v = keys[i];
+    if (v) {
+      mx = v > mx ? v : mx;
+      mn = v < mn ? v : mn;
+      ++c;
+    }
+  }
+  mx = wave_max_u64(mx);
+  mn = ~wave_max_u64(~mn);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+  __syncthreads();
+  if ((tid & (kWave - 1)) == 0) {
+    atomicMax(&ss.mx, (unsigned long long)mx);
+    atomicMin(&ss.mn, (unsigned long long)mn);
+    atomicAdd(&ss.cnt, c);
+  }
+  __syncthreads();
+  *hi = ss.mx;
+  *lo = ss.mn;
+  *cnt = ss.cnt;
+}
+
+// Lower edge of a histogram bin such that at least kk of the nonzero keys of keys[0..n) lie at
+// or above it and at most cap do (or exactly kk when the last level has single-key bins).
+// Requires kk <= (number of nonzero keys) and lo <= every nonzero key <= hi.
+template <int NT>
+__device__ uint64_t select_floor(const uint64_t* keys, int n, int kk, int cap, uint64_t lo, uint64_t hi,
+                                 SelShared& ss) {
+  const int tid = threadIdx.x;
+  const uint64_t R = hi - lo;
+  int shift = R == 0 ? 0 : max(0, 64 - __builtin_clzll(R) - 11);  // (key - lo) >> shift < 2048
+  uint64_t base = lo;
+  int need = kk, above_all = 0;
+  for (;;) {
+    for (int i = tid; i < kSelBins; i += NT) ss.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint64_t v = keys[i];
+      if (v >= base) {
+        const uint64_t bin = (v - base) >> shift;
+        if (bin < (uint64_t)kSelBins) atomicAdd(&ss.hist[bin], 1u);
+      }
+    }
+    __syncthreads();
+    int above;
+    const int thr = find_threshold_bin<kSelBins, NT>(ss.hist, need, &above, ss.scratch);
+    const int in_bin = (int)ss.hist[thr];
+    base += (uint64_t)thr << shift;
+    above_all += above;
+    need -= above;
+    __syncthreads();  // histogram reads done before it is cleared
+    if (above_all + in_bin <= cap || shift == 0) break;
+    shift = max(0, shift - 11);
+  }
+  return base;
+}
+
+// Writes the keys of keys[0..n) that are >= base (base >= 1) to dst[0..) in one pass
+// (per-thread counts, one block prefix sum); returns their number (at most cap are written).
+// The keys are read into registers before any write, so dst may alias keys.
+template <int NT, int PER>
+__device__ int compact_ge(const uint64_t* keys, int n, uint64_t base, uint64_t* dst, int cap, SelShared& ss) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  uint64_t v[PER];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * NT;
+    v[j] = i < n ? keys[i] : 0;
+    c += v[j] >= base;
+  }
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) ss.scratch[w] = inc;
+  __syncthreads();
+  int off = inc - c, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    off += i < w ? ss.scratch[i] : 0;
+    total += ss.scratch[i];
+  }
+  __syncthreads();  // scratch reads and key reads done before dst is written
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (v[j] >= base && off < cap) dst[off++] = v[j];
+  __syncthreads();
+  return min(total, cap);
+}
+
+struct ChunkSmem {
+  uint64_t keys[kMaxSlots + kDecSub];  // carried keys + one sub-chunk
+  SelShared ss;
+};
+
+// Kernel A: grid (Q, C). Candidate slots of chunk c of query q.
+template <int KS>
+__global__ __launch_bounds__(kDecNT) void index_chunk_decode_kernel(DecodeArgs d) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  ChunkSmem& sm = *reinterpret_cast<ChunkSmem*>(smem_raw);
+  const IndexArgs& a = d.a;
+  const int q = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int b = q / a.T;
+  const int nv = min(a.n_valid[q], a.N_cap);
+  const int kk = min(a.k, nv);
+  const int c0 = c * d.chunk, c1 = min(c0 + d.chunk, nv);
+  uint64_t* out = d.cand + ((int64_t)q * d.n_chunks + c) * d.slots;
+  uint4 qa[KS];
+  int qs[KS];
+  float hw[4];
+  load_query<KS>(a, q, qa, qs, hw);
+  int kept = 0;  // keys in sm.keys[0..kept)
+  for (int s0 = c0; s0 < c1; s0 += kDecSub) {
+    const int s1 = min(s0 + kDecSub, c1);
+    uint64_t* dst = sm.keys + kept;
+    stream_range_to<KS, kDecNT>(a, b, s0, s1, qa, qs, hw, [dst](bool p, int el, uint64_t key) {
+      if (p) dst[el] = key;
+    });
+    __syncthreads();
+    const int n = kept + (s1 - s0);
+    kept = n;
+    if (n > d.slots) {  // keep the keys at or above a floor that keeps this chunk's top-kk
+      uint64_t hi, lo;
+      int nz;
+      block_range<kDecNT>(sm.keys, n, sm.ss, &hi, &lo, &nz);
+      const uint64_t base = select_floor<kDecNT>(sm.keys, n, kk, d.slots, lo, hi, sm.ss);
+      kept = compact_ge<kDecNT, (kMaxSlots + kDecSub + kDecNT - 1) / kDecNT>(sm.keys, n, base, sm.keys, d.slots,
+                                                                           sm.ss);
+    }
+  }
+  for (int i = tid; i < d.slots; i += kDecNT) out[i] = i < kept ? sm.keys[i] : 0;
+}
+
+struct FinalSmem {
+  uint64_t keys[kStageMax];
+  uint64_t sel[kSelCap];
+  SelShared ss;
+};
+
+// Kernel B: one workgroup per query; the ordered top-k of its C * slots candidates.
+__global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
+  const IndexArgs& a = d.a;
+  const int q = blockIdx.x, tid = threadIdx.x;
   const int nv = min(a.n_valid[q], a.N_cap);
   const int kk = min(a.k, nv);
   int32_t* oi = a.out_idx + (int64_t)q * a.k;
   float* os = a.out_score ? a.out_score + (int64_t)q * a.k : nullptr;
-  for (int i = kk + tid; i < a.k; i += kFinNT) {  // padding
+  for (int i = kk + tid; i < a.k; i += kDecNT) {  // padding
     oi[i] = -1;
     if (os) os[i] = -INFINITY;
   }
   if (kk == 0) return;
-  const int n_cand = min((int)d.cnt[q], a.N_cap);
-  const bool exact_ok = d.flag[q] == 0 && n_cand >= kk;
-  const uint64_t* cq = d.cand + (int64_t)q * a.N_cap;
-  if (exact_ok && n_cand <= kCapF) {
-    // Histogram of (key - L) over 4096 bins spanning [L, max key]; the bin holding the k-th
-    // best key and every bin above it form a set S' that holds the top-k, and a key of S'
-    // is beaten only by keys of S', so its rank within S' is its final slot.
-    const uint64_t L = d.lbound[q];
-    if (tid == 0) {
-      sm.mx = 0;
-      sm.cnt = 0;
-    }
-    uint64_t mx = 0;
-    for (int i = tid; i < kBins; i += kFinNT) sm.hist[i] = 0;
-    for (int i = tid; i < n_cand; i += kFinNT) {
-      const uint64_t v = cq[i];
-      sm.buf[i] = v;
-      mx = v > mx ? v : mx;
-    }
-    mx = wave_max_u64(mx);
+  const int n = d.n_chunks * d.slots;
+  const uint64_t* src = d.cand + (int64_t)q * n;
+  if (n <= kStageMax) {
+    for (int i = tid; i < n; i += kDecNT) sm.keys[i] = src[i];
     __syncthreads();
-    if ((tid & (kWave - 1)) == 0) atomicMax(&sm.mx, (unsigned long long)mx);
-    __syncthreads();
-    const uint64_t R = sm.mx - L;
-    const int shift = R == 0 ? 0 : max(0, 64 - __builtin_clzll(R) - 12);
-    for (int i = tid; i < n_cand; i += kFinNT) atomicAdd(&sm.hist[(sm.buf[i] - L) >> shift], 1u);
-    __syncthreads();
-    int above;
-    const uint32_t thr = (uint32_t)find_threshold_bin<kBins, kFinNT>(sm.hist, kk, &above, sm.scratch);
-    for (int i0 = 0; i0 < n_cand; i0 += kFinNT) {
-      const int i = i0 + tid;
-      const uint64_t key = i < n_cand ? sm.buf[i] : 0;
-      append_lds(i < n_cand && ((key - L) >> shift) >= thr, key, sm.keys, &sm.cnt, kCapF);
-    }
-    __syncthreads();
-    const int m = min(sm.cnt, kCapF);
-    for (int i = tid; i < m; i += kFinNT) {
-      const uint64_t key = sm.keys[i];
-      int rank = 0;
-      for (int jx = 0; jx < m; ++jx) rank += sm.keys[jx] > key;
-      if (rank < kk) write_key(a, oi, os, rank, key);
-    }
-    return;
+    src = sm.keys;
   }
-  // running top-k: over the candidate list (exact_ok), else over every visible entry
-  uint4 qa[KS];
-  int qs[KS];
-  float hw[4];
-  if (!exact_ok) load_query<KS>(a, q, qa, qs, hw);
-  const int total = exact_ok ? n_cand : nv;
-  int kept = 0;
-  for (int s0 = 0; s0 < total; s0 += kSub) {
-    const int s1 = min(s0 + kSub, total);
-    if (exact_ok) {
-      for (int i = threadIdx.x; i < s1 - s0; i += kFinNT) sm.keys[kept + i] = cq[s0 + i];
-    } else {
-      score_range<KS, kFinNT, 2>(a, q / a.T, s0, s1, qa, qs, hw, sm.keys + kept, sm.wsc[threadIdx.x >> 6]);
-    }
-    __syncthreads();
-    const int nn = kept + (s1 - s0);
-    const int k2 = min(kk, nn);
-    select_topk<kFinNT, kCapF>(sm.keys, nn, k2, sm.buf, &sm.sc);
-    for (int i = threadIdx.x; i < k2; i += kFinNT) sm.keys[i] = sm.buf[i];
-    __syncthreads();
-    kept = k2;
+  uint64_t hi, lo;
+  int nz;
+  block_range<kDecNT>(src, n, sm.ss, &hi, &lo, &nz);
+  const uint64_t base = nz <= kSelCap ? lo : select_floor<kDecNT>(src, n, kk, kSelCap, lo, hi, sm.ss);
+  // keys >= base (at most kSelCap of them; the top-kk among them) into sel, then ranks
+  const int lane = tid & (kWave - 1), w = tid >> 6;
+  int cnt = 0;
+  for (int i = tid; i < n; i += kDecNT) cnt += src[i] >= base;
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
   }
-  for (int i = threadIdx.x; i < kept; i += kFinNT) write_key(a, oi, os, i, sm.keys[i]);
+  if (lane == kWave - 1) sm.ss.scratch[w] = inc;
+  __syncthreads();
+  int off = inc - cnt, m = 0;
+#pragma unroll
+  for (int i = 0; i < kDecNT / kWave; ++i) {
+    off += i < w ? sm.ss.scratch[i] : 0;
+    m += sm.ss.scratch[i];
+  }
+  m = min(m, kSelCap);
+  for (int i = tid; i < n; i += kDecNT) {
+    const uint64_t v = src[i];
+    if (v >= base && off < kSelCap) sm.sel[off++] = v;
+  }
+  __syncthreads();
+  m = __builtin_amdgcn_readfirstlane(m);  // uniform: scalar loop control, independent LDS reads
+  for (int i = tid; i < m; i += kDecNT) {
+    const uint64_t key = sm.sel[i];
+    int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int jx = 0;
+    for (; jx + 8 <= m; jx += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] += sm.sel[jx + u] > key;
+    }
+    for (; jx < m; ++jx) r[0] += sm.sel[jx] > key;
+    const int rank = r[0] + r[1] + r[2] + r[3] + r[4] + r[5] + r[6] + r[7];
+    if (rank < kk) {
+      oi[rank] = (int32_t)(~(uint32_t)key);
+      if (os) os[rank] = ordered_to_score((uint32_t)(key >> 32));
+    }
+  }
 }
 
-static int decode_chunks(int N_cap) { return (N_cap + kChunkA - 1) / kChunkA; }
+// Chunking of kernel A: one workgroup per CU for the whole job (256), chunks of at most
+// kDecSub entries (one LDS pass), multiples of 16.
+static void decode_chunks(int queries, int N_cap, int* chunk, int* n_chunks) {
+  int n = 256 / queries;
+  const int by_lds = (N_cap + kDecSub - 1) / kDecSub;
+  if (n < by_lds) n = by_lds;
+  if (n < 1) n = 1;
+  int c = (N_cap + n - 1) / n;
+  c = (c + 15) & ~15;
+  if (c < 16) c = 16;
+  *chunk = c;
+  *n_chunks = (N_cap + c - 1) / c;
+}
 
-static size_t decode_ws_bytes(int queries, int N_cap) {
-  return (size_t)queries * N_cap * sizeof(uint64_t) + (size_t)queries * (sizeof(uint64_t) + 2 * sizeof(uint32_t));
+static size_t decode_ws_bytes(int queries, int N_cap, int k) {
+  int chunk, n_chunks;
+  decode_chunks(queries, N_cap, &chunk, &n_chunks);
+  return (size_t)queries * n_chunks * (2 * k) * sizeof(uint64_t);
 }
 
 template <int KS>
 static void launch_decode_ks(const DecodeArgs& d, int queries, hipStream_t s) {
-  hipLaunchKernelGGL((index_sample_kernel<KS>), dim3(queries), dim3(kSampNT), 0, s, d);
-  if (d.n_chunks > 0) hipLaunchKernelGGL((index_filter_kernel<KS>), dim3(queries, d.n_chunks), dim3(kIdxNT), 0, s, d);
-  const size_t smem = sizeof(CSmem);
-  (void)hipFuncSetAttribute((const void*)index_final_kernel<KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
-  hipLaunchKernelGGL((index_final_kernel<KS>), dim3(queries), dim3(kFinNT), smem, s, d);
+  const size_t smem_a = sizeof(ChunkSmem), smem_b = sizeof(FinalSmem);
+  (void)hipFuncSetAttribute((const void*)index_chunk_decode_kernel<KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem_a);
+  (void)hipFuncSetAttribute((const void*)index_final_decode_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem_b);
+  hipLaunchKernelGGL((index_chunk_decode_kernel<KS>), dim3(queries, d.n_chunks), dim3(kDecNT), smem_a, s, d);
+  hipLaunchKernelGGL(index_final_decode_kernel, dim3(queries), dim3(kDecNT), smem_b, s, d);
 }
 
 static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipStream_t s) {
   DecodeArgs d;
   d.a = a;
-  d.chunk = kChunkA;
-  d.n_chunks = decode_chunks(a.N_cap);
-  unsigned char* w = reinterpret_cast<unsigned char*>(ws);
-  d.cand = reinterpret_cast<uint64_t*>(w);
-  w += (size_t)queries * a.N_cap * sizeof(uint64_t);
-  d.lbound = reinterpret_cast<uint64_t*>(w);
-  w += (size_t)queries * sizeof(uint64_t);
-  d.cnt = reinterpret_cast<uint32_t*>(w);
-  w += (size_t)queries * sizeof(uint32_t);
-  d.flag = reinterpret_cast<uint32_t*>(w);
+  decode_chunks(queries, a.N_cap > 0 ? a.N_cap : 1, &d.chunk, &d.n_chunks);
+  d.slots = 2 * a.k;
+  d.cand = reinterpret_cast<uint64_t*>(ws);
   if (ks == 1)
     launch_decode_ks<1>(d, queries, s);
   else if (ks == 2)
@@ -670,9 +723,9 @@ static IndexPlan plan_index(int B, int T, int N_cap, int k) {
   p.n_chunks = n_chunks;
   p.cap = k <= 256 ? 512 : 2048;
   p.ws = (size_t)queries * n_chunks * k * sizeof(uint64_t);
-  // decode path: few queries (candidate lists of N_cap keys per query stay small)
-  p.decode = k <= 1024 && (size_t)queries * N_cap <= ((size_t)1 << 26);
-  if (p.decode) p.ws = decode_ws_bytes((int)queries, N_cap);
+  // decode path: few queries (at most one chunk workgroup per CU when they are alone)
+  p.decode = k <= 1024 && queries <= 256;
+  if (p.decode) p.ws = decode_ws_bytes((int)queries, N_cap, k);
   return p;
 }
 
@@ -725,6 +778,8 @@ extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scal
   CSKV_REQUIRE(N_cap == 0 || (ik && ik_scale), CSKV_EINVAL, "csa_index_topk: null key pointer");
   CSKV_REQUIRE(aligned16(iq) && (N_cap == 0 || aligned16(ik)), CSKV_EINVAL,
                "csa_index_topk: iq/ik must be 16-byte aligned");
+  CSKV_REQUIRE(N_cap == 0 || (reinterpret_cast<uintptr_t>(ik_scale) & 3) == 0, CSKV_EINVAL,
+               "csa_index_topk: ik_scale must be 4-byte aligned");
   const int Nc = N_cap > 0 ? N_cap : 1;
   IndexPlan p = plan_index(B, T, Nc, k);
   CSKV_REQUIRE(ws && ws_bytes >= p.ws, CSKV_EWORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes,

@@ -123,7 +123,7 @@ def test_index_topk_when_the_sample_overstates_the_top():
     B, H_I, D_I, k, N = 2, 8, 128, 128, 262144
     iq, iqs = synth.mxfp4_normal((B, 1, H_I, D_I), 141, DEV)
     ik, iks = synth.mxfp4_normal((B, N, D_I), 142, DEV)
-    stride = N // 128                                 # sampled runs of 16 start at g * N / 128
+    stride = N // 64                                  # sampled runs of 16 start at r * N / 64
     for b in range(B):
         for i in range(10):
             ik[b, i * stride] = iq[b, 0, 0]           # key = head-0 query codes: large positive dot
