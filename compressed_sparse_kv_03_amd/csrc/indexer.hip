@@ -203,7 +203,7 @@ __device__ __forceinline__ void stream_range_to(const IndexArgs& a, int b, int e
                                                 const int* qs, const float* hw, Sink sink) {
   // batch size: 8 groups for one 128-wide step (6 in 1024-thread workgroups, whose waves have
   // 128 registers), fewer for wider keys
-  constexpr int U = KS == 1 ? (NT > 512 ? 6 : 8) : (KS == 2 ? 3 : 1);
+  constexpr int U = KS == 1 ? (NT > 512 ? 6 : 8) : (KS == 2 ? 2 : 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
   const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
@@ -423,7 +423,101 @@ struct SelShared {
   int scratch[34];
   unsigned long long mx, mn;
   int cnt;
+  uint32_t mx32, mn32;
 };
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
+// Folds per-lane ranges [mn, mx] of ordered scores into ss.mn32 / ss.mx32 (which thread 0 set
+// to ~0 / 0 before an earlier barrier). The caller's next barrier publishes them.
+__device__ __forceinline__ void fold_score_range(uint32_t mx, uint32_t mn, SelShared& ss) {
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    atomicMax(&ss.mx32, mx);
+    atomicMin(&ss.mn32, mn);
+  }
+}
+
+// Key bounds covering every key whose ordered score lies in [mn32, mx32] (keys are >= 1).
+__device__ __forceinline__ void key_bounds(const SelShared& ss, uint64_t* lo, uint64_t* hi) {
+  const uint64_t l = (uint64_t)ss.mn32 << 32;
+  *lo = l ? l : 1;
+  *hi = ((uint64_t)ss.mx32 << 32) | 0xffffffffull;
+}
+
+// Register-resident forms: every thread holds PER keys (0 = empty). The floor: at least kk
+// nonzero keys at or above it and at most cap (or exactly kk once bins hold single keys).
+// hist must be zero on entry; it is zero again on return.
+template <int NT, int PER>
+__device__ uint64_t reg_select_floor(const uint64_t (&v)[PER], int kk, int cap, uint64_t lo, uint64_t hi,
+                                     SelShared& ss) {
+  const int tid = threadIdx.x;
+  const uint64_t R = hi - lo;
+  int shift = R == 0 ? 0 : max(0, 64 - __builtin_clzll(R) - 11);  // (key - lo) >> shift < 2048
+  uint64_t base = lo;
+  int need = kk, above_all = 0;
+  for (;;) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (v[j] >= base) {
+        const uint64_t bin = (v[j] - base) >> shift;
+        if (bin < (uint64_t)kSelBins) atomicAdd(&ss.hist[bin], 1u);
+      }
+    }
+    __syncthreads();
+    int above;
+    const int thr = find_threshold_bin<kSelBins, NT>(ss.hist, need, &above, ss.scratch);
+    const int in_bin = (int)ss.hist[thr];
+    base += (uint64_t)thr << shift;
+    above_all += above;
+    need -= above;
+    __syncthreads();  // histogram reads done before it is cleared
+    for (int i = tid; i < kSelBins; i += NT) ss.hist[i] = 0;
+    __syncthreads();
+    if (above_all + in_bin <= cap || shift == 0) break;
+    shift = max(0, shift - 11);
+  }
+  return base;
+}
+
+// Writes the register keys >= base (base >= 1) to dst[0..) (at most cap of them, in no
+// particular order) and returns their number. Ends with a barrier.
+template <int NT, int PER>
+__device__ int reg_compact_ge(const uint64_t (&v)[PER], uint64_t base, uint64_t* dst, int cap, SelShared& ss) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) c += v[j] >= base;
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) ss.scratch[w] = inc;
+  __syncthreads();
+  int off = inc - c, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    off += i < w ? ss.scratch[i] : 0;
+    total += ss.scratch[i];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (v[j] >= base && off < cap) dst[off++] = v[j];
+  __syncthreads();
+  return min(total, cap);
+}
 
 // Max, min and count of the nonzero keys of keys[0..n) (block-wide, every thread gets them).
 template <int NT>
@@ -495,42 +589,6 @@ __device__ uint64_t select_floor(const uint64_t* keys, int n, int kk, int cap, u
   return base;
 }
 
-// Writes the keys of keys[0..n) that are >= base (base >= 1) to dst[0..) in one pass
-// (per-thread counts, one block prefix sum); returns their number (at most cap are written).
-// The keys are read into registers before any write, so dst may alias keys.
-template <int NT, int PER>
-__device__ int compact_ge(const uint64_t* keys, int n, uint64_t base, uint64_t* dst, int cap, SelShared& ss) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
-  uint64_t v[PER];
-  int c = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = tid + j * NT;
-    v[j] = i < n ? keys[i] : 0;
-    c += v[j] >= base;
-  }
-  int inc = c;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
-  if (lane == kWave - 1) ss.scratch[w] = inc;
-  __syncthreads();
-  int off = inc - c, total = 0;
-#pragma unroll
-  for (int i = 0; i < NT / kWave; ++i) {
-    off += i < w ? ss.scratch[i] : 0;
-    total += ss.scratch[i];
-  }
-  __syncthreads();  // scratch reads and key reads done before dst is written
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (v[j] >= base && off < cap) dst[off++] = v[j];
-  __syncthreads();
-  return min(total, cap);
-}
-
 struct ChunkSmem {
   uint64_t keys[kMaxSlots + kDecSub];  // carried keys + one sub-chunk
   SelShared ss;
@@ -541,6 +599,7 @@ template <int KS>
 __global__ __launch_bounds__(kDecNT) void index_chunk_decode_kernel(DecodeArgs d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ChunkSmem& sm = *reinterpret_cast<ChunkSmem*>(smem_raw);
+  constexpr int PER = (kMaxSlots + kDecSub + kDecNT - 1) / kDecNT;
   const IndexArgs& a = d.a;
   const int q = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int b = q / a.T;
@@ -548,27 +607,43 @@ __global__ __launch_bounds__(kDecNT) void index_chunk_decode_kernel(DecodeArgs d
   const int kk = min(a.k, nv);
   const int c0 = c * d.chunk, c1 = min(c0 + d.chunk, nv);
   uint64_t* out = d.cand + ((int64_t)q * d.n_chunks + c) * d.slots;
+  for (int i = tid; i < kSelBins; i += kDecNT) sm.ss.hist[i] = 0;
+  if (tid == 0) {
+    sm.ss.mx32 = 0;
+    sm.ss.mn32 = ~0u;
+  }
   uint4 qa[KS];
   int qs[KS];
   float hw[4];
   load_query<KS>(a, q, qa, qs, hw);
-  int kept = 0;  // keys in sm.keys[0..kept)
+  uint32_t mx = 0, mn = ~0u;  // this lane's range of ordered scores (for the histogram bounds)
+  int kept = 0;               // keys in sm.keys[0..kept)
   for (int s0 = c0; s0 < c1; s0 += kDecSub) {
     const int s1 = min(s0 + kDecSub, c1);
     uint64_t* dst = sm.keys + kept;
-    stream_range_to<KS, kDecNT>(a, b, s0, s1, qa, qs, hw, [dst](bool p, int el, uint64_t key) {
-      if (p) dst[el] = key;
+    stream_range_to<KS, kDecNT>(a, b, s0, s1, qa, qs, hw, [dst, &mx, &mn](bool p, int el, uint64_t key) {
+      if (p) {
+        dst[el] = key;
+        const uint32_t sc = (uint32_t)(key >> 32);
+        mx = max(mx, sc);
+        mn = min(mn, sc);
+      }
     });
+    fold_score_range(mx, mn, sm.ss);
     __syncthreads();
     const int n = kept + (s1 - s0);
     kept = n;
     if (n > d.slots) {  // keep the keys at or above a floor that keeps this chunk's top-kk
-      uint64_t hi, lo;
-      int nz;
-      block_range<kDecNT>(sm.keys, n, sm.ss, &hi, &lo, &nz);
-      const uint64_t base = select_floor<kDecNT>(sm.keys, n, kk, d.slots, lo, hi, sm.ss);
-      kept = compact_ge<kDecNT, (kMaxSlots + kDecSub + kDecNT - 1) / kDecNT>(sm.keys, n, base, sm.keys, d.slots,
-                                                                           sm.ss);
+      uint64_t v[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * kDecNT;
+        v[j] = i < n ? sm.keys[i] : 0;
+      }
+      uint64_t lo, hi;
+      key_bounds(sm.ss, &lo, &hi);
+      const uint64_t base = reg_select_floor<kDecNT, PER>(v, kk, d.slots, lo, hi, sm.ss);
+      kept = reg_compact_ge<kDecNT, PER>(v, base, sm.keys, d.slots, sm.ss);
     }
   }
   for (int i = tid; i < d.slots; i += kDecNT) out[i] = i < kept ? sm.keys[i] : 0;
@@ -577,13 +652,45 @@ __global__ __launch_bounds__(kDecNT) void index_chunk_decode_kernel(DecodeArgs d
 struct FinalSmem {
   uint64_t keys[kStageMax];
   uint64_t sel[kSelCap];
+  int rk[kSelCap];
   SelShared ss;
 };
+
+// Ranks sel[0..m) (distinct keys, m <= kSelCap) and writes the ones of rank < kk to their
+// slots. P = kDecNT / m' threads share a key (m' = m rounded up to a power of two), each
+// counting the greater keys in a 1/P slice; the partial ranks meet in an LDS counter.
+__device__ __forceinline__ void rank_write(const uint64_t* sel, int m, int kk, int32_t* oi, float* os, int* rk) {
+  const int tid = threadIdx.x;
+  m = __builtin_amdgcn_readfirstlane(m);
+  int mp = 1;
+  while (mp < m) mp <<= 1;
+  const int P = mp >= kDecNT ? 1 : kDecNT / mp;  // threads per key (power of two)
+  for (int i = tid; i < m; i += kDecNT) rk[i] = 0;
+  __syncthreads();
+  const int part = tid % P, slice = (m + P - 1) / P;
+  const int j0 = part * slice, j1 = min(m, j0 + slice);
+  for (int i = tid / P; i < m; i += kDecNT / P) {
+    const uint64_t key = sel[i];
+    int r = 0;
+    for (int jx = j0; jx < j1; ++jx) r += sel[jx] > key;
+    if (r) atomicAdd(&rk[i], r);
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += kDecNT) {
+    const int rank = rk[i];
+    if (rank < kk) {
+      const uint64_t key = sel[i];
+      oi[rank] = (int32_t)(~(uint32_t)key);
+      if (os) os[rank] = ordered_to_score((uint32_t)(key >> 32));
+    }
+  }
+}
 
 // Kernel B: one workgroup per query; the ordered top-k of its C * slots candidates.
 __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
+  constexpr int PER = kStageMax / kDecNT;
   const IndexArgs& a = d.a;
   const int q = blockIdx.x, tid = threadIdx.x;
   const int nv = min(a.n_valid[q], a.N_cap);
@@ -598,15 +705,48 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
   const int n = d.n_chunks * d.slots;
   const uint64_t* src = d.cand + (int64_t)q * n;
   if (n <= kStageMax) {
-    for (int i = tid; i < n; i += kDecNT) sm.keys[i] = src[i];
+    // register-resident: every slot is loaded once, all loads in flight together
+    for (int i = tid; i < kSelBins; i += kDecNT) sm.ss.hist[i] = 0;
+    if (tid == 0) {
+      sm.ss.mx32 = 0;
+      sm.ss.mn32 = ~0u;
+      sm.ss.cnt = 0;
+    }
+    uint64_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * kDecNT;
+      v[j] = i < n ? src[i] : 0;
+    }
+    uint32_t mx = 0, mn = ~0u;
+    int nz = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (v[j]) {
+        const uint32_t sc = (uint32_t)(v[j] >> 32);
+        mx = max(mx, sc);
+        mn = min(mn, sc);
+        ++nz;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nz += __shfl_xor(nz, o, kWave);
+    __syncthreads();  // range words initialised
+    fold_score_range(mx, mn, sm.ss);
+    if ((tid & (kWave - 1)) == 0) atomicAdd(&sm.ss.cnt, nz);
     __syncthreads();
-    src = sm.keys;
+    uint64_t lo, hi;
+    key_bounds(sm.ss, &lo, &hi);
+    const uint64_t base = sm.ss.cnt <= kSelCap ? lo : reg_select_floor<kDecNT, PER>(v, kk, kSelCap, lo, hi, sm.ss);
+    const int m = reg_compact_ge<kDecNT, PER>(v, base, sm.sel, kSelCap, sm.ss);
+    rank_write(sm.sel, m, kk, oi, os, sm.rk);
+    return;
   }
+  // large candidate lists: histogram passes over global memory
   uint64_t hi, lo;
   int nz;
   block_range<kDecNT>(src, n, sm.ss, &hi, &lo, &nz);
   const uint64_t base = nz <= kSelCap ? lo : select_floor<kDecNT>(src, n, kk, kSelCap, lo, hi, sm.ss);
-  // keys >= base (at most kSelCap of them; the top-kk among them) into sel, then ranks
   const int lane = tid & (kWave - 1), w = tid >> 6;
   int cnt = 0;
   for (int i = tid; i < n; i += kDecNT) cnt += src[i] >= base;
@@ -630,22 +770,7 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
     if (v >= base && off < kSelCap) sm.sel[off++] = v;
   }
   __syncthreads();
-  m = __builtin_amdgcn_readfirstlane(m);  // uniform: scalar loop control, independent LDS reads
-  for (int i = tid; i < m; i += kDecNT) {
-    const uint64_t key = sm.sel[i];
-    int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int jx = 0;
-    for (; jx + 8 <= m; jx += 8) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r[u] += sm.sel[jx + u] > key;
-    }
-    for (; jx < m; ++jx) r[0] += sm.sel[jx] > key;
-    const int rank = r[0] + r[1] + r[2] + r[3] + r[4] + r[5] + r[6] + r[7];
-    if (rank < kk) {
-      oi[rank] = (int32_t)(~(uint32_t)key);
-      if (os) os[rank] = ordered_to_score((uint32_t)(key >> 32));
-    }
-  }
+  rank_write(sm.sel, m, kk, oi, os, sm.rk);
 }
 
 // Chunking of kernel A: one workgroup per CU for the whole job (256), chunks of at most
