@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=30)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (PMC calibration) and exit")
+    ap.add_argument("--index-only", action="store_true",
+                    help="only run --steps csa_index_topk calls on the 1M-context indexer inputs (for profilers)")
     return ap.parse_args()
 
 
@@ -90,6 +92,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": 1 << 30}))
+        return
+
+    if args.index_only:
+        index_only(args, dev)
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
@@ -206,7 +212,8 @@ def main():
             "hybrid_attn_decode_hca": {"median": t_hca[0], "p10": t_hca[1], "p90": t_hca[2]},
         },
         "roofline": {
-            "kernel": "csa_index_topk (index_chunk_kernel + index_merge_kernel), 8 queries x 262144 entries",
+            "kernel": "csa_index_topk (index_chunk_decode_kernel + index_final_decode_kernel), "
+                      "8 queries x 262144 entries",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
@@ -222,6 +229,41 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pairs[0])
     print(json.dumps(rec))
+
+
+def index_only(args, dev):
+    """csa_index_topk alone on the 1M-context decode inputs: 8 queries, 262144 visible entries of
+    8x128 MXFP4 keys, k = 128 (the same shapes as the layer pair's indexer)."""
+    import torch
+
+    from compressed_sparse_kv_03_amd import hybrid, native, synth
+
+    s = hybrid.LayerPairSpec()
+    n_cap = (s.L + s.steps) // s.m_csa + 1
+    n = s.L // s.m_csa
+    iq, iqs = synth.mxfp4_normal((s.B, 1, s.H_I, s.D_I), synth.seed_of(s.seed, s.wid, 11), dev)
+    ik, iks = synth.mxfp4_normal((s.B, n_cap, s.D_I), synth.seed_of(s.seed, s.wid, 10), dev)
+    nv = torch.full((s.B, 1), n, dtype=torch.int32, device=dev)
+    oi = torch.empty((s.B, 1, s.k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(16, native.csa_index_topk_workspace_size(s.B, 1, n_cap, s.H_I, s.D_I, s.k)),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def call():
+        native.csa_index_topk(iq, iqs, None, ik, iks, nv, s.B, 1, n_cap, s.H_I, s.D_I, s.k, oi, None, ws)
+
+    for _ in range(args.warmup):
+        call()
+    ts = []
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    print(json.dumps({"index_only_calls": args.steps, "mean_ms": sum(ts) / len(ts), "min_ms": min(ts)}))
 
 
 def cpu_baseline(pair):
