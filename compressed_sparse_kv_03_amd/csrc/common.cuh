@@ -99,15 +99,6 @@ __device__ __forceinline__ float row16_sum(float v) {
 // Angle p * base^(-2i/d_rope), formed in fp64 and reduced to [-pi, pi] before
 // the fp32 rotation (positions reach 2^20, where an fp32 angle would be off by
 // up to ~0.06 rad).
-__device__ __forceinline__ void rope_cs(double inv_freq, int64_t pos, float* c, float* s) {
-  double a = (double)pos * inv_freq;
-  const double two_pi = 6.283185307179586476925286766559;
-  a = a - two_pi * rint(a / two_pi);
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
-}
 __device__ __forceinline__ double rope_inv_freq(float base, int pair, int d_rope) {
   return pow((double)base, -2.0 * (double)pair / (double)d_rope);
 }

@@ -20,13 +20,34 @@ namespace cskv {
 
 constexpr int kCompressWaves = 4;  // waves per workgroup
 constexpr int kUnroll = 8;
+constexpr int kRopeTab = 64;       // RoPE pairs whose frequency comes from the host table
+
+// base^(-2i/d_rope) for the first kRopeTab pairs, formed on the host in fp64 (a device fp64
+// pow per pair and lane was most of the kernel's time at decode sizes).
+struct RopeTable {
+  double inv_freq[kRopeTab];
+};
+
+// cos / sin of pos * inv_freq: the angle is reduced to [-pi, pi] in fp64, then evaluated in
+// fp32 at the rounded angle and corrected to first order for the rounding (|error| about one
+// fp32 ulp, against several for the plain fp32 evaluation).
+__device__ __forceinline__ void rope_cs_fast(double inv_freq, int64_t pos, float* c, float* s) {
+  double a = (double)pos * inv_freq;
+  a -= 6.283185307179586476925286766559 * rint(a * 0.15915494309189533576888376337251);
+  const float af = (float)a;
+  const float dl = (float)(a - (double)af);
+  float sf, cf;
+  sincosf(af, &sf, &cf);
+  *s = fmaf(dl, cf, sf);
+  *c = fmaf(-dl, sf, cf);
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t x_seq_stride, const float* __restrict__ z,
     int64_t z_seq_stride, const int64_t* __restrict__ pos0, int B, int n_ent, int D, int d_rope,
     int m, int entry_pos_offset, float rope_base, void* __restrict__ out,
-    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0) {
+    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, RopeTable rt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
   if (w >= B * n_ent) return;
@@ -51,18 +72,22 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
 
-  int i = 0;
-  for (; i + kUnroll <= m; i += kUnroll) {
+  // blocks of kUnroll tokens, the last one padded by repeating the final row with weight 0:
+  // every load is unconditional, so a block's loads are all in flight together (a tail loop
+  // of single tokens costs one memory latency per token)
+  for (int i = 0; i < m; i += kUnroll) {
     uint4 v0[kUnroll], v1[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint4* row = reinterpret_cast<const uint4*>(xb + (int64_t)(i + u) * D);
-      v0[u] = has0 ? ld_stream16(row + lane) : make_uint4(0, 0, 0, 0);
-      v1[u] = has1 ? ld_stream16(row + lane + kWave) : make_uint4(0, 0, 0, 0);
+      const int t = min(i + u, m - 1);
+      const uint4* row = reinterpret_cast<const uint4*>(xb + (int64_t)t * D);
+      v0[u] = ld_stream16(row + (has0 ? lane : 0));
+      v1[u] = ld_stream16(row + (has1 ? lane + kWave : 0));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const float a = expf(zb[i + u] - zmax) * inv;
+      const int t = min(i + u, m - 1);
+      const float a = i + u < m ? expf(zb[t] - zmax) * inv : 0.f;
       float f[8];
       unpack8(v0[u], f);
 #pragma unroll
@@ -72,20 +97,13 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
       for (int e = 0; e < 8; ++e) acc1[e] = fmaf(a, f[e], acc1[e]);
     }
   }
-  for (; i < m; ++i) {
-    const uint4* row = reinterpret_cast<const uint4*>(xb + (int64_t)i * D);
-    const float a = expf(zb[i] - zmax) * inv;
-    float f[8];
-    if (has0) {
-      unpack8(row[lane], f);
+  if (!has0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc0[e] = fmaf(a, f[e], acc0[e]);
-    }
-    if (has1) {
-      unpack8(row[lane + kWave], f);
+    for (int e = 0; e < 8; ++e) acc0[e] = 0.f;
+  }
+  if (!has1) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc1[e] = fmaf(a, f[e], acc1[e]);
-    }
+    for (int e = 0; e < 8; ++e) acc1[e] = 0.f;
   }
 
   // partial RoPE on the last d_rope dims, at the entry's position
@@ -100,7 +118,8 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float cs, sn;
-        rope_cs(rope_inv_freq(rope_base, pair0 + q, d_rope), p, &cs, &sn);
+        const int pair = pair0 + q;
+        rope_cs_fast(pair < kRopeTab ? rt.inv_freq[pair] : rope_inv_freq(rope_base, pair, d_rope), p, &cs, &sn);
         const float u0 = acc[2 * q], u1 = acc[2 * q + 1];
         acc[2 * q] = u0 * cs - u1 * sn;
         acc[2 * q + 1] = u0 * sn + u1 * cs;
@@ -178,14 +197,16 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
   const int waves = B * n_ent;
   dim3 grid((waves + kCompressWaves - 1) / kCompressWaves), block(kCompressWaves * kWave);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  RopeTable rt{};
+  for (int i = 0; i < kRopeTab && i < d_rope / 2; ++i) rt.inv_freq[i] = pow((double)rope_base, -2.0 * i / d_rope);
   if (out_dtype == CSKV_BF16)
     compress_kernel<false><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
                                                   d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                  out_seq_stride, out_entry0);
+                                                  out_seq_stride, out_entry0, rt);
   else
     compress_kernel<true><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
                                                  d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                 out_seq_stride, out_entry0);
+                                                 out_seq_stride, out_entry0, rt);
   CSKV_LAUNCH_CHECK(name);
   return CSKV_OK;
 }
