@@ -41,6 +41,9 @@ def parse():
                     help="only run a 1 GiB device copy (PMC calibration) and exit")
     ap.add_argument("--index-only", action="store_true",
                     help="only run --steps csa_index_topk calls on the 1M-context indexer inputs (for profilers)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
+                         "--steps timed runs of each call after one warm-up")
     return ap.parse_args()
 
 
@@ -96,6 +99,9 @@ def main():
 
     if args.index_only:
         index_only(args, dev)
+        return
+    if args.prefill:
+        prefill_bench(args, dev)
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
@@ -264,6 +270,45 @@ def index_only(args, dev):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     print(json.dumps({"index_only_calls": args.steps, "mean_ms": sum(ts) / len(ts), "min_ms": min(ts)}))
+
+
+def prefill_bench(args, dev):
+    """The 128K-token CSA prefill: each call timed alone with HIP events (median of --steps runs)."""
+    import torch
+
+    from compressed_sparse_kv_03_amd import configs, prefill
+
+    w = configs.C4
+    p = prefill.CsaPrefill(w, dev)
+    calls = {"compress": p.compress, "index": p.index, "attend": p.attend}
+    for f in calls.values():  # warm-up, in pipeline order
+        f()
+    torch.cuda.synchronize()
+    work = p.work()
+    peaks = {"compress": ("hbm", PEAK_HBM_GBS, "GB/s"), "index": ("mfma", 10100.0, "TFLOP/s"),
+             "attend": ("mfma", 2500.0, "TFLOP/s")}
+    res = {}
+    for name, f in calls.items():
+        ts = []
+        for _ in range(max(1, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        bound, peak, unit = peaks[name]
+        r = {"ms": round(ms, 4), "bytes": work[name]["bytes"], "GB/s": round(work[name]["bytes"] / ms / 1e6, 1)}
+        if "flops" in work[name]:
+            r["flops"] = work[name]["flops"]
+            r["TFLOP/s"] = round(work[name]["flops"] / ms / 1e9, 1)
+        achieved = r["GB/s"] if bound == "hbm" else r["TFLOP/s"]
+        r["roofline"] = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                         "frac": round(achieved / peak, 4)}
+        res[name] = r
+    print(json.dumps({"prefill": w.name, "runs": max(1, args.steps), "calls": res,
+                      "total_ms": round(sum(r["ms"] for r in res.values()), 4)}))
 
 
 def cpu_baseline(pair):
