@@ -35,6 +35,12 @@ constexpr int kIdxNT = 256;          // threads per workgroup
 constexpr int kSub = 4096;           // entries scored per LDS pass
 constexpr int kMaxMergeKeys = 8192;  // chunk winners merged per query in stage 2
 
+__device__ __forceinline__ f32x4 mfma_fp4_acc(uint4 a, uint4 b, int sa, int sb, f32x4 acc) {
+  i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, acc, 4, 4, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ f32x4 mfma_fp4(uint4 a, uint4 b, int sa, int sb) {
   i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
@@ -820,14 +826,364 @@ static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipS
   return CSKV_OK;
 }
 
+// ---------------------------------------------------------------- many-queries path (prefill)
+//
+// Kernel P (grid B*ceil(T/QB) x C, 512 threads): a workgroup takes QB consecutive queries of
+// one sequence and streams the entries of chunk c that any of them can see through LDS, one
+// tile of KT entries at a time, so an entry is read once per QB queries instead of once per
+// query. Each wave owns two row tiles of the MFMA; with H_I <= 8 a row tile holds two queries
+// (8 rows each), so a wave scores four queries per group of 16 entries. Each query keeps its
+// candidates in an LDS buffer: a key joins when it is at or above the query's threshold, a key
+// value that at least k keys of the buffer reached when it was last reduced, so the buffer
+// always contains the query's top-k of the entries seen so far. A wave reduces a buffer of its
+// own queries when the next tile could overflow it, to between k and k + 64 keys (a pivot
+// search over the keys with ballot counts; keys are distinct), and at the end ranks the
+// survivors and writes the k best (one chunk), or writes them as the chunk's k winners for the
+// merge kernel (several chunks; the two-stage exactness argument of the decode path applies).
+constexpr int kPfNT = 512;
+constexpr int kPfWaves = kPfNT / kWave;
+constexpr int kPfRT = 2;          // MFMA row tiles per wave
+constexpr int kPfCap = 512;       // candidate slots per query
+constexpr int kPfKMax = 128;      // k on this path
+constexpr int kPfPL = kPfCap / kWave;
+constexpr int kPfU = 4;           // entry groups (of 16) per scoring step
+constexpr int kPfMargin = 64;     // a reduction leaves between k and k + kPfMargin keys
+constexpr int kPfRankPL = (kPfKMax + kPfMargin + kWave - 1) / kWave;  // survivors ranked per lane
+constexpr int kPfTileBytes = 10240;  // key codes of one tile (KT x pitch)
+
+template <int KS>
+struct PfTile {
+  static constexpr int KT = KS == 1 ? 128 : (KS == 2 ? 64 : 32);  // entries per tile
+};
+// a buffer is reduced (to k keys) when the next tile could overflow it; between reductions
+// at least kPfCap - KT - k keys join, which keeps reductions rare once the threshold settles
+static_assert(kPfCap - 128 - kPfKMax - kPfMargin >= 192, "room between reductions");
+
+template <int QB>
+struct PfSmem {
+  __align__(16) uint8_t kt[2][kPfTileBytes + 256];  // codes, row pitch = kbytes + 16 (+ read slack)
+  __align__(16) uint8_t st[2][512];                 // E8M0 scales, KT x sbytes
+  uint64_t cand[QB][kPfCap];
+  int cnt[QB];
+  int nv[QB];
+};
+
+// A threshold th with kk <= #{key >= th} <= kk + margin among the n distinct keys buf[0..n)
+// (1 <= kk <= n <= kPfCap), by one wave. Invariant: count(lo) >= kk > count(hi). Each step
+// takes as pivot a key strictly inside (lo, hi) (the first such key of the lowest lane that
+// holds one; the buffer order is unrelated to the key order) and counts the keys at or above
+// it with one comparison, ballot and popcount per slot. While count(lo) > kk + margin >= kk +
+// 1 there are at least two keys in [lo, hi), so a pivot exists. The result is at or below the
+// kk-th largest key (count >= kk).
+__device__ uint64_t wave_threshold(const uint64_t* buf, int n, int kk, int margin) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t v[kPfPL];
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) v[i] = lane + kWave * i < n ? buf[lane + kWave * i] : 0;
+  uint64_t lo = 0, hi = ~0ull;  // every key is >= 0; none reaches ~0 (an ordered score never does)
+  int clo = n;
+  while (clo > kk + margin) {
+    uint64_t cand = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = kPfPL - 1; i >= 0; --i) {
+      const bool in = lane + kWave * i < n && v[i] > lo && v[i] < hi;
+      cand = in ? v[i] : cand;
+      found = found || in;
+    }
+    const uint64_t has = __ballot(found);
+    const int L = __builtin_ctzll(has);
+    const uint64_t piv = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(cand >> 32), L) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((uint32_t)cand, L);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kPfPL; ++i) c += __popcll(__ballot(lane + kWave * i < n && v[i] >= piv));
+    if (c >= kk) {
+      lo = piv;
+      clo = c;
+    } else {
+      hi = piv;
+    }
+  }
+  return lo;
+}
+
+// Keeps the keys >= th of buf[0..n) at the front of buf (order not kept); returns their count.
+__device__ int wave_compact_ge(uint64_t* buf, int n, uint64_t th) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t v[kPfPL];
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) v[i] = lane + kWave * i < n ? buf[lane + kWave * i] : 0;
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) {
+    const bool p = lane + kWave * i < n && v[i] >= th;
+    const uint64_t m = __ballot(p);
+    if (p) buf[base + __popcll(m & lt)] = v[i];
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  return base;
+}
+
+// ReLU of the four accumulator rows (an integer max on the bit pattern: negative floats, -0
+// included, have a negative pattern), weighted by the head weights or, without them, summed
+// (rows past H_I hold a zero query, so their ReLU is 0 either way).
+template <bool HW>
+__device__ __forceinline__ float head_sum(const f32x4& acc, const float* hw) {
+  float r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(max(__float_as_int(acc[i]), 0));
+  if (HW) return fmaf(hw[3], r[3], fmaf(hw[2], r[2], fmaf(hw[1], r[1], hw[0] * r[0])));
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
+// Appends key (score, e) to query q's candidates when it is at or above the query's threshold.
+__device__ __forceinline__ void pf_append(uint64_t (*cand)[kPfCap], int* cnt, int q, float score, int e,
+                                          uint64_t th) {
+  const uint64_t key = make_key(score, (uint32_t)e);
+  if (key >= th) cand[q][atomicAdd(&cnt[q], 1)] = key;
+}
+
+template <int KS, int QPT, bool HW>
+__global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb) {
+  constexpr int KT = PfTile<KS>::KT;
+  constexpr int U = KT / 16 < kPfU ? KT / 16 : kPfU;  // groups per scoring step (divides KT / 16)
+  static_assert((KT / 16) % U == 0 && U % 2 == 0, "whole, paired steps per tile");
+  constexpr int RPQ = 16 / QPT;          // MFMA rows per query
+  constexpr int QW = kPfRT * QPT;        // queries per wave
+  constexpr int QB = kPfWaves * QW;      // queries per workgroup
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  PfSmem<QB>& sm = *reinterpret_cast<PfSmem<QB>*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 4, col = lane & 15;
+  const int b = blockIdx.x / nqb;
+  const int qb = nqb - 1 - (blockIdx.x - b * nqb);  // the longest (causal) blocks start first
+  const int t0 = qb * QB;
+  const int chunk = blockIdx.y;
+  const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
+  const int pitch = kbytes + 16;
+  const int kchunks = kbytes >> 4;       // 16-byte pieces per key
+
+  if (tid < QB) {
+    const int t = t0 + tid;
+    sm.nv[tid] = t < a.T ? min(a.n_valid[(int64_t)b * a.T + t], a.N_cap) : 0;
+    sm.cnt[tid] = 0;
+  }
+  // A operand: lane row `col` is query col / RPQ of the row tile, head col % RPQ
+  uint4 qa[kPfRT][KS];
+  int qs[kPfRT][KS];
+  float hw[kPfRT][4];
+#pragma unroll
+  for (int rt = 0; rt < kPfRT; ++rt) {
+    const int ta = t0 + wave * QW + rt * QPT + col / RPQ, ha = col % RPQ;
+    const bool oka = ta < a.T && ha < a.H_I;
+    const int64_t qrow = ((int64_t)b * a.T + ta) * a.H_I + ha;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool okk = oka && (s * 128 + G * 32) < a.D_I;
+      qa[rt][s] = okk ? *reinterpret_cast<const uint4*>(a.iq + qrow * kbytes + s * 64 + G * 16) : make_uint4(0, 0, 0, 0);
+      qs[rt][s] = okk ? (int)a.iq_scale[qrow * sbytes + s * 4 + G] : 127;
+    }
+    // accumulator rows 4G + r: query (4G + r) / RPQ, head (4G + r) % RPQ
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * G + r;
+      const int tr = t0 + wave * QW + rt * QPT + row / RPQ, hr = row % RPQ;
+      hw[rt][r] = (tr < a.T && hr < a.H_I) ? (a.head_w ? a.head_w[((int64_t)b * a.T + tr) * a.H_I + hr] : 1.0f) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // the query of this lane's scores within a row tile (QPT = 2: lane groups 0, 1 -> query 0,
+  // groups 2, 3 -> query 1; QPT = 1: one query)
+  const int jq = QPT == 2 ? (G >> 1) : 0;
+  int nvq[kPfRT];
+  uint64_t th[kPfRT];
+  float thf[kPfRT];  // the score of th (a key >= th has a score >= thf)
+#pragma unroll
+  for (int rt = 0; rt < kPfRT; ++rt) {
+    nvq[rt] = sm.nv[wave * QW + rt * QPT + jq];
+    th[rt] = 0;
+    thf[rt] = -INFINITY;
+  }
+  int cmax = 0;
+#pragma unroll 1
+  for (int i = 0; i < QB; ++i) cmax = max(cmax, sm.nv[i]);
+  const int c0 = chunk * a.chunk;
+  const int c1 = min(c0 + a.chunk, cmax);
+  const int n_tiles = c0 < c1 ? (c1 - c0 + KT - 1) / KT : 0;
+  const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
+  const uint8_t* iksb = a.ik_scale + (int64_t)b * a.N_cap * sbytes;
+
+  // tile staging: each thread moves at most one piece of 16 code bytes and one scale byte
+  static_assert(KT * 16 <= kPfNT * 16 && KT * (KS * 64) / 16 <= kPfNT, "one piece per thread");
+  uint4 rv;
+  uint8_t rs;
+  const int key_c = tid / kchunks, part_c = tid - key_c * kchunks;
+  const int key_s = tid / sbytes, part_s = tid - key_s * sbytes;
+  auto tile_load = [&](int it) {
+    const int e0 = c0 + it * KT;
+    rv = tid < KT * kchunks ? ld_stream16(ikb + (int64_t)min(e0 + key_c, c1 - 1) * kbytes + 16 * part_c)
+                            : make_uint4(0, 0, 0, 0);
+    rs = tid < KT * sbytes ? iksb[(int64_t)min(e0 + key_s, c1 - 1) * sbytes + part_s] : (uint8_t)127;
+  };
+  auto tile_store = [&](int buf) {
+    if (tid < KT * kchunks) *reinterpret_cast<uint4*>(&sm.kt[buf][key_c * pitch + 16 * part_c]) = rv;
+    if (tid < KT * sbytes) sm.st[buf][tid] = rs;
+  };
+  if (n_tiles > 0) {
+    tile_load(0);
+    tile_store(0);
+  }
+  // every prologue load done here: otherwise the wait for the query operands, merged with the
+  // loop's own loads at the loop head, becomes a wait for the next tile in every iteration
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int it = 0; it < n_tiles; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n_tiles) tile_load(it + 1);
+    const uint8_t* kt = sm.kt[cur];
+    const uint8_t* st = sm.st[cur];
+    const int e0 = c0 + it * KT;
+    // U groups of 16 entries per step: their MFMAs issue back to back, then the scores
+#pragma unroll 1
+    for (int g = 0; g < KT / 16; g += U) {
+      f32x4 acc[U][kPfRT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kl = 16 * (g + u) + col;
+        uint4 kv[KS];
+        int ks[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bool okk = (s * 128 + G * 32) < a.D_I;
+          kv[s] = *reinterpret_cast<const uint4*>(kt + kl * pitch + (okk ? s * 64 + G * 16 : 0));
+          ks[s] = okk ? (int)st[kl * sbytes + s * 4 + G] : 127;
+        }
+#pragma unroll
+        for (int rt = 0; rt < kPfRT; ++rt) {
+          acc[u][rt] = mfma_fp4(qa[rt][0], kv[0], qs[rt][0], ks[0]);
+#pragma unroll
+          for (int s = 1; s < KS; ++s) acc[u][rt] = mfma_fp4_acc(qa[rt][s], kv[s], qs[rt][s], ks[s], acc[u][rt]);
+        }
+      }
+      if constexpr (QPT == 2) {
+        // lane group G holds rows 4G..4G+3: heads 0-3 / 4-7 of query 0 (G = 0, 1) and of query 1
+        // (G = 2, 3). One permlane16 swap of the two groups' partial sums and one add leave
+        // row 0 = group 0's query 0, row 1 = group 1's query 0, row 2 / 3 = query 1: every lane
+        // then owns one (query, entry) score, query G >> 1 (= jq) and entry 16(g + (G & 1)) + col.
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+          const int e = e0 + 16 * (g + u + (G & 1)) + col;
+#pragma unroll
+          for (int rt = 0; rt < kPfRT; ++rt) {
+            const float p0 = head_sum<HW>(acc[u][rt], hw[rt]), p1 = head_sum<HW>(acc[u + 1][rt], hw[rt]);
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+            const float part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (e < nvq[rt] && part >= thf[rt]) pf_append(sm.cand, sm.cnt, wave * QW + rt * QPT + jq, part, e, th[rt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + 16 * (g + u) + col;
+#pragma unroll
+          for (int rt = 0; rt < kPfRT; ++rt) {
+            float part = head_sum<HW>(acc[u][rt], hw[rt]);
+            part += __shfl_xor(part, 16, kWave);
+            part += __shfl_xor(part, 32, kWave);
+            if (G == 0 && e < nvq[rt] && part >= thf[rt]) pf_append(sm.cand, sm.cnt, wave * QW + rt, part, e, th[rt]);
+          }
+        }
+      }
+    }
+    // reduce the wave's buffers that the next tile could overflow
+#pragma unroll
+    for (int rt = 0; rt < kPfRT; ++rt) {
+#pragma unroll
+      for (int j = 0; j < QPT; ++j) {
+        const int q = wave * QW + rt * QPT + j;
+        const int n = __builtin_amdgcn_readfirstlane(sm.cnt[q]);
+        if (n > kPfCap - KT) {
+          const uint64_t kth = wave_threshold(sm.cand[q], n, a.k, kPfMargin);
+          const int m = wave_compact_ge(sm.cand[q], n, kth);
+          if (lane == 0) sm.cnt[q] = m;
+          if (jq == j) {
+            th[rt] = kth;
+            thf[rt] = ordered_to_score((uint32_t)(kth >> 32));
+          }
+        }
+      }
+    }
+    if (it + 1 < n_tiles) tile_store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // final: each query's top min(k, candidates), ranked (one chunk) or as chunk winners
+#pragma unroll 1
+  for (int j = 0; j < QW; ++j) {
+    const int q = wave * QW + j;
+    const int t = t0 + q;
+    if (t >= a.T) continue;
+    const int64_t bq = (int64_t)b * a.T + t;
+    uint64_t* buf = sm.cand[q];
+    int n = __builtin_amdgcn_readfirstlane(sm.cnt[q]);
+    const int kk = min(a.k, n);
+    if (n > kk + kPfMargin) n = wave_compact_ge(buf, n, wave_threshold(buf, n, kk, kPfMargin));
+    // rank the n (<= kk + margin) survivors; those ranked below kk are the answer
+    uint64_t key[kPfRankPL];
+    int rank[kPfRankPL];
+#pragma unroll
+    for (int i = 0; i < kPfRankPL; ++i) {
+      key[i] = lane + kWave * i < n ? buf[lane + kWave * i] : 0;
+      rank[i] = 0;
+    }
+    for (int j2 = 0; j2 < n; ++j2) {
+      const uint64_t x = buf[j2];
+#pragma unroll
+      for (int i = 0; i < kPfRankPL; ++i) rank[i] += x > key[i];
+    }
+    if (a.n_chunks > 1) {
+      uint64_t* out = a.part + (bq * a.n_chunks + chunk) * a.k;
+#pragma unroll
+      for (int i = 0; i < kPfRankPL; ++i)
+        if (lane + kWave * i < n && rank[i] < kk) out[rank[i]] = key[i];
+      for (int i = kk + lane; i < a.k; i += kWave) out[i] = 0;
+      continue;
+    }
+    int32_t* oi = a.out_idx + bq * a.k;
+    float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
+#pragma unroll
+    for (int i = 0; i < kPfRankPL; ++i) {
+      if (lane + kWave * i < n && rank[i] < kk) {
+        oi[rank[i]] = (int32_t)(~(uint32_t)key[i]);
+        if (os) os[rank[i]] = ordered_to_score((uint32_t)(key[i] >> 32));
+      }
+    }
+    for (int i = kk + lane; i < a.k; i += kWave) {
+      oi[i] = -1;
+      if (os) os[i] = -INFINITY;
+    }
+  }
+}
+
 struct IndexPlan {
   int chunk, n_chunks, cap;
   size_t ws;
   bool decode;
+  bool block;    // many-queries path (kernel P)
+  int qpt, nqb;  // kernel P: queries per MFMA row tile, query blocks per sequence
 };
 
-static IndexPlan plan_index(int B, int T, int N_cap, int k) {
+static IndexPlan plan_index(int B, int T, int N_cap, int H_I, int D_I, int k) {
   IndexPlan p;
+  p.block = false;
+  p.qpt = 1;
+  p.nqb = 0;
   // query-parallel path: at least ~1024 workgroups over the whole job; chunks of >= 1024
   // entries (multiples of 16) and no more than kMaxMergeKeys/k chunks per query
   const int max_chunks = kMaxMergeKeys / k > 0 ? kMaxMergeKeys / k : 1;
@@ -851,7 +1207,59 @@ static IndexPlan plan_index(int B, int T, int N_cap, int k) {
   // decode path: few queries (at most one chunk workgroup per CU when they are alone)
   p.decode = k <= 1024 && queries <= 256;
   if (p.decode) p.ws = decode_ws_bytes((int)queries, N_cap, k);
+  // many queries: blocks of consecutive queries share the entry stream (kernel P); chunks of
+  // the entries only when the query blocks alone leave the GPU idle (then the merge kernel)
+  if (!p.decode && k <= kPfKMax) {
+    p.block = true;
+    p.qpt = H_I <= 8 ? 2 : 1;
+    const int QB = kPfWaves * kPfRT * p.qpt;
+    const int KT = D_I <= 128 ? PfTile<1>::KT : (D_I <= 256 ? PfTile<2>::KT : PfTile<4>::KT);
+    p.nqb = (T + QB - 1) / QB;
+    const int64_t nblk = (int64_t)B * p.nqb;
+    int C = (int)((512 + nblk - 1) / nblk);
+    const int cmax_merge = kMaxMergeKeys / k;
+    if (C > cmax_merge) C = cmax_merge;
+    const int cmax_size = (N_cap + 1023) / 1024;  // chunks of at least 1024 entries
+    if (C > cmax_size) C = cmax_size;
+    if (C < 1) C = 1;
+    int chunk = (N_cap + C - 1) / C;
+    chunk = (chunk + KT - 1) / KT * KT;
+    p.chunk = chunk;
+    p.n_chunks = (N_cap + chunk - 1) / chunk;
+    if (p.n_chunks < 1) p.n_chunks = 1;
+    p.cap = 512;
+    p.ws = p.n_chunks > 1 ? (size_t)queries * p.n_chunks * k * sizeof(uint64_t) : 0;
+  }
   return p;
+}
+
+template <int KS, int QPT>
+static void launch_block_ks(const IndexArgs& a, int nqb, hipStream_t s) {
+  constexpr int QB = kPfWaves * kPfRT * QPT;
+  const size_t smem = sizeof(PfSmem<QB>);
+  auto kern = a.head_w ? index_block_kernel<KS, QPT, true> : index_block_kernel<KS, QPT, false>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipLaunchKernelGGL(kern, dim3(a.B * nqb, a.n_chunks), dim3(kPfNT), smem, s, a, nqb);
+}
+
+static int launch_block(const IndexArgs& a, const IndexPlan& p, int ks, hipStream_t s) {
+  if (p.qpt == 2) {
+    if (ks == 1) launch_block_ks<1, 2>(a, p.nqb, s);
+    else if (ks == 2) launch_block_ks<2, 2>(a, p.nqb, s);
+    else launch_block_ks<4, 2>(a, p.nqb, s);
+  } else {
+    if (ks == 1) launch_block_ks<1, 1>(a, p.nqb, s);
+    else if (ks == 2) launch_block_ks<2, 1>(a, p.nqb, s);
+    else launch_block_ks<4, 1>(a, p.nqb, s);
+  }
+  CSKV_LAUNCH_CHECK("csa_index_topk (query blocks)");
+  if (p.n_chunks > 1) {
+    const size_t smem = sizeof(Stage2Smem<512>);
+    (void)hipFuncSetAttribute((const void*)index_merge_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)smem);
+    hipLaunchKernelGGL(index_merge_kernel<512>, dim3(a.B * a.T), dim3(kIdxNT), smem, s, a);
+  }
+  return CSKV_OK;
 }
 
 template <int CAP, int KS>
@@ -882,10 +1290,8 @@ static int launch_index(const IndexArgs& a, int queries, int ks, hipStream_t s) 
 using namespace cskv;
 
 extern "C" CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, int D_I, int k) {
-  (void)H_I;
-  (void)D_I;
   if (B < 1 || T < 1 || N_cap < 0 || k < 1 || k > 1024) return 0;
-  return plan_index(B, T, N_cap > 0 ? N_cap : 1, k).ws;
+  return plan_index(B, T, N_cap > 0 ? N_cap : 1, H_I, D_I, k).ws;
 }
 
 extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scale, const float* head_w,
@@ -906,8 +1312,8 @@ extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scal
   CSKV_REQUIRE(N_cap == 0 || (reinterpret_cast<uintptr_t>(ik_scale) & 3) == 0, CSKV_EINVAL,
                "csa_index_topk: ik_scale must be 4-byte aligned");
   const int Nc = N_cap > 0 ? N_cap : 1;
-  IndexPlan p = plan_index(B, T, Nc, k);
-  CSKV_REQUIRE(ws && ws_bytes >= p.ws, CSKV_EWORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes,
+  IndexPlan p = plan_index(B, T, Nc, H_I, D_I, k);
+  CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes,
                p.ws);
   CSKV_REQUIRE((int64_t)B * T < (1ll << 31), CSKV_ENOTSUP, "csa_index_topk: too many queries");
   IndexArgs a{iq, iq_scale, head_w, ik, ik_scale, n_valid, B, T, N_cap, H_I, D_I, k,
@@ -915,8 +1321,9 @@ extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scal
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int queries = B * T;
   const int ks = (D_I + 127) / 128;
-  int rc = p.decode ? launch_decode(a, queries, ks, ws, s)
-                    : (p.cap == 512 ? launch_index<512>(a, queries, ks, s) : launch_index<2048>(a, queries, ks, s));
+  int rc = p.decode  ? launch_decode(a, queries, ks, ws, s)
+           : p.block ? launch_block(a, p, ks, s)
+                     : (p.cap == 512 ? launch_index<512>(a, queries, ks, s) : launch_index<2048>(a, queries, ks, s));
   if (rc != CSKV_OK) return rc;
   CSKV_LAUNCH_CHECK("csa_index_topk (merge)");
   return CSKV_OK;

@@ -133,3 +133,30 @@ def test_index_topk_when_the_sample_overstates_the_top():
     check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_)
     got = down(oi)[:, 0]
     assert all(set(range(0, 10 * stride, stride)) <= set(got[b].tolist()) for b in range(B))
+
+
+@pytest.mark.parametrize("B,T,H_I,D_I,k,N,ties", [
+    (2, 150, 8, 128, 128, 3000, False),    # two queries per MFMA row tile; ragged last query block
+    (1, 300, 16, 256, 64, 2500, False),    # one query per row tile, two 128-wide k steps
+    (1, 270, 5, 160, 16, 1100, False),     # partial second k step, 5 heads
+    (1, 260, 4, 512, 1, 700, False),       # four k steps, k = 1
+    (2, 200, 8, 128, 100, 9000, True),     # massive score ties, several entry chunks
+])
+def test_index_topk_query_blocks(B, T, H_I, D_I, k, N, ties):
+    """Many queries per call (the query-block path): every row bit-exact, arbitrary n_valid."""
+    say("index query blocks", B, T, H_I, D_I, k, N, ties)
+    rng = np.random.default_rng(T + D_I)
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 151 + D_I, DEV)
+    if ties:
+        base, bsc = synth.mxfp4_normal((6, D_I), 152, DEV)
+        pick = torch.from_numpy(rng.integers(0, 6, (B, N))).to(DEV)
+        ik, iks = base[pick].contiguous(), bsc[pick].contiguous()
+    else:
+        ik, iks = synth.mxfp4_normal((B, N, D_I), 153 + D_I, DEV)
+    nvh = rng.integers(0, N + 1, (B, T)).astype(np.int32)
+    nvh[:, :3] = [0, 1, min(k, N)]
+    hw = None
+    if ties:
+        hw = up(rng.choice(np.array([1.0, -1.0, 0.5, 2.0], np.float32), (B, T, H_I)))
+    oi, os_ = run_index(iq, iqs, ik, iks, up(nvh), k, hw)
+    check_against_oracle(iq, iqs, ik, iks, up(nvh), k, oi, os_, head_w=hw)
