@@ -307,8 +307,49 @@ def prefill_bench(args, dev):
         r["roofline"] = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                          "frac": round(achieved / peak, 4)}
         res[name] = r
-    print(json.dumps({"prefill": w.name, "runs": max(1, args.steps), "calls": res,
-                      "total_ms": round(sum(r["ms"] for r in res.values()), 4)}))
+    total_ms = sum(r["ms"] for r in res.values())
+    rec = {"prefill": w.name, "runs": max(1, args.steps), "calls": res, "total_ms": round(total_ms, 4),
+           "positions_per_s": round(w.L / (total_ms / 1e3), 1)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefill_cpu_baseline(p)
+    print(json.dumps(rec))
+
+
+def prefill_cpu_baseline(p, n_pos=256):
+    """The fp64 oracle on the host cores for a sample of prefill positions (spread over the prompt):
+    index + top-k over the visible entries, the entries those positions select, and attention."""
+    import numpy as np
+
+    from oracle import attention as oatt
+    from oracle import compress as ocomp
+    from oracle import indexer as oidx
+    from oracle import topk as otopk
+
+    w = p.w
+    m = w.m
+    rows = np.linspace(w.L // 8, w.L - 1, n_pos).astype(np.int64)
+    xh = p.x.cpu().numpy().view(np.uint16)
+    zh = p.z.cpu().numpy()[0]
+    ikh, iksh = p.ik.cpu().numpy()[0], p.iks.cpu().numpy()[0]
+    iqh, iqsh = p.iq[0, rows].cpu().numpy(), p.iqs[0, rows].cpu().numpy()
+    qh = p.q[rows].cpu().numpy().view(np.uint16)
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ent = np.zeros((p.N, w.D), np.uint16)
+    for r, t in enumerate(rows):
+        sc = oidx.scores(iqh[r][None], iqsh[r][None], ikh, iksh, np.array([(t + 1) // m]))
+        idx, _ = otopk.topk(sc, w.k)
+        for j in idx[0]:
+            if j >= 0:
+                _, bits, _ = ocomp.compress(xh[j * m:(j + 1) * m], zh[j * m:(j + 1) * m], j * m, m, w.d_rope,
+                                            w.rope_base, "bf16")
+                ent[j] = bits[0]
+        oatt.prefill_one(qh[r], int(t), 0, oatt.Entries(ent, None, "bf16"), m, idx[0], xh, w.W, w.d_rope, w.d_v,
+                         w.rope_base, w.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_pos / dt, 3), "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_pos} positions of the 128K-token prefill (index + top-k over their visible entries, "
+                      f"compression of the entries they select, attention; fp64 numpy oracle, {dt:.1f} s)"}
 
 
 def cpu_baseline(pair):
