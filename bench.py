@@ -41,6 +41,9 @@ def parse():
                     help="only run a 1 GiB device copy (PMC calibration) and exit")
     ap.add_argument("--index-only", action="store_true",
                     help="only run --steps csa_index_topk calls on the 1M-context indexer inputs (for profilers)")
+    ap.add_argument("--share", choices=["none", "reuse", "reindex"], default="none",
+                    help="cross-layer index sharing: the CSA layers of pairs 1.. reuse pair 0's top-k, or "
+                         "re-index pair 0's KV and keys with their own queries")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -110,10 +113,18 @@ def main():
     spec = pairs[0].s
     torch.cuda.synchronize()
 
+    share = None if args.share == "none" else args.share
+
+    def step_all(i):
+        for p_, pr_ in enumerate(pairs):
+            if p_ == 0 or share is None:
+                pr_.step(i)
+            else:
+                pr_.step(i, share=share, src=pairs[0])
+
     # ---- warmup: W eager steps of every pair, then restore the windows
     for i in range(min(W, K)):
-        for pr in pairs:
-            pr.step(i)
+        step_all(i)
     torch.cuda.synchronize()
     for pr in pairs:
         pr.restore()
@@ -122,8 +133,7 @@ def main():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(K):
-            for pr in pairs:
-                pr.step(i)
+            step_all(i)
     torch.cuda.synchronize()
     for pr in pairs:
         pr.restore()
@@ -145,7 +155,9 @@ def main():
     sb = pairs[0].step_bytes()
     sf = pairs[0].step_flops()
     step_bytes = sum(sb.values())
-    hbm_gbs = step_bytes * P / (ms_per_step / 1e3) / 1e9
+    # with reuse, pairs 1.. read no indexer keys
+    stack_bytes = step_bytes * P - (sb["csa_index"] * (P - 1) if share == "reuse" else 0)
+    hbm_gbs = stack_bytes / (ms_per_step / 1e3) / 1e9
 
     # ---- per-call timings with a cold Infinity Cache (512 MB write before each launch)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -207,6 +219,8 @@ def main():
                         "context 2^20, H=64, D=512+64, fp8 entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "tokens_per_step_per_pair": spec.B,
+            **({} if share is None else {"index_sharing": f"{share}: CSA layers of pairs 1..{P - 1} "
+                                                          f"{'take pair 0 top-k' if share == 'reuse' else 're-index pair 0 KV'}"}),
         },
         "hbm_gbs": round(hbm_gbs, 1),
         "step_bytes_per_pair": step_bytes,

@@ -126,11 +126,24 @@ class LayerPair:
         return st
 
     # ------------------------------------------------------------------ one step
-    def step(self, i, stream=None):
+    def step(self, i, stream=None, share=None, src=None):
+        """Decode step i of both layers.
+
+        share (cross-layer index sharing of the CSA layer, with `src` another LayerPair of the
+        same shapes that has already run step i):
+          None      -- the CSA layer has its own KV, indexer keys and query (the default);
+          "reuse"   -- its own KV, but no indexer call: it attends to src's top-k entries;
+          "reindex" -- src's KV, window and indexer keys (no append or compression of its own),
+                       with its own indexer query and hence its own top-k.
+        """
         s = self.s
         B, D, W = s.B, s.D, s.W
         t = int(self.t_host[i])
+        assert share in (None, "reuse", "reindex") and (share is None or src is not None)
+        kv = {"csa": src if share == "reindex" else self, "hca": self}
         for name in ("csa", "hca"):
+            if kv[name] is not self:
+                continue
             native.cskv_ring_append(self.xn[name][i], self.zn[name][i], self.pos[i], self.ring[name],
                                     self.ringz[name], B, D, W, stream)
             m = self.m[name]
@@ -140,12 +153,18 @@ class LayerPair:
                 fn(self.ring[name][:, slot0:], W * D, self.ringz[name][:, slot0:], W, self.pos0c[name][i], B, m, D,
                    s.d_rope, m, 0, s.rope_base, native.CSKV_FP8_E4M3, self.ckv[name], self.scl[name],
                    self.cap[name], self.entry0[name][i], stream)
-        native.csa_index_topk(self.iq[i], self.iqs[i], None, self.ik, self.iks, self.nvalid[i], B, 1,
-                              self.cap["csa"], s.H_I, s.D_I, s.k, self.topk[i], None, self.ws_idx, None, stream)
+        if share == "reuse":
+            topk = src.topk[i]
+        else:
+            ik = kv["csa"]
+            native.csa_index_topk(self.iq[i], self.iqs[i], None, ik.ik, ik.iks, self.nvalid[i], B, 1,
+                                  self.cap["csa"], s.H_I, s.D_I, s.k, self.topk[i], None, self.ws_idx, None, stream)
+            topk = self.topk[i]
         for name in ("csa", "hca"):
-            native.hybrid_attn_decode(self.q[name][i], self.pos[i], self.ckv[name], self.scl[name],
+            c = kv[name]
+            native.hybrid_attn_decode(self.q[name][i], self.pos[i], c.ckv[name], c.scl[name],
                                       native.CSKV_FP8_E4M3, self.cap[name], self.nent[name][i],
-                                      self.topk[i] if name == "csa" else None, s.k, self.ring[name], W, B, s.H, D,
+                                      topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
                                       self.ws_att[name], None, stream)
 

@@ -35,35 +35,34 @@ class Layer:
         self.ring_x, self.ring_z = ring_x, ring_z
         self.k, self.ik, self.ik_scale = k, ik, ik_scale
 
-    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True):
+    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True, sel_from=None, update=True):
         """Positions t [B]; x_new [B, D] bf16; z_new [B]; q [B, H, D] bf16; iq [B, H_I, D_I/2].
 
         Returns (o fp64 [B, H, d_v], lse [B, H], idx int32 [B, k] or None); with
         outputs=False only the state update (window, re-compression) runs.
+
+        Cross-layer index sharing ([P1] section "주요 댓글" on the indexer that chooses what
+        attention reads, and the reuse / re-index layer modes): sel_from [B, k] gives the
+        top-k of another layer, used instead of this layer's own indexer ("reuse"); with
+        update=False the layer only reads its (shared) window and entries, another layer
+        having appended and compressed them ("re-index": its own query, shared KV and keys).
         """
         B = len(t)
         outs, lses, idxs = [], [], []
         for b in range(B):
             tb = int(t[b])
-            self.ring_x[b, tb % self.W] = x_new[b]
-            self.ring_z[b, tb % self.W] = z_new[b]
-            if (tb + 1) % self.m == 0:
-                j = (tb + 1) // self.m - 1
-                assert j == self.n_entries[b], "entry count out of step with position"
-                p0 = tb - self.m + 1
-                slots = np.arange(p0, tb + 1) % self.W
-                _, stored, s = compress.compress(self.ring_x[b, slots], self.ring_z[b, slots], p0,
-                                                 self.m, self.d_rope, self.rope_base, self.dtype)
-                self.ckv[b, j] = stored[0]
-                if s is not None:
-                    self.ckv_scale[b, j] = s[0]
-                self.n_entries[b] = j + 1
-            n = int(self.n_entries[b])
-            assert n == (tb + 1) // self.m
+            if update:
+                self._update(b, tb, x_new[b], z_new[b])
+                n = int(self.n_entries[b])
+                assert n == (tb + 1) // self.m
+            else:
+                n = (tb + 1) // self.m  # the sharing layer has brought the entries up to t
             if not outputs:
                 continue
             sel = None
-            if self.kind == "csa":
+            if self.kind == "csa" and sel_from is not None:
+                sel = np.asarray(sel_from[b])
+            elif self.kind == "csa":
                 sc = indexer.scores(iq[b][None], iq_scale[b][None], self.ik[b, :n], self.ik_scale[b, :n],
                                     np.array([n]))
                 sel, _ = topk_mod.topk(sc, self.k)
@@ -78,3 +77,19 @@ class Layer:
         if not outputs:
             return None, None, None
         return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)
+
+    def _update(self, b, tb, x_new, z_new):
+        """Window append of position tb and, at a block end, its compression (sequence b)."""
+        self.ring_x[b, tb % self.W] = x_new
+        self.ring_z[b, tb % self.W] = z_new
+        if (tb + 1) % self.m == 0:
+            j = (tb + 1) // self.m - 1
+            assert j == self.n_entries[b], "entry count out of step with position"
+            p0 = tb - self.m + 1
+            slots = np.arange(p0, tb + 1) % self.W
+            _, stored, s = compress.compress(self.ring_x[b, slots], self.ring_z[b, slots], p0,
+                                             self.m, self.d_rope, self.rope_base, self.dtype)
+            self.ckv[b, j] = stored[0]
+            if s is not None:
+                self.ckv_scale[b, j] = s[0]
+            self.n_entries[b] = j + 1

@@ -104,3 +104,52 @@ def test_hybrid_loop_1m_sampled_steps():
     pair.run(0, spec.steps)
     torch.cuda.synchronize()
     assert check_loop(pair, {0, 3, 4, 127, 128, 255}) == 12
+
+
+@pytest.mark.parametrize("share", ["reuse", "reindex"])
+def test_hybrid_loop_cross_layer_index_sharing(share):
+    """A second CSA layer that reuses the first layer's top-k (its own KV), or re-indexes the first
+    layer's KV and keys with its own query; checked every step against the oracle run the same way."""
+    from dataclasses import replace
+
+    spec0 = hybrid.LayerPairSpec(B=2, L=2048, steps=40, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
+                                 wid=57)
+    spec1 = replace(spec0, wid=58)
+    say("hybrid sharing", share, spec1)
+    p0, p1 = hybrid.LayerPair(spec0), hybrid.LayerPair(spec1)
+    for i in range(spec0.steps):
+        p0.step(i)
+        p1.step(i, share=share, src=p0)
+    torch.cuda.synchronize()
+    st0, st1 = p0.host_state(), p1.host_state()
+    l0, l1 = oracle_layers(spec0, st0), oracle_layers(spec1, st1)
+    if share == "reindex":  # the second CSA layer reads the first one's entries, window and keys
+        a = l0["csa"]
+        l1["csa"] = ohyb.Layer("csa", spec1.m_csa, spec1.W, spec1.d_rope, spec1.d_v, spec1.rope_base, spec1.scale,
+                               a.ckv, a.ckv_scale, "fp8", a.n_entries, a.ring_x, a.ring_z, k=spec1.k,
+                               ik=st0["ik"], ik_scale=st0["iks"])
+    out = {n: p1.out[n].cpu().numpy() for n in ("csa", "hca")}
+    lse = {n: p1.lse[n].cpu().numpy() for n in ("csa", "hca")}
+    tk1 = p1.topk.cpu().numpy()
+    for i in range(spec0.steps):
+        t = np.full(spec0.B, spec0.L + i)
+        idx0 = None
+        for name, lay in l0.items():
+            h = st0[name]
+            iq = st0["iq"][i][:, 0] if name == "csa" else None
+            iqs = st0["iqs"][i][:, 0] if name == "csa" else None
+            _, _, idx = lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs)
+            if name == "csa":
+                idx0 = idx
+        for name, lay in l1.items():
+            h = st1[name]
+            csa = name == "csa"
+            iq = st1["iq"][i][:, 0] if csa else None
+            iqs = st1["iqs"][i][:, 0] if csa else None
+            o, l, idx = lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs,
+                                 sel_from=idx0 if (csa and share == "reuse") else None,
+                                 update=not (csa and share == "reindex"))
+            if csa and share == "reindex":
+                parity.topk_exact(tk1[i][:, 0], idx, f"re-index top-k step {i}")
+            parity.attn_close(out[name][i], o, f"{share} {name} step {i}")
+            parity.lse_close(lse[name][i], l, None, f"{share} {name} lse step {i}")
