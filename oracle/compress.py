@@ -67,3 +67,16 @@ def magnitude(x_bits, z, m, d_rope):
         mag[:, D - d_rope::2] = pair
         mag[:, D - d_rope + 1::2] = pair
     return mag
+
+
+def index_keys(xk_bits, z, m):
+    """Indexer keys of the entries of one sequence: the per-token keys xk_bits [n_tok, D_I] (bf16
+    bits) pooled with the same softmax weights as the entries (z [n_tok]), then MXFP4-encoded.
+    Reading (the pages give the indexer keys no source of their own): an entry's key is the pooled
+    key of its tokens, stored like the other indexer inputs ([P5] section "두 가지 압축 전략: CSA
+    및 HCA": the indexer runs in FP4). No RoPE.
+    Returns (exact fp64 pooled keys [n, D_I], packed codes [n, D_I/2], E8M0 scales [n, D_I/32])."""
+    k = pool(formats.bf16_to_f64(xk_bits), np.asarray(z, dtype=np.float64), m)
+    packed, scales = formats.f64_to_mxfp4(k)
+    return k, packed, scales
+

@@ -112,3 +112,47 @@ def mxfp4_to_f64(packed, scales):
     D = vals.shape[-1]
     assert s.shape[-1] * 32 == D
     return vals * np.repeat(s, 32, axis=-1)
+
+
+# OCP MX v1.0 encoding. The block exponent range is a reading: [-3, 0] keeps every indexer
+# score exact in fp32 for unit-scale inputs (the span bound of the indexer's exactness argument),
+# and it is the range the configurations' index keys use.
+MX_E_MIN, MX_E_MAX = -3, 0
+E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])  # midpoints between magnitudes
+
+
+def _floor_log2(a):
+    """floor(log2 a) for a > 0, exact at powers of two."""
+    e = np.floor(np.log2(a))
+    e = np.where(a < 2.0 ** e, e - 1, e)
+    return np.where(a >= 2.0 ** (e + 1), e + 1, e)
+
+
+def e2m1_round(mag):
+    """Nearest e2m1 magnitude code (0..7) of mag >= 0, ties to the even code, saturating at 6."""
+    mag = np.asarray(mag, dtype=np.float64)
+    code = np.searchsorted(E2M1_MIDS, mag, side="left")      # number of midpoints below mag
+    at_mid = (code < 7) & (mag == E2M1_MIDS[np.minimum(code, 6)])
+    # on a midpoint: between codes `code` and `code + 1`; keep the even one
+    return np.where(at_mid & (code % 2 == 1), code + 1, code).astype(np.int64)
+
+
+def f64_to_mxfp4(x, e_min=MX_E_MIN, e_max=MX_E_MAX):
+    """MXFP4 encoding of x [..., D] (D % 32 == 0): per block of 32, shared exponent
+    E = floor(log2 max|block|) - 2 (2 is the largest e2m1 exponent), limited to [e_min, e_max]
+    (an all-zero block takes e_min); elements |v| / 2^E rounded to the nearest e2m1 magnitude,
+    ties to the even code, saturating at 6; sign in bit 3. Returns (packed [..., D/2] with
+    element 2i in the low nibble, E8M0 scales [..., D/32] = E + 127)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    xb = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.abs(xb).max(axis=-1)
+    E = np.where(amax > 0, _floor_log2(np.where(amax > 0, amax, 1.0)) - 2, e_min)
+    E = np.clip(E, e_min, e_max).astype(np.int64)
+    mag = np.abs(xb) / (2.0 ** E)[..., None]
+    code = e2m1_round(mag) | np.where(np.signbit(xb) & (mag > 0), 8, 0)
+    code = code.reshape(x.shape).astype(np.uint8)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (E + 127).astype(np.uint8)
+

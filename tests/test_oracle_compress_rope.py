@@ -149,3 +149,26 @@ def test_page_entry_counts():
     n_hca = 2 ** 20 // consts["hca_block"]
     assert n_hca == 8192 and abs(n_hca - consts["hca_entries_1m_approx"]) / 8000 < 0.03
     assert consts["hca_block"] // consts["csa_block"] == consts["hca_vs_csa_memory"]
+
+
+def test_index_keys_pool_with_the_entry_weights():
+    """Pooled indexer keys: identical tokens give that token's key (exactly, with equal logits: the
+    weights are exactly 1/m); uniform logits give the mean (np.mean); the weights are those of the
+    entries (keys equal to the KV rows pool to the un-rotated entries)."""
+    rng = np.random.default_rng(7)
+    m, D_I = 4, 64
+    tok = formats.f64_to_bf16(rng.normal(0, 1, (1, D_I)))
+    xk = np.repeat(tok, 3 * m, axis=0)
+    k, p, s = compress.index_keys(xk, np.zeros(3 * m), m)
+    assert np.array_equal(k, np.repeat(formats.bf16_to_f64(tok), 3, axis=0))
+    p1, s1 = formats.f64_to_mxfp4(formats.bf16_to_f64(tok))
+    assert np.array_equal(p, np.repeat(p1, 3, axis=0)) and np.array_equal(s, np.repeat(s1, 3, axis=0))
+    k, _, _ = compress.index_keys(xk, rng.normal(0, 2, 3 * m), m)
+    assert np.allclose(k, np.repeat(formats.bf16_to_f64(tok), 3, axis=0), rtol=1e-15, atol=0)
+    xk = formats.f64_to_bf16(rng.normal(0, 1, (3 * m, D_I)))
+    k, _, _ = compress.index_keys(xk, np.zeros(3 * m), m)
+    assert np.allclose(k, formats.bf16_to_f64(xk).reshape(3, m, D_I).mean(axis=1), rtol=1e-15, atol=0)
+    z = rng.normal(0, 2, 3 * m)
+    k, _, _ = compress.index_keys(xk, z, m)
+    e, _, _ = compress.compress(xk, z, 0, m, 0, 10000.0, "bf16")
+    assert np.array_equal(k, e)

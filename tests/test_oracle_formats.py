@@ -96,3 +96,63 @@ def test_fp4_unpack_low_nibble_first_and_mx_scale():
     assert list(v[0, :4]) == [1.0, 2.0, -12.0, 12.0]
     assert np.all(v[0, 4:] == 0)
     assert formats.e8m0_to_f64(np.array([127, 0, 254])).tolist() == [1.0, 2.0 ** -127, 2.0 ** 127]
+
+
+def test_mxfp4_encode_hand_values_ties_to_even_and_saturation():
+    """OCP MX v1.0 FP4 by hand: block max 6 -> E = floor(log2 6) - 2 = 0; every midpoint between
+    two e2m1 magnitudes goes to the even code; beyond 6 saturates; a negative value keeps bit 3."""
+    x = np.zeros((1, 32))
+    x[0, :14] = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, -0.75, 0.3, 0.74, 5.99, -0.1]
+    p, s = formats.f64_to_mxfp4(x)
+    assert s.tolist() == [[127]]
+    codes = formats.unpack_fp4(p)[0, :14].tolist()
+    assert codes == [7, 0, 2, 2, 4, 4, 6, 6, 7, 8 | 2, 1, 1, 7, 8 | 0]
+
+
+def test_mxfp4_block_exponent_limits_and_zero_block():
+    """E = floor(log2 amax) - 2 within [-3, 0]: amax 100 would need E = 4 (clipped to 0, values
+    saturate at 6); amax 0.01 would need E = -9 (clipped to -3: 0.01 / 0.125 rounds to 0); amax 1
+    gives E = -2 exactly (a power of two); an all-zero block takes E = -3 and zero codes."""
+    x = np.zeros((4, 32))
+    x[0, 0], x[0, 1] = 100.0, 2.0
+    x[1, 0] = 0.01
+    x[2, 0], x[2, 1] = 1.0, -0.375
+    p, s = formats.f64_to_mxfp4(x)
+    assert s[:, 0].tolist() == [127, 124, 125, 124]
+    c = formats.unpack_fp4(p)
+    assert c[0, :2].tolist() == [7, 4]          # 100 -> 6 (saturated), 2 -> 2.0
+    assert c[1, 0] == 0                          # 0.08 of a step -> 0
+    assert c[2, :2].tolist() == [6, 8 | 3]       # 1 / 0.25 = 4 -> code 6; -0.375 / 0.25 = -1.5 -> code 3
+    assert np.all(c[3] == 0)
+
+
+def test_mxfp4_round_trip_of_representable_values():
+    """Every value on the e2m1 grid times 2^E (with the block maximum fixing E) decodes to itself."""
+    rng = np.random.default_rng(3)
+    for E in range(-3, 1):
+        codes = rng.integers(0, 16, (50, 64))
+        codes[:, 0] = 7                                          # block maxima 6 * 2^E fix E
+        codes[:, 32] = 15
+        v = formats.e2m1_to_f64(codes) * 2.0 ** E
+        p, s = formats.f64_to_mxfp4(v)
+        assert np.all(s == E + 127)
+        back = formats.mxfp4_to_f64(p, s)
+        assert np.array_equal(back, np.where(v == 0, 0.0, v))   # -0 is stored as +0 only when zero
+
+
+def test_mxfp4_nearest_value_brute_force():
+    """Against a brute-force search over all 16 codes: the decoded value is a nearest grid value
+    of v / 2^E (clipped to +-6), and on exact midpoints the even magnitude code is taken."""
+    rng = np.random.default_rng(4)
+    v = rng.normal(0, 1.3, (200, 32))
+    v[:, 5] = rng.choice(formats.E2M1_MIDS, 200) * rng.choice([-1, 1], 200) * 0.5   # exact midpoints
+    p, s = formats.f64_to_mxfp4(v)
+    E = s.astype(np.int64) - 127
+    got = formats.mxfp4_to_f64(p, s) / np.repeat(2.0 ** E, 32, axis=-1)
+    target = np.clip(v / np.repeat(2.0 ** E, 32, axis=-1), -6, 6)
+    grid = formats.e2m1_to_f64(np.arange(16))
+    dist = np.abs(target[..., None] - grid)
+    assert np.allclose(np.abs(got - target), dist.min(axis=-1), rtol=0, atol=0)
+    codes = formats.unpack_fp4(p)
+    mids = np.isin(np.abs(target), formats.E2M1_MIDS)
+    assert mids.any() and np.all((codes[mids] & 7) % 2 == 0)
