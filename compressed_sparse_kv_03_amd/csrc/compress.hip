@@ -170,6 +170,89 @@ __global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __rest
   if (threadIdx.x == 0 && z_new) ring_z[slot] = z_new[b];
 }
 
+// Indexer keys of the entries: the per-token keys pooled with the entries' softmax weights, then
+// MXFP4 (OCP MX v1.0: per 32 values E = floor(log2 amax) - 2 within [-3, 0], elements rounded to
+// the nearest e2m1 magnitude with ties to the even code, saturating at 6). One wavefront per
+// entry; lane l holds key dims [V l, V l + V), so one MX block is 32 / V adjacent lanes.
+constexpr int kMxEMin = -3, kMxEMax = 0;
+
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float mag = fabsf(v);
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) c += mag > mids[i];
+  bool tie = false;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) tie = tie || (c == i && mag == mids[i]);
+  if (tie && (c & 1)) ++c;  // a midpoint goes to the even code
+  return (uint32_t)c | (v < 0.f ? 8u : 0u);
+}
+
+template <int V>
+__global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
+    const uint16_t* __restrict__ xk, int64_t xk_seq_stride, const float* __restrict__ z, int64_t z_seq_stride,
+    int B, int n_ent, int m, uint8_t* __restrict__ out_ik, uint8_t* __restrict__ out_iks, int64_t out_seq_stride,
+    const int32_t* __restrict__ out_entry0) {
+  constexpr int D_I = 64 * V;
+  constexpr int LPB = 32 / V;  // lanes per MX block
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
+  if (w >= B * n_ent) return;
+  const int b = w / n_ent;
+  const int j = w - b * n_ent;
+  const uint16_t* xb = xk + (int64_t)b * xk_seq_stride + (int64_t)j * m * D_I;
+  const float* zb = z + (int64_t)b * z_seq_stride + (int64_t)j * m;
+  float zmax = -INFINITY;
+  for (int i = lane; i < m; i += kWave) zmax = fmaxf(zmax, zb[i]);
+  zmax = wave_max(zmax);
+  float zsum = 0.f;
+  for (int i = lane; i < m; i += kWave) zsum += expf(zb[i] - zmax);
+  zsum = wave_sum(zsum);
+  const float inv = 1.0f / zsum;
+
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int i = 0; i < m; i += kUnroll) {  // kUnroll rows in flight; the last block repeats a row with weight 0
+    uint16_t r[kUnroll][V];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint16_t* row = xb + (int64_t)min(i + u, m - 1) * D_I + V * lane;
+#pragma unroll
+      for (int v = 0; v < V; ++v) r[u][v] = row[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float a = i + u < m ? expf(zb[min(i + u, m - 1)] - zmax) * inv : 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = fmaf(a, __uint_as_float((uint32_t)r[u][v] << 16), acc[v]);
+    }
+  }
+  // block exponent
+  float amax = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) amax = fmaxf(amax, fabsf(acc[v]));
+#pragma unroll
+  for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  int E = kMxEMin;
+  if (amax > 0.f) E = min(kMxEMax, max(kMxEMin, (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 2));
+  const float inv_s = __builtin_amdgcn_ldexpf(1.0f, -E);
+  uint32_t codes[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) codes[v] = e2m1_code(acc[v] * inv_s);
+  const int64_t slot = (int64_t)b * out_seq_stride + (out_entry0 ? out_entry0[b] : 0) + j;
+  uint8_t* ko = out_ik + slot * (D_I / 2);
+  if constexpr (V == 1) {  // pairs of lanes form a byte
+    const uint32_t hi = __shfl_down(codes[0], 1, kWave);
+    if ((lane & 1) == 0) ko[lane >> 1] = (uint8_t)(codes[0] | (hi << 4));
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; v += 2) ko[(V * lane + v) >> 1] = (uint8_t)(codes[v] | (codes[v + 1] << 4));
+  }
+  if (lane % LPB == 0) out_iks[slot * (D_I / 32) + lane / LPB] = (uint8_t)(E + 127);
+}
+
 static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stride, const float* z,
                          int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                          int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
@@ -244,5 +327,48 @@ extern "C" CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_n
   cskv::ring_append_kernel<<<B, 128, 0, reinterpret_cast<hipStream_t>(stream)>>>(x_new, z_new, pos, ring_x,
                                                                                  ring_z, D, W);
   CSKV_LAUNCH_CHECK("cskv_ring_append");
+  return CSKV_OK;
+}
+
+extern "C" CSKV_API int csa_index_key_pool(const uint16_t* xk, int64_t xk_seq_stride, const float* z,
+                                           int64_t z_seq_stride, int B, int n_tok, int D_I, int m, uint8_t* out_ik,
+                                           uint8_t* out_ik_scale, int64_t out_seq_stride, const int32_t* out_entry0,
+                                           void* stream) {
+  const char* name = "csa_index_key_pool";
+  CSKV_REQUIRE(B >= 1 && n_tok >= 0, CSKV_EINVAL, "%s: B=%d n_tok=%d", name, B, n_tok);
+  CSKV_REQUIRE(m >= 1 && m <= 1024, CSKV_EINVAL, "%s: m=%d outside [1, 1024]", name, m);
+  CSKV_REQUIRE(n_tok % m == 0, CSKV_EINVAL, "%s: n_tok=%d is not a multiple of m=%d", name, n_tok, m);
+  CSKV_REQUIRE(D_I == 64 || D_I == 128 || D_I == 256 || D_I == 512, CSKV_ENOTSUP,
+               "%s: D_I=%d not in {64, 128, 256, 512}", name, D_I);
+  if (n_tok == 0) return CSKV_OK;
+  CSKV_REQUIRE(xk && z && out_ik && out_ik_scale, CSKV_EINVAL, "%s: null pointer", name);
+  CSKV_REQUIRE(cskv::aligned16(xk), CSKV_EINVAL, "%s: xk must be 16-byte aligned", name);
+  CSKV_REQUIRE(xk_seq_stride % 8 == 0 && xk_seq_stride >= (int64_t)n_tok * D_I, CSKV_EINVAL,
+               "%s: xk_seq_stride=%lld", name, (long long)xk_seq_stride);
+  CSKV_REQUIRE(z_seq_stride >= n_tok, CSKV_EINVAL, "%s: z_seq_stride=%lld", name, (long long)z_seq_stride);
+  const int n_ent = n_tok / m;
+  CSKV_REQUIRE(out_seq_stride >= n_ent, CSKV_EINVAL, "%s: out_seq_stride=%lld", name, (long long)out_seq_stride);
+  CSKV_REQUIRE((int64_t)B * n_ent < (1ll << 31), CSKV_ENOTSUP, "%s: too many entries", name);
+  const int waves = B * n_ent;
+  dim3 grid((waves + cskv::kCompressWaves - 1) / cskv::kCompressWaves), block(cskv::kCompressWaves * cskv::kWave);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (D_I) {
+    case 64:
+      cskv::index_key_pool_kernel<1><<<grid, block, 0, s>>>(xk, xk_seq_stride, z, z_seq_stride, B, n_ent, m, out_ik,
+                                                            out_ik_scale, out_seq_stride, out_entry0);
+      break;
+    case 128:
+      cskv::index_key_pool_kernel<2><<<grid, block, 0, s>>>(xk, xk_seq_stride, z, z_seq_stride, B, n_ent, m, out_ik,
+                                                            out_ik_scale, out_seq_stride, out_entry0);
+      break;
+    case 256:
+      cskv::index_key_pool_kernel<4><<<grid, block, 0, s>>>(xk, xk_seq_stride, z, z_seq_stride, B, n_ent, m, out_ik,
+                                                            out_ik_scale, out_seq_stride, out_entry0);
+      break;
+    default:
+      cskv::index_key_pool_kernel<8><<<grid, block, 0, s>>>(xk, xk_seq_stride, z, z_seq_stride, B, n_ent, m, out_ik,
+                                                            out_ik_scale, out_seq_stride, out_entry0);
+  }
+  CSKV_LAUNCH_CHECK(name);
   return CSKV_OK;
 }

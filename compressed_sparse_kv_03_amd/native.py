@@ -32,6 +32,7 @@ _SIGS = {
                              _p, _p, _p, _sz, _p], _i),
     "hybrid_attn_prefill_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "cskv_ring_append": ([_p, _p, _p, _p, _p, _i, _i, _i, _p], _i),
+    "csa_index_key_pool": ([_p, _i64, _p, _i64, _i, _i, _i, _i, _p, _p, _i64, _p, _p], _i),
 }
 
 _lib = None
@@ -107,6 +108,12 @@ def hca_compress(x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m,
                  rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0=None, stream=None):
     _compress("hca_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m,
               entry_pos_offset, rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, stream)
+
+
+def csa_index_key_pool(xk, xk_seq_stride, z, z_seq_stride, B, n_tok, D_I, m, out_ik, out_ik_scale,
+                       out_seq_stride, out_entry0=None, stream=None):
+    _check(lib().csa_index_key_pool(_ptr(xk), xk_seq_stride, _ptr(z), z_seq_stride, B, n_tok, D_I, m, _ptr(out_ik),
+                                    _ptr(out_ik_scale), out_seq_stride, _ptr(out_entry0), _stream(stream)))
 
 
 # ------------------------------------------------------------------ indexer + top-k

@@ -98,6 +98,38 @@ CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* 
                  int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
 
 /*
+ * csa_index_key_pool - the indexer key of each compressed entry: the per-token
+ * indexer keys of its m tokens pooled with the entry's softmax weights, then
+ * stored in MXFP4 like the other indexer inputs.
+ * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
+ * HCA": the FP4 indexer scores compressed entries; the pages give the entry keys
+ * no source of their own, so this library derives them the way the entries are
+ * derived: the same pooling weights, no RoPE.)
+ *
+ * For each sequence b and block j in [0, n_tok/m):
+ *   a_i = softmax_i(z[b, j*m + i])                   (the weights of csa_compress)
+ *   k   = sum_i a_i * xk[b, j*m + i, :]              (fp32 accumulation)
+ *   per 32 values of k: E = floor(log2 max|block|) - 2, limited to [-3, 0]
+ *     (an all-zero block takes -3); element code = nearest e2m1 magnitude of
+ *     |v| / 2^E (ties to the even code, saturating at 6), sign bit 3 set for
+ *     v < 0 (OCP MX v1.0 FP4)
+ *   out_ik[b, out_entry0[b] + j, :]       = codes, element 2i in the low nibble of byte i
+ *   out_ik_scale[b, out_entry0[b] + j, :] = E + 127 (E8M0)
+ *
+ * xk         [B, xk_seq_stride] bf16; row r of sequence b at xk + b*xk_seq_stride + r*D_I
+ * z          [B, z_seq_stride] fp32 pooling logits (the ones given to csa_compress)
+ * out_ik     [B, out_seq_stride, D_I/2] bytes; out_ik_scale [B, out_seq_stride, D_I/32]
+ * out_entry0 [B] int32 first entry slot written per sequence, or NULL (= 0)
+ * Requirements: B >= 1, n_tok % m == 0, 1 <= m <= 1024, D_I in {64, 128, 256,
+ * 512}, xk 16-byte aligned, xk_seq_stride % 8 == 0 and >= n_tok*D_I.
+ * Errors: CSKV_EINVAL (null, sizes, alignment), CSKV_ENOTSUP (D_I). The caller
+ * owns every buffer; the call is asynchronous on `stream`.
+ */
+CSKV_API int csa_index_key_pool(const uint16_t* xk, int64_t xk_seq_stride, const float* z, int64_t z_seq_stride,
+                       int B, int n_tok, int D_I, int m, uint8_t* out_ik, uint8_t* out_ik_scale,
+                       int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
+
+/*
  * csa_index_topk - lightning-indexer scores and top-k selection.
  * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
  * HCA": an FP4 indexer scores the compressed entries against the query and

@@ -141,3 +141,41 @@ def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8
     frac = np.count_nonzero(np.asarray(got_codes) != want_codes) / max(e.size, 1)
     if frac > max_frac:
         raise ParityError(f"{what}: {frac:.2e} of codes differ from the oracle's (> {max_frac})")
+
+
+def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_frac=1e-2):
+    """MXFP4 keys from an fp32 pooling vs the exact fp64 pooled keys k_exact [..., D].
+
+    With d = pool_error_bound(mag, m) the bound on |fp32 pooled - exact|: each block exponent is
+    the one of some value within d of the block maximum, and each code lies between the codes of
+    (v - d) and (v + d) under that exponent; at most max_frac of the codes differ from the
+    oracle's own encoding (differences only where v is within d of a rounding midpoint).
+    """
+    k = np.asarray(k_exact, dtype=np.float64)
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    D = k.shape[-1]
+    gs = np.asarray(got_scale).astype(np.int64)
+    kb = k.reshape(k.shape[:-1] + (D // 32, 32))
+    db = d.reshape(kb.shape)
+    amax_lo = np.maximum(np.abs(kb) - db, 0.0).max(axis=-1)   # the fp32 block maximum lies in [lo, hi]
+    amax_hi = (np.abs(kb) + db).max(axis=-1)
+    _, s_lo = formats.f64_to_mxfp4(np.repeat(amax_lo, 32, axis=-1).reshape(k.shape))
+    _, s_hi = formats.f64_to_mxfp4(np.repeat(amax_hi, 32, axis=-1).reshape(k.shape))
+    ok_s = (gs >= s_lo.astype(np.int64)) & (gs <= s_hi.astype(np.int64))
+    if not np.all(ok_s):
+        i = np.argwhere(~ok_s)[0]
+        raise ParityError(f"{what}: block {tuple(i)} scale {gs[tuple(i)]} outside [{s_lo[tuple(i)]}, {s_hi[tuple(i)]}]")
+    E = np.repeat(gs - 127, 32, axis=-1).reshape(k.shape)
+    got = formats.unpack_fp4(got_packed)
+    sval = lambda c: np.where(c & 8, -1, 1) * (c & 7)  # noqa: E731  (monotone in the value)
+    lo = sval(formats.e2m1_round(np.abs(k - d) / 2.0 ** E) | np.where(k - d < 0, 8, 0))
+    hi = sval(formats.e2m1_round(np.abs(k + d) / 2.0 ** E) | np.where(k + d < 0, 8, 0))
+    g = sval(got.astype(np.int64))
+    bad = (g < np.minimum(lo, hi)) | (g > np.maximum(lo, hi))
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise ParityError(f"{what}: element {i} code {got[i]} value {k[i]!r} (E={E[i]}, bound {d[i]:.2e})")
+    want, _ = formats.f64_to_mxfp4(k)
+    frac = np.count_nonzero(got != formats.unpack_fp4(want)) / max(got.size, 1)
+    if frac > max_frac:
+        raise ParityError(f"{what}: {frac:.2e} of codes differ from the oracle's (> {max_frac})")

@@ -17,7 +17,7 @@ def declared():
 
 def test_library_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 13
     L = native.lib()
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
@@ -48,6 +48,18 @@ def test_compress_validation():
         assert L.csa_compress(*args) == -1, args
     assert L.csa_compress(None, 0, None, 0, None, 1, 4, 2048, 0, 4, 0, 1e4, 0, None, None, 1, None, None) == -2
     assert L.hca_compress(None, 0, None, 0, None, 1, 0, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, None) == 0
+
+
+def test_index_key_pool_validation():
+    L = native.lib()
+    # (xk, xks, z, zs, B, n_tok, D_I, m, out, out_scale, oss, e0, stream)
+    assert L.csa_index_key_pool(None, 0, None, 0, 1, 4, 128, 0, None, None, 1, None, None) == -1    # m = 0
+    assert L.csa_index_key_pool(None, 0, None, 0, 1, 6, 128, 4, None, None, 1, None, None) == -1    # n_tok % m
+    assert L.csa_index_key_pool(None, 0, None, 0, 1, 4, 96, 4, None, None, 1, None, None) == -2     # D_I
+    assert L.csa_index_key_pool(None, 512, None, 4, 1, 4, 128, 4, None, None, 1, None, None) == -1  # null
+    assert L.csa_index_key_pool(8, 512, 16, 4, 1, 4, 128, 4, 16, 16, 1, None, None) == -1          # misaligned
+    assert L.csa_index_key_pool(16, 256, 16, 4, 1, 4, 128, 4, 16, 16, 1, None, None) == -1         # stride
+    assert L.csa_index_key_pool(None, 0, None, 0, 1, 0, 128, 4, None, None, 1, None, None) == 0     # empty
 
 
 def test_index_validation():

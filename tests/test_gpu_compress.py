@@ -5,6 +5,7 @@ import torch
 
 from compressed_sparse_kv_03_amd import configs, native, synth
 from oracle import compress as ocomp
+from oracle import formats
 from tests import parity
 from tests.gpu_util import DEV, down, poisoned, say, up
 
@@ -120,3 +121,48 @@ def test_ring_append_writes_slot_pos_mod_w():
         assert np.array_equal(rh[b, pos[b] % W], down(xn)[b]) and zh[b, pos[b] % W] == down(zn)[b]
         others = [i for i in range(W) if i != pos[b] % W]
         assert np.all(rh[b, others].view(np.uint16) == 0xFFFF)
+
+
+@pytest.mark.parametrize("m,D_I", [(4, 128), (128, 128), (1, 64), (13, 256), (4, 512)])
+def test_index_key_pool_matches_oracle(m, D_I):
+    """Pooled MXFP4 indexer keys: every block exponent and code within the fp32 pooling bound of
+    the oracle's, and (nearly) all codes equal; entry slots offset per sequence."""
+    say("index key pool", m, D_I)
+    B, nblk = 3, 37
+    n_tok = nblk * m
+    xk = synth.normal_bf16_bits((B, n_tok, D_I), 1.0, 21, DEV)
+    z = synth.normal((B, n_tok), 2.0, 22, DEV)
+    cap = nblk + 5
+    e0 = np.array([0, 5, 2], np.int32)
+    ik = poisoned((B, cap, D_I // 2), torch.uint8)
+    iks = poisoned((B, cap, D_I // 32), torch.uint8)
+    native.csa_index_key_pool(xk, n_tok * D_I, z, n_tok, B, n_tok, D_I, m, ik, iks, cap, up(e0))
+    xh, zh, ikh, iksh = down(xk).view(np.uint16), down(z), down(ik), down(iks)
+    for b in range(B):
+        k, _, _ = ocomp.index_keys(xh[b], zh[b], m)
+        mag = ocomp.magnitude(xh[b], zh[b], m, 0)
+        sl = slice(e0[b], e0[b] + nblk)
+        parity.mxfp4_close(ikh[b, sl], iksh[b, sl], k, mag, m, f"keys b={b}")
+        others = np.ones(cap, bool)
+        others[sl] = False
+        assert np.all(ikh[b, others] == 0xFF) and np.all(iksh[b, others] == 0xFF), "wrote outside its slots"
+
+
+def test_index_key_pool_exact_dyadic_inputs_bit_exact():
+    """Equal logits (weights exactly 1/4) and keys on a coarse dyadic grid: the fp32 pooling is
+    exact, so every code and exponent must equal the oracle's, midpoint ties included."""
+    say("index key pool exact")
+    B, m, D_I, nblk = 2, 4, 128, 50
+    rng = np.random.default_rng(5)
+    vals = rng.integers(-64, 65, (B, nblk * m, D_I)) / 16.0          # multiples of 1/16 in [-4, 4]
+    vals[:, :, 0] = rng.choice([-6.0, 6.0, 0.0, 2.0], (B, nblk * m))   # vary the block maxima
+    xk_bits = np.stack([formats.f64_to_bf16(v) for v in vals])
+    xk = up(xk_bits.view(np.int16))
+    z = torch.zeros((B, nblk * m), dtype=torch.float32, device=DEV)
+    ik = poisoned((B, nblk, D_I // 2), torch.uint8)
+    iks = poisoned((B, nblk, D_I // 32), torch.uint8)
+    native.csa_index_key_pool(xk, nblk * m * D_I, z, nblk * m, B, nblk * m, D_I, m, ik, iks, nblk)
+    for b in range(B):
+        _, p, s = ocomp.index_keys(xk_bits[b], np.zeros(nblk * m), m)
+        assert np.array_equal(down(ik)[b], p), f"codes differ b={b}"
+        assert np.array_equal(down(iks)[b], s), f"exponents differ b={b}"
