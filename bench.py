@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--share", choices=["none", "reuse", "reindex"], default="none",
                     help="cross-layer index sharing: the CSA layers of pairs 1.. reuse pair 0's top-k, or "
                          "re-index pair 0's KV and keys with their own queries")
+    ap.add_argument("--derive-keys", action="store_true",
+                    help="the CSA layers pool each new entry's indexer key from per-token keys in the loop")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -108,7 +110,7 @@ def main():
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
-    spec_kw = dict(steps=K)
+    spec_kw = dict(steps=K, derive_keys=args.derive_keys)
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec_kw), dev) for p in range(P)]
     spec = pairs[0].s
     torch.cuda.synchronize()
@@ -219,6 +221,7 @@ def main():
                         "context 2^20, H=64, D=512+64, fp8 entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "tokens_per_step_per_pair": spec.B,
+            **({"index_keys": "derived in the loop (per-token keys pooled, MXFP4)"} if args.derive_keys else {}),
             **({} if share is None else {"index_sharing": f"{share}: CSA layers of pairs 1..{P - 1} "
                                                           f"{'take pair 0 top-k' if share == 'reuse' else 're-index pair 0 KV'}"}),
         },

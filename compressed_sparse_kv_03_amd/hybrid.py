@@ -44,6 +44,12 @@ class LayerPairSpec:
     rope_base: float = 10000.0
     seed: int = 0
     wid: int = 5
+    # the CSA layer derives each new entry's indexer key from per-token keys pooled with the
+    # entry's weights (csa_index_key_pool) instead of taking it from the generator
+    derive_keys: bool = False
+    # per-token keys on a 1/16 grid and zero CSA pooling logits: the pooling is exact in fp32
+    # (used by the loop parity test, where the derived keys must equal the oracle's)
+    dyadic_keys: bool = False
 
     @property
     def sigma(self):
@@ -78,9 +84,21 @@ class LayerPair:
             self.q[name] = synth.normal_bf16_bits((T, B, s.H, D), s.sigma, sd(base + 3), device)
             self.xn[name] = synth.normal_bf16_bits((T, B, D), s.sigma, sd(base + 4), device)
             self.zn[name] = synth.normal((T, B), 1.0, sd(base + 5), device)
-        # indexer keys of every entry (future entries' keys are inputs too) and queries
+        # indexer keys of every entry (without derive_keys, future entries' keys are inputs too)
+        # and queries
         self.ik, self.iks = synth.mxfp4_normal((B, self.cap["csa"], s.D_I), sd(10), device)
         self.iq, self.iqs = synth.mxfp4_normal((T, B, 1, s.H_I, s.D_I), sd(11), device)
+        if s.derive_keys:  # per-token indexer keys: the window's and each new token's
+            if s.dyadic_keys:
+                g = synth.generator(sd(12), device)
+                grid = lambda shape: synth.bf16_bits(  # noqa: E731
+                    torch.randint(-64, 65, shape, generator=g, device=device).to(torch.float32) / 16)
+                self.ring_xk, self.xkn = grid((B, s.W, s.D_I)), grid((T, B, s.D_I))
+                self.ringz["csa"].zero_()
+                self.zn["csa"].zero_()
+            else:
+                self.ring_xk = synth.normal_bf16_bits((B, s.W, s.D_I), 1.0, sd(12), device)
+                self.xkn = synth.normal_bf16_bits((T, B, s.D_I), 1.0, sd(13), device)
         # per-step device scalars
         t = s.L + np.arange(T, dtype=np.int64)
         self.t_host = t
@@ -106,6 +124,9 @@ class LayerPair:
             self.ws_att[name] = torch.empty(max(16, n), dtype=torch.uint8, device=device)
         # initial state, for restoring between runs
         self._init = {n: (self.ring[n].clone(), self.ringz[n].clone()) for n in ("csa", "hca")}
+        if s.derive_keys:  # the loop overwrites the keys of new entries
+            self._init["xk"] = self.ring_xk.clone()
+            self._init["ik"] = (self.ik.clone(), self.iks.clone())
 
     # ------------------------------------------------------------------ state
     def restore(self):
@@ -113,6 +134,10 @@ class LayerPair:
         for n in ("csa", "hca"):
             self.ring[n].copy_(self._init[n][0])
             self.ringz[n].copy_(self._init[n][1])
+        if self.s.derive_keys:
+            self.ring_xk.copy_(self._init["xk"])
+            self.ik.copy_(self._init["ik"][0])
+            self.iks.copy_(self._init["ik"][1])
 
     def host_state(self):
         """Host copies of the initial state and inputs (for the oracle)."""
@@ -123,6 +148,9 @@ class LayerPair:
                          ckv=h(self.ckv[n]), scl=h(self.scl[n]), q=h(self.q[n]).view(np.uint16),
                          xn=h(self.xn[n]).view(np.uint16), zn=h(self.zn[n]))
         st["ik"], st["iks"], st["iq"], st["iqs"] = h(self.ik), h(self.iks), h(self.iq), h(self.iqs)
+        if self.s.derive_keys:
+            st["ik"], st["iks"] = h(self._init["ik"][0]), h(self._init["ik"][1])
+            st["ring_xk"], st["xkn"] = h(self._init["xk"]).view(np.uint16), h(self.xkn).view(np.uint16)
         return st
 
     # ------------------------------------------------------------------ one step
@@ -146,6 +174,9 @@ class LayerPair:
                 continue
             native.cskv_ring_append(self.xn[name][i], self.zn[name][i], self.pos[i], self.ring[name],
                                     self.ringz[name], B, D, W, stream)
+            keys = name == "csa" and s.derive_keys
+            if keys:
+                native.cskv_ring_append(self.xkn[i], None, self.pos[i], self.ring_xk, None, B, s.D_I, W, stream)
             m = self.m[name]
             if (t + 1) % m == 0:
                 slot0 = (t - m + 1) % W
@@ -153,6 +184,9 @@ class LayerPair:
                 fn(self.ring[name][:, slot0:], W * D, self.ringz[name][:, slot0:], W, self.pos0c[name][i], B, m, D,
                    s.d_rope, m, 0, s.rope_base, native.CSKV_FP8_E4M3, self.ckv[name], self.scl[name],
                    self.cap[name], self.entry0[name][i], stream)
+                if keys:
+                    native.csa_index_key_pool(self.ring_xk[:, slot0:], W * s.D_I, self.ringz[name][:, slot0:], W, B, m,
+                                              s.D_I, m, self.ik, self.iks, self.cap[name], self.entry0[name][i], stream)
         if share == "reuse":
             topk = src.topk[i]
         else:
@@ -183,11 +217,14 @@ class LayerPair:
         q = s.B * s.H * s.D * 2
         o = s.B * s.H * s.d_v * 2
         win = s.B * s.W * s.D * 2
-        return {
+        out = {
             "csa_index": s.B * n_c * xi + s.B * s.H_I * xi + s.B * s.k * 4,
             "csa_attn": s.B * s.k * e + win + q + o + s.B * s.k * 4,
             "hca_attn": s.B * n_h * e + win + q + o,
         }
+        if s.derive_keys:  # key append (read + write) and, amortised over m steps, the pooling
+            out["csa_keys"] = s.B * (2 * s.D_I * 2 + s.D_I * 2 + 4) + s.B * xi // s.m_csa
+        return out
 
     def step_flops(self):
         s = self.s

@@ -26,7 +26,7 @@ class Layer:
     """State of one layer for a batch of sequences (arrays are modified in place)."""
 
     def __init__(self, kind, m, W, d_rope, d_v, rope_base, scale, ckv, ckv_scale, dtype,
-                 n_entries, ring_x, ring_z, k=None, ik=None, ik_scale=None):
+                 n_entries, ring_x, ring_z, k=None, ik=None, ik_scale=None, ring_xk=None):
         assert kind in ("csa", "hca")
         self.kind, self.m, self.W = kind, m, W
         self.d_rope, self.d_v, self.rope_base, self.scale = d_rope, d_v, rope_base, scale
@@ -34,8 +34,12 @@ class Layer:
         self.n_entries = np.array(n_entries, dtype=np.int64)
         self.ring_x, self.ring_z = ring_x, ring_z
         self.k, self.ik, self.ik_scale = k, ik, ik_scale
+        # per-token indexer keys of the window: when given, each new entry's key is derived from
+        # its tokens' keys (compress.index_keys) instead of being an input
+        self.ring_xk = ring_xk
 
-    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True, sel_from=None, update=True):
+    def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True, sel_from=None, update=True,
+             xk_new=None):
         """Positions t [B]; x_new [B, D] bf16; z_new [B]; q [B, H, D] bf16; iq [B, H_I, D_I/2].
 
         Returns (o fp64 [B, H, d_v], lse [B, H], idx int32 [B, k] or None); with
@@ -52,7 +56,7 @@ class Layer:
         for b in range(B):
             tb = int(t[b])
             if update:
-                self._update(b, tb, x_new[b], z_new[b])
+                self._update(b, tb, x_new[b], z_new[b], None if xk_new is None else xk_new[b])
                 n = int(self.n_entries[b])
                 assert n == (tb + 1) // self.m
             else:
@@ -78,10 +82,12 @@ class Layer:
             return None, None, None
         return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)
 
-    def _update(self, b, tb, x_new, z_new):
+    def _update(self, b, tb, x_new, z_new, xk_new=None):
         """Window append of position tb and, at a block end, its compression (sequence b)."""
         self.ring_x[b, tb % self.W] = x_new
         self.ring_z[b, tb % self.W] = z_new
+        if self.ring_xk is not None:
+            self.ring_xk[b, tb % self.W] = xk_new
         if (tb + 1) % self.m == 0:
             j = (tb + 1) // self.m - 1
             assert j == self.n_entries[b], "entry count out of step with position"
@@ -92,4 +98,8 @@ class Layer:
             self.ckv[b, j] = stored[0]
             if s is not None:
                 self.ckv_scale[b, j] = s[0]
+            if self.ring_xk is not None:
+                _, kp, ks = compress.index_keys(self.ring_xk[b, slots], self.ring_z[b, slots], self.m)
+                self.ik[b, j] = kp[0]
+                self.ik_scale[b, j] = ks[0]
             self.n_entries[b] = j + 1

@@ -15,10 +15,12 @@ def oracle_layers(spec, st):
     layers = {}
     for name, m in (("csa", spec.m_csa), ("hca", spec.m_hca)):
         h = st[name]
+        csa = name == "csa"
         layers[name] = ohyb.Layer(name, m, spec.W, spec.d_rope, spec.d_v, spec.rope_base, spec.scale,
                                   h["ckv"].copy(), h["scl"].copy(), "fp8", np.full(spec.B, spec.L // m),
                                   h["ring"].copy(), h["ringz"].copy(), k=spec.k,
-                                  ik=st["ik"] if name == "csa" else None, ik_scale=st["iks"] if name == "csa" else None)
+                                  ik=st["ik"].copy() if csa else None, ik_scale=st["iks"].copy() if csa else None,
+                                  ring_xk=st["ring_xk"].copy() if (csa and spec.derive_keys) else None)
     return layers
 
 
@@ -37,7 +39,8 @@ def check_loop(pair, sample_steps):
             h = st[name]
             iq = st["iq"][i][:, 0] if name == "csa" else None
             iqs = st["iqs"][i][:, 0] if name == "csa" else None
-            o, l, idx = lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs, outputs=want)
+            xk = st["xkn"][i] if (name == "csa" and spec.derive_keys) else None
+            o, l, idx = lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs, outputs=want, xk_new=xk)
             if want:
                 if idx is not None:
                     parity.topk_exact(tk[i][:, 0], idx, f"{name} top-k step {i}")
@@ -57,6 +60,11 @@ def check_loop(pair, sample_steps):
         gs = pair.scl[name][:, n0:n_end].cpu().numpy().astype(np.float64)
         os_ = layers[name].ckv_scale[:, n0:n_end].astype(np.float64)
         assert np.all(np.abs(gs - os_) <= 1e-5 * os_), f"{name}: new entry scales differ"
+    if spec.derive_keys:  # derived indexer keys of the new entries (exact pooling: identical bytes)
+        n0, n_end = spec.L // spec.m_csa, (spec.L + spec.steps) // spec.m_csa
+        assert np.array_equal(pair.ik[:, n0:n_end].cpu().numpy(), layers["csa"].ik[:, n0:n_end]), "derived keys"
+        assert np.array_equal(pair.iks[:, n0:n_end].cpu().numpy(), layers["csa"].ik_scale[:, n0:n_end]), \
+            "derived key scales"
     return checked
 
 
@@ -64,6 +72,18 @@ def test_hybrid_loop_small_every_step():
     spec = hybrid.LayerPairSpec(B=2, L=2048, steps=300, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
                                 wid=55)
     say("hybrid small", spec)
+    pair = hybrid.LayerPair(spec)
+    pair.run(0, spec.steps)
+    torch.cuda.synchronize()
+    assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
+
+
+def test_hybrid_loop_derived_keys_every_step():
+    """New entries' indexer keys pooled from per-token keys on the GPU (dyadic keys, uniform
+    weights: the pooling is exact, so keys and top-k must match the oracle's bit for bit)."""
+    spec = hybrid.LayerPairSpec(B=2, L=2048, steps=300, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=128,
+                                wid=57, derive_keys=True, dyadic_keys=True)
+    say("hybrid derived keys", spec)
     pair = hybrid.LayerPair(spec)
     pair.run(0, spec.steps)
     torch.cuda.synchronize()

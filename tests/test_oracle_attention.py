@@ -201,3 +201,29 @@ def test_hybrid_loop_equals_one_shot_recomputation():
                     full_ring[p % W] = tokens[b, p]
                 o1, l1 = attention.decode_one(q[b], L + s, ent, n, sel, full_ring, W, dr, dv, 10000.0, 0.3)
                 assert np.allclose(o[b], o1, rtol=0, atol=0) and np.allclose(lse[b], l1, rtol=0, atol=0)
+
+
+def test_hybrid_loop_derived_keys_equal_one_shot_pooling():
+    """Keys derived in the loop (ring of per-token keys) equal pooling the full key history."""
+    rng = np.random.default_rng(7)
+    B, D, dv, dr, W, L, steps, m, DI = 2, 16, 8, 8, 16, 32, 37, 4, 64
+    tokens = _bf16(rng, (B, L + steps, D), 0.5)
+    keys = _bf16(rng, (B, L + steps, DI), 1.0)
+    logits = rng.standard_normal((B, L + steps)).astype(np.float32)
+    cap = (L + steps) // m
+    ring_x = np.zeros((B, W, D), np.uint16)
+    ring_xk = np.zeros((B, W, DI), np.uint16)
+    ring_z = np.zeros((B, W), np.float32)
+    for p in range(L - W, L):
+        ring_x[:, p % W], ring_xk[:, p % W], ring_z[:, p % W] = tokens[:, p], keys[:, p], logits[:, p]
+    ik = np.zeros((B, cap, DI // 2), np.uint8)
+    iks = np.zeros((B, cap, DI // 32), np.uint8)
+    lay = hybrid.Layer("csa", m, W, dr, dv, 10000.0, 0.3, np.zeros((B, cap, D), np.uint8), np.ones((B, cap), np.float32),
+                       "fp8", np.full(B, L // m), ring_x, ring_z, k=4, ik=ik, ik_scale=iks, ring_xk=ring_xk)
+    for s in range(steps):
+        lay.step(np.full(B, L + s), tokens[:, L + s], logits[:, L + s], None, outputs=False, xk_new=keys[:, L + s])
+    n = (L + steps) // m
+    for b in range(B):
+        _, kp, ks = compress.index_keys(keys[b, L:n * m], logits[b, L:n * m], m)
+        assert np.array_equal(ik[b, L // m:n], kp) and np.array_equal(iks[b, L // m:n], ks)
+    assert not ik[:, n:].any()
