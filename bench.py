@@ -46,6 +46,8 @@ def parse():
                          "re-index pair 0's KV and keys with their own queries")
     ap.add_argument("--derive-keys", action="store_true",
                     help="the CSA layers pool each new entry's indexer key from per-token keys in the loop")
+    ap.add_argument("--rms-norm", action="store_true",
+                    help="unit-gain RMSNorm (eps 1e-6) of the new compressed entries and of the queries")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -110,7 +112,7 @@ def main():
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
-    spec_kw = dict(steps=K, derive_keys=args.derive_keys)
+    spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0)
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec_kw), dev) for p in range(P)]
     spec = pairs[0].s
     torch.cuda.synchronize()
@@ -222,6 +224,7 @@ def main():
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "tokens_per_step_per_pair": spec.B,
             **({"index_keys": "derived in the loop (per-token keys pooled, MXFP4)"} if args.derive_keys else {}),
+            **({"normalisation": "RMSNorm (unit gain, eps 1e-6) of new entries and queries"} if args.rms_norm else {}),
             **({} if share is None else {"index_sharing": f"{share}: CSA layers of pairs 1..{P - 1} "
                                                           f"{'take pair 0 top-k' if share == 'reuse' else 're-index pair 0 KV'}"}),
         },

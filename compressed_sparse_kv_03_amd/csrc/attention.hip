@@ -58,6 +58,7 @@ struct AttnArgs {
   int W;
   int nq, H, D, d_rope, d_v;
   float rope_base, scale_log2;  // softmax_scale * log2(e)
+  float q_rms_eps;              // > 0: unit-gain RMSNorm of each query head (folded into its logits)
   int n_splits, keys_per_split;
   uint16_t* out;            // [nq, H, d_v]
   float* out_lse;           // [nq, H]
@@ -80,7 +81,8 @@ __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
   if (a.topk) {
     ks.n_c = a.k;
   } else if (a.n_entries) {
-    ks.n_c = a.n_entries[qi];
+    const int n = a.n_entries[qi];
+    ks.n_c = n < 0 ? 0 : (n < a.N_cap ? n : a.N_cap);
   } else {
     int64_t v = (ks.t + 1) / a.m;
     ks.n_c = (int)(v < a.N_cap ? v : a.N_cap);
@@ -113,6 +115,7 @@ struct AttnSmem {
   float xmax[2][HG][16];                               // per-half row maxima of the tile
   float kscale[kTK];              // per-key logit multiplier (log2 domain), -inf = masked
   float kvscale[kTK];             // per-key value multiplier (fp8 entry scale, else 1)
+  __align__(16) float qscale[HG * 16];  // per-head logit multiplier (query RMSNorm, else 1)
   double inv_freq[kMaxRopePairs];
   int sidx[kMaxSplitIdx];         // this split's top-k slots (CSA)
 };
@@ -296,10 +299,11 @@ __device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, HG>& sm, WaveState
                                                        __builtin_bit_cast(bf16x8, kv[u]), sacc, 0, 0, 0);
   }
   const float ck = sm.kscale[krow], vk = sm.kvscale[krow];
+  const f32x4 qs = *reinterpret_cast<const f32x4*>(&sm.qscale[16 * hg + 4 * g]);  // heads 4g..4g+3
   float x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = ck == -INFINITY ? -INFINITY : sacc[r] * ck;
+    x[r] = ck == -INFINITY ? -INFINITY : sacc[r] * qs[r] * ck;
     const float m_ = row16_max(x[r]);
     if (col == 0) sm.xmax[hf][hg][4 * g + r] = m_;
   }
@@ -433,6 +437,25 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
       else if (h < a.H)
         st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + d0);
     }
+  }
+  // query RMSNorm: 1 / sqrt(mean(q^2) + eps) of each head over its raw D dims, applied to the
+  // logits (scaling q before the product would add a bf16 rounding)
+  {
+    float ss = 0.f;
+    const int h = h0 + col;
+    if (a.q_rms_eps > 0.f && h < a.H) {
+#pragma unroll
+      for (int s = 0; s < KD; ++s) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+      }
+    }
+    ss += __shfl_xor(ss, 16, kWave);
+    ss += __shfl_xor(ss, 32, kWave);
+    if (hf == 0 && g == 0)
+      sm.qscale[hgw * 16 + col] = a.q_rms_eps > 0.f ? 1.0f / sqrtf(ss / (float)D + a.q_rms_eps) : 1.0f;
   }
 #pragma unroll
   for (int n = 0; n < NVH; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -633,12 +656,13 @@ static AttnKernel pick_kernel(int D, int d_v, int nw, bool fp8) {
   return fp8 ? pick_dims<true>(D, d_v, nw) : pick_dims<false>(D, d_v, nw);
 }
 
-static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype) {
+static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype, float q_rms_eps) {
   CSKV_REQUIRE(H >= 1 && H <= 128, CSKV_EINVAL, "%s: H=%d outside [1, 128]", name, H);
   CSKV_REQUIRE(D % 32 == 0 && D >= 32, CSKV_EINVAL, "%s: D=%d must be a positive multiple of 32", name, D);
   CSKV_REQUIRE(d_v % 16 == 0 && d_v >= 16 && d_v <= D, CSKV_EINVAL, "%s: d_v=%d", name, d_v);
   CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL, "%s: d_rope=%d", name, d_rope);
   CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
+  CSKV_REQUIRE(q_rms_eps >= 0.f && q_rms_eps < INFINITY, CSKV_EINVAL, "%s: q_rms_eps=%g", name, (double)q_rms_eps);
   CSKV_REQUIRE(d_rope <= 2 * kMaxRopePairs, CSKV_ENOTSUP, "%s: d_rope=%d > %d", name, d_rope, 2 * kMaxRopePairs);
   CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3, CSKV_EINVAL, "%s: ckv_dtype=%d", name, ckv_dtype);
   CSKV_REQUIRE(d_v % 32 == 0, CSKV_ENOTSUP, "%s: d_v=%d must be a multiple of 32", name, d_v);
@@ -683,10 +707,10 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
                                            const int32_t* n_entries, const int32_t* topk_idx, int k,
                                            const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
                                            float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
-                                           void* ws, size_t ws_bytes, void* stream) {
+                                           void* ws, size_t ws_bytes, float q_rms_eps, void* stream) {
   const char* name = "hybrid_attn_decode";
   CSKV_REQUIRE(B >= 1 && N_cap >= 0, CSKV_EINVAL, "%s: B=%d N_cap=%d", name, B, N_cap);
-  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype);
+  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype, q_rms_eps);
   if (rc) return rc;
   CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
   CSKV_REQUIRE(q && q_pos && out && n_entries, CSKV_EINVAL, "%s: null pointer", name);
@@ -719,6 +743,7 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   a.d_v = d_v;
   a.rope_base = rope_base;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.q_rms_eps = q_rms_eps;
   a.out = out;
   a.out_lse = out_lse;
   return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
@@ -732,11 +757,12 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
                                             const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
                                             int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v,
                                             int m, float rope_base, float softmax_scale, uint16_t* out,
-                                            float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+                                            float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps,
+                                            void* stream) {
   const char* name = "hybrid_attn_prefill";
   CSKV_REQUIRE(T >= 0 && N >= 0 && pos0 >= 0 && m >= 1, CSKV_EINVAL, "%s: T=%d N=%d pos0=%lld m=%d", name, T, N,
                (long long)pos0, m);
-  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype);
+  int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype, q_rms_eps);
   if (rc) return rc;
   if (T == 0) return CSKV_OK;
   CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
@@ -769,6 +795,7 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   a.d_v = d_v;
   a.rope_base = rope_base;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.q_rms_eps = q_rms_eps;
   a.out = out;
   a.out_lse = out_lse;
   return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));

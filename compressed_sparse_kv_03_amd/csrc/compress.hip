@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t x_seq_stride, const float* __restrict__ z,
     int64_t z_seq_stride, const int64_t* __restrict__ pos0, int B, int n_ent, int D, int d_rope,
     int m, int entry_pos_offset, float rope_base, void* __restrict__ out,
-    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, RopeTable rt) {
+    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, float rms_eps,
+    RopeTable rt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
   if (w >= B * n_ent) return;
@@ -104,6 +105,20 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
   if (!has1) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc1[e] = 0.f;
+  }
+
+  // optional unit-gain RMSNorm of the pooled entry (before the rotation, which keeps pair norms)
+  if (rms_eps > 0.f) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += acc0[e] * acc0[e] + acc1[e] * acc1[e];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + rms_eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc0[e] *= r;
+      acc1[e] *= r;
+    }
   }
 
   // partial RoPE on the last d_rope dims, at the entry's position
@@ -257,7 +272,7 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
                          int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                          int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
                          void* out, float* out_scale, int64_t out_seq_stride,
-                         const int32_t* out_entry0, void* stream) {
+                         const int32_t* out_entry0, float rms_eps, void* stream) {
   CSKV_REQUIRE(B >= 1 && n_tok >= 0, CSKV_EINVAL, "%s: B=%d n_tok=%d", name, B, n_tok);
   CSKV_REQUIRE(m >= 1 && m <= 1024, CSKV_EINVAL, "%s: m=%d outside [1, 1024]", name, m);
   CSKV_REQUIRE(n_tok % m == 0, CSKV_EINVAL, "%s: n_tok=%d is not a multiple of m=%d", name, n_tok, m);
@@ -267,6 +282,7 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
                "%s: d_rope=%d must be a multiple of 8 in [0, D]", name, d_rope);
   CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_dtype == CSKV_FP8_E4M3, CSKV_EINVAL,
                "%s: unknown out_dtype %d", name, out_dtype);
+  CSKV_REQUIRE(rms_eps >= 0.f && rms_eps < INFINITY, CSKV_EINVAL, "%s: rms_eps=%g", name, (double)rms_eps);
   if (n_tok == 0) return CSKV_OK;
   CSKV_REQUIRE(x && z && pos0 && out, CSKV_EINVAL, "%s: null pointer", name);
   CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_scale, CSKV_EINVAL, "%s: fp8 output needs out_scale", name);
@@ -285,11 +301,11 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
   if (out_dtype == CSKV_BF16)
     compress_kernel<false><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
                                                   d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                  out_seq_stride, out_entry0, rt);
+                                                  out_seq_stride, out_entry0, rms_eps, rt);
   else
     compress_kernel<true><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
                                                  d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                 out_seq_stride, out_entry0, rt);
+                                                 out_seq_stride, out_entry0, rms_eps, rt);
   CSKV_LAUNCH_CHECK(name);
   return CSKV_OK;
 }
@@ -300,20 +316,20 @@ extern "C" CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, co
                             int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                             int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
                             void* out, float* out_scale, int64_t out_seq_stride,
-                            const int32_t* out_entry0, void* stream) {
+                            const int32_t* out_entry0, float rms_eps, void* stream) {
   return cskv::compress_impl("csa_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
                              d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,
-                             out_seq_stride, out_entry0, stream);
+                             out_seq_stride, out_entry0, rms_eps, stream);
 }
 
 extern "C" CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z,
                             int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                             int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
                             void* out, float* out_scale, int64_t out_seq_stride,
-                            const int32_t* out_entry0, void* stream) {
+                            const int32_t* out_entry0, float rms_eps, void* stream) {
   return cskv::compress_impl("hca_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
                              d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,
-                             out_seq_stride, out_entry0, stream);
+                             out_seq_stride, out_entry0, rms_eps, stream);
 }
 
 extern "C" CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_new, const int64_t* pos,

@@ -50,6 +50,8 @@ class LayerPairSpec:
     # per-token keys on a 1/16 grid and zero CSA pooling logits: the pooling is exact in fp32
     # (used by the loop parity test, where the derived keys must equal the oracle's)
     dyadic_keys: bool = False
+    # > 0: unit-gain RMSNorm (this epsilon) of the new compressed entries and of the queries
+    rms_eps: float = 0.0
 
     @property
     def sigma(self):
@@ -183,7 +185,7 @@ class LayerPair:
                 fn = native.csa_compress if name == "csa" else native.hca_compress
                 fn(self.ring[name][:, slot0:], W * D, self.ringz[name][:, slot0:], W, self.pos0c[name][i], B, m, D,
                    s.d_rope, m, 0, s.rope_base, native.CSKV_FP8_E4M3, self.ckv[name], self.scl[name],
-                   self.cap[name], self.entry0[name][i], stream)
+                   self.cap[name], self.entry0[name][i], stream, rms_eps=s.rms_eps)
                 if keys:
                     native.csa_index_key_pool(self.ring_xk[:, slot0:], W * s.D_I, self.ringz[name][:, slot0:], W, B, m,
                                               s.D_I, m, self.ik, self.iks, self.cap[name], self.entry0[name][i], stream)
@@ -200,7 +202,7 @@ class LayerPair:
                                       native.CSKV_FP8_E4M3, self.cap[name], self.nent[name][i],
                                       topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
-                                      self.ws_att[name], None, stream)
+                                      self.ws_att[name], None, stream, q_rms_eps=s.rms_eps)
 
     def run(self, first, count, stream=None):
         for i in range(first, first + count):

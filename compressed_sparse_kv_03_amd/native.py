@@ -21,15 +21,15 @@ _SIGS = {
     "cskv_abi_version": ([], _i),
     "cskv_strerror": ([_i], ctypes.c_char_p),
     "cskv_last_error": ([], ctypes.c_char_p),
-    "csa_compress": ([_p, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i64, _p, _p], _i),
-    "hca_compress": ([_p, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i64, _p, _p], _i),
+    "csa_compress": ([_p, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i64, _p, _f, _p], _i),
+    "hca_compress": ([_p, _i64, _p, _i64, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i64, _p, _f, _p], _i),
     "csa_index_topk": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "csa_index_topk_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
     "hybrid_attn_decode": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
-                            _p, _p, _p, _sz, _p], _i),
+                            _p, _p, _p, _sz, _f, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "hybrid_attn_prefill": ([_p, _i64, _i, _p, _p, _i, _i, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
-                             _p, _p, _p, _sz, _p], _i),
+                             _p, _p, _p, _sz, _f, _p], _i),
     "hybrid_attn_prefill_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "cskv_ring_append": ([_p, _p, _p, _p, _p, _i, _i, _i, _p], _i),
     "csa_index_key_pool": ([_p, _i64, _p, _i64, _i, _i, _i, _i, _p, _p, _i64, _p, _p], _i),
@@ -91,23 +91,23 @@ def _check(rc):
 
 # ------------------------------------------------------------------ compression
 def _compress(name, x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m, entry_pos_offset,
-              rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, stream):
+              rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, rms_eps, stream):
     fn = getattr(lib(), name)
     _check(fn(_ptr(x), x_seq_stride, _ptr(z), z_seq_stride, _ptr(pos0), B, n_tok, D, d_rope, m,
               entry_pos_offset, rope_base, out_dtype, _ptr(out), _ptr(out_scale), out_seq_stride,
-              _ptr(out_entry0), _stream(stream)))
+              _ptr(out_entry0), rms_eps, _stream(stream)))
 
 
 def csa_compress(x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m, entry_pos_offset,
-                 rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0=None, stream=None):
+                 rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0=None, stream=None, *, rms_eps=0.0):
     _compress("csa_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m,
-              entry_pos_offset, rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, stream)
+              entry_pos_offset, rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, rms_eps, stream)
 
 
 def hca_compress(x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m, entry_pos_offset,
-                 rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0=None, stream=None):
+                 rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0=None, stream=None, *, rms_eps=0.0):
     _compress("hca_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D, d_rope, m,
-              entry_pos_offset, rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, stream)
+              entry_pos_offset, rope_base, out_dtype, out, out_scale, out_seq_stride, out_entry0, rms_eps, stream)
 
 
 def csa_index_key_pool(xk, xk_seq_stride, z, z_seq_stride, B, n_tok, D_I, m, out_ik, out_ik_scale,
@@ -137,13 +137,13 @@ def hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, dense):
 
 def hybrid_attn_decode(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
                        D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, ws, ws_bytes=None,
-                       stream=None):
+                       stream=None, *, q_rms_eps=0.0):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hybrid_attn_decode(_ptr(q), _ptr(q_pos), _ptr(ckv), _ptr(ckv_scale), ckv_dtype, N_cap,
                                     _ptr(n_entries), _ptr(topk_idx), k, _ptr(win), W, B, H, D, d_rope, d_v,
                                     rope_base, softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes,
-                                    _stream(stream)))
+                                    q_rms_eps, _stream(stream)))
 
 
 def hybrid_attn_prefill_workspace_size(T, H, d_v, N, k, W, dense):
@@ -151,13 +151,13 @@ def hybrid_attn_prefill_workspace_size(T, H, d_v, N, k, W, dense):
 
 
 def hybrid_attn_prefill(q, pos0, T, ckv, ckv_scale, ckv_dtype, N, topk_idx, k, x, W, H, D, d_rope, d_v, m,
-                        rope_base, softmax_scale, out, out_lse, ws, ws_bytes=None, stream=None):
+                        rope_base, softmax_scale, out, out_lse, ws, ws_bytes=None, stream=None, *, q_rms_eps=0.0):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hybrid_attn_prefill(_ptr(q), pos0, T, _ptr(ckv), _ptr(ckv_scale), ckv_dtype, N,
                                      _ptr(topk_idx), k, _ptr(x), W, H, D, d_rope, d_v, m, rope_base,
                                      softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes,
-                                     _stream(stream)))
+                                     q_rms_eps, _stream(stream)))
 
 
 # ------------------------------------------------------------------ decode state update

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSKV_ABI_VERSION 1
+#define CSKV_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define CSKV_API __attribute__((visibility("default")))
@@ -70,6 +70,9 @@ CSKV_API const char* cskv_last_error(void);
  * For each sequence b and block j in [0, n_tok/m):
  *   a_i  = softmax_i(z[b, j*m + i]),  i = 0..m-1
  *   e    = sum_i a_i * x[b, j*m + i, :]                  (fp32 accumulation)
+ *   e    = e / sqrt(mean_d(e_d^2) + rms_eps)   if rms_eps > 0 (unit-gain RMSNorm
+ *          of the entry: the pages' "KV normalisation", section "두 가지 압축
+ *          전략: CSA 및 HCA"; rms_eps == 0 leaves e as pooled)
  *   e    = RoPE(e) on dims [D-d_rope, D) at p = pos0[b] + j*m + entry_pos_offset,
  *          pairs (2i, 2i+1) of that slice, theta_i = rope_base^(-2i/d_rope)
  *   out[b, out_entry0[b] + j, :] = bf16_rne(e)                       (CSKV_BF16)
@@ -85,17 +88,17 @@ CSKV_API const char* cskv_last_error(void);
  * out_entry0 [B] int32 first entry slot written per sequence, or NULL (= 0)
  * Requirements: B >= 1, n_tok >= 0 and n_tok % m == 0, 1 <= m <= 1024,
  * D % 8 == 0 and 8 <= D <= 1024, d_rope % 8 == 0 and d_rope <= D,
- * x_seq_stride % 8 == 0. hca_compress is the same operation (named for
- * its use with m = 128).
+ * x_seq_stride % 8 == 0, rms_eps finite and >= 0. hca_compress is the same
+ * operation (named for its use with m = 128).
  */
 CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
                  const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
                  int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
-                 int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
+                 int64_t out_seq_stride, const int32_t* out_entry0, float rms_eps, void* stream);
 CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
                  const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
                  int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
-                 int64_t out_seq_stride, const int32_t* out_entry0, void* stream);
+                 int64_t out_seq_stride, const int32_t* out_entry0, float rms_eps, void* stream);
 
 /*
  * csa_index_key_pool - the indexer key of each compressed entry: the per-token
@@ -168,7 +171,9 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  *   keys = entries {topk_idx[b, i] >= 0} (CSA) or {0..n_entries[b]-1} (topk_idx == NULL, HCA)
  *          plus window tokens at positions [max(0, t-W+1), t], read raw from
  *          ring slot (position mod W) and rotated at their own position
- *   q_rot = RoPE(q[b, h], t); logit = softmax_scale * q_rot . key
+ *   q_rot = RoPE(q[b, h], t); logit = softmax_scale * g_h * q_rot . key, with
+ *   g_h = 1 / sqrt(mean_d(q[b, h, d]^2) + q_rms_eps) if q_rms_eps > 0 (unit-gain
+ *   RMSNorm of the query head, the pages' "query normalisation"), else 1
  *   out[b, h, :] = bf16_rne(sum softmax(logit) * key[:d_v]); out_lse[b, h] = ln(sum exp(logit))
  * Entries are stored rotated: bf16 [B, N_cap, D], or fp8 codes [B, N_cap, D]
  * with fp32 scales ckv_scale [B, N_cap] (value = code * scale).
@@ -177,13 +182,15 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * topk_idx [B, k] int32 (each -1 or in [0, n_entries[b])) or NULL
  * win [B, W, D] bf16 ring of raw tokens; out [B, H, d_v] bf16; out_lse [B, H] fp32 or NULL
  * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
- * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32.
+ * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32,
+ * q_rms_eps finite and >= 0.
  */
 CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
                        const float* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
                        const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H,
                        int D, int d_rope, int d_v, float rope_base, float softmax_scale,
-                       uint16_t* out, float* out_lse, void* ws, size_t ws_bytes, void* stream);
+                       uint16_t* out, float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps,
+                       void* stream);
 CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense);
 
 /*
@@ -202,7 +209,7 @@ CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const v
                         const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
                         int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v, int m,
                         float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
-                        void* ws, size_t ws_bytes, void* stream);
+                        void* ws, size_t ws_bytes, float q_rms_eps, void* stream);
 CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense);
 
 /*

@@ -75,14 +75,23 @@ def key_set(t, entries, sel, win_tokens, win_pos, d_rope, d_v, rope_base):
     return K, K[:, :d_v]
 
 
-def decode_one(q_bits, t, entries, n_entries, topk_idx, ring, W, d_rope, d_v, rope_base, scale):
+def query(q_bits, t, d_rope, rope_base, q_rms_eps=0.0):
+    """Query heads [H, D] as used in the logits: optionally RMS-normalised (unit gain, over
+    the raw D dims; [P5]'s query normalisation), then rotated at position t."""
+    q = formats.bf16_to_f64(q_bits)
+    if q_rms_eps > 0:
+        q = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + q_rms_eps)
+    return rope.apply(q, np.full(q_bits.shape[0], t), d_rope, rope_base)
+
+
+def decode_one(q_bits, t, entries, n_entries, topk_idx, ring, W, d_rope, d_v, rope_base, scale, q_rms_eps=0.0):
     """One decode query for one sequence.
 
     q_bits [H, D] bf16 (unrotated) at position t; entries: Entries;
     n_entries visible entries; topk_idx [k] (CSA) or None (HCA: all j < n_entries);
     ring [W, D] bf16 raw window ring, token at position p held in slot p mod W.
     """
-    q = rope.apply(formats.bf16_to_f64(q_bits), np.full(q_bits.shape[0], t), d_rope, rope_base)
+    q = query(q_bits, t, d_rope, rope_base, q_rms_eps)
     sel = range(n_entries) if topk_idx is None else [j for j in topk_idx if 0 <= j]
     if topk_idx is not None:
         assert all(j < n_entries for j in sel), "selected entry not visible"
@@ -92,14 +101,14 @@ def decode_one(q_bits, t, entries, n_entries, topk_idx, ring, W, d_rope, d_v, ro
     return attend(q, K, V, scale)
 
 
-def prefill_one(q_bits, t, pos0, entries, m, topk_idx, x_bits, W, d_rope, d_v, rope_base, scale):
+def prefill_one(q_bits, t, pos0, entries, m, topk_idx, x_bits, W, d_rope, d_v, rope_base, scale, q_rms_eps=0.0):
     """One prefill row at position t of a prompt whose raw tokens x_bits start at pos0.
 
     Entries visible: j < floor((t+1)/m); topk_idx [k] or None (= all visible).
     Window: raw tokens at positions [max(pos0, t-W+1), t] taken from x_bits.
     """
     n_vis = (t + 1) // m
-    q = rope.apply(formats.bf16_to_f64(q_bits), np.full(q_bits.shape[0], t), d_rope, rope_base)
+    q = query(q_bits, t, d_rope, rope_base, q_rms_eps)
     sel = range(n_vis) if topk_idx is None else [j for j in topk_idx if 0 <= j]
     if topk_idx is not None:
         assert all(j < n_vis for j in sel), "selected entry not visible"

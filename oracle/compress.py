@@ -13,7 +13,12 @@ Readings taken where the pages are silent:
   * the pooled vector is rotated (partial RoPE) AFTER pooling, at position
     p_j = pos0 + j*m + entry_pos_offset (offset 0: the block's first token);
   * storage: bf16 by RNE, or e4m3fn with one fp32 scale per entry,
-    s = max|e|/448 (s = 1 when the entry is all zero), code = RNE_sat(e/s).
+    s = max|e|/448 (s = 1 when the entry is all zero), code = RNE_sat(e/s);
+  * optional KV normalisation ([P5] section "두 가지 압축 전략: CSA 및 HCA": both
+    branches normalise queries and KV): when rms_eps > 0 the pooled entry is
+    divided by sqrt(mean(e^2) + rms_eps) (RMSNorm with unit gain) before the
+    rotation. The rotation keeps each pair's norm, so the order of the two
+    steps does not change the exact result.
 """
 import numpy as np
 
@@ -32,7 +37,13 @@ def pool(x, z, m):
     return np.einsum("jm,jmd->jd", alpha, xb)
 
 
-def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=0):
+def rms_norm(e, eps):
+    """Unit-gain RMSNorm of each row: e / sqrt(mean(e^2) + eps)."""
+    e = np.asarray(e, dtype=np.float64)
+    return e / np.sqrt(np.mean(e * e, axis=-1, keepdims=True) + eps)
+
+
+def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=0, rms_eps=0.0):
     """One sequence.
 
     x_bits [n_tok, D] bf16 bits; z [n_tok] fp32; pos0 = position of x[0].
@@ -42,6 +53,8 @@ def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=
     x = formats.bf16_to_f64(x_bits)
     zz = np.asarray(z, dtype=np.float64)
     e = pool(x, zz, m)
+    if rms_eps > 0:
+        e = rms_norm(e, rms_eps)
     n = e.shape[0]
     p = pos0 + np.arange(n, dtype=np.int64) * m + entry_pos_offset
     e = rope.apply(e, p, d_rope, rope_base)

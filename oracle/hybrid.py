@@ -26,7 +26,7 @@ class Layer:
     """State of one layer for a batch of sequences (arrays are modified in place)."""
 
     def __init__(self, kind, m, W, d_rope, d_v, rope_base, scale, ckv, ckv_scale, dtype,
-                 n_entries, ring_x, ring_z, k=None, ik=None, ik_scale=None, ring_xk=None):
+                 n_entries, ring_x, ring_z, k=None, ik=None, ik_scale=None, ring_xk=None, rms_eps=0.0):
         assert kind in ("csa", "hca")
         self.kind, self.m, self.W = kind, m, W
         self.d_rope, self.d_v, self.rope_base, self.scale = d_rope, d_v, rope_base, scale
@@ -37,6 +37,8 @@ class Layer:
         # per-token indexer keys of the window: when given, each new entry's key is derived from
         # its tokens' keys (compress.index_keys) instead of being an input
         self.ring_xk = ring_xk
+        # > 0: unit-gain RMSNorm of new entries and of the queries (compress.compress, attention.query)
+        self.rms_eps = rms_eps
 
     def step(self, t, x_new, z_new, q, iq=None, iq_scale=None, outputs=True, sel_from=None, update=True,
              xk_new=None):
@@ -75,7 +77,7 @@ class Layer:
             ent = attention.Entries(self.ckv[b], None if self.ckv_scale is None else self.ckv_scale[b],
                                     self.dtype)
             o, lse = attention.decode_one(q[b], tb, ent, n, sel, self.ring_x[b], self.W,
-                                          self.d_rope, self.d_v, self.rope_base, self.scale)
+                                          self.d_rope, self.d_v, self.rope_base, self.scale, self.rms_eps)
             outs.append(o)
             lses.append(lse)
         if not outputs:
@@ -94,7 +96,7 @@ class Layer:
             p0 = tb - self.m + 1
             slots = np.arange(p0, tb + 1) % self.W
             _, stored, s = compress.compress(self.ring_x[b, slots], self.ring_z[b, slots], p0,
-                                             self.m, self.d_rope, self.rope_base, self.dtype)
+                                             self.m, self.d_rope, self.rope_base, self.dtype, rms_eps=self.rms_eps)
             self.ckv[b, j] = stored[0]
             if s is not None:
                 self.ckv_scale[b, j] = s[0]

@@ -92,16 +92,40 @@ def pool_error_bound(mag, m):
     return (m + 10) * 2.0 ** -24 * mag
 
 
-def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_frac=1e-2):
+def rms_error_bound(pooled, mag, e_exact, m, d_rope, eps):
+    """Bound on |fp32 evaluation - exact| of RMS-normalised, rotated entries.
+
+    pooled: the oracle's exact unrotated pooled rows [n, D]; mag as for pool_error_bound;
+    e_exact: the normalised rotated rows. With d the pooling bound and r = 1/sqrt(mean(v^2)
+    + eps), the fp32 factor is within r * delta of r, delta = sum|v| d / sum v^2 + (D + 8)
+    2^-24 (sum of squares, square root, division), so an element is off by at most
+    r d + delta |e| (rotated dims: the pair's |e| summed).
+    """
+    v = np.asarray(pooled, dtype=np.float64)
+    D = v.shape[-1]
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    r = 1.0 / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    delta = (np.abs(v) * d).sum(axis=-1, keepdims=True) / np.maximum((v * v).sum(axis=-1, keepdims=True), 1e-300) \
+        + (D + 8) * 2.0 ** -24
+    ae = np.abs(np.asarray(e_exact, dtype=np.float64))
+    if d_rope:
+        rot = ae[..., D - d_rope:].reshape(ae.shape[:-1] + (d_rope // 2, 2)).sum(axis=-1)
+        ae = ae.copy()
+        ae[..., D - d_rope:] = np.repeat(rot, 2, axis=-1)
+    return r * d + delta * ae
+
+
+def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_frac=1e-2, d=None):
     """bf16 entries: |got - e| <= half a bf16 ulp of (|e| + d) + d, d = pool_error_bound.
 
     e_exact: the oracle's unrounded fp64 entries; mag: the oracle's pooling of |x|
     with the same weights (rotated dims: pair sums). At most max_frac of the
-    elements may round differently from the oracle's own bf16 value.
+    elements may round differently from the oracle's own bf16 value. d: an explicit
+    per-element bound instead (normalised entries: rms_error_bound).
     """
     g = formats.bf16_to_f64(np.asarray(got_bits).view(np.uint16))
     e = np.asarray(e_exact, dtype=np.float64)
-    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m) if d is None else np.asarray(d, np.float64)
     allowed = _ulp(np.abs(e) + d, 8, -126) / 2 + d
     err = np.abs(g - e)
     if not np.all(err <= allowed * (1 + 1e-9)):
@@ -112,7 +136,7 @@ def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_fra
         raise ParityError(f"{what}: {frac:.2e} of elements round differently from the oracle (> {max_frac})")
 
 
-def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8", max_frac=1e-2):
+def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8", max_frac=1e-2, d=None):
     """fp8 entries with per-entry scale s = max|e|/448.
 
     Scale: relative error <= d(amax)/amax + 2^-22. Elements: |code*s - e| <= half an
@@ -120,7 +144,7 @@ def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8
     """
     gs = np.asarray(got_scale, dtype=np.float64)
     e = np.asarray(e_exact, dtype=np.float64)
-    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m) if d is None else np.asarray(d, np.float64)
     amax = np.abs(e).max(axis=-1)
     s_ref = np.where(amax == 0, 1.0, amax / 448.0)
     i_max = np.argmax(np.abs(e), axis=-1)

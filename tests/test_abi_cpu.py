@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
     assert set(names) == set(native.exported_symbols())
-    assert L.cskv_abi_version() == 1
+    assert L.cskv_abi_version() == 2
 
 
 @pytest.mark.parametrize("code,text", [(0, "ok"), (-1, "invalid argument"), (-2, "shape not supported"),
@@ -33,21 +33,22 @@ def test_strerror(code, text):
 
 def test_compress_validation():
     L = native.lib()
-    # (x, xs, z, zs, pos0, B, n_tok, D, d_rope, m, off, base, dtype, out, out_scale, oss, e0, stream)
+    # (x, xs, z, zs, pos0, B, n_tok, D, d_rope, m, off, base, dtype, out, out_scale, oss, e0, rms_eps, stream)
     bad = [
-        (None, 0, None, 0, None, 1, 4, 8, 0, 0, 0, 1e4, 0, None, None, 1, None, None),          # m = 0
-        (None, 0, None, 0, None, 1, 6, 8, 0, 4, 0, 1e4, 0, None, None, 1, None, None),          # n_tok % m
-        (None, 0, None, 0, None, 1, 4, 12, 0, 4, 0, 1e4, 0, None, None, 1, None, None),         # D % 8
-        (None, 0, None, 0, None, 1, 4, 16, 4, 4, 0, 1e4, 0, None, None, 1, None, None),         # d_rope % 8
-        (None, 0, None, 0, None, 1, 4, 16, 0, 4, 0, 1e4, 7, None, None, 1, None, None),         # dtype
-        (None, 64, None, 4, None, 1, 4, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, None),        # null x
-        (16, 64, 16, 4, 16, 1, 4, 16, 0, 4, 0, 1e4, 1, 16, None, 1, None, None),                # fp8 w/o scale
-        (8, 64, 16, 4, 16, 1, 4, 16, 0, 4, 0, 1e4, 0, 16, None, 1, None, None),                 # misaligned
+        (None, 0, None, 0, None, 1, 4, 8, 0, 0, 0, 1e4, 0, None, None, 1, None, 0.0, None),          # m = 0
+        (None, 0, None, 0, None, 1, 6, 8, 0, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None),          # n_tok % m
+        (None, 0, None, 0, None, 1, 4, 12, 0, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None),         # D % 8
+        (None, 0, None, 0, None, 1, 4, 16, 4, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None),         # d_rope % 8
+        (None, 0, None, 0, None, 1, 4, 16, 0, 4, 0, 1e4, 7, None, None, 1, None, 0.0, None),         # dtype
+        (None, 64, None, 4, None, 1, 4, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None),        # null x
+        (16, 64, 16, 4, 16, 1, 4, 16, 0, 4, 0, 1e4, 1, 16, None, 1, None, 0.0, None),                # fp8 w/o scale
+        (8, 64, 16, 4, 16, 1, 4, 16, 0, 4, 0, 1e4, 0, 16, None, 1, None, 0.0, None),                 # misaligned
+        (None, 0, None, 0, None, 1, 4, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, -1.0, None),        # rms_eps < 0
     ]
     for args in bad:
         assert L.csa_compress(*args) == -1, args
-    assert L.csa_compress(None, 0, None, 0, None, 1, 4, 2048, 0, 4, 0, 1e4, 0, None, None, 1, None, None) == -2
-    assert L.hca_compress(None, 0, None, 0, None, 1, 0, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, None) == 0
+    assert L.csa_compress(None, 0, None, 0, None, 1, 4, 2048, 0, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None) == -2
+    assert L.hca_compress(None, 0, None, 0, None, 1, 0, 16, 0, 4, 0, 1e4, 0, None, None, 1, None, 0.0, None) == 0
 
 
 def test_index_key_pool_validation():
@@ -87,7 +88,8 @@ def test_attention_validation():
 
     def dec(**kw):
         a = dict(q=16, qp=16, ckv=16, sc=16, dt=1, N=100, ne=16, tk=None, k=128, win=16, W=128, B=1, H=64,
-                 D=576, dr=64, dv=512, base=1e4, scale=0.04, out=16, lse=None, ws=16, wsb=1 << 30, s=None)
+                 D=576, dr=64, dv=512, base=1e4, scale=0.04, out=16, lse=None, ws=16, wsb=1 << 30, eps=0.0,
+                 s=None)
         a.update(kw)
         return L.hybrid_attn_decode(*a.values())
     assert dec(D=100) == -1
@@ -98,11 +100,13 @@ def test_attention_validation():
     assert dec(q=None) == -1
     assert dec(sc=None) == -1
     assert dec(ws=None, wsb=0) == -3
+    assert dec(eps=-1.0) == -1
+    assert dec(eps=float("nan")) == -1
     assert L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) > 0
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
                                                         k=1, x=16, W=128, H=16, D=128, dr=64, dv=128, m=4,
                                                         base=1e4, scale=0.1, out=16, lse=None, ws=None, wsb=0,
-                                                        s=None), **kw).values())
+                                                        eps=0.0, s=None), **kw).values())
     assert pre(m=0) == -1
     assert pre(T=0) == 0
     assert pre(x=None) == -1

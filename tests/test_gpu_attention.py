@@ -19,7 +19,7 @@ from tests.gpu_util import DEV, down, poisoned, say, up
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, D, d_rope, d_v, scale):
+def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, D, d_rope, d_v, scale, q_rms_eps=0.0):
     B = q.shape[0]
     N_cap = ckv.shape[1]
     wsn = native.hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, topk is None)
@@ -28,19 +28,24 @@ def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, 
     lse = poisoned((B, H), torch.float32)
     dt = native.CSKV_BF16 if dtype == "bf16" else native.CSKV_FP8_E4M3
     native.hybrid_attn_decode(q, q_pos, ckv, ckv_scale, dt, N_cap, n_entries, topk, k, ring, W, B, H, D, d_rope,
-                              d_v, 10000.0, scale, out, lse, ws)
+                              d_v, 10000.0, scale, out, lse, ws, q_rms_eps=q_rms_eps)
     return out, lse
 
 
-def logit_bound(q_bits, t, ent, sel, win_tok, win_pos, d_rope, d_v, scale):
-    """Per-head logit error bound of the bf16 evaluation (tests.parity.rope_logit_bound)."""
+def logit_bound(q_bits, t, ent, sel, win_tok, win_pos, d_rope, d_v, scale, q_rms_eps=0.0):
+    """Per-head logit error bound of the bf16 evaluation (tests.parity.rope_logit_bound). With the
+    query RMSNorm folded into the logits, the bound scales with the normalised query, plus the
+    fp32 factor's own error ((D + 8) 2^-24 relative) times the largest |logit|."""
     K, _ = oatt.key_set(t, ent, sel, win_tok, win_pos, d_rope, d_v, 10000.0)
     n_e = K.shape[0] - len(win_pos)
-    qr = rope.apply(formats.bf16_to_f64(q_bits), np.full(q_bits.shape[0], t), d_rope, 10000.0)
-    return parity.rope_logit_bound(qr, K, d_rope, scale, np.arange(K.shape[0]) >= n_e)
+    qr = oatt.query(q_bits, t, d_rope, 10000.0, q_rms_eps)
+    b = parity.rope_logit_bound(qr, K, d_rope, scale, np.arange(K.shape[0]) >= n_e)
+    if q_rms_eps > 0 and K.shape[0]:
+        b = b + scale * np.abs(qr @ K.T).max(axis=1) * (q_bits.shape[1] + 8) * 2.0 ** -24
+    return b
 
 
-def oracle_decode(qh, tpos, ckvh, sch, dtype, nent, topkh, ringh, W, d_rope, d_v, scale, bs=None):
+def oracle_decode(qh, tpos, ckvh, sch, dtype, nent, topkh, ringh, W, d_rope, d_v, scale, bs=None, q_rms_eps=0.0):
     """Oracle outputs and lse, plus the per-head logit error bound for the lse check."""
     outs, lses, bounds = [], [], []
     for b in (range(qh.shape[0]) if bs is None else bs):
@@ -48,10 +53,10 @@ def oracle_decode(qh, tpos, ckvh, sch, dtype, nent, topkh, ringh, W, d_rope, d_v
         t = int(tpos[b])
         sel = range(int(nent[b])) if topkh is None else [j for j in topkh[b] if j >= 0]
         o, l = oatt.decode_one(qh[b], t, ent, int(nent[b]), None if topkh is None else topkh[b],
-                               ringh[b], W, d_rope, d_v, 10000.0, scale)
+                               ringh[b], W, d_rope, d_v, 10000.0, scale, q_rms_eps=q_rms_eps)
         wpos = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.zeros(0, np.int64)
         wtok = ringh[b][wpos % W] if W > 0 else np.zeros((0, qh.shape[-1]), np.uint16)
-        bounds.append(logit_bound(qh[b], t, ent, sel, wtok, wpos, d_rope, d_v, scale))
+        bounds.append(logit_bound(qh[b], t, ent, sel, wtok, wpos, d_rope, d_v, scale, q_rms_eps))
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses), np.stack(bounds)
@@ -101,6 +106,42 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std):
                                       d_v, scale)
     parity.attn_close(down(out), o_ref)
     parity.lse_close(down(lse), l_ref, bnd)
+
+
+@pytest.mark.parametrize("B,H,D,d_rope,d_v,N,k,W,dtype,dense,eps", [
+    (3, 64, 576, 64, 512, 300, 128, 128, "fp8", True, 1e-6),
+    (2, 16, 128, 64, 128, 500, 64, 128, "bf16", False, 1e-6),
+    (2, 20, 128, 64, 128, 90, 16, 8, "fp8", True, 4.0),          # eps comparable to the mean square
+])
+def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps):
+    """Unit-gain RMSNorm of every query head folded into its logits (q_rms_eps > 0)."""
+    say("decode q-rms", B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps)
+    rng = np.random.default_rng(N + 7)
+    scale = D ** -0.5
+    q = synth.normal_bf16_bits((B, H, D), 1.0, 41, DEV)
+    if dtype == "bf16":
+        ckv, sc = synth.normal_bf16_bits((B, N, D), 1.0, 42, DEV), None
+    else:
+        ckv, sc = synth.fp8_rows_normal((B, N, D), 1.0, 42, DEV)
+    ring = synth.normal_bf16_bits((B, W, D), 1.0, 43, DEV)
+    tpos = np.array([4 * N + 500 + b for b in range(B)], np.int64)
+    nent = np.array([N - b for b in range(B)], np.int32)
+    topk = None
+    if not dense:
+        tk = np.full((B, k), -1, np.int32)
+        for b in range(B):
+            sel = rng.permutation(nent[b])[:k]
+            tk[b, :len(sel)] = sel
+        topk = up(tk)
+    out, lse = run_decode(q, up(tpos), ckv, sc, dtype, up(nent), topk, k, ring, W, H, D, d_rope, d_v, scale,
+                          q_rms_eps=eps)
+    o_ref, l_ref, bnd = oracle_decode(down(q).view(np.uint16), tpos,
+                                      down(ckv).view(np.uint16) if dtype == "bf16" else down(ckv),
+                                      None if sc is None else down(sc), dtype, nent,
+                                      None if topk is None else down(topk), down(ring).view(np.uint16), W, d_rope,
+                                      d_v, scale, q_rms_eps=eps)
+    parity.attn_close(down(out), o_ref, "q-rms attention")
+    parity.lse_close(down(lse), l_ref, bnd, "q-rms lse")
 
 
 def test_decode_peaked_key_dominates():

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_compress(x_bits, z, pos0, m, d_rope, dtype, entry_pos_offset=0, entry0=None, cap_extra=0,
-                 x_stride=None, fn=native.csa_compress):
+                 x_stride=None, fn=native.csa_compress, rms_eps=0.0):
     """x_bits [B, n_tok, D] (device int16) -> device outputs."""
     B, n_tok, D = x_bits.shape[0], x_bits.shape[1], x_bits.shape[2]
     n = n_tok // m
@@ -23,7 +23,7 @@ def run_compress(x_bits, z, pos0, m, d_rope, dtype, entry_pos_offset=0, entry0=N
     osc = poisoned((B, cap), torch.float32) if dtype == "fp8" else None
     e0 = None if entry0 is None else up(np.asarray(entry0, np.int32))
     fn(x_bits, x_stride or n_tok * D, z, z.shape[1], up(np.asarray(pos0, np.int64)), B, n_tok, D, d_rope, m,
-       entry_pos_offset, 10000.0, out_dt, out, osc, cap, e0)
+       entry_pos_offset, 10000.0, out_dt, out, osc, cap, e0, rms_eps=rms_eps)
     return out, osc
 
 
@@ -47,6 +47,32 @@ def test_compress_small_matches_oracle(m, D, d_rope, dtype):
             parity.compress_bf16_close(oh[b].view(np.uint16), e, mag, m, f"b={b}")
         else:
             parity.compress_fp8_close(oh[b], down(osc)[b], e, mag, m, f"b={b}")
+
+
+@pytest.mark.parametrize("m,D,d_rope,dtype,eps", [
+    (4, 576, 64, "fp8", 1e-6), (128, 576, 64, "fp8", 1e-6), (4, 128, 64, "bf16", 1e-6), (13, 64, 16, "bf16", 0.5),
+])
+def test_compress_rms_norm_matches_oracle(m, D, d_rope, dtype, eps):
+    """Unit-gain RMSNorm of each pooled entry (rms_eps > 0), within the fp32 normalisation bound."""
+    say("compress rms", m, D, d_rope, dtype, eps)
+    B, nblk = 2, 21
+    n_tok = nblk * m
+    x = synth.normal_bf16_bits((B, n_tok, D), 0.3, 31, DEV)
+    z = synth.normal((B, n_tok), 2.0, 32, DEV)
+    pos0 = [0, 2 ** 20 - 64 * m]
+    out, osc = run_compress(x, z, pos0, m, d_rope, dtype, rms_eps=eps)
+    xh, zh, oh = down(x).view(np.uint16), down(z), down(out)
+    for b in range(B):
+        e, _, _ = ocomp.compress(xh[b], zh[b], pos0[b], m, d_rope, 10000.0, dtype, rms_eps=eps)
+        mag = ocomp.magnitude(xh[b], zh[b], m, d_rope)
+        v = ocomp.pool(formats.bf16_to_f64(xh[b]), zh[b].astype(np.float64), m)
+        d = parity.rms_error_bound(v, mag, e, m, d_rope, eps)
+        if dtype == "bf16":
+            parity.compress_bf16_close(oh[b].view(np.uint16), e, mag, m, f"rms b={b}", d=d)
+            ms = np.mean(formats.bf16_to_f64(oh[b].view(np.uint16)) ** 2, axis=1)
+            assert np.allclose(ms, np.mean(e * e, axis=1), rtol=1e-2), "mean square of the normalised entries"
+        else:
+            parity.compress_fp8_close(oh[b], down(osc)[b], e, mag, m, f"rms b={b}", d=d)
 
 
 def test_compress_offsets_entry_slots_and_ring_stride():

@@ -227,3 +227,28 @@ def test_hybrid_loop_derived_keys_equal_one_shot_pooling():
         _, kp, ks = compress.index_keys(keys[b, L:n * m], logits[b, L:n * m], m)
         assert np.array_equal(ik[b, L // m:n], kp) and np.array_equal(iks[b, L // m:n], ks)
     assert not ik[:, n:].any()
+
+
+def test_query_rms_norm_is_plain_attention_on_normalised_queries():
+    """m=1, k=N, W=0, no RoPE, q_rms_eps > 0: textbook attention of torch-rms_norm'ed queries;
+    with eps -> 0 the output does not depend on the query's scale."""
+    rng = np.random.default_rng(23)
+    L, H, D = 24, 3, 32
+    x = _bf16(rng, (L, D), 0.5)
+    ent = attention.Entries(x, None, "bf16")
+    q = _bf16(rng, (H, D), 0.5)
+    eps = 1e-5
+    o, lse = attention.decode_one(q, L - 1, ent, L, None, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.4,
+                                  q_rms_eps=eps)
+    qn = torch.nn.functional.rms_norm(torch.from_numpy(formats.bf16_to_f64(q)), (D,), eps=eps).numpy()
+    xf = formats.bf16_to_f64(x)
+    assert np.allclose(o, sdpa(qn, xf, xf, 0.4), rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse, np.log(np.exp(0.4 * qn @ xf.T).sum(axis=1)), atol=1e-12)
+    q4 = formats.f64_to_bf16(4.0 * formats.bf16_to_f64(q))   # exact power-of-two scaling
+    a = attention.decode_one(q, L - 1, ent, L, None, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.4,
+                             q_rms_eps=1e-30)
+    b = attention.decode_one(q4, L - 1, ent, L, None, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.4,
+                             q_rms_eps=1e-30)
+    assert np.allclose(a[0], b[0], rtol=1e-12, atol=1e-14)
+    c = attention.decode_one(q4, L - 1, ent, L, None, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.4)
+    assert not np.allclose(a[0], c[0], rtol=1e-6)

@@ -3,6 +3,7 @@ import math
 import os
 
 import numpy as np
+import torch
 
 from oracle import compress, formats, rope
 
@@ -172,3 +173,32 @@ def test_index_keys_pool_with_the_entry_weights():
     k, _, _ = compress.index_keys(xk, z, m)
     e, _, _ = compress.compress(xk, z, 0, m, 0, 10000.0, "bf16")
     assert np.array_equal(k, e)
+
+
+def test_rms_norm_matches_torch_and_has_unit_mean_square():
+    """The entry normalisation against torch's rms_norm (fp64) and its closed-form mean square."""
+    rng = np.random.default_rng(21)
+    e = rng.standard_normal((7, 96)) * rng.uniform(0.01, 10, (7, 1))
+    eps = 1e-6
+    got = compress.rms_norm(e, eps)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(e), (96,), eps=eps).numpy()
+    assert np.allclose(got, want, rtol=1e-13, atol=0)
+    ms = np.mean(e * e, axis=1)
+    assert np.allclose(np.mean(got * got, axis=1), ms / (ms + eps), rtol=1e-13)
+    # scale invariance: (c e, c^2 eps) normalises to the same vector
+    assert np.allclose(compress.rms_norm(3.0 * e, 9.0 * eps), got, rtol=1e-13)
+
+
+def test_compress_with_rms_norm_is_normalise_then_rotate():
+    """Normalising before or after the rotation gives the same entry (pairs keep their norm);
+    rms_eps = 0 leaves the pooling unchanged."""
+    rng = np.random.default_rng(22)
+    m, D, dr, n = 4, 64, 32, 5
+    x = formats.f64_to_bf16(rng.standard_normal((n * m, D)) * 0.3)
+    z = rng.standard_normal(n * m).astype(np.float32)
+    e_plain, _, _ = compress.compress(x, z, 100, m, dr, 10000.0, "bf16")
+    e_norm, _, _ = compress.compress(x, z, 100, m, dr, 10000.0, "bf16", rms_eps=1e-6)
+    assert np.allclose(e_norm, compress.rms_norm(e_plain, 1e-6), rtol=1e-12, atol=1e-15)
+    pooled = compress.pool(formats.bf16_to_f64(x), z.astype(np.float64), m)
+    rot = rope.apply(compress.rms_norm(pooled, 1e-6), 100 + np.arange(n) * m, dr, 10000.0)
+    assert np.allclose(e_norm, rot, rtol=1e-12, atol=1e-15)

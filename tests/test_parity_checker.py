@@ -85,3 +85,23 @@ def test_compress_checks_reject_errors_beyond_the_fp32_bound():
     badc[2, 7] = np.uint8(int(badc[2, 7]) + 1 if badc[2, 7] & 0x7F < 0x7E else int(badc[2, 7]) - 1)
     with pytest.raises(parity.ParityError):
         parity.compress_fp8_close(badc, s, e, mag, m)
+
+
+def test_rms_bound_rejects_a_missing_or_wrong_normalisation():
+    """The normalised-entry bound accepts the oracle's own rounding and rejects the unnormalised
+    entry and one normalised with a 1% larger factor (planted in oracle outputs)."""
+    from oracle import compress
+    rng = np.random.default_rng(5)
+    m, D, dr = 4, 128, 64
+    x = formats.f64_to_bf16(rng.standard_normal((8 * m, D)) * 0.3)
+    z = rng.standard_normal(8 * m).astype(np.float32)
+    e, bits, _ = compress.compress(x, z, 40, m, dr, 10000.0, "bf16", rms_eps=1e-6)
+    e0, bits0, _ = compress.compress(x, z, 40, m, dr, 10000.0, "bf16")
+    mag = compress.magnitude(x, z, m, dr)
+    v = compress.pool(formats.bf16_to_f64(x), z.astype(np.float64), m)
+    d = parity.rms_error_bound(v, mag, e, m, dr, 1e-6)
+    parity.compress_bf16_close(bits, e, mag, m, d=d)
+    with pytest.raises(parity.ParityError):
+        parity.compress_bf16_close(bits0, e, mag, m, d=d)
+    with pytest.raises(parity.ParityError):
+        parity.compress_bf16_close(formats.f64_to_bf16(e * 1.01), e, mag, m, d=d)
