@@ -116,6 +116,7 @@ struct AttnSmem {
   float kscale[kTK];              // per-key logit multiplier (log2 domain), -inf = masked
   float kvscale[kTK];             // per-key value multiplier (fp8 entry scale, else 1)
   __align__(16) float qscale[HG * 16];  // per-head logit multiplier (query RMSNorm, else 1)
+  float qssr[HG * 16][kMaxRopePairs / 4];  // sum of squares of each raw rotated 8-dim query chunk
   double inv_freq[kMaxRopePairs];
   int sidx[kMaxSplitIdx];         // this split's top-k slots (CSA)
 };
@@ -418,7 +419,16 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (h < a.H) {
         v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + rope0 + 8 * ch);
+        if (a.q_rms_eps > 0.f) {
+          float f[8], ss = 0.f;
+          unpack8(v, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+          sm.qssr[hl][ch] = ss;
+        }
         v = rope8(v, ks.t, sm.inv_freq, 4 * ch);
+      } else if (a.q_rms_eps > 0.f) {
+        sm.qssr[hl][ch] = 0.f;  // padding head (no output)
       }
       *reinterpret_cast<uint4*>(&sm.qr[hl][8 * ch]) = v;
     }
@@ -439,24 +449,30 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
     }
   }
   // query RMSNorm: 1 / sqrt(mean(q^2) + eps) of each head over its raw D dims, applied to the
-  // logits (scaling q before the product would add a bf16 rounding)
-  {
-    float ss = 0.f;
-    const int h = h0 + col;
-    if (a.q_rms_eps > 0.f && h < a.H) {
+  // logits (scaling q before the product would add a bf16 rounding). The unrotated dims come
+  // from this wave's query registers, the rotated ones from the chunk sums taken before the
+  // rotation. Called once the first tile's loads are out, since it waits for the query loads.
+  // Both waves of a head group write the same values.
+  auto write_qscale = [&]() {
+    float r = 1.0f;
+    if (a.q_rms_eps > 0.f) {
+      float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < KD; ++s) {
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + 32 * s + 8 * g), f);
+        if (32 * s + 8 * g < rope0) {
+          float f[8];
+          unpack8(st.qa[s], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        }
       }
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      for (int ch = 0; ch < a.d_rope / 8; ++ch) ss += sm.qssr[hgw * 16 + col][ch];
+      r = 1.0f / sqrtf(ss / (float)D + a.q_rms_eps);
     }
-    ss += __shfl_xor(ss, 16, kWave);
-    ss += __shfl_xor(ss, 32, kWave);
-    if (hf == 0 && g == 0)
-      sm.qscale[hgw * 16 + col] = a.q_rms_eps > 0.f ? 1.0f / sqrtf(ss / (float)D + a.q_rms_eps) : 1.0f;
-  }
+    if (g == 0) sm.qscale[hgw * 16 + col] = r;
+  };
 #pragma unroll
   for (int n = 0; n < NVH; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -473,6 +489,7 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
     const float* sbase = a.ckv_scale ? a.ckv_scale + seq : nullptr;
     TileRegs<KD, HG, FP8> R;
     entry_load<KD, NV, HG, FP8>(a, cbase, sbase, key_begin, e_end, key_begin, sm, R);
+    write_qscale();
     for (int key0 = key_begin; key0 < e_end; key0 += kTK) {
       __syncthreads();
       entry_store<KD, NV, HG, FP8>(a, sm, R);
@@ -486,6 +503,7 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
   if (w_begin < key_end) {
     TileRegs<KD, HG, false> R;
     window_load<KD, NV, HG>(a, qi, ks, w_begin, key_end, R);
+    if (key_begin >= e_end) write_qscale();
     for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
       __syncthreads();
       window_store<KD, NV, HG>(a, ks, key0, key_end, sm, R);
