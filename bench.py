@@ -48,6 +48,9 @@ def parse():
                     help="the CSA layers pool each new entry's indexer key from per-token keys in the loop")
     ap.add_argument("--rms-norm", action="store_true",
                     help="unit-gain RMSNorm (eps 1e-6) of the new compressed entries and of the queries")
+    ap.add_argument("--draft", type=int, default=1,
+                    help="draft tokens checked per decode step (multi-token decode, causal inside the draft; "
+                         "every draft token accepted, value counts positions)")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -112,7 +115,7 @@ def main():
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
-    spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0)
+    spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0, draft=args.draft)
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec_kw), dev) for p in range(P)]
     spec = pairs[0].s
     torch.cuda.synchronize()
@@ -154,7 +157,7 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1)
     ms_per_step = ms / K
-    tokens = spec.B * K * P
+    tokens = spec.B * spec.draft * K * P    # positions checked (every draft token accepted)
     value = tokens / (ms / 1e3)             # layer-pair decode tokens per second
     sb = pairs[0].step_bytes()
     sf = pairs[0].step_flops()
@@ -185,15 +188,16 @@ def main():
     i0 = 0
 
     def run_index():
-        native.csa_index_topk(pr.iq[i0], pr.iqs[i0], None, pr.ik, pr.iks, pr.nvalid[i0], s_.B, 1, pr.cap["csa"],
+        native.csa_index_topk(pr.iq[i0], pr.iqs[i0], None, pr.ik, pr.iks, pr.nvalid[i0], s_.B, s_.draft, pr.cap["csa"],
                               s_.H_I, s_.D_I, s_.k, pr.topk[i0], None, pr.ws_idx)
 
     def run_attn(name):
         def f():
-            native.hybrid_attn_decode(pr.q[name][i0], pr.pos[i0], pr.ckv[name], pr.scl[name], native.CSKV_FP8_E4M3,
+            native.hybrid_attn_decode(pr.q[name][i0], pr.qpos[i0], pr.ckv[name], pr.scl[name], native.CSKV_FP8_E4M3,
                                       pr.cap[name], pr.nent[name][i0], pr.topk[i0] if name == "csa" else None,
                                       s_.k, pr.ring[name], s_.W, s_.B, s_.H, s_.D, s_.d_rope, s_.d_v, s_.rope_base,
-                                      s_.scale, pr.out[name][i0], pr.lse[name][i0], pr.ws_att[name])
+                                      s_.scale, pr.out[name][i0], pr.lse[name][i0], pr.ws_att[name],
+                                      q_rms_eps=s_.rms_eps, T=s_.draft, R=pr.R[name])
         return f
 
     reps = args.kernel_reps
@@ -203,7 +207,7 @@ def main():
     idx_bytes = sb["csa_index"]
     achieved = idx_bytes / (t_idx[3] / 1e3) / 1e9
     idx_sha = source_sha(INDEX_SOURCES)
-    traffic = pmc_traffic(idx_sha)
+    traffic = pmc_traffic(idx_sha) if spec.draft == 1 else None   # counters were taken on one query per sequence
 
     rec = {
         "metric": "hybrid-attn decode tokens/s & HBM GB/s at 1M ctx; indexer+top-k µs/query",
@@ -222,7 +226,8 @@ def main():
             "workload": "c5_hybrid_1m: CSA(m=4,k=128,FP4 indexer 8x128)+HCA(m=128) layer pair, decode batch 8, "
                         "context 2^20, H=64, D=512+64, fp8 entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
-            "tokens_per_step_per_pair": spec.B,
+            "tokens_per_step_per_pair": spec.B * spec.draft,
+            **({"draft_tokens_per_step": spec.draft} if spec.draft > 1 else {}),
             **({"index_keys": "derived in the loop (per-token keys pooled, MXFP4)"} if args.derive_keys else {}),
             **({"normalisation": "RMSNorm (unit gain, eps 1e-6) of new entries and queries"} if args.rms_norm else {}),
             **({} if share is None else {"index_sharing": f"{share}: CSA layers of pairs 1..{P - 1} "
@@ -231,7 +236,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1),
         "step_bytes_per_pair": step_bytes,
         "step_flops_per_pair": sum(sf.values()),
-        "indexer_topk_us_per_query": round(t_idx[0] * 1e3 / spec.B, 3),
+        "indexer_topk_us_per_query": round(t_idx[0] * 1e3 / (spec.B * spec.draft), 3),
         "kernels_cold_ms": {
             "csa_index_topk": {"median": t_idx[0], "p10": t_idx[1], "p90": t_idx[2]},
             "hybrid_attn_decode_csa": {"median": t_csa[0], "p10": t_csa[1], "p90": t_csa[2]},

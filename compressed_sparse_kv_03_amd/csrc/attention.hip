@@ -54,7 +54,9 @@ struct AttnArgs {
   const int32_t* topk;      // [nq, k] or nullptr (dense)
   int k;
   const uint16_t* win;      // decode: ring [nq, W, D]; prefill: x [T, D]
-  int ring;                 // 1: slot = pos mod W, per-query ring; 0: row = pos - pos0 of x
+  int ring;                 // 1: slot = pos mod ring_cap, ring of sequence qi / q_per_seq; 0: row = pos - pos0 of x
+  int ring_cap;             // slots per ring (>= W)
+  int q_per_seq;            // consecutive queries sharing one sequence's ring and cache (decode)
   int W;
   int nq, H, D, d_rope, d_v;
   float rope_base, scale_log2;  // softmax_scale * log2(e)
@@ -225,7 +227,7 @@ __device__ __forceinline__ void window_load(const AttnArgs& a, int qi, const Key
     R.v[j] = make_uint4(0, 0, 0, 0);
     if (c < kTK * TR::CPR && key < key_end) {
       const int64_t pos = ks.w0 + (key - ks.n_c);
-      const int64_t row = a.ring ? ((int64_t)qi * a.W + pos % a.W) : (pos - a.pos0);
+      const int64_t row = a.ring ? ((int64_t)(qi / a.q_per_seq) * a.ring_cap + pos % a.ring_cap) : (pos - a.pos0);
       R.v[j] = *reinterpret_cast<const uint4*>(a.win + row * D + ch * 8);
     }
   }
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
 
   // phase 1: compressed entries
   if (key_begin < e_end) {
-    const int64_t seq = (int64_t)(a.ckv_seq ? qi : 0) * a.ckv_seq;
+    const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
     const void* cbase = FP8 ? (const void*)(reinterpret_cast<const uint8_t*>(a.ckv) + seq * D)
                             : (const void*)(reinterpret_cast<const uint16_t*>(a.ckv) + seq * D);
     const float* sbase = a.ckv_scale ? a.ckv_scale + seq : nullptr;
@@ -725,9 +727,13 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
                                            const int32_t* n_entries, const int32_t* topk_idx, int k,
                                            const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
                                            float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
-                                           void* ws, size_t ws_bytes, float q_rms_eps, void* stream) {
+                                           void* ws, size_t ws_bytes, float q_rms_eps, int T, int R,
+                                           void* stream) {
   const char* name = "hybrid_attn_decode";
   CSKV_REQUIRE(B >= 1 && N_cap >= 0, CSKV_EINVAL, "%s: B=%d N_cap=%d", name, B, N_cap);
+  if (R == 0) R = W;
+  CSKV_REQUIRE(T >= 1 && (int64_t)B * T < (1 << 20), CSKV_EINVAL, "%s: T=%d", name, T);
+  CSKV_REQUIRE(W == 0 || R >= W, CSKV_EINVAL, "%s: ring of %d slots < window %d", name, R, W);
   int rc = check_common(name, H, D, d_rope, d_v, W, ckv_dtype, q_rms_eps);
   if (rc) return rc;
   CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
@@ -737,7 +743,7 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(win), CSKV_EINVAL, "%s: q/ckv/win must be 16-byte aligned",
                name);
   const int max_keys = (topk_idx ? k : N_cap) + W;
-  AttnPlan p = plan_attn(B, H, d_v, max_keys > 0 ? max_keys : 1);
+  AttnPlan p = plan_attn(B * T, H, d_v, max_keys > 0 ? max_keys : 1);
   AttnArgs a{};
   a.q = q;
   a.q_pos = q_pos;
@@ -753,8 +759,10 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   a.k = k;
   a.win = win;
   a.ring = 1;
+  a.ring_cap = R;
+  a.q_per_seq = T;
   a.W = W;
-  a.nq = B;
+  a.nq = B * T;
   a.H = H;
   a.D = D;
   a.d_rope = d_rope;
@@ -805,6 +813,8 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   a.k = k;
   a.win = x;
   a.ring = 0;
+  a.ring_cap = W;
+  a.q_per_seq = 1;
   a.W = W;
   a.nq = T;
   a.H = H;

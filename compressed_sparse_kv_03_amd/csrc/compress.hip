@@ -171,18 +171,20 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
   }
 }
 
+// Workgroup (b, i): token i of sequence b goes to ring slot (pos[b] + i) mod R.
 __global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __restrict__ x_new,
                                                           const float* __restrict__ z_new,
                                                           const int64_t* __restrict__ pos,
                                                           uint16_t* __restrict__ ring_x,
-                                                          float* __restrict__ ring_z, int D, int W) {
-  const int b = blockIdx.x;
-  const int64_t slot = (int64_t)b * W + (pos[b] % W);
+                                                          float* __restrict__ ring_z, int T, int D, int R) {
+  const int b = blockIdx.x, i = blockIdx.y;
+  const int64_t slot = (int64_t)b * R + ((pos[b] + i) % R);
+  const int64_t tok = (int64_t)b * T + i;
   const int cpr = D >> 3;
-  const uint4* src = reinterpret_cast<const uint4*>(x_new + (int64_t)b * D);
+  const uint4* src = reinterpret_cast<const uint4*>(x_new + tok * D);
   uint4* dst = reinterpret_cast<uint4*>(ring_x + slot * D);
   for (int c = threadIdx.x; c < cpr; c += blockDim.x) dst[c] = src[c];
-  if (threadIdx.x == 0 && z_new) ring_z[slot] = z_new[b];
+  if (threadIdx.x == 0 && z_new) ring_z[slot] = z_new[tok];
 }
 
 // Indexer keys of the entries: the per-token keys pooled with the entries' softmax weights, then
@@ -333,15 +335,16 @@ extern "C" CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, co
 }
 
 extern "C" CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_new, const int64_t* pos,
-                                uint16_t* ring_x, float* ring_z, int B, int D, int W, void* stream) {
-  CSKV_REQUIRE(B >= 1 && W >= 1, CSKV_EINVAL, "cskv_ring_append: B=%d W=%d", B, W);
+                                uint16_t* ring_x, float* ring_z, int B, int T, int D, int R, void* stream) {
+  CSKV_REQUIRE(B >= 1 && R >= 1, CSKV_EINVAL, "cskv_ring_append: B=%d R=%d", B, R);
+  CSKV_REQUIRE(T >= 1 && T <= R && T <= 65535, CSKV_EINVAL, "cskv_ring_append: T=%d (ring of %d)", T, R);
   CSKV_REQUIRE(D % 8 == 0 && D >= 8, CSKV_EINVAL, "cskv_ring_append: D=%d", D);
   CSKV_REQUIRE(x_new && pos && ring_x, CSKV_EINVAL, "cskv_ring_append: null pointer");
   CSKV_REQUIRE(!z_new || ring_z, CSKV_EINVAL, "cskv_ring_append: z_new needs ring_z");
   CSKV_REQUIRE(cskv::aligned16(x_new) && cskv::aligned16(ring_x), CSKV_EINVAL,
                "cskv_ring_append: x_new/ring_x must be 16-byte aligned");
-  cskv::ring_append_kernel<<<B, 128, 0, reinterpret_cast<hipStream_t>(stream)>>>(x_new, z_new, pos, ring_x,
-                                                                                 ring_z, D, W);
+  cskv::ring_append_kernel<<<dim3(B, T), 128, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      x_new, z_new, pos, ring_x, ring_z, T, D, R);
   CSKV_LAUNCH_CHECK("cskv_ring_append");
   return CSKV_OK;
 }

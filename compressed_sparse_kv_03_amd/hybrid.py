@@ -8,12 +8,20 @@ CSA 및 HCA": CSA pools 4 tokens per entry and selects top-k with the FP4 indexe
 HCA pools 128 per entry and attends densely.
 
 One decode step at position t (the same t for every sequence of the batch):
-  1. each layer writes its new raw token and pooling logit to ring slot t mod W;
+  1. each layer writes its new raw token and pooling logit to ring slot t mod R;
   2. if (t+1) % m == 0 the layer compresses ring slots of positions [t-m+1, t]
-     (contiguous because m divides W) into entry (t+1)/m - 1;
+     (contiguous because m divides R) into entry (t+1)/m - 1;
   3. CSA: csa_index_topk over the visible entries, then hybrid_attn_decode on
      the selected entries + window; HCA: hybrid_attn_decode over all entries +
      window.
+A draft step (draft = T > 1; page "DeepSeek V4.1 ...", section "DSpark 추측 디코딩":
+the model checks a block of drafted tokens at once) appends T tokens at t0..t0+T-1
+(with every block that completes) and answers T queries per sequence, query j
+seeing entries j < (t0+j+1)/m and the window up to t0+j; the rings have
+R >= W + T - 1 slots. With accept_seed >= 0 each step accepts a seeded number
+of its draft tokens (1..T) and the next step starts after them: its tokens
+overwrite the rejected ring slots and blocks holding rejected tokens are
+compressed again when they complete again.
 Every step is a call of libcskv.so on the current stream; the host only picks
 pointers. All per-step inputs are generated up front and the per-step counts
 live in device arrays, so a run of steps can be captured in one HIP graph.
@@ -52,6 +60,10 @@ class LayerPairSpec:
     dyadic_keys: bool = False
     # > 0: unit-gain RMSNorm (this epsilon) of the new compressed entries and of the queries
     rms_eps: float = 0.0
+    # draft tokens checked per step (1: plain decode) and the acceptance schedule (-1: every
+    # draft token accepted; else the seed of the accepted counts, uniform in 1..draft)
+    draft: int = 1
+    accept_seed: int = -1
 
     @property
     def sigma(self):
@@ -70,65 +82,99 @@ class LayerPair:
         self.s = s
         self.dev = device
         assert s.W % s.m_csa == 0 and s.W % s.m_hca == 0 and s.L % s.m_hca == 0 and s.L % s.m_csa == 0
-        assert s.L >= s.W
+        assert s.L >= s.W and s.draft >= 1
         sd = lambda t: synth.seed_of(s.seed, s.wid, t)  # noqa: E731
-        B, D, T = s.B, s.D, s.steps
-        self.n0 = {"csa": s.L // s.m_csa, "hca": s.L // s.m_hca}
-        self.cap = {"csa": (s.L + T) // s.m_csa + 1, "hca": (s.L + T) // s.m_hca + 1}
+        B, D, T, Td = s.B, s.D, s.steps, s.draft
         self.m = {"csa": s.m_csa, "hca": s.m_hca}
+        # rings of R >= W + Td - 1 slots, a multiple of m (R = W for one-token steps)
+        self.R = {n: -(-(s.W + Td - 1) // m) * m for n, m in self.m.items()}
+        # first draft position of every step
+        if s.accept_seed < 0:
+            acc = np.full(T, Td, np.int64)
+        else:
+            acc = np.random.default_rng(s.accept_seed).integers(1, Td + 1, T).astype(np.int64)
+        t0 = s.L + np.concatenate([[0], np.cumsum(acc)[:-1]]).astype(np.int64)
+        self.t_host, self.accepted = t0, acc
+        last = int(t0[-1]) + Td - 1
+        self.n0 = {"csa": s.L // s.m_csa, "hca": s.L // s.m_hca}
+        self.cap = {n: (last + 1) // m + 1 for n, m in self.m.items()}
         self.ckv, self.scl, self.ring, self.ringz, self.q, self.xn, self.zn = {}, {}, {}, {}, {}, {}, {}
         for li, name in enumerate(("csa", "hca")):
             base = 100 * li
+            R = self.R[name]
             c, sc = synth.fp8_rows_normal((B, self.cap[name], D), s.sigma, sd(base + 0), device)
             self.ckv[name], self.scl[name] = c, sc
-            self.ring[name] = synth.normal_bf16_bits((B, s.W, D), s.sigma, sd(base + 1), device)
-            self.ringz[name] = synth.normal((B, s.W), 1.0, sd(base + 2), device)
-            self.q[name] = synth.normal_bf16_bits((T, B, s.H, D), s.sigma, sd(base + 3), device)
-            self.xn[name] = synth.normal_bf16_bits((T, B, D), s.sigma, sd(base + 4), device)
-            self.zn[name] = synth.normal((T, B), 1.0, sd(base + 5), device)
+            # window tokens at positions L-W .. L-1, in ring slots (position mod R)
+            self.ring[name] = self._to_ring(synth.normal_bf16_bits((B, s.W, D), s.sigma, sd(base + 1), device), R)
+            self.ringz[name] = self._to_ring(synth.normal((B, s.W), 1.0, sd(base + 2), device), R)
+            self.q[name] = synth.normal_bf16_bits((T, B, Td, s.H, D), s.sigma, sd(base + 3), device)
+            self.xn[name] = synth.normal_bf16_bits((T, B, Td, D), s.sigma, sd(base + 4), device)
+            self.zn[name] = synth.normal((T, B, Td), 1.0, sd(base + 5), device)
         # indexer keys of every entry (without derive_keys, future entries' keys are inputs too)
         # and queries
         self.ik, self.iks = synth.mxfp4_normal((B, self.cap["csa"], s.D_I), sd(10), device)
-        self.iq, self.iqs = synth.mxfp4_normal((T, B, 1, s.H_I, s.D_I), sd(11), device)
+        self.iq, self.iqs = synth.mxfp4_normal((T, B, Td, s.H_I, s.D_I), sd(11), device)
         if s.derive_keys:  # per-token indexer keys: the window's and each new token's
             if s.dyadic_keys:
                 g = synth.generator(sd(12), device)
                 grid = lambda shape: synth.bf16_bits(  # noqa: E731
                     torch.randint(-64, 65, shape, generator=g, device=device).to(torch.float32) / 16)
-                self.ring_xk, self.xkn = grid((B, s.W, s.D_I)), grid((T, B, s.D_I))
+                ring_xk, self.xkn = grid((B, s.W, s.D_I)), grid((T, B, Td, s.D_I))
                 self.ringz["csa"].zero_()
                 self.zn["csa"].zero_()
             else:
-                self.ring_xk = synth.normal_bf16_bits((B, s.W, s.D_I), 1.0, sd(12), device)
-                self.xkn = synth.normal_bf16_bits((T, B, s.D_I), 1.0, sd(13), device)
-        # per-step device scalars
-        t = s.L + np.arange(T, dtype=np.int64)
-        self.t_host = t
-        self.pos = torch.from_numpy(np.repeat(t[:, None], B, 1)).to(device)
-        self.nent, self.pos0c, self.entry0 = {}, {}, {}
+                ring_xk = synth.normal_bf16_bits((B, s.W, s.D_I), 1.0, sd(12), device)
+                self.xkn = synth.normal_bf16_bits((T, B, Td, s.D_I), 1.0, sd(13), device)
+            self.ring_xk = self._to_ring(ring_xk, self.R["csa"])
+        # per-step device scalars: the first draft position, every query's position and the
+        # entries it sees, and the blocks each step completes (start position, entry index)
+        rep = lambda a, dt: torch.from_numpy(np.ascontiguousarray(  # noqa: E731
+            np.repeat(np.asarray(a)[:, None], B, 1).astype(dt))).to(device)
+        self.pos = rep(t0, np.int64)                                          # [T, B]
+        tq = t0[:, None] + np.arange(Td)[None, :]                             # [T, Td]
+        self.qpos = torch.from_numpy(np.ascontiguousarray(
+            np.repeat(tq[:, None, :], B, 1).astype(np.int64))).to(device)   # [T, B, Td]
+        self.nent, self.blocks = {}, {}
         for name in ("csa", "hca"):
             m = self.m[name]
-            n_after = (t + 1) // m
-            self.nent[name] = torch.from_numpy(np.repeat(n_after[:, None].astype(np.int32), B, 1)).to(device)
-            self.pos0c[name] = torch.from_numpy(np.repeat((t - m + 1)[:, None], B, 1)).to(device)
-            self.entry0[name] = torch.from_numpy(np.repeat((n_after - 1)[:, None].astype(np.int32), B, 1)).to(device)
-        self.nvalid = self.nent["csa"].view(T, B, 1)
-        # outputs of every step
-        self.out = {n: torch.empty((T, B, s.H, s.d_v), dtype=torch.int16, device=device) for n in ("csa", "hca")}
-        self.lse = {n: torch.empty((T, B, s.H), dtype=torch.float32, device=device) for n in ("csa", "hca")}
-        self.topk = torch.empty((T, B, 1, s.k), dtype=torch.int32, device=device)
+            self.nent[name] = torch.from_numpy(np.ascontiguousarray(
+                np.repeat(((tq + 1) // m)[:, None, :], B, 1).astype(np.int32))).to(device)
+            ends = [[int(e) for e in range(int(t0[i]), int(t0[i]) + Td) if (e + 1) % m == 0] for i in range(T)]
+            flat = [e for es in ends for e in es]
+            p0 = rep(np.array([e - m + 1 for e in flat], np.int64).reshape(-1), np.int64) if flat else None
+            e0 = rep(np.array([(e + 1) // m - 1 for e in flat], np.int64), np.int32) if flat else None
+            blocks, n = [], 0
+            for i in range(T):
+                blocks.append([((e - m + 1) % self.R[name], p0[n + u], e0[n + u]) for u, e in enumerate(ends[i])])
+                n += len(ends[i])
+            self.blocks[name] = blocks
+        self.nvalid = self.nent["csa"]                                        # [T, B, Td]
+        # outputs of every step (query rows b * Td + j)
+        self.out = {n: torch.empty((T, B * Td, s.H, s.d_v), dtype=torch.int16, device=device) for n in ("csa", "hca")}
+        self.lse = {n: torch.empty((T, B * Td, s.H), dtype=torch.float32, device=device) for n in ("csa", "hca")}
+        self.topk = torch.empty((T, B, Td, s.k), dtype=torch.int32, device=device)
         # workspaces
-        self.ws_idx = torch.empty(max(16, native.csa_index_topk_workspace_size(B, 1, self.cap["csa"], s.H_I, s.D_I, s.k)),
-                                  dtype=torch.uint8, device=device)
+        self.ws_idx = torch.empty(max(16, native.csa_index_topk_workspace_size(B, Td, self.cap["csa"], s.H_I, s.D_I,
+                                                                                s.k)), dtype=torch.uint8, device=device)
         self.ws_att = {}
         for name in ("csa", "hca"):
-            n = native.hybrid_attn_decode_workspace_size(B, s.H, s.d_v, self.cap[name], s.k, s.W, name == "hca")
+            n = native.hybrid_attn_decode_workspace_size(B * Td, s.H, s.d_v, self.cap[name], s.k, s.W, name == "hca")
             self.ws_att[name] = torch.empty(max(16, n), dtype=torch.uint8, device=device)
         # initial state, for restoring between runs
         self._init = {n: (self.ring[n].clone(), self.ringz[n].clone()) for n in ("csa", "hca")}
         if s.derive_keys:  # the loop overwrites the keys of new entries
             self._init["xk"] = self.ring_xk.clone()
             self._init["ik"] = (self.ik.clone(), self.iks.clone())
+
+    def _to_ring(self, win, R):
+        """Window rows of positions L-W .. L-1 ([B, W, ...]) placed at ring slots (position mod R)."""
+        s = self.s
+        if R == s.W and s.L % s.W == 0:
+            return win
+        ring = torch.zeros((win.shape[0], R) + tuple(win.shape[2:]), dtype=win.dtype, device=win.device)
+        slots = torch.from_numpy((s.L - s.W + np.arange(s.W)) % R).to(win.device)
+        ring[:, slots] = win
+        return ring
 
     # ------------------------------------------------------------------ state
     def restore(self):
@@ -142,22 +188,26 @@ class LayerPair:
             self.iks.copy_(self._init["ik"][1])
 
     def host_state(self):
-        """Host copies of the initial state and inputs (for the oracle)."""
+        """Host copies of the initial state and inputs (for the oracle). Per-step token inputs are
+        [steps, B, draft, ...], without the draft axis for one-token steps."""
         h = lambda t: t.cpu().numpy()  # noqa: E731
+        one = self.s.draft == 1
+        hs = lambda t: h(t[:, :, 0] if one else t)  # noqa: E731
         st = {}
         for n in ("csa", "hca"):
             st[n] = dict(ring=h(self._init[n][0]).view(np.uint16), ringz=h(self._init[n][1]),
-                         ckv=h(self.ckv[n]), scl=h(self.scl[n]), q=h(self.q[n]).view(np.uint16),
-                         xn=h(self.xn[n]).view(np.uint16), zn=h(self.zn[n]))
+                         ckv=h(self.ckv[n]), scl=h(self.scl[n]), q=hs(self.q[n]).view(np.uint16),
+                         xn=hs(self.xn[n]).view(np.uint16), zn=hs(self.zn[n]))
         st["ik"], st["iks"], st["iq"], st["iqs"] = h(self.ik), h(self.iks), h(self.iq), h(self.iqs)
+        st["t0"], st["accepted"], st["R"] = self.t_host.copy(), self.accepted.copy(), dict(self.R)
         if self.s.derive_keys:
             st["ik"], st["iks"] = h(self._init["ik"][0]), h(self._init["ik"][1])
-            st["ring_xk"], st["xkn"] = h(self._init["xk"]).view(np.uint16), h(self.xkn).view(np.uint16)
+            st["ring_xk"], st["xkn"] = h(self._init["xk"]).view(np.uint16), hs(self.xkn).view(np.uint16)
         return st
 
     # ------------------------------------------------------------------ one step
     def step(self, i, stream=None, share=None, src=None):
-        """Decode step i of both layers.
+        """Decode step i of both layers (draft tokens t0 .. t0 + draft - 1).
 
         share (cross-layer index sharing of the CSA layer, with `src` another LayerPair of the
         same shapes that has already run step i):
@@ -167,42 +217,40 @@ class LayerPair:
                        with its own indexer query and hence its own top-k.
         """
         s = self.s
-        B, D, W = s.B, s.D, s.W
-        t = int(self.t_host[i])
+        B, D, W, Td = s.B, s.D, s.W, s.draft
         assert share in (None, "reuse", "reindex") and (share is None or src is not None)
         kv = {"csa": src if share == "reindex" else self, "hca": self}
         for name in ("csa", "hca"):
             if kv[name] is not self:
                 continue
+            R, m = self.R[name], self.m[name]
             native.cskv_ring_append(self.xn[name][i], self.zn[name][i], self.pos[i], self.ring[name],
-                                    self.ringz[name], B, D, W, stream)
+                                    self.ringz[name], B, D, R, stream, T=Td)
             keys = name == "csa" and s.derive_keys
             if keys:
-                native.cskv_ring_append(self.xkn[i], None, self.pos[i], self.ring_xk, None, B, s.D_I, W, stream)
-            m = self.m[name]
-            if (t + 1) % m == 0:
-                slot0 = (t - m + 1) % W
-                fn = native.csa_compress if name == "csa" else native.hca_compress
-                fn(self.ring[name][:, slot0:], W * D, self.ringz[name][:, slot0:], W, self.pos0c[name][i], B, m, D,
+                native.cskv_ring_append(self.xkn[i], None, self.pos[i], self.ring_xk, None, B, s.D_I, R, stream, T=Td)
+            fn = native.csa_compress if name == "csa" else native.hca_compress
+            for slot0, p0, e0 in self.blocks[name][i]:
+                fn(self.ring[name][:, slot0:], R * D, self.ringz[name][:, slot0:], R, p0, B, m, D,
                    s.d_rope, m, 0, s.rope_base, native.CSKV_FP8_E4M3, self.ckv[name], self.scl[name],
-                   self.cap[name], self.entry0[name][i], stream, rms_eps=s.rms_eps)
+                   self.cap[name], e0, stream, rms_eps=s.rms_eps)
                 if keys:
-                    native.csa_index_key_pool(self.ring_xk[:, slot0:], W * s.D_I, self.ringz[name][:, slot0:], W, B, m,
-                                              s.D_I, m, self.ik, self.iks, self.cap[name], self.entry0[name][i], stream)
+                    native.csa_index_key_pool(self.ring_xk[:, slot0:], R * s.D_I, self.ringz[name][:, slot0:], R, B, m,
+                                              s.D_I, m, self.ik, self.iks, self.cap[name], e0, stream)
         if share == "reuse":
             topk = src.topk[i]
         else:
             ik = kv["csa"]
-            native.csa_index_topk(self.iq[i], self.iqs[i], None, ik.ik, ik.iks, self.nvalid[i], B, 1,
+            native.csa_index_topk(self.iq[i], self.iqs[i], None, ik.ik, ik.iks, self.nvalid[i], B, Td,
                                   self.cap["csa"], s.H_I, s.D_I, s.k, self.topk[i], None, self.ws_idx, None, stream)
             topk = self.topk[i]
         for name in ("csa", "hca"):
             c = kv[name]
-            native.hybrid_attn_decode(self.q[name][i], self.pos[i], c.ckv[name], c.scl[name],
+            native.hybrid_attn_decode(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
                                       native.CSKV_FP8_E4M3, self.cap[name], self.nent[name][i],
                                       topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
-                                      self.ws_att[name], None, stream, q_rms_eps=s.rms_eps)
+                                      self.ws_att[name], None, stream, q_rms_eps=s.rms_eps, T=Td, R=c.R[name])
 
     def run(self, first, count, stream=None):
         for i in range(first, first + count):
@@ -210,27 +258,29 @@ class LayerPair:
 
     # ------------------------------------------------------------------ accounting
     def step_bytes(self):
-        """Algorithmic HBM bytes of one decode step (both layers), by component."""
+        """Algorithmic HBM bytes of one decode step (both layers), by component. A draft step reads
+        each sequence's keys and entries once for all of its draft queries."""
         s = self.s
         n_c = self.n0["csa"]
         n_h = self.n0["hca"]
+        Td = s.draft
         e = s.D + 4                          # fp8 entry + fp32 scale
         xi = s.D_I // 2 + s.D_I // 32        # MXFP4 key
-        q = s.B * s.H * s.D * 2
-        o = s.B * s.H * s.d_v * 2
-        win = s.B * s.W * s.D * 2
+        q = s.B * Td * s.H * s.D * 2
+        o = s.B * Td * s.H * s.d_v * 2
+        win = s.B * (s.W + Td - 1) * s.D * 2
         out = {
-            "csa_index": s.B * n_c * xi + s.B * s.H_I * xi + s.B * s.k * 4,
-            "csa_attn": s.B * s.k * e + win + q + o + s.B * s.k * 4,
+            "csa_index": s.B * n_c * xi + s.B * Td * s.H_I * xi + s.B * Td * s.k * 4,
+            "csa_attn": s.B * Td * s.k * e + win + q + o + s.B * Td * s.k * 4,
             "hca_attn": s.B * n_h * e + win + q + o,
         }
         if s.derive_keys:  # key append (read + write) and, amortised over m steps, the pooling
-            out["csa_keys"] = s.B * (2 * s.D_I * 2 + s.D_I * 2 + 4) + s.B * xi // s.m_csa
+            out["csa_keys"] = Td * (s.B * (2 * s.D_I * 2 + s.D_I * 2 + 4) + s.B * xi // s.m_csa)
         return out
 
     def step_flops(self):
         s = self.s
-        n_c, n_h = self.n0["csa"], self.n0["hca"]
-        idx = 2 * s.B * n_c * s.H_I * s.D_I
-        att = lambda nk: 2 * s.B * s.H * nk * (s.D + s.d_v)  # noqa: E731
+        n_c, n_h, Td = self.n0["csa"], self.n0["hca"], s.draft
+        idx = 2 * s.B * Td * n_c * s.H_I * s.D_I
+        att = lambda nk: 2 * s.B * Td * s.H * nk * (s.D + s.d_v)  # noqa: E731
         return {"csa_index": idx, "csa_attn": att(s.k + s.W), "hca_attn": att(n_h + s.W)}

@@ -26,12 +26,12 @@ _SIGS = {
     "csa_index_topk": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "csa_index_topk_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
     "hybrid_attn_decode": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
-                            _p, _p, _p, _sz, _f, _p], _i),
+                            _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "hybrid_attn_prefill": ([_p, _i64, _i, _p, _p, _i, _i, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                              _p, _p, _p, _sz, _f, _p], _i),
     "hybrid_attn_prefill_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
-    "cskv_ring_append": ([_p, _p, _p, _p, _p, _i, _i, _i, _p], _i),
+    "cskv_ring_append": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _p], _i),
     "csa_index_key_pool": ([_p, _i64, _p, _i64, _i, _i, _i, _i, _p, _p, _i64, _p, _p], _i),
 }
 
@@ -137,13 +137,15 @@ def hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, dense):
 
 def hybrid_attn_decode(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
                        D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, ws, ws_bytes=None,
-                       stream=None, *, q_rms_eps=0.0):
+                       stream=None, *, q_rms_eps=0.0, T=1, R=0):
+    """B sequences x T queries (rows b*T + j of q, q_pos, n_entries, topk_idx, out, out_lse);
+    rings of R slots (0: R = W)."""
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hybrid_attn_decode(_ptr(q), _ptr(q_pos), _ptr(ckv), _ptr(ckv_scale), ckv_dtype, N_cap,
                                     _ptr(n_entries), _ptr(topk_idx), k, _ptr(win), W, B, H, D, d_rope, d_v,
                                     rope_base, softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes,
-                                    q_rms_eps, _stream(stream)))
+                                    q_rms_eps, T, R, _stream(stream)))
 
 
 def hybrid_attn_prefill_workspace_size(T, H, d_v, N, k, W, dense):
@@ -161,6 +163,7 @@ def hybrid_attn_prefill(q, pos0, T, ckv, ckv_scale, ckv_dtype, N, topk_idx, k, x
 
 
 # ------------------------------------------------------------------ decode state update
-def cskv_ring_append(x_new, z_new, pos, ring_x, ring_z, B, D, W, stream=None):
-    _check(lib().cskv_ring_append(_ptr(x_new), _ptr(z_new), _ptr(pos), _ptr(ring_x), _ptr(ring_z), B, D, W,
+def cskv_ring_append(x_new, z_new, pos, ring_x, ring_z, B, D, R, stream=None, *, T=1):
+    """T tokens per sequence (x_new [B, T, D]) into rings of R slots: slot (pos[b] + i) mod R."""
+    _check(lib().cskv_ring_append(_ptr(x_new), _ptr(z_new), _ptr(pos), _ptr(ring_x), _ptr(ring_z), B, T, D, R,
                                   _stream(stream)))

@@ -161,36 +161,42 @@ CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scale, const fl
 CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, int D_I, int k);
 
 /*
- * hybrid_attn_decode - one decode query per sequence: shared-KV MQA attention
- * over compressed entries plus the sliding window, one joint softmax per head.
- * (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및
- * HCA": CSA attends to its top-k entries with a window branch alongside, HCA
- * attends to all of its entries; MQA shares one KV head; partial RoPE.)
+ * hybrid_attn_decode - T decode queries per sequence (T = 1: plain decode; T > 1:
+ * a draft of T tokens checked in one step, causal inside the draft): shared-KV
+ * MQA attention over compressed entries plus the sliding window, one joint
+ * softmax per head. (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지
+ * 압축 전략: CSA 및 HCA": CSA attends to its top-k entries with a window branch
+ * alongside, HCA attends to all of its entries; MQA shares one KV head; partial
+ * RoPE. Page "DeepSeek V4.1 ...", section "DSpark 추측 디코딩": the model checks
+ * a block of drafted tokens at once.)
  *
- * For sequence b with query position t = q_pos[b]:
- *   keys = entries {topk_idx[b, i] >= 0} (CSA) or {0..n_entries[b]-1} (topk_idx == NULL, HCA)
- *          plus window tokens at positions [max(0, t-W+1), t], read raw from
- *          ring slot (position mod W) and rotated at their own position
- *   q_rot = RoPE(q[b, h], t); logit = softmax_scale * g_h * q_rot . key, with
- *   g_h = 1 / sqrt(mean_d(q[b, h, d]^2) + q_rms_eps) if q_rms_eps > 0 (unit-gain
+ * Query r = b*T + j (sequence b, draft token j) at position t = q_pos[r]:
+ *   keys = entries {topk_idx[r, i] >= 0} (CSA) or {0..n_entries[r]-1} (topk_idx == NULL, HCA)
+ *          of sequence b, plus window tokens at positions [max(0, t-W+1), t], read raw
+ *          from ring slot (position mod R) of sequence b and rotated at their own position
+ *   q_rot = RoPE(q[r, h], t); logit = softmax_scale * g_h * q_rot . key, with
+ *   g_h = 1 / sqrt(mean_d(q[r, h, d]^2) + q_rms_eps) if q_rms_eps > 0 (unit-gain
  *   RMSNorm of the query head, the pages' "query normalisation"), else 1
- *   out[b, h, :] = bf16_rne(sum softmax(logit) * key[:d_v]); out_lse[b, h] = ln(sum exp(logit))
+ *   out[r, h, :] = bf16_rne(sum softmax(logit) * key[:d_v]); out_lse[r, h] = ln(sum exp(logit))
  * Entries are stored rotated: bf16 [B, N_cap, D], or fp8 codes [B, N_cap, D]
  * with fp32 scales ckv_scale [B, N_cap] (value = code * scale).
  *
- * q [B, H, D] bf16 (unrotated); q_pos [B] int64; n_entries [B] int32 <= N_cap
- * topk_idx [B, k] int32 (each -1 or in [0, n_entries[b])) or NULL
- * win [B, W, D] bf16 ring of raw tokens; out [B, H, d_v] bf16; out_lse [B, H] fp32 or NULL
+ * q [B*T, H, D] bf16 (unrotated); q_pos [B*T] int64; n_entries [B*T] int32 <= N_cap
+ * (causal inside a draft: each query its own count); topk_idx [B*T, k] int32 (each -1
+ * or in [0, n_entries[r])) or NULL; win [B, R, D] bf16 rings of raw tokens (R = 0 means
+ * R = W; a T-token step needs R >= W + T - 1 so that no query's window has been
+ * overwritten); out [B*T, H, d_v] bf16; out_lse [B*T, H] fp32 or NULL; ws of at least
+ * hybrid_attn_decode_workspace_size(B*T, ...) bytes.
  * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
- * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W, W + k or W + N_cap fits int32,
- * q_rms_eps finite and >= 0.
+ * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W <= R, T >= 1,
+ * W + k or W + N_cap fits int32, q_rms_eps finite and >= 0.
  */
 CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
                        const float* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
                        const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H,
                        int D, int d_rope, int d_v, float rope_base, float softmax_scale,
                        uint16_t* out, float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps,
-                       void* stream);
+                       int T, int R, void* stream);
 CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense);
 
 /*
@@ -213,16 +219,18 @@ CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const v
 CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense);
 
 /*
- * cskv_ring_append - decode state update: write each sequence's new raw token
- * and pooling logit into its window ring at slot pos[b] mod W. (The window
- * keeps the latest W tokens: page "딥시크 V4 분석 ...", section "쉽게 이해하기".)
+ * cskv_ring_append - decode state update: write each sequence's T new raw
+ * tokens and pooling logits into its ring at slots (pos[b] + i) mod R. (The
+ * window keeps the latest W tokens: page "딥시크 V4 분석 ...", section "쉽게
+ * 이해하기"; a ring of R >= W + T - 1 slots keeps every window of a T-token
+ * step intact while its later tokens are appended.)
  *
- * x_new [B, D] bf16; z_new [B] fp32 or NULL; pos [B] int64;
- * ring_x [B, W, D] bf16; ring_z [B, W] fp32 or NULL (with z_new).
- * Requirements: D % 8 == 0, W >= 1.
+ * x_new [B, T, D] bf16; z_new [B, T] fp32 or NULL; pos [B] int64 (position of token 0);
+ * ring_x [B, R, D] bf16; ring_z [B, R] fp32 or NULL (with z_new).
+ * Requirements: D % 8 == 0, 1 <= T <= R.
  */
 CSKV_API int cskv_ring_append(const uint16_t* x_new, const float* z_new, const int64_t* pos,
-                     uint16_t* ring_x, float* ring_z, int B, int D, int W, void* stream);
+                     uint16_t* ring_x, float* ring_z, int B, int T, int D, int R, void* stream);
 
 #ifdef __cplusplus
 }

@@ -84,19 +84,22 @@ def query(q_bits, t, d_rope, rope_base, q_rms_eps=0.0):
     return rope.apply(q, np.full(q_bits.shape[0], t), d_rope, rope_base)
 
 
-def decode_one(q_bits, t, entries, n_entries, topk_idx, ring, W, d_rope, d_v, rope_base, scale, q_rms_eps=0.0):
+def decode_one(q_bits, t, entries, n_entries, topk_idx, ring, W, d_rope, d_v, rope_base, scale, q_rms_eps=0.0,
+               ring_cap=None):
     """One decode query for one sequence.
 
     q_bits [H, D] bf16 (unrotated) at position t; entries: Entries;
     n_entries visible entries; topk_idx [k] (CSA) or None (HCA: all j < n_entries);
-    ring [W, D] bf16 raw window ring, token at position p held in slot p mod W.
+    ring [R, D] bf16 raw token ring (R = ring_cap, default W), token at position p held in
+    slot p mod R; the window is positions [max(0, t-W+1), t].
     """
+    R = W if ring_cap is None else ring_cap
     q = query(q_bits, t, d_rope, rope_base, q_rms_eps)
     sel = range(n_entries) if topk_idx is None else [j for j in topk_idx if 0 <= j]
     if topk_idx is not None:
         assert all(j < n_entries for j in sel), "selected entry not visible"
     wpos = np.arange(max(0, t - W + 1), t + 1)
-    wtok = ring[wpos % W] if W > 0 else np.zeros((0, entries.D), np.uint16)
+    wtok = ring[wpos % R] if W > 0 else np.zeros((0, entries.D), np.uint16)
     K, V = key_set(t, entries, sel, wtok, wpos if W > 0 else [], d_rope, d_v, rope_base)
     return attend(q, K, V, scale)
 

@@ -15,7 +15,16 @@ Readings taken where the pages are silent:
     compressed into entry (t+1)/m - 1 at position t-m+1; then the layer
     attends with its query at t;
   * the indexer key of each CSA entry is an input (already present in the key
-    buffer); only its visibility (j < n_entries) changes during the loop.
+    buffer); only its visibility (j < n_entries) changes during the loop;
+  * a draft step ([P4] section "DSpark 추측 디코딩": the model checks a block of
+    drafted tokens at once) appends all T draft tokens (with their block
+    compressions) and then answers the T queries, query j seeing what a
+    one-token step at t0 + j would see (entries j < (t0+j+1)/m, window up to
+    t0 + j). The ring has R >= W + T - 1 slots (slot = position mod R, R a
+    multiple of m) so that no query's window is overwritten. When only the
+    first a draft tokens are accepted the next step starts at t0 + a: its
+    tokens overwrite the rejected ring slots, and a block that held a rejected
+    token is compressed again when it completes again.
 """
 import numpy as np
 
@@ -33,6 +42,8 @@ class Layer:
         self.ckv, self.ckv_scale, self.dtype = ckv, ckv_scale, dtype
         self.n_entries = np.array(n_entries, dtype=np.int64)
         self.ring_x, self.ring_z = ring_x, ring_z
+        self.R = ring_x.shape[1]   # ring slots (W for one-token steps)
+        assert self.R >= W and self.R % m == 0
         self.k, self.ik, self.ik_scale = k, ik, ik_scale
         # per-token indexer keys of the window: when given, each new entry's key is derived from
         # its tokens' keys (compress.index_keys) instead of being an input
@@ -77,24 +88,60 @@ class Layer:
             ent = attention.Entries(self.ckv[b], None if self.ckv_scale is None else self.ckv_scale[b],
                                     self.dtype)
             o, lse = attention.decode_one(q[b], tb, ent, n, sel, self.ring_x[b], self.W,
-                                          self.d_rope, self.d_v, self.rope_base, self.scale, self.rms_eps)
+                                          self.d_rope, self.d_v, self.rope_base, self.scale, self.rms_eps,
+                                          ring_cap=self.R)
             outs.append(o)
             lses.append(lse)
         if not outputs:
             return None, None, None
         return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)
 
+    def step_draft(self, t0, x_new, z_new, q, iq=None, iq_scale=None, xk_new=None):
+        """One step of T draft tokens per sequence at positions t0[b] .. t0[b] + T - 1.
+
+        x_new [B, T, D], z_new [B, T], q [B, T, H, D], iq [B, T, H_I, D_I/2], iq_scale
+        [B, T, H_I, D_I/32], xk_new [B, T, D_I] or None. Returns (o [B, T, H, d_v], lse [B, T, H],
+        idx [B, T, k] or None).
+        """
+        B, T = x_new.shape[0], x_new.shape[1]
+        for b in range(B):
+            for j in range(T):
+                self._update(b, int(t0[b]) + j, x_new[b, j], z_new[b, j], None if xk_new is None else xk_new[b, j])
+        outs, lses, idxs = [], [], []
+        for b in range(B):
+            ob, lb, ib = [], [], []
+            ent = attention.Entries(self.ckv[b], None if self.ckv_scale is None else self.ckv_scale[b], self.dtype)
+            for j in range(T):
+                tj = int(t0[b]) + j
+                n = (tj + 1) // self.m
+                sel = None
+                if self.kind == "csa":
+                    sc = indexer.scores(iq[b, j][None], iq_scale[b, j][None], self.ik[b, :n], self.ik_scale[b, :n],
+                                        np.array([n]))
+                    sel = topk_mod.topk(sc, self.k)[0][0]
+                    ib.append(sel)
+                o, lse = attention.decode_one(q[b, j], tj, ent, n, sel, self.ring_x[b], self.W, self.d_rope,
+                                              self.d_v, self.rope_base, self.scale, self.rms_eps, ring_cap=self.R)
+                ob.append(o)
+                lb.append(lse)
+            outs.append(np.stack(ob))
+            lses.append(np.stack(lb))
+            if ib:
+                idxs.append(np.stack(ib))
+        return np.stack(outs), np.stack(lses), (np.stack(idxs) if idxs else None)
+
     def _update(self, b, tb, x_new, z_new, xk_new=None):
         """Window append of position tb and, at a block end, its compression (sequence b)."""
-        self.ring_x[b, tb % self.W] = x_new
-        self.ring_z[b, tb % self.W] = z_new
+        self.ring_x[b, tb % self.R] = x_new
+        self.ring_z[b, tb % self.R] = z_new
         if self.ring_xk is not None:
-            self.ring_xk[b, tb % self.W] = xk_new
+            self.ring_xk[b, tb % self.R] = xk_new
         if (tb + 1) % self.m == 0:
             j = (tb + 1) // self.m - 1
-            assert j == self.n_entries[b], "entry count out of step with position"
+            # j < n_entries: the block is compressed again after a rejected draft token
+            assert j <= self.n_entries[b], "entry count out of step with position"
             p0 = tb - self.m + 1
-            slots = np.arange(p0, tb + 1) % self.W
+            slots = np.arange(p0, tb + 1) % self.R
             _, stored, s = compress.compress(self.ring_x[b, slots], self.ring_z[b, slots], p0,
                                              self.m, self.d_rope, self.rope_base, self.dtype, rms_eps=self.rms_eps)
             self.ckv[b, j] = stored[0]

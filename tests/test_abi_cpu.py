@@ -89,7 +89,7 @@ def test_attention_validation():
     def dec(**kw):
         a = dict(q=16, qp=16, ckv=16, sc=16, dt=1, N=100, ne=16, tk=None, k=128, win=16, W=128, B=1, H=64,
                  D=576, dr=64, dv=512, base=1e4, scale=0.04, out=16, lse=None, ws=16, wsb=1 << 30, eps=0.0,
-                 s=None)
+                 T=1, R=0, s=None)
         a.update(kw)
         return L.hybrid_attn_decode(*a.values())
     assert dec(D=100) == -1
@@ -101,6 +101,8 @@ def test_attention_validation():
     assert dec(sc=None) == -1
     assert dec(ws=None, wsb=0) == -3
     assert dec(eps=-1.0) == -1
+    assert dec(T=0) == -1
+    assert dec(R=100) == -1                  # ring smaller than the window
     assert dec(eps=float("nan")) == -1
     assert L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) > 0
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
@@ -110,3 +112,13 @@ def test_attention_validation():
     assert pre(m=0) == -1
     assert pre(T=0) == 0
     assert pre(x=None) == -1
+
+
+def test_ring_append_validation():
+    L = native.lib()
+    # (x_new, z_new, pos, ring_x, ring_z, B, T, D, R, stream)
+    assert L.cskv_ring_append(16, None, 16, 16, None, 1, 0, 64, 8, None) == -1     # T = 0
+    assert L.cskv_ring_append(16, None, 16, 16, None, 1, 9, 64, 8, None) == -1     # T > R
+    assert L.cskv_ring_append(16, None, 16, 16, None, 1, 2, 60, 8, None) == -1     # D % 8
+    assert L.cskv_ring_append(16, 16, 16, 16, None, 1, 2, 64, 8, None) == -1       # z_new without ring_z
+    assert L.cskv_ring_append(None, None, 16, 16, None, 1, 2, 64, 8, None) == -1   # null

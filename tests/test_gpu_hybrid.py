@@ -210,3 +210,49 @@ def test_hybrid_loop_cross_layer_index_sharing(share):
                 parity.topk_exact(tk1[i][:, 0], idx, f"re-index top-k step {i}")
             parity.attn_close(out[name][i], o, f"{share} {name} step {i}")
             parity.lse_close(lse[name][i], l, None, f"{share} {name} lse step {i}")
+
+
+@pytest.mark.parametrize("draft,accept_seed", [(4, 3), (6, -1)])
+def test_hybrid_loop_draft_steps(draft, accept_seed):
+    """Multi-token decode: draft tokens checked per step, causal inside the draft, with a seeded
+    number of accepted tokens per step (rejected ones overwritten by the next draft). Every query of
+    every step against the oracle's draft step: top-k bit-exact, attention within the parity bounds,
+    and the entries written by the loop (recompressed after rejections) within one fp8 step."""
+    spec = hybrid.LayerPairSpec(B=2, L=2048, steps=70, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
+                                wid=59, draft=draft, accept_seed=accept_seed)
+    say("hybrid draft", spec)
+    pair = hybrid.LayerPair(spec)
+    pair.run(0, spec.steps)
+    torch.cuda.synchronize()
+    st = pair.host_state()
+    layers = {}
+    for name, m in (("csa", spec.m_csa), ("hca", spec.m_hca)):
+        h = st[name]
+        layers[name] = ohyb.Layer(name, m, spec.W, spec.d_rope, spec.d_v, spec.rope_base, spec.scale,
+                                  h["ckv"].copy(), h["scl"].copy(), "fp8", np.full(spec.B, spec.L // m),
+                                  h["ring"].copy(), h["ringz"].copy(), k=spec.k,
+                                  ik=st["ik"].copy() if name == "csa" else None,
+                                  ik_scale=st["iks"].copy() if name == "csa" else None)
+    out = {n: pair.out[n].cpu().numpy() for n in ("csa", "hca")}
+    lse = {n: pair.lse[n].cpu().numpy() for n in ("csa", "hca")}
+    tk = pair.topk.cpu().numpy()
+    B, T = spec.B, draft
+    for i in range(spec.steps):
+        t0 = np.full(B, st["t0"][i])
+        for name, lay in layers.items():
+            h = st[name]
+            csa = name == "csa"
+            o, l, idx = lay.step_draft(t0, h["xn"][i], h["zn"][i], h["q"][i], st["iq"][i] if csa else None,
+                                       st["iqs"][i] if csa else None)
+            if idx is not None:
+                parity.topk_exact(tk[i], idx, f"draft top-k step {i}")
+            parity.attn_close(out[name][i], o.reshape(B * T, spec.H, spec.d_v), f"draft {name} step {i}")
+            parity.lse_close(lse[name][i], l.reshape(B * T, spec.H), None, f"draft {name} lse step {i}")
+    last = int(st["t0"][-1]) + draft          # entries of complete blocks up to the last position
+    for name in ("csa", "hca"):
+        n0, n_end = spec.L // pair.m[name], last // pair.m[name]
+        g = pair.ckv[name][:, n0:n_end].cpu().numpy().astype(np.int64)
+        o_ = layers[name].ckv[:, n0:n_end].astype(np.int64)
+        ordered = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)  # noqa: E731
+        d = np.abs(ordered(g) - ordered(o_))
+        assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-2 * max(d.size, 1), f"{name} entries"

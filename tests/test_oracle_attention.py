@@ -252,3 +252,58 @@ def test_query_rms_norm_is_plain_attention_on_normalised_queries():
     assert np.allclose(a[0], b[0], rtol=1e-12, atol=1e-14)
     c = attention.decode_one(q4, L - 1, ent, L, None, np.zeros((1, D), np.uint16), 0, 0, D, 10000.0, 0.4)
     assert not np.allclose(a[0], c[0], rtol=1e-6)
+
+
+def _layer(kind, m, W, R, B, L, D, dr, dv, cap, rng, tokens, logits, ik, iks, k):
+    ckv = np.zeros((B, cap, D), np.uint8)
+    scl = np.ones((B, cap), np.float32)
+    n0 = L // m
+    for b in range(B):
+        _, c, s = compress.compress(tokens[b, :L], logits[b, :L], 0, m, dr, 10000.0, "fp8")
+        ckv[b, :n0], scl[b, :n0] = c, s
+    ring_x = np.zeros((B, R, D), np.uint16)
+    ring_z = np.zeros((B, R), np.float32)
+    for p in range(L - W, L):
+        ring_x[:, p % R] = tokens[:, p]
+        ring_z[:, p % R] = logits[:, p]
+    return hybrid.Layer(kind, m, W, dr, dv, 10000.0, 0.3, ckv, scl, "fp8", np.full(B, n0), ring_x, ring_z, k=k,
+                        ik=ik.copy(), ik_scale=iks.copy())
+
+
+def test_draft_steps_equal_single_steps_and_rejected_tokens_leave_no_trace():
+    """A draft step answers query j exactly as a one-token step at t0 + j; after only the first
+    draft token is accepted, the next draft (re-drafted tokens) matches one-token steps over the
+    accepted history: rejected tokens leave no trace in the ring or the entries."""
+    rng = np.random.default_rng(8)
+    B, H, D, dv, dr, W, L, T, m = 2, 2, 16, 8, 8, 8, 32, 3, 4
+    HI, DI, k = 2, 32, 4
+    n_tok = L + 16
+    tokens = _bf16(rng, (B, n_tok, D), 0.5)
+    logits = rng.standard_normal((B, n_tok)).astype(np.float32)
+    cap = n_tok // m + 1
+    ik = rng.integers(0, 256, (B, cap, DI // 2), dtype=np.uint8)
+    iks = rng.integers(126, 128, (B, cap, DI // 32), dtype=np.uint8)
+    q = _bf16(rng, (B, 8, H, D), 0.5)
+    iq = rng.integers(0, 256, (B, 8, HI, DI // 2), dtype=np.uint8)
+    iqs = np.full((B, 8, HI, 1), 127, np.uint8)
+    rejected = _bf16(rng, (B, 2, D), 0.5)       # draft tokens 1 and 2 of the first step
+    for kind, mm in (("csa", m), ("hca", 8)):
+        R = -(-(W + T - 1) // mm) * mm           # >= W + T - 1, a multiple of m
+        a = _layer(kind, mm, W, R, B, L, D, dr, dv, cap, rng, tokens, logits, ik, iks, k)
+        s1 = _layer(kind, mm, W, W, B, L, D, dr, dv, cap, rng, tokens, logits, ik, iks, k)
+        # step 1: draft of 3 at L (tokens L, rejected, rejected); only token L is accepted
+        x1 = np.concatenate([tokens[:, L:L + 1], rejected], axis=1)
+        z1 = np.concatenate([logits[:, L:L + 1], rng.standard_normal((B, 2)).astype(np.float32)], axis=1)
+        o1, l1, _ = a.step_draft(np.full(B, L), x1, z1, q[:, 0:3], iq[:, 0:3], iqs[:, 0:3])
+        # step 2: draft of 3 at L + 1 (the real tokens L+1 .. L+3)
+        o2, l2, i2 = a.step_draft(np.full(B, L + 1), tokens[:, L + 1:L + 4], logits[:, L + 1:L + 4], q[:, 3:6],
+                                  iq[:, 3:6], iqs[:, 3:6])
+        # the same history one token at a time: L (query 0), then L+1 .. L+3 (queries 3..5)
+        for j, (tq, qi) in enumerate([(L, 0), (L + 1, 3), (L + 2, 4), (L + 3, 5)]):
+            o, lse, idx = s1.step(np.full(B, tq), tokens[:, tq], logits[:, tq], q[:, qi], iq[:, qi], iqs[:, qi])
+            got_o, got_l = (o1[:, 0], l1[:, 0]) if j == 0 else (o2[:, j - 1], l2[:, j - 1])
+            assert np.allclose(got_o, o, rtol=0, atol=0) and np.allclose(got_l, lse, rtol=0, atol=0), (kind, j)
+            if kind == "csa" and j > 0:
+                assert np.array_equal(i2[:, j - 1], idx)
+        n = (L + 4) // mm
+        assert np.array_equal(a.ckv[:, :n], s1.ckv[:, :n]) and np.array_equal(a.ckv_scale[:, :n], s1.ckv_scale[:, :n])
