@@ -14,7 +14,8 @@ One decode step at position t (the same t for every sequence of the batch):
   3. CSA: csa_index_topk over the visible entries, then hybrid_attn_decode on
      the selected entries + window; HCA: hybrid_attn_decode over all entries +
      window.
-A draft step (draft = T > 1; page "DeepSeek V4.1 ...", section "DSpark 추측 디코딩":
+A draft step (draft = T > 1; the blog post on DeepSeek V4.1 Flash at jjy0501.blogspot.com,
+section "DSpark 추측 디코딩":
 the model checks a block of drafted tokens at once) appends T tokens at t0..t0+T-1
 (with every block that completes) and answers T queries per sequence, query j
 seeing entries j < (t0+j+1)/m and the window up to t0+j; the rings have

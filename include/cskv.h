@@ -167,7 +167,8 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * softmax per head. (Page "DeepSeek-V4가 ... 달성하는 방법", section "두 가지
  * 압축 전략: CSA 및 HCA": CSA attends to its top-k entries with a window branch
  * alongside, HCA attends to all of its entries; MQA shares one KV head; partial
- * RoPE. Page "DeepSeek V4.1 ...", section "DSpark 추측 디코딩": the model checks
+ * RoPE. The blog post on DeepSeek V4.1 Flash (jjy0501.blogspot.com), section
+ * "DSpark 추측 디코딩": the model checks
  * a block of drafted tokens at once.)
  *
  * Query r = b*T + j (sequence b, draft token j) at position t = q_pos[r]:
