@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--draft", type=int, default=1,
                     help="draft tokens checked per decode step (multi-token decode, causal inside the draft; "
                          "every draft token accepted, value counts positions)")
+    ap.add_argument("--kv", choices=["fp8", "mxfp4"], default="fp8",
+                    help="storage of the compressed entries (mxfp4: OCP MX e2m1 codes + E8M0 per 32 dims)")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -115,7 +117,8 @@ def main():
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
-    spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0, draft=args.draft)
+    spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0, draft=args.draft,
+                   kv_dtype=args.kv)
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec_kw), dev) for p in range(P)]
     spec = pairs[0].s
     torch.cuda.synchronize()
@@ -193,7 +196,7 @@ def main():
 
     def run_attn(name):
         def f():
-            native.hybrid_attn_decode(pr.q[name][i0], pr.qpos[i0], pr.ckv[name], pr.scl[name], native.CSKV_FP8_E4M3,
+            native.hybrid_attn_decode(pr.q[name][i0], pr.qpos[i0], pr.ckv[name], pr.scl[name], pr.kv_code,
                                       pr.cap[name], pr.nent[name][i0], pr.topk[i0] if name == "csa" else None,
                                       s_.k, pr.ring[name], s_.W, s_.B, s_.H, s_.D, s_.d_rope, s_.d_v, s_.rope_base,
                                       s_.scale, pr.out[name][i0], pr.lse[name][i0], pr.ws_att[name],
@@ -220,11 +223,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 KV / mxfp4 indexer / bf16 MFMA, fp32 accumulate",
+        "dtype": f"{'mxfp4' if args.kv == 'mxfp4' else 'fp8-e4m3'} KV / mxfp4 indexer / bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) draws; no checkpoints)",
         "config": {
             "workload": "c5_hybrid_1m: CSA(m=4,k=128,FP4 indexer 8x128)+HCA(m=128) layer pair, decode batch 8, "
-                        "context 2^20, H=64, D=512+64, fp8 entries, bf16 window 128",
+                        f"context 2^20, H=64, D=512+64, {args.kv} entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "tokens_per_step_per_pair": spec.B * spec.draft,
             **({"draft_tokens_per_step": spec.draft} if spec.draft > 1 else {}),

@@ -45,8 +45,8 @@ struct AttnArgs {
   const int64_t* q_pos;     // [nq] (decode) or nullptr (prefill: pos0 + row)
   int64_t pos0;
   const void* ckv;          // [B_kv, N_cap, D] bf16 bits or fp8 codes
-  const float* ckv_scale;   // [B_kv, N_cap] (fp8)
-  int fp8;
+  const void* ckv_scale;    // fp32 [B_kv, N_cap] (fp8) or E8M0 bytes [B_kv, N_cap, D/32] (MXFP4)
+  int kv;                   // kKvBf16, kKvFp8 or kKvMxfp4
   int N_cap;
   int64_t ckv_seq;          // entries between sequences (0: all queries share one cache)
   const int32_t* n_entries; // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))
@@ -141,24 +141,30 @@ __device__ __forceinline__ uint4 rope8(uint4 v, int64_t pos, const double* inv_f
   return pack8(f);
 }
 
+// Storage of the compressed entries (ckv_dtype): bf16 rows, e4m3fn rows with one fp32 scale per
+// row, or MXFP4 rows (e2m1 codes, one E8M0 exponent per 32 dims).
+enum { kKvBf16 = 0, kKvFp8 = 1, kKvMxfp4 = 2 };
+
 // One tile's raw bytes in registers: every thread's chunks are loaded with independent
 // loads (issued back to back, consumed one tile later), so a tile costs one memory latency.
-// Entry tiles of an fp8 cache hold 8 bytes per 16-byte bf16 chunk; bf16 rows hold 16.
-template <int KD, int HG, bool NARROW>
+// A chunk is 8 dims of a bf16 row (16 bytes) or of an fp8 row (8 bytes), or one MX block of 32
+// dims of an MXFP4 row (16 bytes of codes and its exponent byte).
+template <int KD, int HG, int KV>
 struct TileRegs {
-  static constexpr int CPR = KD * 4;                      // 16-byte bf16 chunks per row
+  static constexpr int CPR = KV == kKvMxfp4 ? KD : KD * 4;  // chunks per row
   static constexpr int NT = 2 * HG * kWave;
   static constexpr int ITERS = (kTK * CPR + NT - 1) / NT;
-  typename std::conditional<NARROW, uint2, uint4>::type v[ITERS];
+  typename std::conditional<KV == kKvFp8, uint2, uint4>::type v[ITERS];
+  uint32_t bs[KV == kKvMxfp4 ? ITERS : 1];  // MXFP4: the chunk's E8M0 byte
   float sc;
 };
 
 // Entry tiles: keys [key0, key_end) all below n_c.
-template <int KD, int NV, int HG, bool FP8>
-__device__ __forceinline__ void entry_load(const AttnArgs& a, const void* cbase, const float* sbase, int key0,
+template <int KD, int NV, int HG, int KV>
+__device__ __forceinline__ void entry_load(const AttnArgs& a, const void* cbase, const void* sbase, int key0,
                                            int key_end, int key_begin, const AttnSmem<KD, NV, HG>& sm,
-                                           TileRegs<KD, HG, FP8>& R) {
-  using TR = TileRegs<KD, HG, FP8>;
+                                           TileRegs<KD, HG, KV>& R) {
+  using TR = TileRegs<KD, HG, KV>;
   constexpr int D = KD * 32;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
@@ -166,35 +172,58 @@ __device__ __forceinline__ void entry_load(const AttnArgs& a, const void* cbase,
     const int r = c / TR::CPR, ch = c - r * TR::CPR;
     const int key = key0 + r;
     const int idx = (c < kTK * TR::CPR && key < key_end) ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
-    if constexpr (FP8) {
+    if constexpr (KV == kKvFp8) {
       R.v[j] = make_uint2(0, 0);
       if (idx >= 0)
         R.v[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(cbase) + (int64_t)idx * D + ch * 8);
-    } else {
+    } else if constexpr (KV == kKvBf16) {
       R.v[j] = make_uint4(0, 0, 0, 0);
       if (idx >= 0)
         R.v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cbase) + (int64_t)idx * D + ch * 8);
+    } else {
+      R.v[j] = make_uint4(0, 0, 0, 0);
+      R.bs[j] = 0;
+      if (idx >= 0) {
+        const int64_t blk = (int64_t)idx * KD + ch;  // MX block: 16 code bytes, 1 exponent byte
+        R.v[j] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(cbase) + blk * 16);
+        R.bs[j] = reinterpret_cast<const uint8_t*>(sbase)[blk];
+      }
     }
   }
   R.sc = -1.f;  // masked
   if (threadIdx.x < kTK) {
     const int key = key0 + threadIdx.x;
     const int idx = key < key_end ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
-    if (idx >= 0) R.sc = FP8 ? sbase[idx] : 1.f;
+    if (idx >= 0) R.sc = KV == kKvFp8 ? reinterpret_cast<const float*>(sbase)[idx] : 1.f;
   }
 }
 
-template <int KD, int NV, int HG, bool FP8>
+template <int KD, int NV, int HG, int KV>
 __device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD, NV, HG>& sm,
-                                            const TileRegs<KD, HG, FP8>& R) {
-  using TR = TileRegs<KD, HG, FP8>;
+                                            const TileRegs<KD, HG, KV>& R) {
+  using TR = TileRegs<KD, HG, KV>;
 #pragma unroll
   for (int j = 0; j < TR::ITERS; ++j) {
     const int c = threadIdx.x + j * TR::NT;
     const int r = c / TR::CPR, ch = c - r * TR::CPR;
     if (c >= kTK * TR::CPR) continue;
+    if constexpr (KV == kKvMxfp4) {
+      // exact e2m1 * 2^E -> bf16, two values (one code byte, low nibble first) per instruction
+      const float s = __builtin_amdgcn_ldexpf(1.0f, (int)R.bs[j] - 127);
+      const uint32_t w[4] = {R.v[j].x, R.v[j].y, R.v[j].z, R.v[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], s, 0));
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], s, 1));
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], s, 2));
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], s, 3));
+        *reinterpret_cast<uint4*>(&sm.kt[r][32 * ch + 8 * q]) = o;
+      }
+      continue;
+    }
     uint4 v;
-    if constexpr (FP8) {
+    if constexpr (KV == kKvFp8) {
       // exact e4m3 -> bf16 widening, two values per instruction
       const uint32_t w0 = R.v[j].x, w1 = R.v[j].y;
       v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
@@ -383,7 +412,7 @@ __device__ __forceinline__ void tile_compute(AttnSmem<KD, NV, HG>& sm, WaveState
   }
 }
 
-template <int KD, int NV, int HG, bool FP8>
+template <int KD, int NV, int HG, int KV>
 __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
   constexpr int D = KD * 32;
   constexpr int NT = 2 * HG * kWave;
@@ -486,17 +515,19 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
   // phase 1: compressed entries
   if (key_begin < e_end) {
     const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
-    const void* cbase = FP8 ? (const void*)(reinterpret_cast<const uint8_t*>(a.ckv) + seq * D)
-                            : (const void*)(reinterpret_cast<const uint16_t*>(a.ckv) + seq * D);
-    const float* sbase = a.ckv_scale ? a.ckv_scale + seq : nullptr;
-    TileRegs<KD, HG, FP8> R;
-    entry_load<KD, NV, HG, FP8>(a, cbase, sbase, key_begin, e_end, key_begin, sm, R);
+    // bytes per row: codes and scales
+    constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);
+    constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);
+    const void* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
+    const void* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
+    TileRegs<KD, HG, KV> R;
+    entry_load<KD, NV, HG, KV>(a, cbase, sbase, key_begin, e_end, key_begin, sm, R);
     write_qscale();
     for (int key0 = key_begin; key0 < e_end; key0 += kTK) {
       __syncthreads();
-      entry_store<KD, NV, HG, FP8>(a, sm, R);
+      entry_store<KD, NV, HG, KV>(a, sm, R);
       __syncthreads();
-      if (key0 + kTK < e_end) entry_load<KD, NV, HG, FP8>(a, cbase, sbase, key0 + kTK, e_end, key_begin, sm, R);
+      if (key0 + kTK < e_end) entry_load<KD, NV, HG, KV>(a, cbase, sbase, key0 + kTK, e_end, key_begin, sm, R);
       tile_compute<KD, NV, HG>(sm, st, hgw, hf);
     }
   }
@@ -652,28 +683,29 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
 
 typedef void (*AttnKernel)(AttnArgs);
 
-template <int KD, int NV, bool FP8>
+template <int KD, int NV, int KV>
 static AttnKernel pick_nw(int hg) {
   switch (hg) {
-    case 1: return attn_kernel<KD, NV, 1, FP8>;
-    case 2: return attn_kernel<KD, NV, 2, FP8>;
-    case 3: return attn_kernel<KD, NV, 3, FP8>;
-    default: return attn_kernel<KD, NV, 4, FP8>;
+    case 1: return attn_kernel<KD, NV, 1, KV>;
+    case 2: return attn_kernel<KD, NV, 2, KV>;
+    case 3: return attn_kernel<KD, NV, 3, KV>;
+    default: return attn_kernel<KD, NV, 4, KV>;
   }
 }
 
-template <bool FP8>
+template <int KV>
 static AttnKernel pick_dims(int D, int d_v, int nw) {
-  if (D == 576 && d_v == 512) return pick_nw<18, 32, FP8>(nw);
-  if (D == 128 && d_v == 128) return pick_nw<4, 8, FP8>(nw);
-  if (D == 64 && d_v == 32) return pick_nw<2, 2, FP8>(nw);
-  if (D == 256 && d_v == 128) return pick_nw<8, 8, FP8>(nw);
+  if (D == 576 && d_v == 512) return pick_nw<18, 32, KV>(nw);
+  if (D == 128 && d_v == 128) return pick_nw<4, 8, KV>(nw);
+  if (D == 64 && d_v == 32) return pick_nw<2, 2, KV>(nw);
+  if (D == 256 && d_v == 128) return pick_nw<8, 8, KV>(nw);
   return nullptr;
 }
 
 // Compiled (D, d_v) pairs.
-static AttnKernel pick_kernel(int D, int d_v, int nw, bool fp8) {
-  return fp8 ? pick_dims<true>(D, d_v, nw) : pick_dims<false>(D, d_v, nw);
+static AttnKernel pick_kernel(int D, int d_v, int nw, int kv) {
+  return kv == kKvFp8 ? pick_dims<kKvFp8>(D, d_v, nw)
+                      : (kv == kKvMxfp4 ? pick_dims<kKvMxfp4>(D, d_v, nw) : pick_dims<kKvBf16>(D, d_v, nw));
 }
 
 static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype, float q_rms_eps) {
@@ -684,9 +716,10 @@ static int check_common(const char* name, int H, int D, int d_rope, int d_v, int
   CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
   CSKV_REQUIRE(q_rms_eps >= 0.f && q_rms_eps < INFINITY, CSKV_EINVAL, "%s: q_rms_eps=%g", name, (double)q_rms_eps);
   CSKV_REQUIRE(d_rope <= 2 * kMaxRopePairs, CSKV_ENOTSUP, "%s: d_rope=%d > %d", name, d_rope, 2 * kMaxRopePairs);
-  CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3, CSKV_EINVAL, "%s: ckv_dtype=%d", name, ckv_dtype);
+  CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3 || ckv_dtype == CSKV_MXFP4, CSKV_EINVAL,
+               "%s: ckv_dtype=%d", name, ckv_dtype);
   CSKV_REQUIRE(d_v % 32 == 0, CSKV_ENOTSUP, "%s: d_v=%d must be a multiple of 32", name, d_v);
-  CSKV_REQUIRE(pick_kernel(D, d_v, 1, false) != nullptr, CSKV_ENOTSUP,
+  CSKV_REQUIRE(pick_kernel(D, d_v, 1, kKvBf16) != nullptr, CSKV_ENOTSUP,
                "%s: (D, d_v) = (%d, %d) not compiled (576/512, 128/128, 256/128, 64/32)", name, D, d_v);
   return CSKV_OK;
 }
@@ -702,7 +735,7 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
     a.part_ml = a.part_o + (size_t)a.nq * p.n_splits * a.H * a.d_v;
   }
   const int head_groups = (a.H + 16 * p.nw - 1) / (16 * p.nw);
-  AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw, a.fp8 != 0);
+  AttnKernel kern = pick_kernel(a.D, a.d_v, p.nw, a.kv);
   hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(2 * p.nw * kWave), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {
@@ -723,7 +756,7 @@ extern "C" CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d
 }
 
 extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
-                                           const float* ckv_scale, int ckv_dtype, int N_cap,
+                                           const void* ckv_scale, int ckv_dtype, int N_cap,
                                            const int32_t* n_entries, const int32_t* topk_idx, int k,
                                            const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
                                            float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
@@ -750,7 +783,7 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   a.pos0 = 0;
   a.ckv = ckv;
   a.ckv_scale = ckv_scale;
-  a.fp8 = ckv_dtype == CSKV_FP8_E4M3;
+  a.kv = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
   a.N_cap = N_cap;
   a.ckv_seq = N_cap;
   a.n_entries = n_entries;
@@ -780,7 +813,7 @@ extern "C" CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int 
 }
 
 extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,
-                                            const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
+                                            const void* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
                                             int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v,
                                             int m, float rope_base, float softmax_scale, uint16_t* out,
                                             float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps,
@@ -804,7 +837,7 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   a.pos0 = pos0;
   a.ckv = ckv;
   a.ckv_scale = ckv_scale;
-  a.fp8 = ckv_dtype == CSKV_FP8_E4M3;
+  a.kv = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
   a.N_cap = N;
   a.ckv_seq = 0;
   a.n_entries = nullptr;

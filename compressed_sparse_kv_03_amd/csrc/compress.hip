@@ -42,12 +42,31 @@ __device__ __forceinline__ void rope_cs_fast(double inv_freq, int64_t pos, float
   *c = fmaf(-dl, sf, cf);
 }
 
-template <bool FP8>
+// Nearest e2m1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even code,
+// saturating at 6), sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float mag = fabsf(v);
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) c += mag > mids[i];
+  bool tie = false;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) tie = tie || (c == i && mag == mids[i]);
+  if (tie && (c & 1)) ++c;  // a midpoint goes to the even code
+  return (uint32_t)c | (v < 0.f ? 8u : 0u);
+}
+
+// Storage of a compressed entry: bf16, e4m3fn with one fp32 scale per entry, or OCP MXFP4
+// (e2m1 codes, one E8M0 exponent per 32 dims).
+enum { kOutBf16 = 0, kOutFp8 = 1, kOutMxfp4 = 2 };
+
+template <int OUT>
 __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t x_seq_stride, const float* __restrict__ z,
     int64_t z_seq_stride, const int64_t* __restrict__ pos0, int B, int n_ent, int D, int d_rope,
     int m, int entry_pos_offset, float rope_base, void* __restrict__ out,
-    float* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, float rms_eps,
+    void* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, float rms_eps,
     RopeTable rt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
@@ -143,11 +162,11 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
   }
 
   const int64_t slot = (int64_t)b * out_seq_stride + (out_entry0 ? out_entry0[b] : 0) + j;
-  if (!FP8) {
+  if constexpr (OUT == kOutBf16) {
     uint16_t* o = reinterpret_cast<uint16_t*>(out) + slot * D;
     if (has0) *reinterpret_cast<uint4*>(o + 8 * lane) = pack8(acc0);
     if (has1) *reinterpret_cast<uint4*>(o + 8 * (lane + kWave)) = pack8(acc1);
-  } else {
+  } else if constexpr (OUT == kOutFp8) {
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(acc0[e]), fabsf(acc1[e])));
@@ -167,7 +186,32 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
       wv.y = f32x4_to_fp8(acc1[4] / s, acc1[5] / s, acc1[6] / s, acc1[7] / s);
       *reinterpret_cast<uint2*>(o + 8 * (lane + kWave)) = wv;
     }
-    if (lane == 0) out_scale[slot] = s;
+    if (lane == 0) reinterpret_cast<float*>(out_scale)[slot] = s;
+  } else {
+    // MXFP4: an MX block of 32 dims is 4 adjacent lanes' 8-dim chunks; E = floor(log2 amax) - 2
+    // limited to the E8M0 range [-127, 127] (an all-zero block takes -127)
+    uint8_t* o = reinterpret_cast<uint8_t*>(out) + slot * (D / 2);
+    uint8_t* os = reinterpret_cast<uint8_t*>(out_scale) + slot * (D / 32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + h * kWave;
+      const float* acc = h ? acc1 : acc0;
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(acc[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+      int E = -127;
+      if (amax > 0.f) E = min(127, max(-127, (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 2));
+      const float inv_s = __builtin_amdgcn_ldexpf(1.0f, -E);
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= e2m1_code(acc[e] * inv_s) << (4 * e);
+      if (c < cpr) {
+        *reinterpret_cast<uint32_t*>(o + 4 * c) = w;
+        if ((c & 3) == 0) os[c >> 2] = (uint8_t)(E + 127);
+      }
+    }
   }
 }
 
@@ -193,18 +237,6 @@ __global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __rest
 // entry; lane l holds key dims [V l, V l + V), so one MX block is 32 / V adjacent lanes.
 constexpr int kMxEMin = -3, kMxEMax = 0;
 
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float mag = fabsf(v);
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < 7; ++i) c += mag > mids[i];
-  bool tie = false;
-#pragma unroll
-  for (int i = 0; i < 7; ++i) tie = tie || (c == i && mag == mids[i]);
-  if (tie && (c & 1)) ++c;  // a midpoint goes to the even code
-  return (uint32_t)c | (v < 0.f ? 8u : 0u);
-}
 
 template <int V>
 __global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
@@ -273,7 +305,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
 static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stride, const float* z,
                          int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                          int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
-                         void* out, float* out_scale, int64_t out_seq_stride,
+                         void* out, void* out_scale, int64_t out_seq_stride,
                          const int32_t* out_entry0, float rms_eps, void* stream) {
   CSKV_REQUIRE(B >= 1 && n_tok >= 0, CSKV_EINVAL, "%s: B=%d n_tok=%d", name, B, n_tok);
   CSKV_REQUIRE(m >= 1 && m <= 1024, CSKV_EINVAL, "%s: m=%d outside [1, 1024]", name, m);
@@ -282,12 +314,13 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
   CSKV_REQUIRE(D <= 1024, CSKV_ENOTSUP, "%s: D=%d > 1024", name, D);
   CSKV_REQUIRE(d_rope >= 0 && d_rope % 8 == 0 && d_rope <= D, CSKV_EINVAL,
                "%s: d_rope=%d must be a multiple of 8 in [0, D]", name, d_rope);
-  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_dtype == CSKV_FP8_E4M3, CSKV_EINVAL,
+  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_dtype == CSKV_FP8_E4M3 || out_dtype == CSKV_MXFP4, CSKV_EINVAL,
                "%s: unknown out_dtype %d", name, out_dtype);
+  CSKV_REQUIRE(out_dtype != CSKV_MXFP4 || D % 32 == 0, CSKV_EINVAL, "%s: MXFP4 needs D %% 32 == 0 (D=%d)", name, D);
   CSKV_REQUIRE(rms_eps >= 0.f && rms_eps < INFINITY, CSKV_EINVAL, "%s: rms_eps=%g", name, (double)rms_eps);
   if (n_tok == 0) return CSKV_OK;
   CSKV_REQUIRE(x && z && pos0 && out, CSKV_EINVAL, "%s: null pointer", name);
-  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_scale, CSKV_EINVAL, "%s: fp8 output needs out_scale", name);
+  CSKV_REQUIRE(out_dtype == CSKV_BF16 || out_scale, CSKV_EINVAL, "%s: fp8/MXFP4 output needs out_scale", name);
   CSKV_REQUIRE(aligned16(x) && aligned16(out), CSKV_EINVAL, "%s: x/out must be 16-byte aligned", name);
   CSKV_REQUIRE(x_seq_stride % 8 == 0 && x_seq_stride >= (int64_t)n_tok * D, CSKV_EINVAL,
                "%s: x_seq_stride=%lld", name, (long long)x_seq_stride);
@@ -300,14 +333,16 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   RopeTable rt{};
   for (int i = 0; i < kRopeTab && i < d_rope / 2; ++i) rt.inv_freq[i] = pow((double)rope_base, -2.0 * i / d_rope);
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D, d_rope, m, entry_pos_offset,
+                                rope_base, out, out_scale, out_seq_stride, out_entry0, rms_eps, rt);
+  };
   if (out_dtype == CSKV_BF16)
-    compress_kernel<false><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
-                                                  d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                  out_seq_stride, out_entry0, rms_eps, rt);
+    launch(compress_kernel<kOutBf16>);
+  else if (out_dtype == CSKV_FP8_E4M3)
+    launch(compress_kernel<kOutFp8>);
   else
-    compress_kernel<true><<<grid, block, 0, s>>>(x, x_seq_stride, z, z_seq_stride, pos0, B, n_ent, D,
-                                                 d_rope, m, entry_pos_offset, rope_base, out, out_scale,
-                                                 out_seq_stride, out_entry0, rms_eps, rt);
+    launch(compress_kernel<kOutMxfp4>);
   CSKV_LAUNCH_CHECK(name);
   return CSKV_OK;
 }
@@ -317,7 +352,7 @@ static int compress_impl(const char* name, const uint16_t* x, int64_t x_seq_stri
 extern "C" CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, const float* z,
                             int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                             int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
-                            void* out, float* out_scale, int64_t out_seq_stride,
+                            void* out, void* out_scale, int64_t out_seq_stride,
                             const int32_t* out_entry0, float rms_eps, void* stream) {
   return cskv::compress_impl("csa_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
                              d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,
@@ -327,7 +362,7 @@ extern "C" CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, co
 extern "C" CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z,
                             int64_t z_seq_stride, const int64_t* pos0, int B, int n_tok, int D,
                             int d_rope, int m, int entry_pos_offset, float rope_base, int out_dtype,
-                            void* out, float* out_scale, int64_t out_seq_stride,
+                            void* out, void* out_scale, int64_t out_seq_stride,
                             const int32_t* out_entry0, float rms_eps, void* stream) {
   return cskv::compress_impl("hca_compress", x, x_seq_stride, z, z_seq_stride, pos0, B, n_tok, D,
                              d_rope, m, entry_pos_offset, rope_base, out_dtype, out, out_scale,

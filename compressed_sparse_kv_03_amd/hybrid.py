@@ -65,6 +65,8 @@ class LayerPairSpec:
     # draft token accepted; else the seed of the accepted counts, uniform in 1..draft)
     draft: int = 1
     accept_seed: int = -1
+    # storage of the compressed entries: "fp8" (e4m3fn + fp32 scale per entry) or "mxfp4"
+    kv_dtype: str = "fp8"
 
     @property
     def sigma(self):
@@ -83,7 +85,8 @@ class LayerPair:
         self.s = s
         self.dev = device
         assert s.W % s.m_csa == 0 and s.W % s.m_hca == 0 and s.L % s.m_hca == 0 and s.L % s.m_csa == 0
-        assert s.L >= s.W and s.draft >= 1
+        assert s.L >= s.W and s.draft >= 1 and s.kv_dtype in ("fp8", "mxfp4")
+        self.kv_code = native.CSKV_MXFP4 if s.kv_dtype == "mxfp4" else native.CSKV_FP8_E4M3
         sd = lambda t: synth.seed_of(s.seed, s.wid, t)  # noqa: E731
         B, D, T, Td = s.B, s.D, s.steps, s.draft
         self.m = {"csa": s.m_csa, "hca": s.m_hca}
@@ -103,7 +106,8 @@ class LayerPair:
         for li, name in enumerate(("csa", "hca")):
             base = 100 * li
             R = self.R[name]
-            c, sc = synth.fp8_rows_normal((B, self.cap[name], D), s.sigma, sd(base + 0), device)
+            gen = synth.mxfp4_rows_normal if s.kv_dtype == "mxfp4" else synth.fp8_rows_normal
+            c, sc = gen((B, self.cap[name], D), s.sigma, sd(base + 0), device)
             self.ckv[name], self.scl[name] = c, sc
             # window tokens at positions L-W .. L-1, in ring slots (position mod R)
             self.ring[name] = self._to_ring(synth.normal_bf16_bits((B, s.W, D), s.sigma, sd(base + 1), device), R)
@@ -233,7 +237,7 @@ class LayerPair:
             fn = native.csa_compress if name == "csa" else native.hca_compress
             for slot0, p0, e0 in self.blocks[name][i]:
                 fn(self.ring[name][:, slot0:], R * D, self.ringz[name][:, slot0:], R, p0, B, m, D,
-                   s.d_rope, m, 0, s.rope_base, native.CSKV_FP8_E4M3, self.ckv[name], self.scl[name],
+                   s.d_rope, m, 0, s.rope_base, self.kv_code, self.ckv[name], self.scl[name],
                    self.cap[name], e0, stream, rms_eps=s.rms_eps)
                 if keys:
                     native.csa_index_key_pool(self.ring_xk[:, slot0:], R * s.D_I, self.ringz[name][:, slot0:], R, B, m,
@@ -248,7 +252,7 @@ class LayerPair:
         for name in ("csa", "hca"):
             c = kv[name]
             native.hybrid_attn_decode(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
-                                      native.CSKV_FP8_E4M3, self.cap[name], self.nent[name][i],
+                                      self.kv_code, self.cap[name], self.nent[name][i],
                                       topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
                                       self.ws_att[name], None, stream, q_rms_eps=s.rms_eps, T=Td, R=c.R[name])
@@ -265,7 +269,7 @@ class LayerPair:
         n_c = self.n0["csa"]
         n_h = self.n0["hca"]
         Td = s.draft
-        e = s.D + 4                          # fp8 entry + fp32 scale
+        e = s.D // 2 + s.D // 32 if s.kv_dtype == "mxfp4" else s.D + 4   # stored entry bytes
         xi = s.D_I // 2 + s.D_I // 32        # MXFP4 key
         q = s.B * Td * s.H * s.D * 2
         o = s.B * Td * s.H * s.d_v * 2

@@ -14,6 +14,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcskv.so
 
 CSKV_BF16 = 0
 CSKV_FP8_E4M3 = 1
+CSKV_MXFP4 = 2
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 

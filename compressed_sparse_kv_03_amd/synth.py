@@ -64,14 +64,15 @@ def fp8_rows(x):
     return codes, s.to(torch.float32)
 
 
-def mxfp4(x):
-    """x [..., D] fp32 (D % 32 == 0) -> (packed uint8 [..., D/2], scale E8M0 uint8 [..., D/32])."""
+def mxfp4(x, e_min=MX_EXP_MIN, e_max=MX_EXP_MAX):
+    """x [..., D] fp32 (D % 32 == 0) -> (packed uint8 [..., D/2], scale E8M0 uint8 [..., D/32]);
+    block exponents limited to [e_min, e_max] (indexer vectors: [-3, 0])."""
     D = x.shape[-1]
     assert D % 32 == 0
     xb = x.reshape(*x.shape[:-1], D // 32, 32)
     amax = xb.abs().amax(dim=-1, keepdim=True)
     e = torch.floor(torch.log2(torch.clamp(amax, min=2.0 ** -30))) - 2
-    e = torch.clamp(e, MX_EXP_MIN, MX_EXP_MAX)
+    e = torch.clamp(e, e_min, e_max)
     mag = (xb.abs() / torch.exp2(e)).reshape(*x.shape[:-1], D)
     mids = torch.tensor(_E2M1_MIDS, device=x.device, dtype=torch.float32)
     lower = torch.bucketize(mag, mids, right=False)                   # ties -> lower code
@@ -94,6 +95,21 @@ def mxfp4_normal(shape, seed, device, chunk_rows=1 << 20):
         e = min(rows, s + chunk_rows)
         x = torch.randn(e - s, D, generator=g, device=device, dtype=torch.float32)
         packed[s:e], scale[s:e] = mxfp4(x)
+    return packed.view(*lead, D // 2), scale.view(*lead, D // 32)
+
+
+def mxfp4_rows_normal(shape, std, seed, device, chunk_rows=1 << 18):
+    """N(0, std^2) rows -> MXFP4 KV entries (codes [..., D/2], E8M0 [..., D/32], exponents over the
+    whole E8M0 range), in chunks of rows."""
+    *lead, D = shape
+    rows = math.prod(lead)
+    packed = torch.empty(rows, D // 2, dtype=torch.uint8, device=device)
+    scale = torch.empty(rows, D // 32, dtype=torch.uint8, device=device)
+    g = generator(seed, device)
+    for s in range(0, rows, chunk_rows):
+        e = min(rows, s + chunk_rows)
+        x = torch.randn(e - s, D, generator=g, device=device, dtype=torch.float32) * std
+        packed[s:e], scale[s:e] = mxfp4(x, -127, 127)
     return packed.view(*lead, D // 2), scale.view(*lead, D // 32)
 
 

@@ -55,6 +55,7 @@ extern "C" {
 /* Storage dtypes of compressed entries. */
 #define CSKV_BF16 0
 #define CSKV_FP8_E4M3 1
+#define CSKV_MXFP4 2   /* OCP MXFP4: e2m1 codes [.., D/2] (element 2i in the low nibble) + E8M0 [.., D/32] */
 
 CSKV_API int cskv_abi_version(void);
 CSKV_API const char* cskv_strerror(int code);
@@ -78,26 +79,34 @@ CSKV_API const char* cskv_last_error(void);
  *   out[b, out_entry0[b] + j, :] = bf16_rne(e)                       (CSKV_BF16)
  *     or  s = max|e| / 448 (1 if e == 0); codes = e4m3_rne_sat(e / s),
  *         out_scale[b, out_entry0[b] + j] = s                        (CSKV_FP8_E4M3)
+ *     or  per 32 dims E = floor(log2 max|e_blk|) - 2 in [-127, 127] (-127 if all zero),
+ *         codes = nearest e2m1 of e_blk / 2^E (ties to the even code, saturating at 6),
+ *         out_scale = E + 127 as one byte per block                  (CSKV_MXFP4; OCP MX v1.0.
+ *         The blog post on DeepSeek V4.1 Flash, jjy0501.blogspot.com, paragraph on the
+ *         global attention state under "SWA Bounded Replay": the main KV cache is kept in
+ *         HBM at FP4 precision.)
  *
  * x        [B, x_seq_stride] bf16; row r of sequence b at x + b*x_seq_stride + r*D
  *          (a ring slice works: rows are contiguous within a sequence)
  * z        [B, z_seq_stride] fp32 pooling logits, z + b*z_seq_stride + r
  * pos0     [B] int64, position of row 0 of each sequence
- * out      bf16 [B, out_seq_stride, D] or fp8 codes [B, out_seq_stride, D]
- * out_scale fp32 [B, out_seq_stride] (fp8 only; ignored for bf16)
+ * out      bf16 [B, out_seq_stride, D], fp8 codes [B, out_seq_stride, D] or MXFP4 codes
+ *          [B, out_seq_stride, D/2]
+ * out_scale fp32 [B, out_seq_stride] (fp8), uint8 E8M0 [B, out_seq_stride, D/32] (MXFP4);
+ *          ignored for bf16
  * out_entry0 [B] int32 first entry slot written per sequence, or NULL (= 0)
  * Requirements: B >= 1, n_tok >= 0 and n_tok % m == 0, 1 <= m <= 1024,
- * D % 8 == 0 and 8 <= D <= 1024, d_rope % 8 == 0 and d_rope <= D,
+ * D % 8 == 0 (MXFP4: D % 32 == 0) and 8 <= D <= 1024, d_rope % 8 == 0 and d_rope <= D,
  * x_seq_stride % 8 == 0, rms_eps finite and >= 0. hca_compress is the same
  * operation (named for its use with m = 128).
  */
 CSKV_API int csa_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
                  const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
-                 int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
+                 int entry_pos_offset, float rope_base, int out_dtype, void* out, void* out_scale,
                  int64_t out_seq_stride, const int32_t* out_entry0, float rms_eps, void* stream);
 CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* z, int64_t z_seq_stride,
                  const int64_t* pos0, int B, int n_tok, int D, int d_rope, int m,
-                 int entry_pos_offset, float rope_base, int out_dtype, void* out, float* out_scale,
+                 int entry_pos_offset, float rope_base, int out_dtype, void* out, void* out_scale,
                  int64_t out_seq_stride, const int32_t* out_entry0, float rms_eps, void* stream);
 
 /*
@@ -179,8 +188,9 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  *   g_h = 1 / sqrt(mean_d(q[r, h, d]^2) + q_rms_eps) if q_rms_eps > 0 (unit-gain
  *   RMSNorm of the query head, the pages' "query normalisation"), else 1
  *   out[r, h, :] = bf16_rne(sum softmax(logit) * key[:d_v]); out_lse[r, h] = ln(sum exp(logit))
- * Entries are stored rotated: bf16 [B, N_cap, D], or fp8 codes [B, N_cap, D]
- * with fp32 scales ckv_scale [B, N_cap] (value = code * scale).
+ * Entries are stored rotated: bf16 [B, N_cap, D], fp8 codes [B, N_cap, D] with fp32
+ * scales ckv_scale [B, N_cap] (value = code * scale), or MXFP4 codes [B, N_cap, D/2]
+ * with E8M0 bytes ckv_scale [B, N_cap, D/32] (value = e2m1(code) * 2^(byte - 127)).
  *
  * q [B*T, H, D] bf16 (unrotated); q_pos [B*T] int64; n_entries [B*T] int32 <= N_cap
  * (causal inside a draft: each query its own count); topk_idx [B*T, k] int32 (each -1
@@ -193,7 +203,7 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * W + k or W + N_cap fits int32, q_rms_eps finite and >= 0.
  */
 CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
-                       const float* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
+                       const void* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
                        const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H,
                        int D, int d_rope, int d_v, float rope_base, float softmax_scale,
                        uint16_t* out, float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps,
@@ -213,7 +223,7 @@ CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_c
  * Requirements as in decode, plus m >= 1.
  */
 CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,
-                        const float* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
+                        const void* ckv_scale, int ckv_dtype, int N, const int32_t* topk_idx,
                         int k, const uint16_t* x, int W, int H, int D, int d_rope, int d_v, int m,
                         float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
                         void* ws, size_t ws_bytes, float q_rms_eps, void* stream);

@@ -25,9 +25,12 @@ from . import formats, rope
 
 
 def decode_entries(ckv, ckv_scale, dtype):
-    """Stored entries -> fp64 vectors. bf16 bits, or e4m3 codes times per-entry fp32 scale."""
+    """Stored entries -> fp64 vectors. bf16 bits, e4m3 codes times per-entry fp32 scale, or
+    MXFP4 codes with per-32 E8M0 scales."""
     if dtype == "bf16":
         return formats.bf16_to_f64(ckv)
+    if dtype == "mxfp4":
+        return formats.mxfp4_to_f64(ckv, ckv_scale)
     assert dtype == "fp8"
     return formats.e4m3_to_f64(ckv) * np.asarray(ckv_scale, dtype=np.float64)[..., None]
 
@@ -51,7 +54,7 @@ class Entries:
 
     def __init__(self, ckv, ckv_scale, dtype):
         self.ckv, self.scale, self.dtype = ckv, ckv_scale, dtype
-        self.D = ckv.shape[-1]
+        self.D = ckv.shape[-1] * (2 if dtype == "mxfp4" else 1)
 
     def rows(self, sel):
         sel = np.asarray(sel, dtype=np.int64)

@@ -13,7 +13,9 @@ Readings taken where the pages are silent:
   * the pooled vector is rotated (partial RoPE) AFTER pooling, at position
     p_j = pos0 + j*m + entry_pos_offset (offset 0: the block's first token);
   * storage: bf16 by RNE, or e4m3fn with one fp32 scale per entry,
-    s = max|e|/448 (s = 1 when the entry is all zero), code = RNE_sat(e/s);
+    s = max|e|/448 (s = 1 when the entry is all zero), code = RNE_sat(e/s), or
+    OCP MXFP4 (next-row N4; [P4]: the main KV cache kept at FP4 precision) with
+    the block exponent over the whole E8M0 range [-127, 127];
   * optional KV normalisation ([P5] section "두 가지 압축 전략: CSA 및 HCA": both
     branches normalise queries and KV): when rms_eps > 0 the pooled entry is
     divided by sqrt(mean(e^2) + rms_eps) (RMSNorm with unit gain) before the
@@ -48,7 +50,8 @@ def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=
 
     x_bits [n_tok, D] bf16 bits; z [n_tok] fp32; pos0 = position of x[0].
     Returns (exact fp64 rotated entries [n, D], stored, scale) where stored is
-    bf16 bits [n, D] (scale None) or e4m3 codes [n, D] with fp32 scales [n].
+    bf16 bits [n, D] (scale None), e4m3 codes [n, D] with fp32 scales [n], or MXFP4
+    codes [n, D/2] with E8M0 scales [n, D/32].
     """
     x = formats.bf16_to_f64(x_bits)
     zz = np.asarray(z, dtype=np.float64)
@@ -60,6 +63,9 @@ def compress(x_bits, z, pos0, m, d_rope, rope_base, out_dtype, entry_pos_offset=
     e = rope.apply(e, p, d_rope, rope_base)
     if out_dtype == "bf16":
         return e, formats.f64_to_bf16(e), None
+    if out_dtype == "mxfp4":
+        codes, scales = formats.f64_to_mxfp4(e, formats.MX_KV_E_MIN, formats.MX_KV_E_MAX)
+        return e, codes, scales
     assert out_dtype == "fp8"
     amax = np.abs(e).max(axis=1)
     s = np.where(amax == 0, 1.0, amax / formats.E4M3_MAX).astype(np.float32)

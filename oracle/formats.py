@@ -118,6 +118,8 @@ def mxfp4_to_f64(packed, scales):
 # score exact in fp32 for unit-scale inputs (the span bound of the indexer's exactness argument),
 # and it is the range the configurations' index keys use.
 MX_E_MIN, MX_E_MAX = -3, 0
+# the full E8M0 range, for stored KV entries (no exactness constraint there)
+MX_KV_E_MIN, MX_KV_E_MAX = -127, 127
 E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])  # midpoints between magnitudes
 
 

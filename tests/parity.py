@@ -167,7 +167,8 @@ def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8
         raise ParityError(f"{what}: {frac:.2e} of codes differ from the oracle's (> {max_frac})")
 
 
-def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_frac=1e-2):
+def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_frac=1e-2,
+                e_range=(formats.MX_E_MIN, formats.MX_E_MAX), d=None):
     """MXFP4 keys from an fp32 pooling vs the exact fp64 pooled keys k_exact [..., D].
 
     With d = pool_error_bound(mag, m) the bound on |fp32 pooled - exact|: each block exponent is
@@ -176,15 +177,15 @@ def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_f
     oracle's own encoding (differences only where v is within d of a rounding midpoint).
     """
     k = np.asarray(k_exact, dtype=np.float64)
-    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m) if d is None else np.asarray(d, np.float64)
     D = k.shape[-1]
     gs = np.asarray(got_scale).astype(np.int64)
     kb = k.reshape(k.shape[:-1] + (D // 32, 32))
     db = d.reshape(kb.shape)
     amax_lo = np.maximum(np.abs(kb) - db, 0.0).max(axis=-1)   # the fp32 block maximum lies in [lo, hi]
     amax_hi = (np.abs(kb) + db).max(axis=-1)
-    _, s_lo = formats.f64_to_mxfp4(np.repeat(amax_lo, 32, axis=-1).reshape(k.shape))
-    _, s_hi = formats.f64_to_mxfp4(np.repeat(amax_hi, 32, axis=-1).reshape(k.shape))
+    _, s_lo = formats.f64_to_mxfp4(np.repeat(amax_lo, 32, axis=-1).reshape(k.shape), *e_range)
+    _, s_hi = formats.f64_to_mxfp4(np.repeat(amax_hi, 32, axis=-1).reshape(k.shape), *e_range)
     ok_s = (gs >= s_lo.astype(np.int64)) & (gs <= s_hi.astype(np.int64))
     if not np.all(ok_s):
         i = np.argwhere(~ok_s)[0]
@@ -199,7 +200,7 @@ def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_f
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
         raise ParityError(f"{what}: element {i} code {got[i]} value {k[i]!r} (E={E[i]}, bound {d[i]:.2e})")
-    want, _ = formats.f64_to_mxfp4(k)
+    want, _ = formats.f64_to_mxfp4(k, *e_range)
     frac = np.count_nonzero(got != formats.unpack_fp4(want)) / max(got.size, 1)
     if frac > max_frac:
         raise ParityError(f"{what}: {frac:.2e} of codes differ from the oracle's (> {max_frac})")

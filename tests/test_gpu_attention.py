@@ -26,7 +26,7 @@ def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, 
     ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((B, H, d_v), torch.int16)
     lse = poisoned((B, H), torch.float32)
-    dt = native.CSKV_BF16 if dtype == "bf16" else native.CSKV_FP8_E4M3
+    dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
     native.hybrid_attn_decode(q, q_pos, ckv, ckv_scale, dt, N_cap, n_entries, topk, k, ring, W, B, H, D, d_rope,
                               d_v, 10000.0, scale, out, lse, ws, q_rms_eps=q_rms_eps)
     return out, lse
@@ -70,6 +70,9 @@ CASES = [
     (2, 20, 128, 64, 128, 90, 16, 8, "fp8", True, 1.0),            # ragged head group, short window
     (2, 4, 64, 16, 32, 50, 40, 0, "bf16", False, 1.0),             # no window; k > visible entries
     (2, 48, 256, 0, 128, 333, 64, 128, "bf16", True, 0.5),         # no RoPE
+    (3, 64, 576, 64, 512, 700, 128, 128, "mxfp4", False, None),    # MXFP4 entries (gather)
+    (3, 64, 576, 64, 512, 300, 128, 128, "mxfp4", True, None),     # MXFP4 entries (dense)
+    (2, 20, 128, 64, 128, 90, 16, 8, "mxfp4", True, 1.0),
 ]
 
 
@@ -83,6 +86,8 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std):
     if dtype == "bf16":
         ckv = synth.normal_bf16_bits((B, N, D), sig, 2, DEV)
         sc = None
+    elif dtype == "mxfp4":
+        ckv, sc = synth.mxfp4_rows_normal((B, N, D), sig, 2, DEV)
     else:
         ckv, sc = synth.fp8_rows_normal((B, N, D), sig, 2, DEV)
     ring = synth.normal_bf16_bits((B, max(W, 1), D), sig, 3, DEV)
@@ -274,6 +279,7 @@ PREFILL = [
     (260, 37, 4, 64, 576, 64, 512, 16, 16, False, "bf16"),
     (400, 0, 128, 20, 128, 64, 128, 0, 64, True, "fp8"),
     (130, 5, 4, 4, 64, 16, 32, 0, 8, True, "bf16"),
+    (260, 37, 4, 64, 576, 64, 512, 16, 16, False, "mxfp4"),
 ]
 
 
@@ -288,6 +294,8 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype):
     if dtype == "bf16":
         ckv = synth.normal_bf16_bits((N, D), sig, 43, DEV)
         sc = None
+    elif dtype == "mxfp4":
+        ckv, sc = synth.mxfp4_rows_normal((N, D), sig, 43, DEV)
     else:
         ckv, sc = synth.fp8_rows_normal((N, D), sig, 43, DEV)
     topk = None
@@ -303,7 +311,7 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype):
     ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((T, H, d_v), torch.int16)
     lse = poisoned((T, H), torch.float32)
-    dt = native.CSKV_BF16 if dtype == "bf16" else native.CSKV_FP8_E4M3
+    dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
     native.hybrid_attn_prefill(q, pos0, T, ckv, sc, dt, N, topk, max(k, 1), x, W, H, D, d_rope, d_v, m, 10000.0,
                                D ** -0.5, out, lse, ws)
     qh, xh = down(q).view(np.uint16), down(x).view(np.uint16)

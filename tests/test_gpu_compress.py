@@ -18,9 +18,13 @@ def run_compress(x_bits, z, pos0, m, d_rope, dtype, entry_pos_offset=0, entry0=N
     B, n_tok, D = x_bits.shape[0], x_bits.shape[1], x_bits.shape[2]
     n = n_tok // m
     cap = n + cap_extra
-    out_dt = native.CSKV_BF16 if dtype == "bf16" else native.CSKV_FP8_E4M3
-    out = poisoned((B, cap, D), torch.int16 if dtype == "bf16" else torch.uint8)
-    osc = poisoned((B, cap), torch.float32) if dtype == "fp8" else None
+    out_dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
+    if dtype == "mxfp4":
+        out = poisoned((B, cap, D // 2), torch.uint8)
+        osc = poisoned((B, cap, D // 32), torch.uint8)
+    else:
+        out = poisoned((B, cap, D), torch.int16 if dtype == "bf16" else torch.uint8)
+        osc = poisoned((B, cap), torch.float32) if dtype == "fp8" else None
     e0 = None if entry0 is None else up(np.asarray(entry0, np.int32))
     fn(x_bits, x_stride or n_tok * D, z, z.shape[1], up(np.asarray(pos0, np.int64)), B, n_tok, D, d_rope, m,
        entry_pos_offset, 10000.0, out_dt, out, osc, cap, e0, rms_eps=rms_eps)
@@ -73,6 +77,30 @@ def test_compress_rms_norm_matches_oracle(m, D, d_rope, dtype, eps):
             assert np.allclose(ms, np.mean(e * e, axis=1), rtol=1e-2), "mean square of the normalised entries"
         else:
             parity.compress_fp8_close(oh[b], down(osc)[b], e, mag, m, f"rms b={b}", d=d)
+
+
+@pytest.mark.parametrize("m,D,d_rope,eps", [(4, 576, 64, 0.0), (128, 576, 64, 0.0), (13, 64, 16, 0.0),
+                                            (4, 576, 64, 1e-6)])
+def test_compress_mxfp4_matches_oracle(m, D, d_rope, eps):
+    """MXFP4 entries (OCP: per-32 E8M0 exponent over the whole range, nearest e2m1 with ties to
+    even) from the fp32 pooling: exponents and codes within the pooling bound of the exact entry."""
+    say("compress mxfp4", m, D, d_rope, eps)
+    B, nblk = 3, 29
+    n_tok = nblk * m
+    x = synth.normal_bf16_bits((B, n_tok, D), 0.5, 51, DEV)
+    z = synth.normal((B, n_tok), 2.0, 52, DEV)
+    pos0 = [0, 2 ** 20 - 64 * m, 77]
+    out, osc = run_compress(x, z, pos0, m, d_rope, "mxfp4", rms_eps=eps)
+    xh, zh, oh, sh = down(x).view(np.uint16), down(z), down(out), down(osc)
+    for b in range(B):
+        e, _, _ = ocomp.compress(xh[b], zh[b], pos0[b], m, d_rope, 10000.0, "mxfp4", rms_eps=eps)
+        mag = ocomp.magnitude(xh[b], zh[b], m, d_rope)
+        d = None
+        if eps > 0:
+            v = ocomp.pool(formats.bf16_to_f64(xh[b]), zh[b].astype(np.float64), m)
+            d = parity.rms_error_bound(v, mag, e, m, d_rope, eps)
+        parity.mxfp4_close(oh[b], sh[b], e, mag, m, f"mxfp4 entries b={b}",
+                           e_range=(formats.MX_KV_E_MIN, formats.MX_KV_E_MAX), d=d)
 
 
 def test_compress_offsets_entry_slots_and_ring_stride():

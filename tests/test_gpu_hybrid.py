@@ -19,7 +19,7 @@ def oracle_layers(spec, st):
         h = st[name]
         csa = name == "csa"
         layers[name] = ohyb.Layer(name, m, spec.W, spec.d_rope, spec.d_v, spec.rope_base, spec.scale,
-                                  h["ckv"].copy(), h["scl"].copy(), "fp8", np.full(spec.B, spec.L // m),
+                                  h["ckv"].copy(), h["scl"].copy(), spec.kv_dtype, np.full(spec.B, spec.L // m),
                                   h["ring"].copy(), h["ringz"].copy(), k=spec.k,
                                   ik=st["ik"].copy() if csa else None, ik_scale=st["iks"].copy() if csa else None,
                                   ring_xk=st["ring_xk"].copy() if (csa and spec.derive_keys) else None,
@@ -34,12 +34,23 @@ def lse_bounds(spec, lay, t, q, idx):
     for b in range(len(t)):
         tb = int(t[b])
         n = int(lay.n_entries[b])
-        ent = oatt.Entries(lay.ckv[b], lay.ckv_scale[b], "fp8")
+        ent = oatt.Entries(lay.ckv[b], lay.ckv_scale[b], spec.kv_dtype)
         sel = range(n) if idx is None else [j for j in idx[b] if j >= 0]
         wpos = np.arange(max(0, tb - spec.W + 1), tb + 1)
         out.append(logit_bound(q[b], tb, ent, sel, lay.ring_x[b][wpos % spec.W], wpos, spec.d_rope, spec.d_v,
                                spec.scale, spec.rms_eps))
     return np.stack(out)
+
+
+def check_mxfp4_entries(g_codes, g_scales, o_codes, o_scales, what):
+    """MXFP4 entries of the loop against the oracle's: exponents within one (rarely different),
+    codes within one e2m1 step, at most 1% of either different."""
+    from oracle import formats
+    ordered = lambda c: np.where(c & 8, -(c & 7), c & 7).astype(np.int64)  # noqa: E731
+    d = np.abs(ordered(formats.unpack_fp4(g_codes)) - ordered(formats.unpack_fp4(o_codes)))
+    ds = np.abs(g_scales.astype(np.int64) - o_scales.astype(np.int64))
+    assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-2 * max(d.size, 1), f"{what}: mxfp4 codes"
+    assert ds.max(initial=0) <= 1 and np.count_nonzero(ds) <= 1e-2 * max(ds.size, 1), f"{what}: mxfp4 exponents"
 
 
 def check_loop(pair, sample_steps):
@@ -66,10 +77,14 @@ def check_loop(pair, sample_steps):
                 bnd = lse_bounds(spec, lay, t, h["q"][i], idx) if spec.rms_eps > 0 else None
                 parity.lse_close(lse[name][i], l, bnd, f"{name} lse step {i}")
                 checked += 1
-    # the re-compressed entries written by the loop match the oracle's (fp8 codes within one step)
+    # the re-compressed entries written by the loop match the oracle's (codes within one step)
     for name in ("csa", "hca"):
         n_end = (spec.L + spec.steps) // pair.m[name]
         n0 = spec.L // pair.m[name]
+        if spec.kv_dtype == "mxfp4":
+            check_mxfp4_entries(pair.ckv[name][:, n0:n_end].cpu().numpy(), pair.scl[name][:, n0:n_end].cpu().numpy(),
+                                layers[name].ckv[:, n0:n_end], layers[name].ckv_scale[:, n0:n_end], name)
+            continue
         g_codes = pair.ckv[name][:, n0:n_end].cpu().numpy().astype(np.int64)
         o_codes = layers[name].ckv[:, n0:n_end].astype(np.int64)
         ordered = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)  # noqa: E731
@@ -121,6 +136,18 @@ def test_hybrid_loop_rms_norm_every_step():
     spec = hybrid.LayerPairSpec(B=2, L=2048, steps=260, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
                                 wid=58, rms_eps=0.01)
     say("hybrid rms", spec)
+    pair = hybrid.LayerPair(spec)
+    pair.run(0, spec.steps)
+    torch.cuda.synchronize()
+    assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
+
+
+def test_hybrid_loop_mxfp4_entries_every_step():
+    """MXFP4 compressed KV (OCP MX: e2m1 codes, per-32 E8M0 exponents) written by the loop and read
+    by both attention layers; every step against the oracle loop storing its own MXFP4 entries."""
+    spec = hybrid.LayerPairSpec(B=2, L=2048, steps=260, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
+                                wid=60, kv_dtype="mxfp4")
+    say("hybrid mxfp4", spec)
     pair = hybrid.LayerPair(spec)
     pair.run(0, spec.steps)
     torch.cuda.synchronize()

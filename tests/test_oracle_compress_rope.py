@@ -202,3 +202,15 @@ def test_compress_with_rms_norm_is_normalise_then_rotate():
     pooled = compress.pool(formats.bf16_to_f64(x), z.astype(np.float64), m)
     rot = rope.apply(compress.rms_norm(pooled, 1e-6), 100 + np.arange(n) * m, dr, 10000.0)
     assert np.allclose(e_norm, rot, rtol=1e-12, atol=1e-15)
+
+
+def test_compress_mxfp4_is_the_encoding_of_the_exact_entry():
+    rng = np.random.default_rng(24)
+    m, D, dr, n = 4, 128, 64, 6
+    x = formats.f64_to_bf16(rng.standard_normal((n * m, D)) * 0.2)
+    z = rng.standard_normal(n * m).astype(np.float32)
+    e, codes, scales = compress.compress(x, z, 12, m, dr, 10000.0, "mxfp4")
+    want_c, want_s = formats.f64_to_mxfp4(e, -127, 127)
+    assert np.array_equal(codes, want_c) and np.array_equal(scales, want_s)
+    e_bf, _, _ = compress.compress(x, z, 12, m, dr, 10000.0, "bf16")
+    assert np.array_equal(e, e_bf)      # same exact entry, only the storage differs

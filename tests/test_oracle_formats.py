@@ -156,3 +156,21 @@ def test_mxfp4_nearest_value_brute_force():
     codes = formats.unpack_fp4(p)
     mids = np.isin(np.abs(target), formats.E2M1_MIDS)
     assert mids.any() and np.all((codes[mids] & 7) % 2 == 0)
+
+
+def test_mxfp4_full_exponent_range_for_kv_entries():
+    """KV entries use the whole E8M0 range: E = floor(log2 amax) - 2 unclipped; decoding is
+    within one e2m1 step (2^(E+1) at the top of a block, after saturation at 6 * 2^E)."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((6, 64)) * np.array([1e-30, 1e-3, 1.0, 7.0, 1e4, 1e30])[:, None]
+    codes, scales = formats.f64_to_mxfp4(x, formats.MX_KV_E_MIN, formats.MX_KV_E_MAX)
+    amax = np.abs(x.reshape(6, 2, 32)).max(axis=-1)
+    E = np.floor(np.log2(amax)) - 2
+    assert np.array_equal(scales.astype(np.int64) - 127, E.astype(np.int64))
+    back = formats.mxfp4_to_f64(codes, scales)
+    assert np.all(np.abs(back - x) <= np.repeat(2.0 ** (E + 1), 32, axis=-1))
+    # one hand value: amax 12 -> E = 1, 12 / 2 = 6 -> code 7; 5 / 2 = 2.5 ties to code 4 (2.0)
+    v = np.zeros(32)
+    v[0], v[1] = 12.0, -5.0
+    c, s = formats.f64_to_mxfp4(v[None], formats.MX_KV_E_MIN, formats.MX_KV_E_MAX)
+    assert s[0, 0] == 128 and (c[0, 0] & 0xF) == 7 and (c[0, 0] >> 4) == 0x8 | 4
