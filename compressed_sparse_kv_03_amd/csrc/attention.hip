@@ -583,69 +583,85 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
 }
 
 // One workgroup per (query, head): log-sum-exp merge of the split partials. Thread t owns
-// dims 4t..4t+3; every split's weight comes from LDS and the partial loads are independent.
+// dims 4t..4t+3 (d_v <= 4 * kCombNT). Split rows are read in batches of kCombBatch into two
+// alternating register buffers, each batch requested before the previous one is summed; the
+// first batch and every split's (m, l) are requested together, so the weights are formed while
+// the first rows are in flight. The split count is padded to a multiple of two batches with
+// rows clamped to the last split and zero weights, which keeps every load unconditional (the
+// waits exact, and no load moved behind a loop exit).
 constexpr int kMaxSplits = 256;
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  __shared__ float wsh[kMaxSplits];
-  __shared__ float red[2];
-  const int qi = blockIdx.x, h = blockIdx.y;
-  const int S = a.n_splits;
-  const int64_t base = (int64_t)qi * S;
-  const int lane = threadIdx.x & (kWave - 1);
+constexpr int kCombNT = 128;
+constexpr int kCombBatch = 8;
+__global__ __launch_bounds__(kCombNT) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wsh[kMaxSplits + 2 * kCombBatch];
+  __shared__ float red[2][2];
+  const int qi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int S = a.n_splits, SP = (S + 2 * kCombBatch - 1) / (2 * kCombBatch) * (2 * kCombBatch);
+  const int lane = tid & (kWave - 1), w = tid >> 6;
+  const int64_t base = (int64_t)qi * S, srow = (int64_t)a.H * a.d_v;
+  const int dd = min(4 * tid, a.d_v - 4);  // threads past d_v read the last dims and store nothing
+  const float* po = a.part_o + (base * a.H + h) * a.d_v + dd;  // split s at po[s * srow]
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + base * a.H + h;  // split s at pml[s * H]
+  float2 ml[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ml[j] = pml[min(tid + j * kCombNT, S - 1) * a.H];
+  f32x4 v0[kCombBatch], v1[kCombBatch];
+#pragma unroll
+  for (int u = 0; u < kCombBatch; ++u) v0[u] = *reinterpret_cast<const f32x4*>(po + min(u, S - 1) * srow);
   float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const float m = a.part_ml[((base + s) * a.H + h) * 2];
-    wsh[s] = m;
-    mloc = fmaxf(mloc, m);
-  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (tid + j * kCombNT < S) mloc = fmaxf(mloc, ml[j].x);
   mloc = wave_max(mloc);
-  if (lane == 0) red[threadIdx.x >> 6] = mloc;
+  if (lane == 0) red[0][w] = mloc;
   __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
+  const float M = fmaxf(red[0][0], red[0][1]);
   const float Mb = M == -INFINITY ? 0.f : M;
   float lloc = 0.f;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const float w = exp2f(wsh[s] - Mb);
-    wsh[s] = w;
-    lloc += w * a.part_ml[((base + s) * a.H + h) * 2 + 1];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sp = tid + j * kCombNT;
+    if (sp < S) {
+      const float wt = exp2f(ml[j].x - Mb);
+      wsh[sp] = wt;
+      lloc += wt * ml[j].y;
+    } else if (sp < SP) {
+      wsh[sp] = 0.f;
+    }
   }
   lloc = wave_sum(lloc);
+  if (lane == 0) red[1][w] = lloc;
   __syncthreads();
-  if (lane == 0) red[threadIdx.x >> 6] = lloc;
-  __syncthreads();
-  const float L = red[0] + red[1];
+  const float L = red[1][0] + red[1][1];
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d0 = 4 * threadIdx.x; d0 < a.d_v; d0 += 4 * blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      float4 v[8];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](f32x4 (&v)[kCombBatch], int s0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = *reinterpret_cast<const float4*>(a.part_o + ((base + s + u) * a.H + h) * a.d_v + d0);
+    for (int u = 0; u < kCombBatch; ++u) v[u] = *reinterpret_cast<const f32x4*>(po + min(s0 + u, S - 1) * srow);
+  };
+  auto sum = [&](const f32x4 (&v)[kCombBatch], int s0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = wsh[s + u];
-        acc.x += w * v[u].x;
-        acc.y += w * v[u].y;
-        acc.z += w * v[u].z;
-        acc.w += w * v[u].w;
-      }
+    for (int u = 0; u < kCombBatch; ++u) {
+      const float wt = wsh[s0 + u];
+      acc.x += wt * v[u].x;
+      acc.y += wt * v[u].y;
+      acc.z += wt * v[u].z;
+      acc.w += wt * v[u].w;
     }
-    for (; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((base + s) * a.H + h) * a.d_v + d0);
-      const float w = wsh[s];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
-    }
+  };
+  for (int s0 = 0; s0 < SP; s0 += 2 * kCombBatch) {  // v0 holds rows s0.. on entry
+    fetch(v1, s0 + kCombBatch);
+    sum(v0, s0);
+    fetch(v0, min(s0 + 2 * kCombBatch, SP - kCombBatch));  // the last one re-reads rows already summed
+    sum(v1, s0 + kCombBatch);
+  }
+  if (4 * tid < a.d_v) {
     uint2 packed;
     packed.x = pack_bf16x2(acc.x * inv, acc.y * inv);
     packed.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-    *reinterpret_cast<uint2*>(a.out + ((int64_t)qi * a.H + h) * a.d_v + d0) = packed;
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)qi * a.H + h) * a.d_v + dd) = packed;
   }
-  if (threadIdx.x == 0 && a.out_lse)
+  if (tid == 0 && a.out_lse)
     a.out_lse[(int64_t)qi * a.H + h] = L > 0.f ? (Mb + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -739,7 +755,8 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(2 * p.nw * kWave), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.nq, a.H), dim3(128), 0, s, a);
+    CSKV_REQUIRE(a.d_v <= 4 * kCombNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name, a.d_v, 4 * kCombNT);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.nq, a.H), dim3(kCombNT), 0, s, a);
     CSKV_LAUNCH_CHECK(name);
   }
   return CSKV_OK;
