@@ -215,20 +215,28 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
   }
 }
 
-// Workgroup (b, i): token i of sequence b goes to ring slot (pos[b] + i) mod R.
+// Workgroup (b, i): token i of sequence b goes to ring slot (pos[b] + i) mod R. The position, z
+// and the token's first row chunk are all requested before any is used, so the copy waits for
+// one memory round trip; rows longer than 8 * blockDim.x bf16 continue in a loop.
 __global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __restrict__ x_new,
                                                           const float* __restrict__ z_new,
                                                           const int64_t* __restrict__ pos,
                                                           uint16_t* __restrict__ ring_x,
                                                           float* __restrict__ ring_z, int T, int D, int R) {
   const int b = blockIdx.x, i = blockIdx.y;
-  const int64_t slot = (int64_t)b * R + ((pos[b] + i) % R);
   const int64_t tok = (int64_t)b * T + i;
   const int cpr = D >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x_new + tok * D);
+  const int c0 = threadIdx.x;
+  const int64_t p = pos[b];
+  const float z = z_new ? z_new[tok] : 0.f;
+  uint4 v0 = {0u, 0u, 0u, 0u};
+  if (c0 < cpr) v0 = src[c0];
+  const int64_t slot = (int64_t)b * R + ((p + i) % R);
   uint4* dst = reinterpret_cast<uint4*>(ring_x + slot * D);
-  for (int c = threadIdx.x; c < cpr; c += blockDim.x) dst[c] = src[c];
-  if (threadIdx.x == 0 && z_new) ring_z[slot] = z_new[tok];
+  if (c0 < cpr) dst[c0] = v0;
+  for (int c = c0 + blockDim.x; c < cpr; c += blockDim.x) dst[c] = src[c];
+  if (c0 == 0 && z_new) ring_z[slot] = z;
 }
 
 // Indexer keys of the entries: the per-token keys pooled with the entries' softmax weights, then
