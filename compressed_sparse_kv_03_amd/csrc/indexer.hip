@@ -364,9 +364,48 @@ struct DecodeArgs {
   int chunk, n_chunks, slots;
 };
 
+// Cross-lane integer scans and reductions on DPP row operations (rows of 16 lanes) and
+// readlane of the row results, instead of permutes through LDS. Every lane of the wave must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr0(int x) {  // row shift: lanes shifted in from outside the row read 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_perm(int x) {  // quad permutation or row rotation (all sources valid)
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+
+// Inclusive prefix sum over the lanes of the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_shr0<0x111>(v);  // row_shr:1
+  v += dpp_shr0<0x112>(v);  // row_shr:2
+  v += dpp_shr0<0x114>(v);  // row_shr:4
+  v += dpp_shr0<0x118>(v);  // row_shr:8
+  const int r = (threadIdx.x & (kWave - 1)) >> 4;
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+
+// Reduction over the lanes of the wave (every lane gets the result).
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int v, Op op) {
+  v = op(v, dpp_perm<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_perm<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_perm<0x124>(v));  // row_ror:4
+  v = op(v, dpp_perm<0x128>(v));  // row_ror:8
+  return op(op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+            op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return wave_reduce_i32(v, [](int a, int b) { return a + b; });
+}
+
 // Highest bin b (scanning from the top) whose cumulative count reaches kk; returns b and the
 // count strictly above it in *above. NT is the block size (<= 1024); NB is a power of two.
-// kk >= 1 and total >= kk. scratch holds at least 34 ints. Every thread must call it.
+// kk >= 1 and total >= kk. scratch holds at least 34 ints. Every thread must call it, after a
+// barrier that follows every earlier read of scratch; it ends with a barrier.
 template <int NB, int NT>
 __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int* scratch) {
   constexpr int PER = NB >= NT ? NB / NT : 1;
@@ -379,13 +418,7 @@ __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int*
 #pragma unroll
     for (int i = 1; i <= PER; ++i) s += hist[top - i];
   }
-  int inc = s;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += v;
-  }
-  __syncthreads();
+  const int inc = wave_incl_scan(s);
   if (lane == kWave - 1) scratch[w] = inc;
   if (t == 0) {  // defaults (bin 0) in case the counts do not reach kk
     scratch[32] = 0;
@@ -393,9 +426,9 @@ __device__ int find_threshold_bin(const uint32_t* hist, int kk, int* above, int*
   }
   __syncthreads();
   int wbase = 0;
-  for (int i = 0; i < w; ++i) wbase += scratch[i];
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) wbase += i < w ? scratch[i] : 0;
   const int incl = inc + wbase, excl = incl - s;
-  __syncthreads();
   if (t < ACTIVE && excl < kk && incl >= kk) {
     int c = excl;
     for (int i = 1; i <= PER; ++i) {
@@ -433,14 +466,10 @@ struct SelShared {
 };
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
+  return (uint32_t)wave_reduce_i32((int)v, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
+  return (uint32_t)wave_reduce_i32((int)v, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
 }
 
 // Folds per-lane ranges [mn, mx] of ordered scores into ss.mn32 / ss.mx32 (which thread 0 set
@@ -504,12 +533,7 @@ __device__ int reg_compact_ge(const uint64_t (&v)[PER], uint64_t base, uint64_t*
   int c = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) c += v[j] >= base;
-  int inc = c;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
+  const int inc = wave_incl_scan(c);
   if (lane == kWave - 1) ss.scratch[w] = inc;
   __syncthreads();
   int off = inc - c, total = 0;
@@ -546,8 +570,7 @@ __device__ void block_range(const uint64_t* keys, int n, SelShared& ss, uint64_t
   }
   mx = wave_max_u64(mx);
   mn = ~wave_max_u64(~mn);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+  c = wave_sum_i32(c);
   __syncthreads();
   if ((tid & (kWave - 1)) == 0) {
     atomicMax(&ss.mx, (unsigned long long)mx);
@@ -735,8 +758,7 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
         ++nz;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) nz += __shfl_xor(nz, o, kWave);
+    nz = wave_sum_i32(nz);
     __syncthreads();  // range words initialised
     fold_score_range(mx, mn, sm.ss);
     if ((tid & (kWave - 1)) == 0) atomicAdd(&sm.ss.cnt, nz);
@@ -756,12 +778,7 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
   const int lane = tid & (kWave - 1), w = tid >> 6;
   int cnt = 0;
   for (int i = tid; i < n; i += kDecNT) cnt += src[i] >= base;
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
+  const int inc = wave_incl_scan(cnt);
   if (lane == kWave - 1) sm.ss.scratch[w] = inc;
   __syncthreads();
   int off = inc - cnt, m = 0;
