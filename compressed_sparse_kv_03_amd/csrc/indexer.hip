@@ -351,7 +351,8 @@ __global__ __launch_bounds__(kIdxNT) void index_merge_kernel(IndexArgs a) {
 // k keys overall, hence by fewer than k keys of its own chunk, so it is among its chunk's
 // passing keys; the top-k of the union of those is the global top-k. No step depends on the
 // data's distribution, and nothing is carried between calls.
-constexpr int kDecNT = 1024;     // threads of both decode kernels
+constexpr int kDecNT = 1024;     // threads of kernel A
+constexpr int kFinNT = 512;      // threads of kernel B (fewer waves per barrier)
 constexpr int kDecSub = 8448;    // entries a chunk workgroup holds in LDS at once
 constexpr int kSelBins = 2048;   // histogram bins per refinement level
 constexpr int kSelCap = 1024;    // kernel B: keys ranked directly
@@ -686,26 +687,41 @@ struct FinalSmem {
 };
 
 // Ranks sel[0..m) (distinct keys, m <= kSelCap) and writes the ones of rank < kk to their
-// slots. P = kDecNT / m' threads share a key (m' = m rounded up to a power of two), each
-// counting the greater keys in a 1/P slice; the partial ranks meet in an LDS counter.
+// slots. Each thread takes two keys and counts the greater keys in a 1/P slice, comparing every
+// key it reads with both (P = min(NT, 2 NT / m') threads per key pair, m' = m rounded up to a
+// power of two, so the pairs advance by at least one per step); the partial ranks meet in an
+// LDS counter.
+template <int NT>
 __device__ __forceinline__ void rank_write(const uint64_t* sel, int m, int kk, int32_t* oi, float* os, int* rk) {
+  constexpr int KPT = 2;
   const int tid = threadIdx.x;
   m = __builtin_amdgcn_readfirstlane(m);
   int mp = 1;
   while (mp < m) mp <<= 1;
-  const int P = mp >= kDecNT ? 1 : kDecNT / mp;  // threads per key (power of two)
-  for (int i = tid; i < m; i += kDecNT) rk[i] = 0;
+  const int P = mp >= NT * KPT ? 1 : min(NT, NT * KPT / mp);  // threads per key pair (power of two, <= NT)
+  for (int i = tid; i < m; i += NT) rk[i] = 0;
   __syncthreads();
   const int part = tid % P, slice = (m + P - 1) / P;
   const int j0 = part * slice, j1 = min(m, j0 + slice);
-  for (int i = tid / P; i < m; i += kDecNT / P) {
-    const uint64_t key = sel[i];
-    int r = 0;
-    for (int jx = j0; jx < j1; ++jx) r += sel[jx] > key;
-    if (r) atomicAdd(&rk[i], r);
+  for (int ib = (tid / P) * KPT; ib < m; ib += (NT / P) * KPT) {
+    uint64_t key[KPT];
+    int r[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      key[u] = ib + u < m ? sel[ib + u] : ~0ull;  // no key is greater than ~0
+      r[u] = 0;
+    }
+    for (int jx = j0; jx < j1; ++jx) {
+      const uint64_t x = sel[jx];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) r[u] += x > key[u];
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (ib + u < m && r[u]) atomicAdd(&rk[ib + u], r[u]);
   }
   __syncthreads();
-  for (int i = tid; i < m; i += kDecNT) {
+  for (int i = tid; i < m; i += NT) {
     const int rank = rk[i];
     if (rank < kk) {
       const uint64_t key = sel[i];
@@ -716,17 +732,17 @@ __device__ __forceinline__ void rank_write(const uint64_t* sel, int m, int kk, i
 }
 
 // Kernel B: one workgroup per query; the ordered top-k of its C * slots candidates.
-__global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d) {
+__global__ __launch_bounds__(kFinNT) void index_final_decode_kernel(DecodeArgs d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
-  constexpr int PER = kStageMax / kDecNT;
+  constexpr int PER = kStageMax / kFinNT;
   const IndexArgs& a = d.a;
   const int q = blockIdx.x, tid = threadIdx.x;
   const int nv = min(a.n_valid[q], a.N_cap);
   const int kk = min(a.k, nv);
   int32_t* oi = a.out_idx + (int64_t)q * a.k;
   float* os = a.out_score ? a.out_score + (int64_t)q * a.k : nullptr;
-  for (int i = kk + tid; i < a.k; i += kDecNT) {  // padding
+  for (int i = kk + tid; i < a.k; i += kFinNT) {  // padding
     oi[i] = -1;
     if (os) os[i] = -INFINITY;
   }
@@ -735,7 +751,7 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
   const uint64_t* src = d.cand + (int64_t)q * n;
   if (n <= kStageMax) {
     // register-resident: every slot is loaded once, all loads in flight together
-    for (int i = tid; i < kSelBins; i += kDecNT) sm.ss.hist[i] = 0;
+    for (int i = tid; i < kSelBins; i += kFinNT) sm.ss.hist[i] = 0;
     if (tid == 0) {
       sm.ss.mx32 = 0;
       sm.ss.mn32 = ~0u;
@@ -744,7 +760,7 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
     uint64_t v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int i = tid + j * kDecNT;
+      const int i = tid + j * kFinNT;
       v[j] = i < n ? src[i] : 0;
     }
     uint32_t mx = 0, mn = ~0u;
@@ -765,35 +781,35 @@ __global__ __launch_bounds__(kDecNT) void index_final_decode_kernel(DecodeArgs d
     __syncthreads();
     uint64_t lo, hi;
     key_bounds(sm.ss, &lo, &hi);
-    const uint64_t base = sm.ss.cnt <= kSelCap ? lo : reg_select_floor<kDecNT, PER>(v, kk, kSelCap, lo, hi, sm.ss);
-    const int m = reg_compact_ge<kDecNT, PER>(v, base, sm.sel, kSelCap, sm.ss);
-    rank_write(sm.sel, m, kk, oi, os, sm.rk);
+    const uint64_t base = sm.ss.cnt <= kSelCap ? lo : reg_select_floor<kFinNT, PER>(v, kk, kSelCap, lo, hi, sm.ss);
+    const int m = reg_compact_ge<kFinNT, PER>(v, base, sm.sel, kSelCap, sm.ss);
+    rank_write<kFinNT>(sm.sel, m, kk, oi, os, sm.rk);
     return;
   }
   // large candidate lists: histogram passes over global memory
   uint64_t hi, lo;
   int nz;
-  block_range<kDecNT>(src, n, sm.ss, &hi, &lo, &nz);
-  const uint64_t base = nz <= kSelCap ? lo : select_floor<kDecNT>(src, n, kk, kSelCap, lo, hi, sm.ss);
+  block_range<kFinNT>(src, n, sm.ss, &hi, &lo, &nz);
+  const uint64_t base = nz <= kSelCap ? lo : select_floor<kFinNT>(src, n, kk, kSelCap, lo, hi, sm.ss);
   const int lane = tid & (kWave - 1), w = tid >> 6;
   int cnt = 0;
-  for (int i = tid; i < n; i += kDecNT) cnt += src[i] >= base;
+  for (int i = tid; i < n; i += kFinNT) cnt += src[i] >= base;
   const int inc = wave_incl_scan(cnt);
   if (lane == kWave - 1) sm.ss.scratch[w] = inc;
   __syncthreads();
   int off = inc - cnt, m = 0;
 #pragma unroll
-  for (int i = 0; i < kDecNT / kWave; ++i) {
+  for (int i = 0; i < kFinNT / kWave; ++i) {
     off += i < w ? sm.ss.scratch[i] : 0;
     m += sm.ss.scratch[i];
   }
   m = min(m, kSelCap);
-  for (int i = tid; i < n; i += kDecNT) {
+  for (int i = tid; i < n; i += kFinNT) {
     const uint64_t v = src[i];
     if (v >= base && off < kSelCap) sm.sel[off++] = v;
   }
   __syncthreads();
-  rank_write(sm.sel, m, kk, oi, os, sm.rk);
+  rank_write<kFinNT>(sm.sel, m, kk, oi, os, sm.rk);
 }
 
 // Chunking of kernel A: one workgroup per CU for the whole job (256), chunks of at most
@@ -824,7 +840,7 @@ static void launch_decode_ks(const DecodeArgs& d, int queries, hipStream_t s) {
   (void)hipFuncSetAttribute((const void*)index_final_decode_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem_b);
   hipLaunchKernelGGL((index_chunk_decode_kernel<KS>), dim3(queries, d.n_chunks), dim3(kDecNT), smem_a, s, d);
-  hipLaunchKernelGGL(index_final_decode_kernel, dim3(queries), dim3(kDecNT), smem_b, s, d);
+  hipLaunchKernelGGL(index_final_decode_kernel, dim3(queries), dim3(kFinNT), smem_b, s, d);
 }
 
 static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipStream_t s) {
