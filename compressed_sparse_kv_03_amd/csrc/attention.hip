@@ -744,6 +744,8 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   for (int i = 0; i < a.d_rope / 2; ++i) a.inv_freq[i] = pow((double)a.rope_base, -2.0 * (double)i / (double)a.d_rope);
   CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "%s: workspace %zu < %zu bytes", name,
                ws_bytes, p.ws);
+  CSKV_REQUIRE(p.n_splits == 1 || a.d_v <= 4 * kCombNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name,
+               a.d_v, 4 * kCombNT);
   a.n_splits = p.n_splits;
   a.keys_per_split = p.keys_per_split;
   if (p.n_splits > 1) {
@@ -755,7 +757,6 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   hipLaunchKernelGGL(kern, dim3(a.nq, p.n_splits * head_groups), dim3(2 * p.nw * kWave), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {
-    CSKV_REQUIRE(a.d_v <= 4 * kCombNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name, a.d_v, 4 * kCombNT);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(a.nq, a.H), dim3(kCombNT), 0, s, a);
     CSKV_LAUNCH_CHECK(name);
   }
