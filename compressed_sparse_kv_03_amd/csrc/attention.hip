@@ -586,9 +586,10 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
 // dims 4t..4t+3 (d_v <= 4 * kCombNT). Split rows are read in batches of kCombBatch into two
 // alternating register buffers, each batch requested before the previous one is summed; the
 // first batch and every split's (m, l) are requested together, so the weights are formed while
-// the first rows are in flight. The split count is padded to a multiple of two batches with
-// rows clamped to the last split and zero weights, which keeps every load unconditional (the
-// waits exact, and no load moved behind a loop exit).
+// the first rows are in flight. The split count is padded to a whole batch with rows clamped to
+// the last split and zero weights, so every load of a batch is unconditional; each exit of the
+// loop sums its last batch itself, so no fetch is ever left unused (which would let the
+// compiler move it behind the exit) and the waits stay exact.
 constexpr int kMaxSplits = 256;
 constexpr int kCombNT = 128;
 constexpr int kCombBatch = 8;
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(kCombNT) void attn_combine_kernel(AttnArgs a) {
   __shared__ float wsh[kMaxSplits + 2 * kCombBatch];
   __shared__ float red[2][2];
   const int qi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int S = a.n_splits, SP = (S + 2 * kCombBatch - 1) / (2 * kCombBatch) * (2 * kCombBatch);
+  const int S = a.n_splits, SP = (S + kCombBatch - 1) / kCombBatch * kCombBatch;
   const int lane = tid & (kWave - 1), w = tid >> 6;
   const int64_t base = (int64_t)qi * S, srow = (int64_t)a.H * a.d_v;
   const int dd = min(4 * tid, a.d_v - 4);  // threads past d_v read the last dims and store nothing
@@ -649,10 +650,18 @@ __global__ __launch_bounds__(kCombNT) void attn_combine_kernel(AttnArgs a) {
       acc.w += wt * v[u].w;
     }
   };
-  for (int s0 = 0; s0 < SP; s0 += 2 * kCombBatch) {  // v0 holds rows s0.. on entry
+  for (int s0 = 0;; s0 += 2 * kCombBatch) {  // v0 holds rows s0.. on entry
+    if (s0 + kCombBatch >= SP) {  // v0 is the last batch
+      sum(v0, s0);
+      break;
+    }
     fetch(v1, s0 + kCombBatch);
     sum(v0, s0);
-    fetch(v0, min(s0 + 2 * kCombBatch, SP - kCombBatch));  // the last one re-reads rows already summed
+    if (s0 + 2 * kCombBatch >= SP) {  // v1 is the last batch
+      sum(v1, s0 + kCombBatch);
+      break;
+    }
+    fetch(v0, s0 + 2 * kCombBatch);
     sum(v1, s0 + kCombBatch);
   }
   if (4 * tid < a.d_v) {
