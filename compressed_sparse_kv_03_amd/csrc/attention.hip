@@ -429,6 +429,27 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
   const int h0 = wg_hg * 16 * HG + hgw * 16;  // this wave's first head
   const int rope0 = D - a.d_rope;
 
+  // The query loads depend on nothing else: request them first (this wave's unrotated dims into
+  // its registers, this thread's first rotated chunk for the LDS copy), so that their latency
+  // overlaps the position, entry-count and top-k loads below.
+  const int rc = a.d_rope / 8;  // rotated 8-dim chunks per head
+  WaveState<KD, NVH> st;
+  {
+    const int h = h0 + col;
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      st.qa[s] = make_uint4(0, 0, 0, 0);
+      if (d0 < rope0 && h < a.H) st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + d0);
+    }
+  }
+  auto q_chunk = [&](int c) {  // raw rotated-part chunk c (head-local index c / rc) of this workgroup
+    const int hl = c / rc, h = wg_hg * 16 * HG + hl;
+    return h < a.H ? *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + rope0 + 8 * (c - hl * rc))
+                   : make_uint4(0, 0, 0, 0);
+  };
+  const uint4 qc0 = (int)threadIdx.x < HG * 16 * rc ? q_chunk(threadIdx.x) : make_uint4(0, 0, 0, 0);
+
   for (int i = threadIdx.x; i < a.d_rope / 2; i += NT) sm.inv_freq[i] = a.inv_freq[i];
 
   const KeySpace ks = key_space(a, qi);
@@ -441,15 +462,21 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i < n_sel; i += NT) sm.sidx[i] = a.topk[(int64_t)qi * a.k + key_begin + i];
   }
   __syncthreads();  // inv_freq and sidx ready
-  // rotated query dims -> LDS (each thread rotates whole 8-dim chunks of the WG's heads)
-  {
-    const int rc = a.d_rope / 8;  // rotated chunks per head
+  const bool has_e = key_begin < e_end;
+  const int w_begin = max(key_begin, ks.n_c);
+  const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
+  constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);  // bytes per row: codes
+  constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);    // and scales
+  const void* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
+  const void* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
+  // rotated query dims -> LDS (each thread rotates whole 8-dim chunks of the WG's heads), then
+  // this wave's rotated dims into its query registers; every thread calls it once
+  auto rotate_query = [&]() {
     for (int c = threadIdx.x; c < HG * 16 * rc; c += NT) {
       const int hl = c / rc, ch = c - hl * rc;
       const int h = wg_hg * 16 * HG + hl;
-      uint4 v = make_uint4(0, 0, 0, 0);
+      uint4 v = c == (int)threadIdx.x ? qc0 : q_chunk(c);
       if (h < a.H) {
-        v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + rope0 + 8 * ch);
         if (a.q_rms_eps > 0.f) {
           float f[8], ss = 0.f;
           unpack8(v, f);
@@ -463,22 +490,13 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
       }
       *reinterpret_cast<uint4*>(&sm.qr[hl][8 * ch]) = v;
     }
-  }
-  __syncthreads();
-
-  WaveState<KD, NVH> st;
-  {
-    const int h = h0 + col;
+    __syncthreads();
 #pragma unroll
     for (int s = 0; s < KD; ++s) {
       const int d0 = 32 * s + 8 * g;
-      st.qa[s] = make_uint4(0, 0, 0, 0);
-      if (d0 >= rope0)
-        st.qa[s] = *reinterpret_cast<const uint4*>(&sm.qr[hgw * 16 + col][d0 - rope0]);
-      else if (h < a.H)
-        st.qa[s] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + d0);
+      if (d0 >= rope0) st.qa[s] = *reinterpret_cast<const uint4*>(&sm.qr[hgw * 16 + col][d0 - rope0]);
     }
-  }
+  };
   // query RMSNorm: 1 / sqrt(mean(q^2) + eps) of each head over its raw D dims, applied to the
   // logits (scaling q before the product would add a bf16 rounding). The unrotated dims come
   // from this wave's query registers, the rotated ones from the chunk sums taken before the
@@ -512,16 +530,13 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
     st.l[r] = 0.f;
   }
 
-  // phase 1: compressed entries
-  if (key_begin < e_end) {
-    const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
-    // bytes per row: codes and scales
-    constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);
-    constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);
-    const void* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
-    const void* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
+  TileRegs<KD, HG, false> RW;  // window tiles
+  // phase 1: compressed entries. A split's first tile (entries, else window tokens) is requested
+  // before the query rotation, whose arithmetic then overlaps the loads.
+  if (has_e) {
     TileRegs<KD, HG, KV> R;
     entry_load<KD, NV, HG, KV>(a, cbase, sbase, key_begin, e_end, key_begin, sm, R);
+    rotate_query();
     write_qscale();
     for (int key0 = key_begin; key0 < e_end; key0 += kTK) {
       __syncthreads();
@@ -530,18 +545,21 @@ __global__ __launch_bounds__(2 * HG * kWave) void attn_kernel(AttnArgs a) {
       if (key0 + kTK < e_end) entry_load<KD, NV, HG, KV>(a, cbase, sbase, key0 + kTK, e_end, key_begin, sm, R);
       tile_compute<KD, NV, HG>(sm, st, hgw, hf);
     }
+  } else {
+    if (w_begin < key_end) window_load<KD, NV, HG>(a, qi, ks, w_begin, key_end, RW);
+    rotate_query();
   }
   // phase 2: window tokens
-  const int w_begin = max(key_begin, ks.n_c);
   if (w_begin < key_end) {
-    TileRegs<KD, HG, false> R;
-    window_load<KD, NV, HG>(a, qi, ks, w_begin, key_end, R);
-    if (key_begin >= e_end) write_qscale();
+    if (has_e)
+      window_load<KD, NV, HG>(a, qi, ks, w_begin, key_end, RW);
+    else
+      write_qscale();
     for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
       __syncthreads();
-      window_store<KD, NV, HG>(a, ks, key0, key_end, sm, R);
+      window_store<KD, NV, HG>(a, ks, key0, key_end, sm, RW);
       __syncthreads();
-      if (key0 + kTK < key_end) window_load<KD, NV, HG>(a, qi, ks, key0 + kTK, key_end, R);
+      if (key0 + kTK < key_end) window_load<KD, NV, HG>(a, qi, ks, key0 + kTK, key_end, RW);
       tile_compute<KD, NV, HG>(sm, st, hgw, hf);
     }
   }
