@@ -9,10 +9,16 @@
 //
 // Design (HBM-bound stream): one wavefront per output entry. Lane l owns the
 // 16-byte chunks l and l+64 of the D-dim row, so each token row is read by one
-// coalesced 1 KiB wave load (+ a short tail when D > 512). The m pooling
-// weights are wave-uniform scalars; tokens are read 8 at a time to keep
-// several loads in flight per lane. The fp8 scale needs the entry's max |e|,
-// which is a wave reduction with no LDS and no barrier.
+// coalesced 1 KiB wave load (+ a short tail when D > 512). The arithmetic is
+// fp64 from the bf16 inputs to the storage rounding (pooling weights, pooled
+// sums, RMSNorm, the RoPE angle and its sine and cosine, the fp8 scale), and
+// the stored value is rounded once, from fp64, to its format: the stored entry
+// is then the correct rounding of the exact entry except where the exact value
+// lies within a few fp64 ulps of a rounding midpoint. fp64 runs at half the
+// fp32 vector rate on this GPU, far above what a stream of bf16 tokens needs.
+// The m pooling weights are computed once per token into the wave's LDS slot
+// and read back as wave-uniform values; the fp8 scale needs the entry's
+// max |e|, a wave reduction with no LDS and no barrier.
 #include "common.cuh"
 #include "host_util.h"
 
@@ -21,6 +27,7 @@ namespace cskv {
 constexpr int kCompressWaves = 4;  // waves per workgroup
 constexpr int kUnroll = 8;
 constexpr int kRopeTab = 64;       // RoPE pairs whose frequency comes from the host table
+constexpr int kMaxBlock = 1024;    // largest m
 
 // base^(-2i/d_rope) for the first kRopeTab pairs, formed on the host in fp64 (a device fp64
 // pow per pair and lane was most of the kernel's time at decode sizes).
@@ -28,25 +35,50 @@ struct RopeTable {
   double inv_freq[kRopeTab];
 };
 
-// cos / sin of pos * inv_freq: the angle is reduced to [-pi, pi] in fp64, then evaluated in
-// fp32 at the rounded angle and corrected to first order for the rounding (|error| about one
-// fp32 ulp, against several for the plain fp32 evaluation).
-__device__ __forceinline__ void rope_cs_fast(double inv_freq, int64_t pos, float* c, float* s) {
-  double a = (double)pos * inv_freq;
-  a -= 6.283185307179586476925286766559 * rint(a * 0.15915494309189533576888376337251);
-  const float af = (float)a;
-  const float dl = (float)(a - (double)af);
-  float sf, cf;
-  sincosf(af, &sf, &cf);
-  *s = fmaf(dl, cf, sf);
-  *c = fmaf(-dl, sf, cf);
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
 }
 
-// Nearest e2m1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even code,
-// saturating at 6), sign in bit 3.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float mag = fabsf(v);
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+// floor(log2 |v|) of a finite nonzero double (exact: from the binary exponent).
+__device__ __forceinline__ int floor_log2_d(double v) {
+  int ex;
+  (void)frexp(v, &ex);  // |v| = f * 2^ex with f in [0.5, 1)
+  return ex - 1;
+}
+
+// fp64 -> bf16 bits, round to nearest even (finite values in the bf16 range; +-0 -> 0).
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+  if (v == 0.0) return 0u;
+  const int e = max(floor_log2_d(v), -126);
+  const double r = ldexp(rint(ldexp(v, 7 - e)), e - 7);  // 8 significant bits; scalings exact
+  return __float_as_uint((float)r) >> 16;              // exact: r has 8 significant bits
+}
+
+// fp64 -> OCP e4m3fn code: round to nearest even on 4 significant bits (quantum 2^-9 below
+// 2^-6), saturating at 448; a strictly negative value keeps the sign bit when it rounds to 0.
+__device__ __forceinline__ uint32_t f64_to_e4m3(double v) {
+  const double a = fabs(v);
+  int code = 0;
+  if (a > 0.0) {
+    const int e = max(floor_log2_d(a), -6);
+    const int r = (int)rint(ldexp(a, 3 - e));  // in [0, 16]; 16 carries into the next binade
+    code = min((e + 7) * 8 + r - 8, 0x7E);      // e = -6 gives code = r (subnormals, 2^-6)
+  }
+  return (uint32_t)code | (v < 0.0 ? 0x80u : 0u);
+}
+
+// Nearest e2m1 code of v in units of the block scale (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+// ties to the even code, saturating at 6), sign in bit 3 for a strictly negative value.
+__device__ __forceinline__ uint32_t e2m1_code_d(double v) {
+  const double mag = fabs(v);
+  const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
   int c = 0;
 #pragma unroll
   for (int i = 0; i < 7; ++i) c += mag > mids[i];
@@ -54,7 +86,32 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 #pragma unroll
   for (int i = 0; i < 7; ++i) tie = tie || (c == i && mag == mids[i]);
   if (tie && (c & 1)) ++c;  // a midpoint goes to the even code
-  return (uint32_t)c | (v < 0.f ? 8u : 0u);
+  return (uint32_t)c | (v < 0.0 ? 8u : 0u);
+}
+
+// MXFP4 block exponent of a block whose largest magnitude is amax: floor(log2 amax) - 2 (the
+// largest e2m1 exponent) limited to [e_min, e_max]; an all-zero block takes e_min.
+__device__ __forceinline__ int mx_block_exp(double amax, int e_min, int e_max) {
+  return amax > 0.0 ? min(e_max, max(e_min, floor_log2_d(amax) - 2)) : e_min;
+}
+
+// The softmax weights of a block's m pooling logits into w[0..m) (this wave's LDS slot):
+// a_i = exp(z_i - max z) / sum_i' exp(z_i' - max z) in fp64. Ends with the slot readable.
+__device__ __forceinline__ void pool_weights(const float* zb, int m, double* w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float zmax = -INFINITY;
+  for (int i = lane; i < m; i += kWave) zmax = fmaxf(zmax, zb[i]);
+  zmax = wave_max(zmax);
+  double zsum = 0.0;
+  for (int i = lane; i < m; i += kWave) {
+    const double e = exp((double)zb[i] - (double)zmax);
+    w[i] = e;
+    zsum += e;
+  }
+  zsum = wave_sum_d(zsum);
+  for (int i = lane; i < m; i += kWave) w[i] = w[i] / zsum;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the weights are in LDS (wave-local slot)
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Storage of a compressed entry: bf16, e4m3fn with one fp32 scale per entry, or OCP MXFP4
@@ -68,35 +125,23 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     int m, int entry_pos_offset, float rope_base, void* __restrict__ out,
     void* __restrict__ out_scale, int64_t out_seq_stride, const int32_t* __restrict__ out_entry0, float rms_eps,
     RopeTable rt) {
+  __shared__ double wsh[kCompressWaves][kMaxBlock];
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
+  const int wl = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + wl);
   if (w >= B * n_ent) return;
   const int b = w / n_ent;
   const int j = w - b * n_ent;
   const uint16_t* xb = x + (int64_t)b * x_seq_stride + (int64_t)j * m * D;
   const float* zb = z + (int64_t)b * z_seq_stride + (int64_t)j * m;
-
-  // softmax over the block's m logits
-  float zmax = -INFINITY;
-  for (int i = lane; i < m; i += kWave) zmax = fmaxf(zmax, zb[i]);
-  zmax = wave_max(zmax);
-  float zsum = 0.f;
-  for (int i = lane; i < m; i += kWave) zsum += expf(zb[i] - zmax);
-  zsum = wave_sum(zsum);
-  const float inv = 1.0f / zsum;
+  double* wt = wsh[wl];
 
   const int cpr = D >> 3;  // 16-byte chunks per row
   const bool has0 = lane < cpr;
   const bool has1 = lane + kWave < cpr;
-  float acc0[8], acc1[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
-
-  // blocks of kUnroll tokens, the last one padded by repeating the final row with weight 0:
-  // every load is unconditional, so a block's loads are all in flight together (a tail loop
-  // of single tokens costs one memory latency per token)
-  for (int i = 0; i < m; i += kUnroll) {
-    uint4 v0[kUnroll], v1[kUnroll];
+  // the first block of token rows is requested before the weights are formed
+  uint4 v0[kUnroll], v1[kUnroll];
+  auto load_block = [&](int i) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = min(i + u, m - 1);
@@ -104,57 +149,68 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
       v0[u] = ld_stream16(row + (has0 ? lane : 0));
       v1[u] = ld_stream16(row + (has1 ? lane + kWave : 0));
     }
+  };
+  load_block(0);
+  pool_weights(zb, m, wt);
+
+  double acc0[8], acc1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.0;
+  // blocks of kUnroll tokens, the last one padded by repeating the final row with weight 0:
+  // every load is unconditional, so a block's loads are all in flight together
+  for (int i = 0; i < m; i += kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = min(i + u, m - 1);
-      const float a = i + u < m ? expf(zb[t] - zmax) * inv : 0.f;
+      const double a = i + u < m ? wt[i + u] : 0.0;
       float f[8];
       unpack8(v0[u], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc0[e] = fmaf(a, f[e], acc0[e]);
+      for (int e = 0; e < 8; ++e) acc0[e] = fma(a, (double)f[e], acc0[e]);
       unpack8(v1[u], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc1[e] = fmaf(a, f[e], acc1[e]);
+      for (int e = 0; e < 8; ++e) acc1[e] = fma(a, (double)f[e], acc1[e]);
     }
+    if (i + kUnroll < m) load_block(i + kUnroll);
   }
   if (!has0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc0[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc0[e] = 0.0;
   }
   if (!has1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc1[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc1[e] = 0.0;
   }
 
   // optional unit-gain RMSNorm of the pooled entry (before the rotation, which keeps pair norms)
   if (rms_eps > 0.f) {
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += acc0[e] * acc0[e] + acc1[e] * acc1[e];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + rms_eps);
+    ss = wave_sum_d(ss);
+    const double r = sqrt(ss / (double)D + (double)rms_eps);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      acc0[e] *= r;
-      acc1[e] *= r;
+      acc0[e] /= r;
+      acc1[e] /= r;
     }
   }
 
-  // partial RoPE on the last d_rope dims, at the entry's position
+  // partial RoPE on the last d_rope dims, at the entry's position (angle, sine and cosine in fp64)
   const int64_t p = pos0[b] + (int64_t)j * m + entry_pos_offset;
   const int rope0 = D - d_rope;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = lane + h * kWave;
-    float* acc = h ? acc1 : acc0;
+    double* acc = h ? acc1 : acc0;
     if (c < cpr && 8 * c >= rope0) {
       const int pair0 = (8 * c - rope0) >> 1;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float cs, sn;
         const int pair = pair0 + q;
-        rope_cs_fast(pair < kRopeTab ? rt.inv_freq[pair] : rope_inv_freq(rope_base, pair, d_rope), p, &cs, &sn);
-        const float u0 = acc[2 * q], u1 = acc[2 * q + 1];
+        const double ang = (double)p * (pair < kRopeTab ? rt.inv_freq[pair] : rope_inv_freq(rope_base, pair, d_rope));
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double u0 = acc[2 * q], u1 = acc[2 * q + 1];
         acc[2 * q] = u0 * cs - u1 * sn;
         acc[2 * q + 1] = u0 * sn + u1 * cs;
       }
@@ -164,27 +220,33 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
   const int64_t slot = (int64_t)b * out_seq_stride + (out_entry0 ? out_entry0[b] : 0) + j;
   if constexpr (OUT == kOutBf16) {
     uint16_t* o = reinterpret_cast<uint16_t*>(out) + slot * D;
-    if (has0) *reinterpret_cast<uint4*>(o + 8 * lane) = pack8(acc0);
-    if (has1) *reinterpret_cast<uint4*>(o + 8 * (lane + kWave)) = pack8(acc1);
-  } else if constexpr (OUT == kOutFp8) {
-    float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(acc0[e]), fabsf(acc1[e])));
-    amax = wave_max(amax);
-    float s = amax / 448.0f;
-    if (amax == 0.f) s = 1.0f;
-    uint8_t* o = reinterpret_cast<uint8_t*>(out) + slot * D;
-    if (has0) {
-      uint2 wv;
-      wv.x = f32x4_to_fp8(acc0[0] / s, acc0[1] / s, acc0[2] / s, acc0[3] / s);
-      wv.y = f32x4_to_fp8(acc0[4] / s, acc0[5] / s, acc0[6] / s, acc0[7] / s);
-      *reinterpret_cast<uint2*>(o + 8 * lane) = wv;
+    for (int h = 0; h < 2; ++h) {
+      const double* acc = h ? acc1 : acc0;
+      uint4 pk;
+      pk.x = f64_to_bf16_rne(acc[0]) | (f64_to_bf16_rne(acc[1]) << 16);
+      pk.y = f64_to_bf16_rne(acc[2]) | (f64_to_bf16_rne(acc[3]) << 16);
+      pk.z = f64_to_bf16_rne(acc[4]) | (f64_to_bf16_rne(acc[5]) << 16);
+      pk.w = f64_to_bf16_rne(acc[6]) | (f64_to_bf16_rne(acc[7]) << 16);
+      if (h ? has1 : has0) *reinterpret_cast<uint4*>(o + 8 * (lane + h * kWave)) = pk;
     }
-    if (has1) {
+  } else if constexpr (OUT == kOutFp8) {
+    double amax = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmax(amax, fmax(fabs(acc0[e]), fabs(acc1[e])));
+    amax = wave_max_d(amax);
+    const float s = amax == 0.0 ? 1.0f : (float)(amax / 448.0);  // fp32 scale, rounded from fp64
+    const double sd = (double)s;
+    uint8_t* o = reinterpret_cast<uint8_t*>(out) + slot * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const double* acc = h ? acc1 : acc0;
       uint2 wv;
-      wv.x = f32x4_to_fp8(acc1[0] / s, acc1[1] / s, acc1[2] / s, acc1[3] / s);
-      wv.y = f32x4_to_fp8(acc1[4] / s, acc1[5] / s, acc1[6] / s, acc1[7] / s);
-      *reinterpret_cast<uint2*>(o + 8 * (lane + kWave)) = wv;
+      wv.x = f64_to_e4m3(acc[0] / sd) | (f64_to_e4m3(acc[1] / sd) << 8) | (f64_to_e4m3(acc[2] / sd) << 16) |
+             (f64_to_e4m3(acc[3] / sd) << 24);
+      wv.y = f64_to_e4m3(acc[4] / sd) | (f64_to_e4m3(acc[5] / sd) << 8) | (f64_to_e4m3(acc[6] / sd) << 16) |
+             (f64_to_e4m3(acc[7] / sd) << 24);
+      if (h ? has1 : has0) *reinterpret_cast<uint2*>(o + 8 * (lane + h * kWave)) = wv;
     }
     if (lane == 0) reinterpret_cast<float*>(out_scale)[slot] = s;
   } else {
@@ -195,20 +257,18 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = lane + h * kWave;
-      const float* acc = h ? acc1 : acc0;
-      float amax = 0.f;
+      const double* acc = h ? acc1 : acc0;
+      double amax = 0.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(acc[e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-      int E = -127;
-      if (amax > 0.f) E = min(127, max(-127, (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 2));
-      const float inv_s = __builtin_amdgcn_ldexpf(1.0f, -E);
-      uint32_t w = 0;
+      for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(acc[e]));
+      amax = fmax(amax, __shfl_xor(amax, 1, kWave));
+      amax = fmax(amax, __shfl_xor(amax, 2, kWave));
+      const int E = mx_block_exp(amax, -127, 127);
+      uint32_t wv = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w |= e2m1_code(acc[e] * inv_s) << (4 * e);
+      for (int e = 0; e < 8; ++e) wv |= e2m1_code_d(ldexp(acc[e], -E)) << (4 * e);
       if (c < cpr) {
-        *reinterpret_cast<uint32_t*>(o + 4 * c) = w;
+        *reinterpret_cast<uint32_t*>(o + 4 * c) = wv;
         if ((c & 3) == 0) os[c >> 2] = (uint8_t)(E + 127);
       }
     }
@@ -239,12 +299,12 @@ __global__ __launch_bounds__(256) void ring_append_kernel(const uint16_t* __rest
   if (c0 == 0 && z_new) ring_z[slot] = z;
 }
 
-// Indexer keys of the entries: the per-token keys pooled with the entries' softmax weights, then
-// MXFP4 (OCP MX v1.0: per 32 values E = floor(log2 amax) - 2 within [-3, 0], elements rounded to
-// the nearest e2m1 magnitude with ties to the even code, saturating at 6). One wavefront per
-// entry; lane l holds key dims [V l, V l + V), so one MX block is 32 / V adjacent lanes.
+// Indexer keys of the entries: the per-token keys pooled with the entries' softmax weights (in
+// fp64, like the entries), then MXFP4 (OCP MX v1.0: per 32 values E = floor(log2 amax) - 2
+// within [-3, 0], elements rounded to the nearest e2m1 magnitude with ties to the even code,
+// saturating at 6). One wavefront per entry; lane l holds key dims [V l, V l + V), so one MX
+// block is 32 / V adjacent lanes.
 constexpr int kMxEMin = -3, kMxEMax = 0;
-
 
 template <int V>
 __global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
@@ -253,24 +313,21 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
     const int32_t* __restrict__ out_entry0) {
   constexpr int D_I = 64 * V;
   constexpr int LPB = 32 / V;  // lanes per MX block
+  __shared__ double wsh[kCompressWaves][kMaxBlock];
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + (threadIdx.x >> 6));
+  const int wl = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kCompressWaves + wl);
   if (w >= B * n_ent) return;
   const int b = w / n_ent;
   const int j = w - b * n_ent;
   const uint16_t* xb = xk + (int64_t)b * xk_seq_stride + (int64_t)j * m * D_I;
   const float* zb = z + (int64_t)b * z_seq_stride + (int64_t)j * m;
-  float zmax = -INFINITY;
-  for (int i = lane; i < m; i += kWave) zmax = fmaxf(zmax, zb[i]);
-  zmax = wave_max(zmax);
-  float zsum = 0.f;
-  for (int i = lane; i < m; i += kWave) zsum += expf(zb[i] - zmax);
-  zsum = wave_sum(zsum);
-  const float inv = 1.0f / zsum;
+  double* wt = wsh[wl];
+  pool_weights(zb, m, wt);
 
-  float acc[V];
+  double acc[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int v = 0; v < V; ++v) acc[v] = 0.0;
   for (int i = 0; i < m; i += kUnroll) {  // kUnroll rows in flight; the last block repeats a row with weight 0
     uint16_t r[kUnroll][V];
 #pragma unroll
@@ -281,23 +338,21 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void index_key_pool_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const float a = i + u < m ? expf(zb[min(i + u, m - 1)] - zmax) * inv : 0.f;
+      const double a = i + u < m ? wt[i + u] : 0.0;
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] = fmaf(a, __uint_as_float((uint32_t)r[u][v] << 16), acc[v]);
+      for (int v = 0; v < V; ++v) acc[v] = fma(a, (double)__uint_as_float((uint32_t)r[u][v] << 16), acc[v]);
     }
   }
   // block exponent
-  float amax = 0.f;
+  double amax = 0.0;
 #pragma unroll
-  for (int v = 0; v < V; ++v) amax = fmaxf(amax, fabsf(acc[v]));
+  for (int v = 0; v < V; ++v) amax = fmax(amax, fabs(acc[v]));
 #pragma unroll
-  for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  int E = kMxEMin;
-  if (amax > 0.f) E = min(kMxEMax, max(kMxEMin, (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 2));
-  const float inv_s = __builtin_amdgcn_ldexpf(1.0f, -E);
+  for (int o = 1; o < LPB; o <<= 1) amax = fmax(amax, __shfl_xor(amax, o, kWave));
+  const int E = mx_block_exp(amax, kMxEMin, kMxEMax);
   uint32_t codes[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) codes[v] = e2m1_code(acc[v] * inv_s);
+  for (int v = 0; v < V; ++v) codes[v] = e2m1_code_d(ldexp(acc[v], -E));
   const int64_t slot = (int64_t)b * out_seq_stride + (out_entry0 ? out_entry0[b] : 0) + j;
   uint8_t* ko = out_ik + slot * (D_I / 2);
   if constexpr (V == 1) {  // pairs of lanes form a byte

@@ -164,7 +164,7 @@ class LayerPair:
         self.ws_att = {}
         for name in ("csa", "hca"):
             n = native.hybrid_attn_decode_workspace_size(B * Td, s.H, s.d_v, self.cap[name], s.k, s.W, name == "hca")
-            self.ws_att[name] = torch.empty(max(16, n), dtype=torch.uint8, device=device)
+            self.ws_att[name] = torch.zeros(max(16, n), dtype=torch.uint8, device=device)
         # initial state, for restoring between runs
         self._init = {n: (self.ring[n].clone(), self.ringz[n].clone()) for n in ("csa", "hca")}
         if s.derive_keys:  # the loop overwrites the keys of new entries

@@ -34,7 +34,7 @@ class CsaPrefill:
         self.lse = torch.empty((L, w.H), dtype=torch.float32, device=device)
         self.ws_idx = torch.empty(max(16, native.csa_index_topk_workspace_size(1, L, N, w.H_I, w.D_I, w.k)),
                                   dtype=torch.uint8, device=device)
-        self.ws_att = torch.empty(max(16, native.hybrid_attn_prefill_workspace_size(L, w.H, w.d_v, N, w.k, w.W, 0)),
+        self.ws_att = torch.zeros(max(16, native.hybrid_attn_prefill_workspace_size(L, w.H, w.d_v, N, w.k, w.W, 0)),
                                   dtype=torch.uint8, device=device)
 
     def compress(self, stream=None):

@@ -70,7 +70,9 @@ CSKV_API const char* cskv_last_error(void);
  *
  * For each sequence b and block j in [0, n_tok/m):
  *   a_i  = softmax_i(z[b, j*m + i]),  i = 0..m-1
- *   e    = sum_i a_i * x[b, j*m + i, :]                  (fp32 accumulation)
+ *   e    = sum_i a_i * x[b, j*m + i, :]
+ *   (every step through the rotation below is evaluated in fp64 and the stored value is
+ *   rounded once, from fp64, to its format)
  *   e    = e / sqrt(mean_d(e_d^2) + rms_eps)   if rms_eps > 0 (unit-gain RMSNorm
  *          of the entry: the pages' "KV normalisation", section "두 가지 압축
  *          전략: CSA 및 HCA"; rms_eps == 0 leaves e as pooled)
@@ -120,7 +122,7 @@ CSKV_API int hca_compress(const uint16_t* x, int64_t x_seq_stride, const float* 
  *
  * For each sequence b and block j in [0, n_tok/m):
  *   a_i = softmax_i(z[b, j*m + i])                   (the weights of csa_compress)
- *   k   = sum_i a_i * xk[b, j*m + i, :]              (fp32 accumulation)
+ *   k   = sum_i a_i * xk[b, j*m + i, :]              (evaluated in fp64)
  *   per 32 values of k: E = floor(log2 max|block|) - 2, limited to [-3, 0]
  *     (an all-zero block takes -3); element code = nearest e2m1 magnitude of
  *     |v| / 2^E (ties to the even code, saturating at 6), sign bit 3 set for
@@ -197,9 +199,13 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * or in [0, n_entries[r])) or NULL; win [B, R, D] bf16 rings of raw tokens (R = 0 means
  * R = W; a T-token step needs R >= W + T - 1 so that no query's window has been
  * overwritten); out [B*T, H, d_v] bf16; out_lse [B*T, H] fp32 or NULL; ws of at least
- * hybrid_attn_decode_workspace_size(B*T, ...) bytes.
+ * hybrid_attn_decode_workspace_size(B*T, ...) bytes (none when that size is 0). The workspace
+ * starts with the counters of the key-split merge: they must be zero before the first call
+ * that uses the workspace (allocate it zeroed, outside any captured graph), and every call
+ * leaves them zero. Calls sharing a workspace must not run concurrently.
  * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
- * d_rope % 8 == 0, d_rope <= min(D, 128), 1 <= H <= 128, 0 <= W <= R, T >= 1,
+ * d_rope % 8 == 0, d_rope <= min(D, 64), 1 <= H <= 128, W >= 0, T >= 1, R >= W + T - 1 when
+ * W > 0 (CSKV_EINVAL otherwise; with R = 0 a draft of T > 1 tokens is refused),
  * W + k or W + N_cap fits int32, q_rms_eps finite and >= 0.
  */
 CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
@@ -219,7 +225,8 @@ CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_c
  *
  * q [T, H, D] bf16; ckv / ckv_scale as in decode with N entries;
  * topk_idx [T, k] or NULL; x [T, D] bf16 raw tokens of the prompt;
- * out [T, H, d_v] bf16; out_lse [T, H] fp32 or NULL.
+ * out [T, H, d_v] bf16; out_lse [T, H] fp32 or NULL; ws as in decode (zeroed before its first
+ * use, left zeroed by every call).
  * Requirements as in decode, plus m >= 1.
  */
 CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,

@@ -36,9 +36,18 @@ def scores(iq, iq_scale, ik, ik_scale, n_valid, head_w=None):
         assert spread <= 30, "MXFP4 scale spread too wide for an exact fp64 evaluation"
     q = formats.mxfp4_to_f64(iq, iq_scale)      # [T, H, D]
     k = formats.mxfp4_to_f64(ik, ik_scale)      # [N, D]
+    return scores_decoded(q, k, n_valid, head_w)
+
+
+def scores_decoded(q, k, n_valid, head_w=None):
+    """The same scores from decoded (exact fp64) MXFP4 values: q [T, H_I, D_I], k [N, D_I].
+
+    Callers that score many queries against one key set decode the keys once. The dot products
+    are one matrix product (every product and partial sum is a dyadic rational that fp64 holds
+    exactly, so the summation order does not change the result)."""
     T, H, D = q.shape
     N = k.shape[0]
-    dots = np.einsum("thd,nd->thn", q, k)       # exact: dyadic terms, fp64 has room
+    dots = (q.reshape(T * H, D) @ k.T).reshape(T, H, N)
     relu = np.maximum(dots, 0.0)
     w = np.ones((T, H)) if head_w is None else np.asarray(head_w, dtype=np.float64)
     s = np.einsum("th,thn->tn", w, relu)

@@ -17,11 +17,16 @@ def topk(scores, k):
     idx = np.full((T, k), -1, dtype=np.int32)
     sc = np.full((T, k), -np.inf, dtype=np.float32)
     for t in range(T):
-        row = scores[t]
+        row = scores[t] + 0.0
         vis = np.nonzero(np.isfinite(row))[0]
         if vis.size == 0:
             continue
-        order = np.lexsort((vis, -(row[vis] + 0.0)))   # primary: score desc; secondary: index asc
+        if vis.size > k:
+            # the first k entries in (score desc, index asc) order all score at least the k-th
+            # largest visible score, so only those entries need sorting
+            kth = np.partition(row[vis], vis.size - k)[vis.size - k]
+            vis = vis[row[vis] >= kth]
+        order = np.lexsort((vis, -row[vis]))   # primary: score desc; secondary: index asc
         take = vis[order[:k]]
         idx[t, :take.size] = take
         sc[t, :take.size] = row[take]

@@ -25,7 +25,12 @@ def down(t):
 
 
 def poisoned(shape, dtype):
-    """Output buffer filled with 0xFF bytes so unwritten elements show up (NaN for floats, -1 for ints)."""
+    """Output buffer holding a value no kernel writes, so unwritten elements show up: all-ones bytes
+    for floats and bf16 bits (NaN) and for bytes, 0x5A5A5A5A for int32 (not -1, the top-k pad, and
+    larger than any entry index here)."""
     t = torch.empty(shape, dtype=dtype, device=DEV)
-    t.view(torch.uint8).fill_(0xFF)
+    if dtype == torch.int32:
+        t.fill_(0x5A5A5A5A)
+    else:
+        t.view(torch.uint8).fill_(0xFF)
     return t

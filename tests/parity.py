@@ -82,31 +82,37 @@ def _ulp(v, p, emin):
     return 2.0 ** (np.floor(np.log2(v)) - (p - 1))
 
 
-def pool_error_bound(mag, m):
-    """Bound on |fp32 pooled value - exact|: (m + 10) * 2^-24 * sum_i a_i |x_i| (RoPE pairs summed).
+# Relative rounding unit of the GPU's compression arithmetic. The kernels evaluate the pooling
+# weights, the pooled sums, the RMSNorm factor and the rotation in fp64 (unit 2^-53); 2^-50
+# leaves room for the few roundings of the library functions (exp, sin, cos, sqrt).
+EVAL_UNIT = 2.0 ** -50
 
-    A sum of m fp32 products a_i*x_i carries at most about m units of 2^-24 of
-    sum|a_i x_i|; the a_i (fp32 exp and divide) and the fp32 rotation add a few
-    more units; 10 covers them.
+
+def pool_error_bound(mag, m, unit=EVAL_UNIT):
+    """Bound on |evaluated pooled value - exact|: (m + 10) * unit * sum_i a_i |x_i| (RoPE pairs
+    summed).
+
+    A sum of m products a_i*x_i carries at most about m units of sum|a_i x_i|; the a_i (exp and
+    divide) and the rotation add a few more units; 10 covers them.
     """
-    return (m + 10) * 2.0 ** -24 * mag
+    return (m + 10) * unit * mag
 
 
-def rms_error_bound(pooled, mag, e_exact, m, d_rope, eps):
-    """Bound on |fp32 evaluation - exact| of RMS-normalised, rotated entries.
+def rms_error_bound(pooled, mag, e_exact, m, d_rope, eps, unit=EVAL_UNIT):
+    """Bound on |evaluation - exact| of RMS-normalised, rotated entries.
 
     pooled: the oracle's exact unrotated pooled rows [n, D]; mag as for pool_error_bound;
     e_exact: the normalised rotated rows. With d the pooling bound and r = 1/sqrt(mean(v^2)
-    + eps), the fp32 factor is within r * delta of r, delta = sum|v| d / sum v^2 + (D + 8)
-    2^-24 (sum of squares, square root, division), so an element is off by at most
+    + eps), the evaluated factor is within r * delta of r, delta = sum|v| d / sum v^2 + (D + 8)
+    unit (sum of squares, square root, division), so an element is off by at most
     r d + delta |e| (rotated dims: the pair's |e| summed).
     """
     v = np.asarray(pooled, dtype=np.float64)
     D = v.shape[-1]
-    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m)
+    d = pool_error_bound(np.asarray(mag, dtype=np.float64), m, unit)
     r = 1.0 / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
     delta = (np.abs(v) * d).sum(axis=-1, keepdims=True) / np.maximum((v * v).sum(axis=-1, keepdims=True), 1e-300) \
-        + (D + 8) * 2.0 ** -24
+        + (D + 8) * unit
     ae = np.abs(np.asarray(e_exact, dtype=np.float64))
     if d_rope:
         rot = ae[..., D - d_rope:].reshape(ae.shape[:-1] + (d_rope // 2, 2)).sum(axis=-1)
@@ -115,7 +121,7 @@ def rms_error_bound(pooled, mag, e_exact, m, d_rope, eps):
     return r * d + delta * ae
 
 
-def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_frac=1e-2, d=None):
+def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_frac=1e-3, d=None):
     """bf16 entries: |got - e| <= half a bf16 ulp of (|e| + d) + d, d = pool_error_bound.
 
     e_exact: the oracle's unrounded fp64 entries; mag: the oracle's pooling of |x|
@@ -136,7 +142,7 @@ def compress_bf16_close(got_bits, e_exact, mag, m, what="compress bf16", max_fra
         raise ParityError(f"{what}: {frac:.2e} of elements round differently from the oracle (> {max_frac})")
 
 
-def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8", max_frac=1e-2, d=None):
+def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8", max_frac=1e-3, d=None):
     """fp8 entries with per-entry scale s = max|e|/448.
 
     Scale: relative error <= d(amax)/amax + 2^-22. Elements: |code*s - e| <= half an
@@ -167,11 +173,11 @@ def compress_fp8_close(got_codes, got_scale, e_exact, mag, m, what="compress fp8
         raise ParityError(f"{what}: {frac:.2e} of codes differ from the oracle's (> {max_frac})")
 
 
-def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_frac=1e-2,
+def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_frac=1e-3,
                 e_range=(formats.MX_E_MIN, formats.MX_E_MAX), d=None):
-    """MXFP4 keys from an fp32 pooling vs the exact fp64 pooled keys k_exact [..., D].
+    """MXFP4 values from the GPU's pooling vs the exact fp64 pooled values k_exact [..., D].
 
-    With d = pool_error_bound(mag, m) the bound on |fp32 pooled - exact|: each block exponent is
+    With d = pool_error_bound(mag, m) the bound on |evaluated pooled - exact|: each block exponent is
     the one of some value within d of the block maximum, and each code lies between the codes of
     (v - d) and (v + d) under that exponent; at most max_frac of the codes differ from the
     oracle's own encoding (differences only where v is within d of a rounding midpoint).
@@ -182,7 +188,7 @@ def mxfp4_close(got_packed, got_scale, k_exact, mag, m, what="mxfp4 keys", max_f
     gs = np.asarray(got_scale).astype(np.int64)
     kb = k.reshape(k.shape[:-1] + (D // 32, 32))
     db = d.reshape(kb.shape)
-    amax_lo = np.maximum(np.abs(kb) - db, 0.0).max(axis=-1)   # the fp32 block maximum lies in [lo, hi]
+    amax_lo = np.maximum(np.abs(kb) - db, 0.0).max(axis=-1)   # the evaluated block maximum lies in [lo, hi]
     amax_hi = (np.abs(kb) + db).max(axis=-1)
     _, s_lo = formats.f64_to_mxfp4(np.repeat(amax_lo, 32, axis=-1).reshape(k.shape), *e_range)
     _, s_hi = formats.f64_to_mxfp4(np.repeat(amax_hi, 32, axis=-1).reshape(k.shape), *e_range)

@@ -103,6 +103,8 @@ def test_attention_validation():
     assert dec(eps=-1.0) == -1
     assert dec(T=0) == -1
     assert dec(R=100) == -1                  # ring smaller than the window
+    assert dec(T=2) == -1                    # a 2-token draft needs R >= W + 1 (R = 0 means R = W)
+    assert dec(T=3, R=129) == -1             # ... and a 3-token one R >= W + 2
     assert dec(eps=float("nan")) == -1
     assert L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) > 0
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa

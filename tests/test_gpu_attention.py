@@ -23,7 +23,7 @@ def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, 
     B = q.shape[0]
     N_cap = ckv.shape[1]
     wsn = native.hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, topk is None)
-    ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((B, H, d_v), torch.int16)
     lse = poisoned((B, H), torch.float32)
     dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
@@ -238,8 +238,10 @@ def test_decode_c1_end_to_end():
     parity.lse_close(down(lse), l[None])
 
 
-def test_decode_c3_full_size_sampled():
-    """HCA decode at 1M context: GPU-compressed fp8 cache; one sequence checked against the oracle's chain."""
+def test_decode_c3_gpu_compressed_sequences():
+    """HCA decode at 1M context on the GPU-compressed fp8 cache: four sequences (the first, the last
+    and two between) checked against the oracle's own chain (compression of every block of the
+    sequence, then attention)."""
     w = configs.C3
     say("decode", w.name)
     n = w.L // w.m
@@ -256,21 +258,41 @@ def test_decode_c3_full_size_sampled():
     out, lse = run_decode(q, up(np.full(w.B, t, np.int64)), ckv, sc, "fp8", up(np.full(w.B, n, np.int32)), None, 0,
                           ring, w.W, w.H, w.D, w.d_rope, w.d_v, w.softmax_scale)
     oh, lh = down(out), down(lse)
-    b = 11
-    codes = np.empty((n, w.D), np.uint8)
-    scales = np.empty(n, np.float32)
-    step = 256
-    for j0 in range(0, n, step):
-        xs = x[b, j0 * w.m:(j0 + step) * w.m].cpu().numpy().view(np.uint16)
-        zs = z[b, j0 * w.m:(j0 + step) * w.m].cpu().numpy()
-        _, c, s = ocomp.compress(xs, zs, j0 * w.m, w.m, w.d_rope, w.rope_base, "fp8")
-        codes[j0:j0 + step], scales[j0:j0 + step] = c, s
-    ring_h = down(ring)[b].view(np.uint16)
-    o, l = oatt.decode_one(down(q)[b].view(np.uint16), t, oatt.Entries(codes, scales, "fp8"), n, None, ring_h, w.W,
-                           w.d_rope, w.d_v, w.rope_base, w.softmax_scale)
-    parity.attn_close(oh[b], o)
-    parity.lse_close(lh[b], l)
+    for b in (0, 5, 11, w.B - 1):
+        codes = np.empty((n, w.D), np.uint8)
+        scales = np.empty(n, np.float32)
+        step = 256
+        for j0 in range(0, n, step):
+            xs = x[b, j0 * w.m:(j0 + step) * w.m].cpu().numpy().view(np.uint16)
+            zs = z[b, j0 * w.m:(j0 + step) * w.m].cpu().numpy()
+            _, c, s = ocomp.compress(xs, zs, j0 * w.m, w.m, w.d_rope, w.rope_base, "fp8")
+            codes[j0:j0 + step], scales[j0:j0 + step] = c, s
+        ring_h = down(ring)[b].view(np.uint16)
+        o, l = oatt.decode_one(down(q)[b].view(np.uint16), t, oatt.Entries(codes, scales, "fp8"), n, None, ring_h,
+                               w.W, w.d_rope, w.d_v, w.rope_base, w.softmax_scale)
+        parity.attn_close(oh[b], o, f"c3 sequence {b}")
+        parity.lse_close(lh[b], l, None, f"c3 lse sequence {b}")
+        say("c3 chain checked, sequence", b)
     del x
+
+
+def test_decode_c3_all_sequences():
+    """HCA decode at the full 1M-context shape (B=16, 8192 fp8 entries each, window 128, 64 heads):
+    the whole output tensor against the oracle, on caches drawn directly from the generator."""
+    w = configs.C3
+    say("decode", w.name, "generated caches")
+    n = w.L // w.m
+    t = w.L - 1
+    q = synth.normal_bf16_bits((w.B, w.H, w.D), w.sigma, synth.seed_of(1, w.wid, 2), DEV)
+    ckv, sc = synth.fp8_rows_normal((w.B, n, w.D), w.sigma, synth.seed_of(1, w.wid, 3), DEV)
+    ring = synth.normal_bf16_bits((w.B, w.W, w.D), w.sigma, synth.seed_of(1, w.wid, 4), DEV)
+    nent = np.full(w.B, n, np.int32)
+    out, lse = run_decode(q, up(np.full(w.B, t, np.int64)), ckv, sc, "fp8", up(nent), None, 0, ring, w.W, w.H, w.D,
+                          w.d_rope, w.d_v, w.softmax_scale)
+    o_ref, l_ref, bnd = oracle_decode(down(q).view(np.uint16), np.full(w.B, t), down(ckv), down(sc), "fp8", nent,
+                                      None, down(ring).view(np.uint16), w.W, w.d_rope, w.d_v, w.softmax_scale)
+    parity.attn_close(down(out), o_ref, "c3 all sequences")
+    parity.lse_close(down(lse), l_ref, bnd, "c3 all sequences lse")
 
 
 PREFILL = [
@@ -308,7 +330,7 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype):
             tk[r, :len(sel)] = sel
         topk = up(tk)
     wsn = native.hybrid_attn_prefill_workspace_size(T, H, d_v, N, k, W, dense)
-    ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((T, H, d_v), torch.int16)
     lse = poisoned((T, H), torch.float32)
     dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]

@@ -57,7 +57,7 @@ def test_compress_small_matches_oracle(m, D, d_rope, dtype):
     (4, 576, 64, "fp8", 1e-6), (128, 576, 64, "fp8", 1e-6), (4, 128, 64, "bf16", 1e-6), (13, 64, 16, "bf16", 0.5),
 ])
 def test_compress_rms_norm_matches_oracle(m, D, d_rope, dtype, eps):
-    """Unit-gain RMSNorm of each pooled entry (rms_eps > 0), within the fp32 normalisation bound."""
+    """Unit-gain RMSNorm of each pooled entry (rms_eps > 0), within the normalisation bound."""
     say("compress rms", m, D, d_rope, dtype, eps)
     B, nblk = 2, 21
     n_tok = nblk * m
@@ -83,7 +83,7 @@ def test_compress_rms_norm_matches_oracle(m, D, d_rope, dtype, eps):
                                             (4, 576, 64, 1e-6)])
 def test_compress_mxfp4_matches_oracle(m, D, d_rope, eps):
     """MXFP4 entries (OCP: per-32 E8M0 exponent over the whole range, nearest e2m1 with ties to
-    even) from the fp32 pooling: exponents and codes within the pooling bound of the exact entry."""
+    even) from the GPU's pooling: exponents and codes within the pooling bound of the exact entry."""
     say("compress mxfp4", m, D, d_rope, eps)
     B, nblk = 3, 29
     n_tok = nblk * m
@@ -179,8 +179,8 @@ def test_ring_append_writes_slot_pos_mod_w():
 
 @pytest.mark.parametrize("m,D_I", [(4, 128), (128, 128), (1, 64), (13, 256), (4, 512)])
 def test_index_key_pool_matches_oracle(m, D_I):
-    """Pooled MXFP4 indexer keys: every block exponent and code within the fp32 pooling bound of
-    the oracle's, and (nearly) all codes equal; entry slots offset per sequence."""
+    """Pooled MXFP4 indexer keys: every block exponent and code within the pooling bound of the
+    oracle's, and (nearly) all codes equal; entry slots offset per sequence."""
     say("index key pool", m, D_I)
     B, nblk = 3, 37
     n_tok = nblk * m
@@ -203,8 +203,8 @@ def test_index_key_pool_matches_oracle(m, D_I):
 
 
 def test_index_key_pool_exact_dyadic_inputs_bit_exact():
-    """Equal logits (weights exactly 1/4) and keys on a coarse dyadic grid: the fp32 pooling is
-    exact, so every code and exponent must equal the oracle's, midpoint ties included."""
+    """Equal logits (weights exactly 1/4) and keys on a coarse dyadic grid: the pooling is exact,
+    so every code and exponent must equal the oracle's, midpoint ties included."""
     say("index key pool exact")
     B, m, D_I, nblk = 2, 4, 128, 50
     rng = np.random.default_rng(5)

@@ -44,13 +44,13 @@ def lse_bounds(spec, lay, t, q, idx):
 
 def check_mxfp4_entries(g_codes, g_scales, o_codes, o_scales, what):
     """MXFP4 entries of the loop against the oracle's: exponents within one (rarely different),
-    codes within one e2m1 step, at most 1% of either different."""
+    codes within one e2m1 step, at most 1e-3 of either different."""
     from oracle import formats
     ordered = lambda c: np.where(c & 8, -(c & 7), c & 7).astype(np.int64)  # noqa: E731
     d = np.abs(ordered(formats.unpack_fp4(g_codes)) - ordered(formats.unpack_fp4(o_codes)))
     ds = np.abs(g_scales.astype(np.int64) - o_scales.astype(np.int64))
-    assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-2 * max(d.size, 1), f"{what}: mxfp4 codes"
-    assert ds.max(initial=0) <= 1 and np.count_nonzero(ds) <= 1e-2 * max(ds.size, 1), f"{what}: mxfp4 exponents"
+    assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-3 * max(d.size, 1), f"{what}: mxfp4 codes"
+    assert ds.max(initial=0) <= 1 and np.count_nonzero(ds) <= 1e-3 * max(ds.size, 1), f"{what}: mxfp4 exponents"
 
 
 def check_loop(pair, sample_steps):
@@ -90,12 +90,12 @@ def check_loop(pair, sample_steps):
         ordered = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)  # noqa: E731
         d = np.abs(ordered(g_codes) - ordered(o_codes))
         assert d.max(initial=0) <= 1, f"{name}: a new fp8 code differs by {d.max()} steps"
-        assert np.count_nonzero(d) <= 1e-2 * d.size, f"{name}: {np.count_nonzero(d) / d.size:.2e} of codes differ"
+        assert np.count_nonzero(d) <= 1e-3 * d.size, f"{name}: {np.count_nonzero(d) / d.size:.2e} of codes differ"
         gs = pair.scl[name][:, n0:n_end].cpu().numpy().astype(np.float64)
         os_ = layers[name].ckv_scale[:, n0:n_end].astype(np.float64)
-        rtol = 1e-4 if spec.rms_eps > 0 else 1e-5   # normalised entries: the fp32 factor's own error
-        assert np.all(np.abs(gs - os_) <= rtol * os_), f"{name}: new entry scales differ"
-    if spec.derive_keys:  # derived indexer keys of the new entries (exact pooling: identical bytes)
+        # both sides round the same fp64 value amax / 448 to fp32
+        assert np.all(np.abs(gs - os_) <= 2.0 ** -22 * os_), f"{name}: new entry scales differ"
+    if spec.derive_keys:  # derived indexer keys of the new entries (fp64 pooling: identical bytes)
         n0, n_end = spec.L // spec.m_csa, (spec.L + spec.steps) // spec.m_csa
         assert np.array_equal(pair.ik[:, n0:n_end].cpu().numpy(), layers["csa"].ik[:, n0:n_end]), "derived keys"
         assert np.array_equal(pair.iks[:, n0:n_end].cpu().numpy(), layers["csa"].ik_scale[:, n0:n_end]), \
@@ -113,11 +113,14 @@ def test_hybrid_loop_small_every_step():
     assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
 
 
-def test_hybrid_loop_derived_keys_every_step():
-    """New entries' indexer keys pooled from per-token keys on the GPU (dyadic keys, uniform
-    weights: the pooling is exact, so keys and top-k must match the oracle's bit for bit)."""
+@pytest.mark.parametrize("dyadic", [True, False])
+def test_hybrid_loop_derived_keys_every_step(dyadic):
+    """New entries' indexer keys pooled from per-token keys on the GPU, keys and top-k against the
+    oracle's bit for bit. dyadic: keys on a 1/16 grid with uniform weights (the pooling is exact,
+    ties at e2m1 midpoints included); otherwise N(0,1) keys and logits (the GPU pools in fp64 and
+    encodes from fp64, so its codes are the oracle's)."""
     spec = hybrid.LayerPairSpec(B=2, L=2048, steps=300, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=128,
-                                wid=57, derive_keys=True, dyadic_keys=True)
+                                wid=57, derive_keys=True, dyadic_keys=dyadic)
     say("hybrid derived keys", spec)
     pair = hybrid.LayerPair(spec)
     pair.run(0, spec.steps)
@@ -125,16 +128,17 @@ def test_hybrid_loop_derived_keys_every_step():
     assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
 
 
-def test_hybrid_loop_rms_norm_every_step():
+@pytest.mark.parametrize("eps", [1e-6, 0.01])
+def test_hybrid_loop_rms_norm_every_step(eps):
     """Entries and queries RMS-normalised (unit gain) in the loop: new entries' fp8 codes within one
-    step of the oracle's and every step's top-k and attention within the parity bounds. eps = 0.01 is
-    of the order of the inputs' mean square (1/D), so the factor still varies per vector (about 7x
-    to 9x here) while the logits stay as spread as in the other loop tests: with eps -> 0 every
-    entry becomes unit-RMS and the occasional one-step difference between the GPU's and the
-    oracle's own fp8 codes of an entry (both round their own fp32/fp64 values) shows in the output
-    of a sharply peaked softmax. The kernels are checked at eps = 1e-6 by the per-call tests."""
+    step of the oracle's and every step's top-k and attention within the parity bounds. eps = 1e-6
+    is the operating value (every entry and query becomes unit-RMS: the sharpest softmax of the
+    loop tests); eps = 0.01 is of the order of the inputs' mean square (1/D), so the factor still
+    varies per vector. The GPU pools and normalises in fp64 and rounds to fp8 from fp64, so its new
+    entries carry the oracle's codes; an independently rounded cache (one e4m3 step apart in a
+    dominant entry) can move this softmax's output by more than the tolerance."""
     spec = hybrid.LayerPairSpec(B=2, L=2048, steps=260, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
-                                wid=58, rms_eps=0.01)
+                                wid=58, rms_eps=eps)
     say("hybrid rms", spec)
     pair = hybrid.LayerPair(spec)
     pair.run(0, spec.steps)
@@ -180,14 +184,33 @@ def test_hybrid_loop_graph_replays_match_eager():
         assert torch.equal(pair.topk, ref_tk), f"replay {rep}: top-k differs from eager"
 
 
-def test_hybrid_loop_1m_sampled_steps():
-    """The 1M-context pair (B=8, 256 steps): sampled steps against the oracle loop."""
+def test_hybrid_loop_1m():
+    """The 1M-context pair (B=8, 256 steps): the top-k of every step and sequence bit-exact against
+    the oracle's indexer over the same keys, and both layers' attention on sampled steps (block
+    ends of the CSA and HCA layers among them) against the oracle loop."""
+    from oracle import formats
+    from oracle import indexer as oidx
+    from oracle import topk as otopk
+
     spec = hybrid.LayerPairSpec()
     say("hybrid 1M", spec)
     pair = hybrid.LayerPair(spec)
     pair.run(0, spec.steps)
     torch.cuda.synchronize()
-    assert check_loop(pair, {0, 3, 4, 127, 128, 255}) == 12
+    tk = pair.topk.cpu().numpy()
+    ik, iks = pair.ik.cpu().numpy(), pair.iks.cpu().numpy()
+    iq, iqs = pair.iq.cpu().numpy(), pair.iqs.cpu().numpy()
+    nv = pair.nvalid.cpu().numpy()
+    blk = 8
+    for b in range(spec.B):
+        kdec = formats.mxfp4_to_f64(ik[b], iks[b])
+        for s0 in range(0, spec.steps, blk):
+            q = formats.mxfp4_to_f64(iq[s0:s0 + blk, b, 0], iqs[s0:s0 + blk, b, 0])
+            want = otopk.topk(oidx.scores_decoded(q, kdec, nv[s0:s0 + blk, b, 0]), spec.k)[0]
+            parity.topk_exact(tk[s0:s0 + blk, b, 0], want, f"1M top-k sequence {b} steps {s0}..{s0 + blk - 1}")
+        say("hybrid 1M top-k of every step, sequence", b)
+    steps = {0, 1, 3, 4, 5, 126, 127, 128, 129, 252, 255}
+    assert check_loop(pair, steps) == 2 * len(steps)
 
 
 @pytest.mark.parametrize("share", ["reuse", "reindex"])
@@ -282,4 +305,4 @@ def test_hybrid_loop_draft_steps(draft, accept_seed):
         o_ = layers[name].ckv[:, n0:n_end].astype(np.int64)
         ordered = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)  # noqa: E731
         d = np.abs(ordered(g) - ordered(o_))
-        assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-2 * max(d.size, 1), f"{name} entries"
+        assert d.max(initial=0) <= 1 and np.count_nonzero(d) <= 1e-3 * max(d.size, 1), f"{name} entries"

@@ -160,3 +160,45 @@ def test_index_topk_query_blocks(B, T, H_I, D_I, k, N, ties):
         hw = up(rng.choice(np.array([1.0, -1.0, 0.5, 2.0], np.float32), (B, T, H_I)))
     oi, os_ = run_index(iq, iqs, ik, iks, up(nvh), k, hw)
     check_against_oracle(iq, iqs, ik, iks, up(nvh), k, oi, os_, head_w=hw)
+
+
+@pytest.mark.parametrize("B,T,N,k,ties", [(1, 300, 1024, 128, False), (1, 300, 1024, 128, True),
+                                          (2, 150, 1000, 128, False)])
+def test_index_topk_query_blocks_single_chunk_k128(B, T, N, k, ties):
+    """Few query blocks over at most 1024 entries: the query-block kernel takes one entry chunk and
+    writes each row's ordered top-k itself (no merge kernel), after many reductions of the per-query
+    candidate buffers (k = 128 of up to 1024 visible entries). Every row bit-exact."""
+    say("index query blocks single chunk", B, T, N, k, ties)
+    rng = np.random.default_rng(T + N)
+    iq, iqs = synth.mxfp4_normal((B, T, 8, 128), 161, DEV)
+    if ties:
+        base, bsc = synth.mxfp4_normal((4, 128), 162, DEV)
+        pick = torch.from_numpy(rng.integers(0, 4, (B, N))).to(DEV)
+        ik, iks = base[pick].contiguous(), bsc[pick].contiguous()
+    else:
+        ik, iks = synth.mxfp4_normal((B, N, 128), 163, DEV)
+    nvh = np.minimum(N, (np.arange(T)[None, :] * 7 + 3 + 11 * np.arange(B)[:, None])).astype(np.int32)
+    nvh[:, :3] = [0, 1, k]
+    oi, os_ = run_index(iq, iqs, ik, iks, up(nvh), k)
+    check_against_oracle(iq, iqs, ik, iks, up(nvh), k, oi, os_)
+
+
+def test_index_topk_query_blocks_many_rows_single_chunk():
+    """16384 causal queries over 8192 entries: enough query blocks that each takes the whole entry
+    range in one chunk (64 tiles, the c4 prefill's regime at a quarter of its length). 512 rows
+    against the oracle, and every row against the decode kernels (calls of 256 queries)."""
+    say("index query blocks many rows")
+    T, N, k = 16384, 8192, 128
+    iq, iqs = synth.mxfp4_normal((1, T, 8, 128), 171, DEV)
+    ik, iks = synth.mxfp4_normal((1, N, 128), 172, DEV)
+    nvh = ((np.arange(T) + 1) // 2).clip(max=N).astype(np.int32)[None]
+    nv = up(nvh)
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    rows = sorted(set(np.random.default_rng(1).choice(T, 500, replace=False).tolist()) | {0, 1, 2, 255, 256, T - 1})
+    check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, rows=rows)
+    ref, _ = run_index(iq[:, :256], iqs[:, :256], ik, iks, nv[:, :256], k)
+    bad = 0
+    for t0 in range(0, T, 256):
+        r, _ = run_index(iq[:, t0:t0 + 256], iqs[:, t0:t0 + 256], ik, iks, nv[:, t0:t0 + 256], k)
+        bad += int((r[0] != oi[0, t0:t0 + 256]).any(dim=1).sum().item())
+    assert bad == 0, f"{bad} rows differ from the decode kernels"

@@ -1,25 +1,54 @@
 """The CSA prefill pipeline (compress -> causal index + top-k -> attention) on one prompt, at a
-reduced length and at the full 128K-token workload, checked against the oracle on sampled
-positions: top-k bit-exact, the entries those positions select within the compression bound,
-and the attention output / lse of those positions."""
+reduced length and at the full 128K-token workload, checked against the oracle: top-k bit-exact
+on every row of the short prompt and, on the long one, on 4096 seeded rows plus every row below
+640 and every row within 4 of a multiple of 128; every compressed entry within the compression
+bound; the attention output and lse of the same rows. On the long prompt every row's top-k is also
+compared with the decode kernels' top-k (csa_index_topk called with at most 256 queries, the path
+checked against the oracle at the 1M-entry decode shape), so that no row of the query-block
+kernel goes unchecked."""
 import numpy as np
 import pytest
 import torch
 
-from compressed_sparse_kv_03_amd import configs, prefill
+from compressed_sparse_kv_03_amd import configs, native, prefill
 from oracle import attention as oatt
 from oracle import compress as ocomp
+from oracle import formats
 from oracle import indexer as oidx
 from oracle import topk as otopk
 from tests import parity
-from tests.gpu_util import DEV, down, say
+from tests.gpu_util import down, say
 from tests.test_gpu_attention import logit_bound
 
 pytestmark = pytest.mark.gpu
 
+DEV = "cuda:0"
+
+
+def sample_rows(L, seed=0, n_random=4096):
+    """Every row of a short prompt; on a long one a seeded sample plus the rows near the start and
+    around the 128-token boundaries (where windows, blocks and visibility change)."""
+    if L <= 8192:
+        return np.arange(L)
+    rng = np.random.default_rng(seed)
+    t = np.arange(L)
+    near = (t < 640) | (t % 128 <= 4) | (t % 128 >= 124) | (t == L - 1)
+    return np.union1d(rng.choice(L, n_random, replace=False), t[near])
+
+
+def oracle_topk_rows(iqh, iqsh, kdec, rows, m, k, block=64):
+    """The oracle's top-k of the given rows (iqh/iqsh hold those rows), keys decoded once."""
+    out = np.empty((len(rows), k), np.int32)
+    for s in range(0, len(rows), block):
+        r = rows[s:s + block]
+        q = formats.mxfp4_to_f64(iqh[s:s + block], iqsh[s:s + block])
+        sc = oidx.scores_decoded(q, kdec, (r + 1) // m)
+        out[s:s + block] = otopk.topk(sc, k)[0]
+    return out
+
 
 @pytest.mark.parametrize("L", [8192, configs.C4.L])
-def test_prefill_pipeline_sampled(L):
+def test_prefill_pipeline(L):
     w = configs.C4 if L == configs.C4.L else prefill.scaled(configs.C4, L)
     say("prefill pipeline", w.name, L)
     p = prefill.CsaPrefill(w, DEV)
@@ -28,46 +57,57 @@ def test_prefill_pipeline_sampled(L):
     p.attend()
     torch.cuda.synchronize()
     m, N, k, W = w.m, p.N, w.k, w.W
-    rng = np.random.default_rng(L)
-    rows = sorted(set(rng.integers(0, L, 5).tolist()) | {0, m - 1, m, 4 * k + 3, L - 1})
-    rows = [t for t in rows if t < L]
+    rows = sample_rows(L)
+    say("prefill pipeline rows checked", len(rows))
     xh = down(p.x).view(np.uint16)
     zh = down(p.z)[0]
     iqh, iqsh = down(p.iq[0, rows]), down(p.iqs[0, rows])
-    ikh, iksh = down(p.ik)[0], down(p.iks)[0]
+    kdec = formats.mxfp4_to_f64(down(p.ik)[0], down(p.iks)[0])
     oi = down(p.idx[0, rows])
 
-    # 1) indexer: bit-exact top-k of every sampled position
-    want_idx = {}
-    for r, t in enumerate(rows):
-        sc = oidx.scores(iqh[r][None], iqsh[r][None], ikh, iksh, np.array([(t + 1) // m]))
-        idx, _ = otopk.topk(sc, k)
-        parity.topk_exact(oi[r], idx[0], f"top-k t={t}")
-        want_idx[t] = idx[0]
+    # 1) indexer: bit-exact top-k of every checked row
+    want_idx = oracle_topk_rows(iqh, iqsh, kdec, rows, m, k)
+    parity.topk_exact(oi, want_idx, f"prefill top-k L={L}")
+    say("prefill top-k checked", L)
 
-    # 2) compression: the entries those positions select (plus the first and last), from the
-    #    oracle's own blocks
-    need = sorted({int(j) for t in rows for j in want_idx[t] if j >= 0} | {0, N - 1})
+    # 2) compression: every entry against the oracle's own blocks
     ckh = down(p.ckv).view(np.uint16)
     ent_bits = np.zeros((N, w.D), np.uint16)
-    for j in need:
-        xb, zb = xh[j * m:(j + 1) * m], zh[j * m:(j + 1) * m]
-        e, bits, _ = ocomp.compress(xb, zb, j * m, m, w.d_rope, w.rope_base, "bf16")
-        mag = ocomp.magnitude(xb, zb, m, w.d_rope)
-        parity.compress_bf16_close(ckh[j][None], e, mag, m, f"entry {j}")
-        ent_bits[j] = bits[0]
+    step = 4096
+    for j0 in range(0, N, step):
+        j1 = min(N, j0 + step)
+        xb, zb = xh[j0 * m:j1 * m], zh[j0 * m:j1 * m]
+        e, bits, _ = ocomp.compress(xb, zb, j0 * m, m, w.d_rope, w.rope_base, "bf16")
+        parity.compress_bf16_close(ckh[j0:j1], e, ocomp.magnitude(xb, zb, m, w.d_rope), m, f"entries {j0}..{j1}")
+        ent_bits[j0:j1] = bits
 
-    # 3) attention of the sampled positions over the oracle's entries and top-k
+    say("prefill entries checked", L)
+    # 3) attention of the checked rows over the oracle's entries and top-k
     ent = oatt.Entries(ent_bits, None, "bf16")
     qh = down(p.q[rows]).view(np.uint16)
     outs, lses, bnds = [], [], []
     for r, t in enumerate(rows):
-        o, lse = oatt.prefill_one(qh[r], t, 0, ent, m, want_idx[t], xh, W, w.d_rope, w.d_v, w.rope_base,
+        t = int(t)
+        o, lse = oatt.prefill_one(qh[r], t, 0, ent, m, want_idx[r], xh, W, w.d_rope, w.d_v, w.rope_base,
                                   w.softmax_scale)
         wpos = np.arange(max(0, t - W + 1), t + 1)
-        bnds.append(logit_bound(qh[r], t, ent, [j for j in want_idx[t] if j >= 0], xh[wpos], wpos, w.d_rope,
+        bnds.append(logit_bound(qh[r], t, ent, [j for j in want_idx[r] if j >= 0], xh[wpos], wpos, w.d_rope,
                                 w.d_v, w.softmax_scale))
         outs.append(o)
         lses.append(lse)
     parity.attn_close(down(p.out[rows]), np.stack(outs), f"prefill attention L={L}")
     parity.lse_close(down(p.lse[rows]), np.stack(lses), np.stack(bnds), f"prefill lse L={L}")
+    say("prefill attention checked", L)
+
+    # 4) every row's top-k against the decode kernels' (calls of 256 queries)
+    if L > 8192:
+        ws = torch.empty(max(16, native.csa_index_topk_workspace_size(1, 256, N, w.H_I, w.D_I, k)),
+                         dtype=torch.uint8, device=DEV)
+        ref = torch.empty((1, 256, k), dtype=torch.int32, device=DEV)
+        bad = 0
+        for t0 in range(0, L, 256):
+            native.csa_index_topk(p.iq[:, t0:t0 + 256], p.iqs[:, t0:t0 + 256], None, p.ik, p.iks, p.nv[:, t0:t0 + 256],
+                                  1, 256, N, w.H_I, w.D_I, k, ref, None, ws)
+            bad += int((ref[0] != p.idx[0, t0:t0 + 256]).any(dim=1).sum().item())
+        torch.cuda.synchronize()
+        assert bad == 0, f"{bad} rows of the prefill top-k differ from the decode kernels' top-k"

@@ -121,3 +121,29 @@ def test_topk_permutation_and_low_entry_invariance():
         assert set(perm[idx_p[0]].tolist()) == set(idx[0].tolist())
     s2 = np.concatenate([s, np.full((1, 1), s[0, idx[0, -1]] - 1)], axis=1)
     assert np.array_equal(topk.topk(s2, 20)[0], idx)
+
+
+def test_topk_selection_prefilter_keeps_ties_at_the_cut():
+    """Rows longer than k go through a selection of the entries scoring at least the k-th largest
+    score: with few distinct scores the cut falls inside a run of ties, which must be resolved by
+    the lower index exactly as a full sort does (Python sorted over every visible entry)."""
+    rng = np.random.default_rng(16)
+    for T, N, k, levels in ((4, 3000, 128, 3), (3, 700, 1, 2), (2, 129, 128, 1), (5, 4000, 77, 40)):
+        s = rng.integers(0, levels, (T, N)).astype(np.float64)
+        nv = rng.integers(k, N + 1, T)
+        masked = np.where(np.arange(N)[None] < nv[:, None], s, -np.inf)
+        idx, _ = topk.topk(masked, k)
+        for t in range(T):
+            want = sorted(range(nv[t]), key=lambda j: (-s[t, j], j))[:k]
+            assert idx[t].tolist() == want, (T, N, k, levels, t)
+
+
+def test_decoded_scores_match_the_packed_entry_point():
+    rng = np.random.default_rng(17)
+    iq, iqs = rand_mxfp4(rng, (3, 4, 64))
+    ik, iks = rand_mxfp4(rng, (500, 64))
+    hw = rng.choice([1.0, -0.5, 2.0], (3, 4))
+    nv = np.array([500, 17, 0])
+    a = indexer.scores(iq, iqs, ik, iks, nv, hw)
+    b = indexer.scores_decoded(formats.mxfp4_to_f64(iq, iqs), formats.mxfp4_to_f64(ik, iks), nv, hw)
+    assert np.array_equal(a, b)
