@@ -34,9 +34,9 @@
 // MFMA (for entry keys, stored exactly, the query remainder only), so the
 // rotation adds no bf16 rounding to the logits.
 // A query's splits write unnormalised partial outputs with their (max, sum) in
-// fp32; the last split of each (query, head group) to finish (a counter in the
-// workspace, reset by that split) merges them (log-sum-exp merge) and writes
-// the output. One split writes the output directly.
+// fp32 and a second launch merges them (log-sum-exp merge; merging in the last
+// split to finish needs an agent-scope release per workgroup, an L2 write-back
+// that costs more than the launch). One split writes the output directly.
 #include <math.h>
 
 #include "common.cuh"
@@ -55,9 +55,9 @@ constexpr int kTK8 = 64;             // keys per fp8 entry tile
 constexpr int kTK16 = 32;            // keys per bf16 tile
 constexpr int kRB = 2;               // 32-dim blocks holding rotated dims (d_rope <= 64)
 constexpr int kMaxRopePairs = 32;
-constexpr int kMaxSplitKeys = 1024;  // top-k slots staged per split
+constexpr int kMaxSplitKeys = 4096;  // key rows staged per split
 constexpr int kMaxSplits = 64;
-constexpr int kTargetWG = 256;      // workgroups a launch aims at (one per CU)
+constexpr int kTargetWG = 512;      // workgroups a launch aims at (two per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may run ahead of the exponent base
@@ -91,7 +91,6 @@ struct AttnArgs {
   int xcd_map;               // 1: a query's workgroups are issued to one XCD (round-robin dispatch)
   uint16_t* out;             // [nq, H, d_v]
   float* out_lse;            // [nq, H]
-  uint32_t* counters;        // [nq * n_hg] finished splits; zero between calls
   float* part_o;             // [nq, n_hg, n_splits, 16, d_v]
   float* part_ml;            // [nq, n_hg, n_splits, 16, 2]
   double rev_freq[kMaxRopePairs];  // RoPE frequencies base^(-2i/d_rope) / (2 pi), formed on the host in fp64
@@ -193,79 +192,77 @@ struct AttnSmem {
   __align__(16) uint16_t qrh[kHG][2 * kMaxRopePairs];  // rotated query dims: bf16 value
   __align__(16) uint16_t qrl[kHG][2 * kMaxRopePairs];  // and bf16 remainder
   int sidx[kMaxSplitKeys];
-  int last;
 };
 
-// One tile's raw rows in registers: chunk c of the tile (16 bytes of a row; an MX block of 32
-// dims with its exponent byte for MXFP4) goes to thread c mod kNT. Entry tiles and window tiles
-// share the buffer (the first window tile is requested while the last entry tile is computed).
+// One tile's raw rows in registers. Thread t owns row t / TPR of the tile and its 16-byte chunks
+// t % TPR + TPR i (an MX block of 32 dims with its exponent byte for MXFP4), so it looks its row
+// up once and issues its loads from one base address. In a window row, thread j of the row also
+// owns the row's rotated chunk j (d_rope <= 64: at most 8 of them). Entry tiles and window tiles
+// share the registers (the first window tile is requested while the last entry tile is computed).
 template <int KD, int KV>
 struct EntryGeom {
   static constexpr int TK = KV == kKvFp8 ? kTK8 : kTK16;
+  static constexpr int TPR = kNT / TK;  // threads per row
   static constexpr int CPR = KV == kKvFp8 ? KD * 2 : (KV == kKvBf16 ? KD * 4 : KD);  // chunks per row
-  static constexpr int ITERS = (TK * CPR + kNT - 1) / kNT;
+  static constexpr int NC = (CPR + TPR - 1) / TPR;  // chunks per thread
 };
 template <int KD>
 struct WinGeom {
+  static constexpr int TPR = kNT / kTK16;
   static constexpr int CPR = KD * 4;
-  static constexpr int ITERS = (kTK16 * CPR + kNT - 1) / kNT;
+  static constexpr int NC = (CPR + TPR - 1) / TPR;
 };
 template <int KD, int KV>
 struct TileRegs {
-  static constexpr int NV = EntryGeom<KD, KV>::ITERS > WinGeom<KD>::ITERS ? EntryGeom<KD, KV>::ITERS
-                                                                         : WinGeom<KD>::ITERS;
+  static constexpr int NV = EntryGeom<KD, KV>::NC > WinGeom<KD>::NC ? EntryGeom<KD, KV>::NC : WinGeom<KD>::NC;
   uint4 v[NV];
   uint4 rot;  // window tiles: this thread's rotated chunk
-  uint32_t bs[KV == kKvMxfp4 ? EntryGeom<KD, KV>::ITERS : 1];
+  uint32_t bs[KV == kKvMxfp4 ? EntryGeom<KD, KV>::NC : 1];
   float sc;
+  int row;    // -1: masked
 };
 
+// Tile loads. The rows of a split's keys were resolved into sm.sidx (entry row in the cache,
+// window row in win, -1 = masked). Loads are unconditional (a masked row reads row 0, a chunk past
+// the row end its last chunk); the store writes zeros for a masked row (a masked key gets p = 0,
+// which must not meet a non-finite value in the MFMA).
 template <int KD, int KV>
-__device__ __forceinline__ void entry_load(const AttnArgs& a, const uint8_t* cbase, const uint8_t* sbase,
-                                           int key0, int key_end, int key_begin, const AttnSmem<KD>& sm,
-                                           TileRegs<KD, KV>& R) {
-  using ER = EntryGeom<KD, KV>;
+__device__ __forceinline__ void entry_load(const uint8_t* cbase, const uint8_t* sbase, int key0, int key_end,
+                                           int key_begin, const AttnSmem<KD>& sm, TileRegs<KD, KV>& R) {
+  using EG = EntryGeom<KD, KV>;
   constexpr int D = KD * 32;
   constexpr int RB = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);  // code bytes per row
+  const int r = threadIdx.x / EG::TPR, c0 = threadIdx.x % EG::TPR;
+  const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
+  R.row = row;
+  const int64_t rr = max(row, 0);
+  const uint8_t* src = cbase + rr * RB;
 #pragma unroll
-  for (int j = 0; j < ER::ITERS; ++j) {
-    const int c = threadIdx.x + j * kNT;
-    const int r = c / ER::CPR, ch = c - r * ER::CPR;
-    const int key = key0 + r;
-    int idx = (c < ER::TK * ER::CPR && key < key_end) ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
-    if (idx >= a.N_cap) idx = -1;
-    R.v[j] = make_uint4(0, 0, 0, 0);
-    if constexpr (KV == kKvMxfp4) R.bs[j] = 127;
-    if (idx >= 0) {
-      R.v[j] = *reinterpret_cast<const uint4*>(cbase + (int64_t)idx * RB + ch * 16);
-      if constexpr (KV == kKvMxfp4) R.bs[j] = sbase[(int64_t)idx * KD + ch];
-    }
+  for (int i = 0; i < EG::NC; ++i) {
+    const int ch = EG::CPR % EG::TPR == 0 ? c0 + EG::TPR * i : min(c0 + EG::TPR * i, EG::CPR - 1);
+    R.v[i] = *reinterpret_cast<const uint4*>(src + 16 * ch);
+    if constexpr (KV == kKvMxfp4) R.bs[i] = sbase[rr * KD + ch];
   }
-  R.sc = -1.f;  // masked
-  if (threadIdx.x < ER::TK) {
-    const int key = key0 + threadIdx.x;
-    int idx = key < key_end ? (a.topk ? sm.sidx[key - key_begin] : key) : -1;
-    if (idx >= a.N_cap) idx = -1;
-    if (idx >= 0) R.sc = KV == kKvFp8 ? reinterpret_cast<const float*>(sbase)[idx] : 1.f;
-  }
+  R.sc = KV == kKvFp8 ? reinterpret_cast<const float*>(sbase)[rr] : 1.f;
 }
 
 template <int KD, int KV>
 __device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD>& sm, const TileRegs<KD, KV>& R) {
-  using ER = EntryGeom<KD, KV>;
+  using EG = EntryGeom<KD, KV>;
+  const int r = threadIdx.x / EG::TPR, c0 = threadIdx.x % EG::TPR;
+  const bool ok = R.row >= 0;
 #pragma unroll
-  for (int j = 0; j < ER::ITERS; ++j) {
-    const int c = threadIdx.x + j * kNT;
-    const int r = c / ER::CPR, ch = c - r * ER::CPR;
-    if (c >= ER::TK * ER::CPR) continue;
+  for (int i = 0; i < EG::NC; ++i) {
+    const int ch = c0 + EG::TPR * i;
+    if (EG::CPR % EG::TPR != 0 && ch >= EG::CPR) continue;
     if constexpr (KV == kKvFp8) {
-      *reinterpret_cast<uint4*>(&sm.t.k8[r][16 * ch]) = R.v[j];
+      *reinterpret_cast<uint4*>(&sm.t.k8[r][16 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
     } else if constexpr (KV == kKvBf16) {
-      *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = R.v[j];
+      *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
     } else {
       // exact e2m1 * 2^E -> bf16, two values (one code byte, low nibble first) per instruction
-      const float s = __builtin_amdgcn_ldexpf(1.0f, (int)R.bs[j] - 127);
-      const uint32_t wd[4] = {R.v[j].x, R.v[j].y, R.v[j].z, R.v[j].w};
+      const float s = __builtin_amdgcn_ldexpf(1.0f, (int)R.bs[i] - 127);
+      const uint32_t wd[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint4 o;
@@ -273,72 +270,59 @@ __device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD>& sm,
         o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 1));
         o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 2));
         o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 3));
-        *reinterpret_cast<uint4*>(&sm.t.b.k16[r][32 * ch + 8 * q]) = o;
+        *reinterpret_cast<uint4*>(&sm.t.b.k16[r][32 * ch + 8 * q]) = ok ? o : make_uint4(0, 0, 0, 0);
       }
     }
   }
-  if (threadIdx.x < ER::TK) {
-    const float sc = R.sc;
-    sm.kscale[threadIdx.x] = sc < 0.f ? -INFINITY : a.scale_log2 * sc;
-    sm.kvscale[threadIdx.x] = sc < 0.f ? 0.f : sc;
+  if (c0 == 0) {
+    sm.kscale[r] = ok ? a.scale_log2 * R.sc : -INFINITY;
+    sm.kvscale[r] = ok ? R.sc : 0.f;
   }
 }
 
-// Window rows: the unrotated chunks of a row through the generic chunk mapping, the rotated ones
-// (32 keys x d_rope/8 <= kNT chunks) one per thread in v[NV - 1]... held in rot.
+// Window rows: thread j of a row takes its unrotated chunks j + 8 i and, for j < d_rope/8, the
+// rotated chunk j.
 template <int KD, int KV>
-__device__ __forceinline__ void window_load(const AttnArgs& a, int qi, const KeySpace& ks, int key0, int key_end,
-                                            int rope0, TileRegs<KD, KV>& R) {
-  using WR = WinGeom<KD>;
+__device__ __forceinline__ void window_load(const AttnArgs& a, int key0, int key_end, int key_begin, int rope0,
+                                            const AttnSmem<KD>& sm, TileRegs<KD, KV>& R) {
+  using WG = WinGeom<KD>;
   constexpr int D = KD * 32;
-  auto row_of = [&](int key) -> int64_t {
-    const int64_t pos = ks.w0 + (key - ks.n_c);
-    return a.ring ? ((int64_t)(qi / a.q_per_seq) * a.ring_cap + pos % a.ring_cap) : (pos - a.pos0);
-  };
+  const int r = threadIdx.x / WG::TPR, c0 = threadIdx.x % WG::TPR;
+  const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
+  R.row = row;
+  const uint16_t* src = a.win + (int64_t)max(row, 0) * D;
+  const int nu = rope0 >> 3;  // unrotated chunks
 #pragma unroll
-  for (int j = 0; j < WR::ITERS; ++j) {
-    const int c = threadIdx.x + j * kNT;
-    const int r = c / WR::CPR, ch = c - r * WR::CPR;
-    const int key = key0 + r;
-    R.v[j] = make_uint4(0, 0, 0, 0);
-    if (c < kTK16 * WR::CPR && key < key_end && 8 * ch < rope0)
-      R.v[j] = *reinterpret_cast<const uint4*>(a.win + row_of(key) * D + ch * 8);
-  }
-  const int rc = a.d_rope >> 3;  // rotated chunks per row
-  R.rot = make_uint4(0, 0, 0, 0);
-  if (rc > 0 && (int)threadIdx.x < kTK16 * rc) {
-    const int r = threadIdx.x / rc, ch = threadIdx.x - r * rc;
-    const int key = key0 + r;
-    if (key < key_end) R.rot = *reinterpret_cast<const uint4*>(a.win + row_of(key) * D + rope0 + ch * 8);
-  }
+  for (int i = 0; i < WG::NC; ++i) R.v[i] = *reinterpret_cast<const uint4*>(src + 8 * min(c0 + WG::TPR * i, WG::CPR - 1));
+  R.rot = *reinterpret_cast<const uint4*>(src + min(rope0 + 8 * c0, D - 8));
+  (void)nu;
 }
 
-// Window rows into the bf16 tile; each thread rotates its rotated chunk at the token's position,
-// the remainder going to klo.
+// Window rows into the bf16 tile; the rotated chunk is rotated at the token's position here, the
+// remainder going to klo.
 template <int KD, int KV>
-__device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, int key_end, int rope0,
-                                             int rb0, AttnSmem<KD>& sm, const TileRegs<KD, KV>& R) {
-  using WR = WinGeom<KD>;
+__device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, int rope0,
+                                             AttnSmem<KD>& sm, const TileRegs<KD, KV>& R) {
+  using WG = WinGeom<KD>;
+  constexpr int D = KD * 32;
+  const int r = threadIdx.x / WG::TPR, c0 = threadIdx.x % WG::TPR;
+  const int nu = rope0 >> 3;
+  const bool ok = R.row >= 0;
 #pragma unroll
-  for (int j = 0; j < WR::ITERS; ++j) {
-    const int c = threadIdx.x + j * kNT;
-    const int r = c / WR::CPR, ch = c - r * WR::CPR;
-    if (c < kTK16 * WR::CPR && 8 * ch < rope0) *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = R.v[j];
+  for (int i = 0; i < WG::NC; ++i) {
+    const int ch = c0 + WG::TPR * i;
+    if (ch < nu) *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
   }
-  const int rc = a.d_rope >> 3;
-  if (rc > 0 && (int)threadIdx.x < kTK16 * rc) {
-    const int r = threadIdx.x / rc, ch = threadIdx.x - r * rc;
-    const int key = key0 + r;
-    uint4 hi, lo;
-    rope8_hi_lo(R.rot, key < key_end ? ks.w0 + (key - ks.n_c) : 0, a.rev_freq, 4 * ch, &hi, &lo);
-    const int d0 = rope0 + 8 * ch;
+  if (8 * c0 < a.d_rope) {
+    uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
+    if (ok) rope8_hi_lo(R.rot, ks.w0 + (key0 + r - ks.n_c), a.rev_freq, 4 * c0, &hi, &lo);
+    const int d0 = rope0 + 8 * c0;
     *reinterpret_cast<uint4*>(&sm.t.b.k16[r][d0]) = hi;
-    *reinterpret_cast<uint4*>(&sm.t.b.klo[r][d0 - 32 * rb0]) = lo;
+    *reinterpret_cast<uint4*>(&sm.t.b.klo[r][d0 - (D - 64)]) = lo;
   }
-  if (threadIdx.x < kTK16) {
-    const bool ok = key0 + (int)threadIdx.x < key_end;
-    sm.kscale[threadIdx.x] = ok ? a.scale_log2 : -INFINITY;
-    sm.kvscale[threadIdx.x] = ok ? 1.f : 0.f;
+  if (c0 == 0) {
+    sm.kscale[r] = ok ? a.scale_log2 : -INFINITY;
+    sm.kvscale[r] = ok ? 1.f : 0.f;
   }
 }
 
@@ -352,15 +336,16 @@ struct WaveState {
 };
 
 // S for keys [16w, 16w + 16) of the tile staged in LDS. F8: fp8 rows; WIN: window rows (key
-// remainders of the rotated blocks in klo).
+// remainders of the last 64 dims in klo). The rotated dims (d_rope <= 64) lie in the last two
+// 32-dim blocks, whose query remainders (qlo) and window-key remainders are zero outside them.
 template <int KD, bool F8, bool WIN>
-__device__ __forceinline__ f32x4 tile_qk(const AttnSmem<KD>& sm, const uint4* qa, const uint4* qlo, int rb0,
-                                         int nrb) {
+__device__ __forceinline__ f32x4 tile_qk(const AttnSmem<KD>& sm, const uint4* qa, const uint4* qlo) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int krow = 16 * w + col;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   constexpr int BQ = 3;  // operand reads in flight ahead of the MFMAs
+  constexpr int RB0 = KD >= kRB ? KD - kRB : 0;  // first block that may hold rotated dims
 #pragma unroll
   for (int s0 = 0; s0 < KD; s0 += BQ) {
     bf16x8 kb[BQ];
@@ -381,13 +366,11 @@ __device__ __forceinline__ f32x4 tile_qk(const AttnSmem<KD>& sm, const uint4* qa
       const int s = s0 + u;
       if (s < KD) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[s]), kb[u], acc, 0, 0, 0);
-        const int rr = s - rb0;  // rotated block: the query remainder, and for window keys theirs
-        if (rr >= 0 && rr < nrb) {
-          const uint4 ql = rr == 0 ? qlo[0] : qlo[1];
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ql), kb[u], acc, 0, 0, 0);
+        if (s >= RB0) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qlo[s - RB0]), kb[u], acc, 0, 0, 0);
           if constexpr (WIN) {
-            const bf16x8 kl =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.t.b.klo[krow][32 * rr + 8 * g]));
+            const bf16x8 kl = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(&sm.t.b.klo[krow][32 * (s - RB0) + 8 * g]));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[s]), kl, acc, 0, 0, 0);
           }
         }
@@ -400,10 +383,11 @@ __device__ __forceinline__ f32x4 tile_qk(const AttnSmem<KD>& sm, const uint4* qa
 // O += P V over the staged tile (NKS steps of 32 keys) for this wave's value dims. P (A operand):
 // lane (head col, group g) holds keys 8g..8g+7 of a step; V (B operand): lane (dim col, group g)
 // holds the same keys of its dim.
-template <int KD, int NO, bool F8, int NKS>
-__device__ __forceinline__ void tile_pv(const AttnSmem<KD>& sm, WaveState<NO>& st, int nvb) {
+template <int KD, int NO, bool F8, int NKS, int NVB>
+__device__ __forceinline__ void tile_pv(const AttnSmem<KD>& sm, WaveState<NO>& st) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
+  constexpr bool kEven = NO * 4 == NVB;  // every wave owns NO value dim blocks
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int kb0 = 32 * ks + 8 * g;
@@ -422,7 +406,7 @@ __device__ __forceinline__ void tile_pv(const AttnSmem<KD>& sm, WaveState<NO>& s
       for (int u = 0; u < BV; ++u) {
         const int n = n0 + u;
         const int nb = w * NO + n;  // value dim block of this wave
-        if (n < NO && nb < nvb) {
+        if (n < NO && (kEven || nb < NVB)) {
           if constexpr (F8) {
             const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (lds_i32x2*)(&sm.t.k8[kb0 + (col >> 1)][16 * nb + 8 * (col & 1)]));
@@ -439,7 +423,8 @@ __device__ __forceinline__ void tile_pv(const AttnSmem<KD>& sm, WaveState<NO>& s
 #pragma unroll
       for (int u = 0; u < BV; ++u) {
         const int n = n0 + u;
-        if (n < NO && w * NO + n < nvb) st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[u], st.o[n], 0, 0, 0);
+        if (n < NO && (kEven || w * NO + n < NVB))
+          st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[u], st.o[n], 0, 0, 0);
       }
     }
   }
@@ -509,7 +494,7 @@ __device__ __forceinline__ void tile_softmax(AttnSmem<KD>& sm, WaveState<NO>& st
 }
 
 template <int KD, int NVB, int KV>
-__global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kNT, 2) void attn_kernel(AttnArgs a) {
   constexpr int D = KD * 32;
   constexpr int NO = (NVB + 3) / 4;  // value dim blocks per wave
   constexpr bool F8 = KV == kKvFp8;
@@ -527,8 +512,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
   const int hg = qh % a.n_hg, qi = qh / a.n_hg;
   const int h0 = hg * kHG;
   const int rope0 = D - a.d_rope;
-  const int rb0 = rope0 >> 5;                   // first 32-dim block holding rotated dims
-  const int nrb = a.d_rope > 0 ? KD - rb0 : 0;  // <= kRB
+  constexpr int RB0 = KD >= kRB ? KD - kRB : 0;  // first block that may hold rotated dims
 
   // the query's raw dims: requested first, they depend on nothing else
   uint4 qa[KD], qlo[kRB];
@@ -546,11 +530,28 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
   const int key_end = min(n_keys, key_begin + a.keys_per_split);
   const int e_end = min(key_end, ks.n_c);  // entry keys [key_begin, e_end), window keys after
   const int w_begin = max(key_begin, ks.n_c);
-  if (a.topk) {
-    for (int i = tid; i < e_end - key_begin; i += kNT) sm.sidx[i] = a.topk[(int64_t)qi * a.k + key_begin + i];
+  // the rows of this split's keys: entry rows in the sequence's cache (top-k slot or dense
+  // index; out of range = masked), then window rows in win (ring slot or prompt row)
+  {
+    const int64_t wseq = a.ring ? (int64_t)(qi / a.q_per_seq) * a.ring_cap : -a.pos0;
+    const int64_t wbase = a.ring ? ks.w0 % a.ring_cap : ks.w0;  // row of window key 0 before wrapping
+    for (int i = tid; i < key_end - key_begin; i += kNT) {
+      const int key = key_begin + i;
+      int row;
+      if (key < ks.n_c) {
+        row = a.topk ? a.topk[(int64_t)qi * a.k + key] : key;
+        if (row >= a.N_cap) row = -1;
+      } else {
+        int64_t slot = wbase + (key - ks.n_c);
+        if (a.ring && slot >= a.ring_cap) slot -= a.ring_cap;  // n_w <= W <= ring_cap
+        row = (int)(wseq + slot);
+      }
+      sm.sidx[i] = row;
+    }
   }
-  if ((rope0 & 31) && tid < kTK16) {  // dims of a rotated block below rope0 have no remainder
-    for (int d = 32 * rb0; d < rope0; ++d) sm.t.b.klo[tid][d - 32 * rb0] = 0;
+  if (tid < kTK16) {  // window remainders of the last 64 dims below rope0 are zero
+    for (int d = D - 64; d < rope0; ++d)
+      if (d >= 0) sm.t.b.klo[tid][d - (D - 64)] = 0;
   }
   __syncthreads();  // sidx ready
 
@@ -565,9 +566,9 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
   const bool has_e = key_begin < e_end;
   TileRegs<KD, KV> RT;
   if (has_e)
-    entry_load<KD, KV>(a, cbase, sbase, key_begin, e_end, key_begin, sm, RT);
+    entry_load<KD, KV>(cbase, sbase, key_begin, e_end, key_begin, sm, RT);
   else if (w_begin < key_end)
-    window_load<KD, KV>(a, qi, ks, w_begin, key_end, rope0, RT);
+    window_load<KD, KV>(a, w_begin, key_end, key_begin, rope0, sm, RT);
 
   // the query's rotated dims: each of the 16 heads x d_rope/8 chunks rotated once at t (a bf16
   // value and a bf16 remainder) into LDS
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
     if (d0 >= rope0) {
       qa[s] = *reinterpret_cast<const uint4*>(&sm.qrh[col][d0 - rope0]);
       const uint4 lo = *reinterpret_cast<const uint4*>(&sm.qrl[col][d0 - rope0]);
-      if (s == rb0)
+      if (s == RB0)
         qlo[0] = lo;
       else
         qlo[1] = lo;
@@ -632,25 +633,25 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
       entry_store<KD, KV>(a, sm, RT);
       __syncthreads();
       if (key0 + TKE < e_end)
-        entry_load<KD, KV>(a, cbase, sbase, key0 + TKE, e_end, key_begin, sm, RT);
+        entry_load<KD, KV>(cbase, sbase, key0 + TKE, e_end, key_begin, sm, RT);
       else if (w_begin < key_end)
-        window_load<KD, KV>(a, qi, ks, w_begin, key_end, rope0, RT);
+        window_load<KD, KV>(a, w_begin, key_end, key_begin, rope0, sm, RT);
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if (16 * w < TKE) s = tile_qk<KD, F8, false>(sm, qa, qlo, rb0, nrb);
+      if (16 * w < TKE) s = tile_qk<KD, F8, false>(sm, qa, qlo);
       tile_softmax<KD, NO>(sm, st, s, TKE);
-      tile_pv<KD, NO, F8, TKE / 32>(sm, st, NVB);
+      tile_pv<KD, NO, F8, TKE / 32, NVB>(sm, st);
     }
   }
   // phase 2: window tokens
   for (int key0 = w_begin; key0 < key_end; key0 += kTK16) {
     __syncthreads();
-    window_store<KD, KV>(a, ks, key0, key_end, rope0, rb0, sm, RT);
+    window_store<KD, KV>(a, ks, key0, rope0, sm, RT);
     __syncthreads();
-    if (key0 + kTK16 < key_end) window_load<KD, KV>(a, qi, ks, key0 + kTK16, key_end, rope0, RT);
+    if (key0 + kTK16 < key_end) window_load<KD, KV>(a, key0 + kTK16, key_end, key_begin, rope0, sm, RT);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if (16 * w < kTK16) s = tile_qk<KD, false, true>(sm, qa, qlo, rb0, nrb);
+    if (16 * w < kTK16) s = tile_qk<KD, false, true>(sm, qa, qlo);
     tile_softmax<KD, NO>(sm, st, s, kTK16);
-    tile_pv<KD, NO, false, 1>(sm, st, NVB);
+    tile_pv<KD, NO, false, 1, NVB>(sm, st);
   }
 
   // the key sums of the waves (same exponent base): l = sum over waves
@@ -697,63 +698,84 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
       a.part_ml[(pbase + 4 * g + r) * 2 + 1] = lt[r];
     }
   }
-  // the last split of (query, head group) to finish merges; the counter is reset for the next call
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(&a.counters[qh], 1u);
-    const int last = done == (uint32_t)a.n_splits - 1;
-    if (last) atomicExch(&a.counters[qh], 0u);
-    sm.last = last;
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-  // merge: thread t takes head t / 16 and dims 4 (t % 16) + 64 i
-  const int hm = tid >> 4;
-  const int hr = h0 + hm;
-  const int64_t hbase = (int64_t)qh * a.n_splits * kHG + hm;  // row of split s: hbase + s * kHG
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[(hbase + (int64_t)s * kHG) * 2]);
-  const float Mb = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[(hbase + (int64_t)s * kHG) * 2]);
-    L += exp2f(ml.x - Mb) * ml.y;
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  if (hr < a.H) {
-    for (int d = 4 * (tid & 15); d < a.d_v; d += 64) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      constexpr int SB = 8;  // splits requested together
-      for (int s0 = 0; s0 < a.n_splits; s0 += SB) {
-        f32x4 v[SB];
-        float wt[SB];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int s = min(s0 + u, a.n_splits - 1);
-          const int64_t row = hbase + (int64_t)s * kHG;
-          v[u] = *reinterpret_cast<const f32x4*>(a.part_o + row * a.d_v + d);
-          wt[u] = s0 + u < a.n_splits ? exp2f(a.part_ml[row * 2] - Mb) : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) acc += wt[u] * v[u];
+}
+
+// One workgroup per (query, head): log-sum-exp merge of the split partials. Thread t owns dims
+// 4t..4t+3 (d_v <= 4 * kMergeNT). Split rows are read kMergeBatch at a time, the batch requested
+// before the previous one is summed; rows past the last split repeat it with weight 0, so every
+// load is unconditional.
+constexpr int kMergeNT = 128;
+constexpr int kMergeBatch = 8;
+__global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float wsh[kMaxSplits + kMergeBatch];
+  __shared__ float red[2];
+  const int qi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int S = a.n_splits;
+  const int64_t row0 = ((int64_t)(qi * a.n_hg + h / kHG) * S) * kHG + h % kHG;  // split s: row0 + s * kHG
+  const int dd = min(4 * tid, a.d_v - 4);  // threads past d_v read the last dims and store nothing
+  if (tid < kWave) {
+    float mx = -INFINITY;
+    for (int sp = tid; sp < S; sp += kWave) mx = fmaxf(mx, a.part_ml[(row0 + (int64_t)sp * kHG) * 2]);
+    mx = wave_max(mx);
+    const float Mb = mx == -INFINITY ? 0.f : mx;
+    float l = 0.f;
+    for (int sp = tid; sp < S + kMergeBatch; sp += kWave) {
+      float wt = 0.f;
+      if (sp < S) {
+        const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[(row0 + (int64_t)sp * kHG) * 2]);
+        wt = exp2f(ml.x - Mb);
+        l += wt * ml.y;
       }
-      uint2 packed;
-      packed.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-      packed.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-      *reinterpret_cast<uint2*>(a.out + ((int64_t)qi * a.H + hr) * a.d_v + d) = packed;
+      wsh[sp] = wt;
     }
-    if ((tid & 15) == 0 && a.out_lse)
-      a.out_lse[(int64_t)qi * a.H + hr] = L > 0.f ? (Mb + log2f(L)) * kLn2 : -INFINITY;
+    l = wave_sum(l);
+    if (tid == 0) {
+      red[0] = Mb;
+      red[1] = l;
+    }
   }
+  __syncthreads();
+  const float Mb = red[0], L = red[1];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](f32x4 (&v)[kMergeBatch], int s0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(a.part_o + (row0 + (int64_t)min(s0 + u, S - 1) * kHG) * a.d_v + dd);
+  };
+  auto sum = [&](const f32x4 (&v)[kMergeBatch], int s0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) acc += wsh[s0 + u] * v[u];
+  };
+  f32x4 v0[kMergeBatch], v1[kMergeBatch];
+  fetch(v0, 0);
+  for (int s0 = 0;; s0 += 2 * kMergeBatch) {  // v0 holds rows s0.. on entry
+    if (s0 + kMergeBatch >= S) {
+      sum(v0, s0);
+      break;
+    }
+    fetch(v1, s0 + kMergeBatch);
+    sum(v0, s0);
+    if (s0 + 2 * kMergeBatch >= S) {
+      sum(v1, s0 + kMergeBatch);
+      break;
+    }
+    fetch(v0, s0 + 2 * kMergeBatch);
+    sum(v1, s0 + kMergeBatch);
+  }
+  if (4 * tid < a.d_v) {
+    uint2 packed;
+    packed.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    packed.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)qi * a.H + h) * a.d_v + dd) = packed;
+  }
+  if (tid == 0 && a.out_lse) a.out_lse[(int64_t)qi * a.H + h] = L > 0.f ? (Mb + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- host side
 struct AttnPlan {
   int n_hg, n_splits, keys_per_split;
-  size_t ws;        // bytes: counters (256-byte aligned region) + partials
-  size_t ws_count;  // bytes of the counter region
+  size_t ws;  // bytes of the split partials
 };
 
 // Splits of a query's key set: about two workgroups per CU over the whole job, each split a
@@ -763,7 +785,7 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
   AttnPlan p;
   p.n_hg = (H + kHG - 1) / kHG;
   const int64_t base = (int64_t)nq * p.n_hg;
-  int splits = (int)((kTargetWG + base - 1) / base);
+  int splits = (int)(kTargetWG / base);
   if (splits < 1) splits = 1;
   int per = (max_keys + splits - 1) / splits;
   per = (per + 63) / 64 * 64;
@@ -775,13 +797,7 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
   if (splits < 1) splits = 1;
   p.n_splits = splits;
   p.keys_per_split = per;
-  if (splits > 1) {
-    p.ws_count = ((size_t)base * sizeof(uint32_t) + 255) / 256 * 256;
-    p.ws = p.ws_count + (size_t)base * splits * kHG * ((size_t)d_v + 2) * sizeof(float);
-  } else {
-    p.ws_count = 0;
-    p.ws = 0;
-  }
+  p.ws = splits > 1 ? (size_t)base * splits * kHG * ((size_t)d_v + 2) * sizeof(float) : 0;
   return p;
 }
 
@@ -825,9 +841,12 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   a.n_hg = p.n_hg;
   a.n_splits = p.n_splits;
   a.keys_per_split = p.keys_per_split;
+  CSKV_REQUIRE(p.n_splits <= kMaxSplits, CSKV_ENOTSUP, "%s: %d key splits > %d (key set too large)", name,
+               p.n_splits, kMaxSplits);
+  CSKV_REQUIRE(p.n_splits == 1 || a.d_v <= 4 * kMergeNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name,
+               a.d_v, 4 * kMergeNT);
   if (p.n_splits > 1) {
-    a.counters = reinterpret_cast<uint32_t*>(ws);
-    a.part_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.ws_count);
+    a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * p.n_hg * p.n_splits * kHG * a.d_v;
   }
   const int64_t total = (int64_t)a.nq * p.n_hg * p.n_splits;
@@ -836,6 +855,10 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   AttnKernel kern = pick_kernel(a.D, a.d_v, a.kv_dtype);
   hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(kNT), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
+  if (p.n_splits > 1) {
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.nq, a.H), dim3(kMergeNT), 0, s, a);
+    CSKV_LAUNCH_CHECK(name);
+  }
   return CSKV_OK;
 }
 

@@ -199,10 +199,9 @@ CSKV_API size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int H_I, 
  * or in [0, n_entries[r])) or NULL; win [B, R, D] bf16 rings of raw tokens (R = 0 means
  * R = W; a T-token step needs R >= W + T - 1 so that no query's window has been
  * overwritten); out [B*T, H, d_v] bf16; out_lse [B*T, H] fp32 or NULL; ws of at least
- * hybrid_attn_decode_workspace_size(B*T, ...) bytes (none when that size is 0). The workspace
- * starts with the counters of the key-split merge: they must be zero before the first call
- * that uses the workspace (allocate it zeroed, outside any captured graph), and every call
- * leaves them zero. Calls sharing a workspace must not run concurrently.
+ * hybrid_attn_decode_workspace_size(B*T, ...) bytes (none when that size is 0): the partial
+ * results of the key splits, merged by a second launch. Calls sharing a workspace must not run
+ * concurrently. A key set needing more than 64 splits of 4096 keys is refused (CSKV_ENOTSUP).
  * Requirements: D % 32 == 0, D <= 1024, d_v % 16 == 0, d_v <= D, d_v <= 512,
  * d_rope % 8 == 0, d_rope <= min(D, 64), 1 <= H <= 128, W >= 0, T >= 1, R >= W + T - 1 when
  * W > 0 (CSKV_EINVAL otherwise; with R = 0 a draft of T > 1 tokens is refused),
@@ -225,8 +224,7 @@ CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_c
  *
  * q [T, H, D] bf16; ckv / ckv_scale as in decode with N entries;
  * topk_idx [T, k] or NULL; x [T, D] bf16 raw tokens of the prompt;
- * out [T, H, d_v] bf16; out_lse [T, H] fp32 or NULL; ws as in decode (zeroed before its first
- * use, left zeroed by every call).
+ * out [T, H, d_v] bf16; out_lse [T, H] fp32 or NULL; ws as in decode.
  * Requirements as in decode, plus m >= 1.
  */
 CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int T, const void* ckv,
