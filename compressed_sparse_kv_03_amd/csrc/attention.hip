@@ -39,6 +39,8 @@
 // that costs more than the launch). One split writes the output directly.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.cuh"
 #include "host_util.h"
 
@@ -872,14 +874,14 @@ extern "C" CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d
   return plan_attn(B, H, d_v, max_keys > 0 ? max_keys : 1).ws;
 }
 
-extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
-                                           const void* ckv_scale, int ckv_dtype, int N_cap,
-                                           const int32_t* n_entries, const int32_t* topk_idx, int k,
-                                           const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
-                                           float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
-                                           void* ws, size_t ws_bytes, float q_rms_eps, int T, int R,
-                                           void* stream) {
-  const char* name = "hybrid_attn_decode";
+namespace cskv {
+
+// Checks the decode arguments and fills the kernel arguments and the split plan.
+static int decode_setup(const char* name, const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                        const void* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
+                        const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H, int D, int d_rope,
+                        int d_v, float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
+                        float q_rms_eps, int T, int R, AttnArgs& a, AttnPlan& p) {
   CSKV_REQUIRE(B >= 1 && N_cap >= 0, CSKV_EINVAL, "%s: B=%d N_cap=%d", name, B, N_cap);
   if (R == 0) R = W;
   CSKV_REQUIRE(T >= 1 && (int64_t)B * T < (1 << 20), CSKV_EINVAL, "%s: T=%d", name, T);
@@ -894,8 +896,8 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(win), CSKV_EINVAL, "%s: q/ckv/win must be 16-byte aligned",
                name);
   const int max_keys = (topk_idx ? k : N_cap) + W;
-  AttnPlan p = plan_attn(B * T, H, d_v, max_keys > 0 ? max_keys : 1);
-  AttnArgs a{};
+  p = plan_attn(B * T, H, d_v, max_keys > 0 ? max_keys : 1);
+  a = AttnArgs{};
   a.q = q;
   a.q_pos = q_pos;
   a.pos0 = 0;
@@ -923,7 +925,79 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   a.q_rms_eps = q_rms_eps;
   a.out = out;
   a.out_lse = out_lse;
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                                           const void* ckv_scale, int ckv_dtype, int N_cap,
+                                           const int32_t* n_entries, const int32_t* topk_idx, int k,
+                                           const uint16_t* win, int W, int B, int H, int D, int d_rope, int d_v,
+                                           float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
+                                           void* ws, size_t ws_bytes, float q_rms_eps, int T, int R,
+                                           void* stream) {
+  const char* name = "hybrid_attn_decode";
+  AttnArgs a;
+  AttnPlan p;
+  const int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
+                              D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, a, p);
+  if (rc) return rc;
   return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Scratch of hybrid_attn_decode_noalloc: the key-split partials, in a device array of fixed size.
+// Each GPU holds its own copy for the life of the process; its address on a device is looked up
+// once, with that device current, and that address (not the host-side name of the array) is what
+// the kernels receive.
+static __device__ __align__(256) unsigned char scratch[CSKV_NOALLOC_SCRATCH_BYTES];
+
+namespace cskv {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(const char* name, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  CSKV_REQUIRE(e == hipSuccess, CSKV_EHIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+  CSKV_REQUIRE(dev >= 0 && dev < kMaxDevices, CSKV_ENOTSUP, "%s: device %d >= %d", name, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    CSKV_REQUIRE(e == hipSuccess && ptr, CSKV_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", name, dev,
+                 hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+extern "C" CSKV_API int hybrid_attn_decode_noalloc(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                                                   const void* ckv_scale, int ckv_dtype, int N_cap,
+                                                   const int32_t* n_entries, const int32_t* topk_idx, int k,
+                                                   const uint16_t* win, int W, int B, int H, int D, int d_rope,
+                                                   int d_v, float rope_base, float softmax_scale, uint16_t* out,
+                                                   float* out_lse, float q_rms_eps, int T, int R, void* stream) {
+  const char* name = "hybrid_attn_decode_noalloc";
+  AttnArgs a;
+  AttnPlan p;
+  int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H, D,
+                        d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, a, p);
+  if (rc) return rc;
+  CSKV_REQUIRE(p.ws <= (size_t)CSKV_NOALLOC_SCRATCH_BYTES, CSKV_EWORKSPACE,
+               "%s: the key splits need %zu bytes of scratch > the static %zu bytes (use hybrid_attn_decode)", name,
+               p.ws, (size_t)CSKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (p.ws > 0) {
+    rc = scratch_address(name, &ws);
+    if (rc) return rc;
+  }
+  return launch_attn(name, a, p, ws, (size_t)CSKV_NOALLOC_SCRATCH_BYTES, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense) {

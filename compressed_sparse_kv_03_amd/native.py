@@ -29,6 +29,8 @@ _SIGS = {
     "hybrid_attn_decode": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                             _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "hybrid_attn_decode_noalloc": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
+                                    _p, _p, _f, _i, _i, _p], _i),
     "hybrid_attn_prefill": ([_p, _i64, _i, _p, _p, _i, _i, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                              _p, _p, _p, _sz, _f, _p], _i),
     "hybrid_attn_prefill_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
@@ -147,6 +149,19 @@ def hybrid_attn_decode(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, to
                                     _ptr(n_entries), _ptr(topk_idx), k, _ptr(win), W, B, H, D, d_rope, d_v,
                                     rope_base, softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes,
                                     q_rms_eps, T, R, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024   # CSKV_NOALLOC_SCRATCH_BYTES
+
+
+def hybrid_attn_decode_noalloc(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
+                               D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, stream=None, *,
+                               q_rms_eps=0.0, T=1, R=0):
+    """hybrid_attn_decode with the split partials in the library's static per-GPU scratch."""
+    _check(lib().hybrid_attn_decode_noalloc(_ptr(q), _ptr(q_pos), _ptr(ckv), _ptr(ckv_scale), ckv_dtype, N_cap,
+                                            _ptr(n_entries), _ptr(topk_idx), k, _ptr(win), W, B, H, D, d_rope,
+                                            d_v, rope_base, softmax_scale, _ptr(out), _ptr(out_lse), q_rms_eps,
+                                            T, R, _stream(stream)))
 
 
 def hybrid_attn_prefill_workspace_size(T, H, d_v, N, k, W, dense):

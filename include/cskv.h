@@ -216,6 +216,28 @@ CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const v
 CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense);
 
 /*
+ * hybrid_attn_decode_noalloc - hybrid_attn_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It computes the same result with the same kernels; the
+ * key-split partials live in a static device array of CSKV_NOALLOC_SCRATCH_BYTES that each GPU
+ * holds from the first call on it until the process ends. No call allocates or frees device
+ * memory.
+ *
+ * Arguments, layouts and requirements as in hybrid_attn_decode. A call whose
+ * hybrid_attn_decode_workspace_size(B*T, ...) exceeds CSKV_NOALLOC_SCRATCH_BYTES is refused
+ * with CSKV_EWORKSPACE before anything is enqueued. All calls on one GPU share that GPU's
+ * array (every partial is written before it is read, so nothing needs clearing between calls):
+ * calls that may overlap on one GPU (different streams, or host threads) race and must not
+ * be issued.
+ */
+#define CSKV_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+CSKV_API int hybrid_attn_decode_noalloc(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                       const void* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
+                       const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H,
+                       int D, int d_rope, int d_v, float rope_base, float softmax_scale,
+                       uint16_t* out, float* out_lse, float q_rms_eps, int T, int R, void* stream);
+
+/*
  * hybrid_attn_prefill - the same attention for every row of one prompt.
  * Row r is position t = pos0 + r. It sees entries j < min(N, floor((t+1)/m))
  * (CSA: those listed in topk_idx[r]; HCA: all of them when topk_idx == NULL)

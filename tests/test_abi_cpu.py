@@ -17,7 +17,7 @@ def declared():
 
 def test_library_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 14
     L = native.lib()
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
@@ -107,6 +107,19 @@ def test_attention_validation():
     assert dec(T=3, R=129) == -1             # ... and a 3-token one R >= W + 2
     assert dec(eps=float("nan")) == -1
     assert L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) > 0
+
+    def dec_na(**kw):     # the allocation-free variant: same arguments without ws / ws_bytes
+        a = dict(q=16, qp=16, ckv=16, sc=16, dt=1, N=100, ne=16, tk=None, k=128, win=16, W=128, B=1, H=64,
+                 D=576, dr=64, dv=512, base=1e4, scale=0.04, out=16, lse=None, eps=0.0, T=1, R=0, s=None)
+        a.update(kw)
+        return L.hybrid_attn_decode_noalloc(*a.values())
+    assert dec_na(D=100) == -1
+    assert dec_na(q=None) == -1
+    assert dec_na(T=2) == -1
+    # 16 queries over 65536 dense entries need 17 splits of partials: more than the static scratch,
+    # refused before any HIP call
+    assert L.hybrid_attn_decode_workspace_size(16, 64, 512, 65536, 0, 128, 1) > native.NOALLOC_SCRATCH_BYTES
+    assert dec_na(B=16, N=65536) == -3
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
                                                         k=1, x=16, W=128, H=16, D=128, dr=64, dv=128, m=4,
                                                         base=1e4, scale=0.1, out=16, lse=None, ws=None, wsb=0,

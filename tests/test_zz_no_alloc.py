@@ -1,0 +1,92 @@
+"""hybrid_attn_decode_noalloc (key-split partials in the library's static per-GPU scratch) against
+hybrid_attn_decode with a caller-allocated workspace, on two calls in a row, the second smaller:
+the same kernels and split plan run, so outputs and lse must agree bit for bit. The first call is
+also checked against the oracle on one sequence, and a call whose splits need more than the
+static scratch must be refused before anything runs."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_kv_03_amd import configs, native, synth
+from oracle import attention as oatt
+from tests import parity
+from tests.gpu_util import DEV, down, poisoned, say, up
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3}
+
+
+def both(q, q_pos, ckv, sc, dtype, nent, topk, k, ring, W, H, D, d_rope, d_v, scale):
+    """Outputs of the workspace entry point and of the allocation-free one on the same inputs."""
+    B, N_cap = q.shape[0], ckv.shape[1]
+    wsn = native.hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, topk is None)
+    assert 0 < wsn <= native.NOALLOC_SCRATCH_BYTES, wsn   # the split path, within the static scratch
+    ws = torch.zeros(wsn, dtype=torch.uint8, device=DEV)
+    res = []
+    for noalloc in (False, True):
+        out = poisoned((B, H, d_v), torch.int16)
+        lse = poisoned((B, H), torch.float32)
+        if noalloc:
+            native.hybrid_attn_decode_noalloc(q, q_pos, ckv, sc, DT[dtype], N_cap, nent, topk, k, ring, W, B, H, D,
+                                              d_rope, d_v, 10000.0, scale, out, lse)
+        else:
+            native.hybrid_attn_decode(q, q_pos, ckv, sc, DT[dtype], N_cap, nent, topk, k, ring, W, B, H, D, d_rope,
+                                      d_v, 10000.0, scale, out, lse, ws)
+        res.append((down(out), down(lse)))
+    return res
+
+
+def test_noalloc_matches_workspace_entry_point_twice():
+    # call 1: the HCA layer of the 1M-context hybrid decode (B=8, 8192 fp8 entries, window 128)
+    w = configs.C5
+    n, t = w.L // 128, w.L - 1
+    say("noalloc call 1: hca", w.B, n)
+    q = synth.normal_bf16_bits((w.B, w.H, w.D), w.sigma, synth.seed_of(7, w.wid, 2), DEV)
+    ckv, sc = synth.fp8_rows_normal((w.B, n, w.D), w.sigma, synth.seed_of(7, w.wid, 3), DEV)
+    ring = synth.normal_bf16_bits((w.B, w.W, w.D), w.sigma, synth.seed_of(7, w.wid, 4), DEV)
+    nent = np.full(w.B, n, np.int32)
+    (o_ws, l_ws), (o_na, l_na) = both(q, up(np.full(w.B, t, np.int64)), ckv, sc, "fp8", up(nent), None, 0, ring, w.W,
+                                      w.H, w.D, w.d_rope, w.d_v, w.softmax_scale)
+    assert np.array_equal(o_na, o_ws), "noalloc output differs from the workspace entry point (call 1)"
+    assert np.array_equal(l_na.view(np.uint32), l_ws.view(np.uint32)), "noalloc lse differs (call 1)"
+    b = w.B - 1
+    o, l = oatt.decode_one(down(q)[b].view(np.uint16), t, oatt.Entries(down(ckv)[b], down(sc)[b], "fp8"), n, None,
+                           down(ring)[b].view(np.uint16), w.W, w.d_rope, w.d_v, 10000.0, w.softmax_scale)
+    parity.attn_close(o_na[b], o, "noalloc call 1 vs oracle")
+    parity.lse_close(l_na[b], l, None, "noalloc call 1 lse vs oracle")
+
+    # call 2, smaller: CSA top-k over 700 bf16 entries, B=3
+    B, H, D, d_rope, d_v, N, k, W = 3, 64, 576, 64, 512, 700, 128, 128
+    say("noalloc call 2: csa", B, N)
+    rng = np.random.default_rng(11)
+    q2 = synth.normal_bf16_bits((B, H, D), D ** -0.5, synth.seed_of(8, 2, 2), DEV)
+    ckv2 = synth.normal_bf16_bits((B, N, D), D ** -0.5, synth.seed_of(8, 2, 3), DEV)
+    ring2 = synth.normal_bf16_bits((B, W, D), D ** -0.5, synth.seed_of(8, 2, 4), DEV)
+    nent2 = np.array([700, 450, 129], np.int32)
+    tpos2 = nent2.astype(np.int64) * 4 + 3
+    topk2 = np.full((B, k), -1, np.int32)
+    for i in range(B):
+        sel = rng.choice(nent2[i], min(k, nent2[i]) - 5, replace=False)
+        topk2[i, :sel.size] = sel
+    (o_ws, l_ws), (o_na, l_na) = both(q2, up(tpos2), ckv2, None, "bf16", up(nent2), up(topk2), k, ring2, W, H, D,
+                                      d_rope, d_v, D ** -0.5)
+    assert np.array_equal(o_na, o_ws), "noalloc output differs from the workspace entry point (call 2)"
+    assert np.array_equal(l_na.view(np.uint32), l_ws.view(np.uint32)), "noalloc lse differs (call 2)"
+
+
+def test_noalloc_refuses_more_than_the_static_scratch():
+    # B=16 queries over 65536 dense entries need 17 splits of 4096 keys: more than 32 MiB of partials
+    B, H, D, d_v, N, W = 16, 64, 576, 512, 65536, 128
+    assert native.hybrid_attn_decode_workspace_size(B, H, d_v, N, 0, W, True) > native.NOALLOC_SCRATCH_BYTES
+    q = torch.zeros((B, H, D), dtype=torch.int16, device=DEV)
+    ckv = torch.zeros((B, N, D), dtype=torch.uint8, device=DEV)
+    sc = torch.ones((B, N), dtype=torch.float32, device=DEV)
+    ring = torch.zeros((B, W, D), dtype=torch.int16, device=DEV)
+    out = torch.zeros((B, H, d_v), dtype=torch.int16, device=DEV)
+    with pytest.raises(native.CskvError) as e:
+        native.hybrid_attn_decode_noalloc(q, up(np.full(B, N * 128, np.int64)), ckv, sc, DT["fp8"], N,
+                                          up(np.full(B, N, np.int32)), None, 0, ring, W, B, H, D, 64, d_v, 10000.0,
+                                          D ** -0.5, out, None)
+    assert e.value.code == -3
+    torch.cuda.synchronize()
