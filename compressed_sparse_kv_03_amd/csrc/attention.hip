@@ -9,26 +9,22 @@
 // 100만 토큰 컨텍스트를 저비용에 구현한 방법", section "쉽게 이해하기": the window
 // holds the latest 128 tokens. Entries and window tokens share one softmax.
 //
-// Design. One query (a decode sequence, or one prefill row) has H heads and a
-// key set of compressed entries (a top-k list or a dense range) followed by
-// window tokens. A workgroup of four waves takes one query, one group of 16
-// heads (the 16 rows of a v_mfma_f32_16x16x32_bf16) and one contiguous split of
-// the key set; two workgroups share a CU. Keys are staged through LDS a tile at
-// a time, the next tile's rows travelling in registers while the current one
-// is computed:
-//   fp8 entries: 64-key tiles kept as e4m3 codes (half the LDS bytes of bf16);
-//     operands are widened exactly to bf16 as they are read, the per-entry
-//     scale is folded into the logit and into P;
-//   bf16 and MXFP4 entries, window tokens: 32-key tiles of bf16 (MXFP4 widened
-//     exactly with its block scale; window tokens rotated at their own
-//     position while staged).
-// Per tile, wave w computes S = Q K^T for keys [16w, 16w+16) over all D dims
-// with the rotated query in registers (A operand) and key rows read from LDS
-// (B operand); the tile's per-head maxima meet in LDS; the online softmax runs
-// in the log2 domain; P^T goes to LDS as [key][head]; then wave w computes
-// O += P V for a quarter of the value dims, P read with the transposed LDS read
-// ds_read_b64_tr_b16 and V (the first d_v dims of the same rows) with
-// ds_read_b64_tr_b8 (fp8 tiles) or ds_read_b64_tr_b16 (bf16 tiles).
+// Design. A workgroup of four waves takes one query, a block of 64 heads and one
+// contiguous split of the query's key set (compressed entries, then window
+// tokens); one workgroup runs per CU. Keys are staged through LDS 64 at a time
+// as bf16 rows: fp8 and MXFP4 entries are widened exactly as they are stored
+// (once per key, not once per head group), window tokens are rotated at their
+// own position. The next tile's rows travel in registers while the current one
+// is computed. Every product is a v_mfma_f32_32x32x16_bf16 with the keys or the
+// value dims as rows and 32 heads as columns, so each K and V element read from
+// LDS serves 32 heads and each lane owns one head:
+//   S^T = K Q^T: wave (h, k) takes heads [32h, 32h+32) and keys [32k, 32k+32);
+//     the query's dims stay in registers for the whole split (B operand);
+//   softmax in the log2 domain per head, the two key halves meeting in LDS;
+//     P^T goes to LDS as [head][key];
+//   O^T += V^T P^T: wave (h, v) takes heads [32h, 32h+32) and value dims
+//     [v d_v/2, (v+1) d_v/2); V^T is read with the transposed LDS read
+//     ds_read_b64_tr_b16.
 // The rotated dims of the query and of window keys carry 16 significant bits:
 // they are split into a bf16 value and a bf16 remainder and both go through the
 // MFMA (for entry keys, stored exactly, the query remainder only), so the
@@ -41,30 +37,31 @@
 
 #include <mutex>
 
+#include "attention_call.h"
 #include "common.cuh"
 #include "host_util.h"
 
 namespace cskv {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kNT = 256;             // threads per workgroup (4 waves)
-constexpr int kHG = 16;              // heads per workgroup
-constexpr int kTK8 = 64;             // keys per fp8 entry tile
-constexpr int kTK16 = 32;            // keys per bf16 tile
-constexpr int kRB = 2;               // 32-dim blocks holding rotated dims (d_rope <= 64)
+constexpr int kNT = 512;             // threads per workgroup (8 waves)
+constexpr int kHB = 64;              // heads per workgroup
+constexpr int kTK = 64;              // keys per tile
+constexpr int kTPR = kNT / kTK;      // staging threads per key row
 constexpr int kMaxRopePairs = 32;
-constexpr int kMaxSplitKeys = 4096;  // key rows staged per split
+constexpr int kMaxSplitKeys = 2048;  // key rows listed per split
 constexpr int kMaxSplits = 64;
-constexpr int kTargetWG = 512;      // workgroups a launch aims at (two per CU)
+constexpr int kCUs = 256;            // one workgroup per CU
+constexpr int kMergeTiles = 2;       // the merge launch, in tile times (split planning)
+constexpr int kWgFixedTiles = 2;     // a workgroup's prologue and epilogue, in tile times
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may run ahead of the exponent base
 
-enum { kKvBf16 = 0, kKvFp8 = 1, kKvMxfp4 = 2 };
 
 struct AttnArgs {
   const uint16_t* q;         // [nq, H, D]
@@ -88,14 +85,15 @@ struct AttnArgs {
   float rope_base;
   float scale_log2;          // softmax_scale * log2(e)
   float q_rms_eps;           // > 0: unit-gain RMSNorm of each query head (folded into its logits)
-  int n_hg;                  // head groups of 16
+  int n_hb;                  // head blocks of 64
   int n_splits, keys_per_split;
-  int xcd_map;               // 1: a query's workgroups are issued to one XCD (round-robin dispatch)
+  int n_esplits;             // n_esplits < n_splits: splits [0, n_esplits) take keys_per_split entry keys
+                             // each, the rest win_per_split window keys each; else all keys in order
+  int win_per_split;
   uint16_t* out;             // [nq, H, d_v]
   float* out_lse;            // [nq, H]
-  float* part_o;             // [nq, n_hg, n_splits, 16, d_v]
-  float* part_ml;            // [nq, n_hg, n_splits, 16, 2]
-  double rev_freq[kMaxRopePairs];  // RoPE frequencies base^(-2i/d_rope) / (2 pi), formed on the host in fp64
+  float* part_o;             // [nq, n_hb, n_splits, 64, d_v]
+  float* part_ml;            // [nq, n_hb, n_splits, 64, 2]
 };
 
 // Per query: entry-key count, window start position and count.
@@ -109,7 +107,9 @@ struct KeySpace {
 __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
   KeySpace ks;
   ks.t = a.q_pos ? a.q_pos[qi] : a.pos0 + qi;
-  if (a.topk) {
+  if (a.N_cap == 0) {
+    ks.n_c = 0;  // no cache (every top-k slot would be masked)
+  } else if (a.topk) {
     ks.n_c = a.k;
   } else if (a.n_entries) {
     const int n = a.n_entries[qi];
@@ -161,106 +161,212 @@ __device__ __forceinline__ void rope8_hi_lo(uint4 v, int64_t pos, const double* 
 }
 
 // Eight e4m3 codes (two dwords, element i in byte i) -> eight bf16 (exact).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   uint4 v;
   v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
   v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
   v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
   v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-  return __builtin_bit_cast(bf16x8, v);
+  return v;
 }
 
+// Two floats to packed bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// v if ok, else zeros (component selects on values, so that register arrays stay in registers)
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-// LDS. Tiles: fp8 rows of D + 16 bytes, bf16 rows of D + 16 elements (both keep the MFMA operand
-// reads and the transposed reads free of bank conflicts), window remainders of the rotated
-// 32-dim blocks in klo. P^T is [key][head].
-template <int KD>
+// LDS. fp8 entry tiles live in a ring of kStages tiles of codes, chunk-major ([16-byte chunk of
+// dims][key][16 bytes]: a wave-wide request fills one chunk of all 64 keys, and the MFMA operand
+// reads and transposed reads touch consecutive 16-byte slots), filled by direct global-to-LDS
+// loads two tiles ahead of use; the per-entry scales beside them. bf16 tiles
+// (window tokens; bf16 and MXFP4 entries) overlay the ring: rows of D + 8 elements, and klo, window
+// keys' remainders of the last 64 dims (zero where not rotated). Rows are 16 bytes apart modulo
+// 256, so the MFMA operand reads and the transposed reads are free of bank conflicts. P^T is
+// [head][key]; xs carries the half of a block's partial logits that the other wave of the block
+// needs.
+constexpr int kStages = 3;
+template <int D>
 struct AttnSmem {
   union {
-    __align__(16) uint8_t k8[kTK8][KD * 32 + 16];
     struct {
-      __align__(16) uint16_t k16[kTK16][KD * 32 + 16];
-      __align__(16) uint16_t klo[kTK16][kRB * 32 + 8];
+      __align__(16) uint8_t k8[kStages][D / 16][kTK][16];
+      __align__(16) float sc[kStages][kTK];
+    } r;
+    struct {
+      __align__(16) uint16_t k[kTK][D + 8];
+      __align__(16) uint16_t klo[kTK][64 + 8];
     } b;
   } t;
-  __align__(16) uint16_t pt[kTK8][kHG];
-  float xmax[4][kHG];
-  float lsum[4][kHG];
-  float kscale[kTK8];   // per-key logit multiplier (log2 domain), -inf = masked
-  float kvscale[kTK8];  // per-key value multiplier (fp8 entry scale, else 1), 0 = masked
-  __align__(16) float qscale[kHG];
-  __align__(16) uint16_t qrh[kHG][2 * kMaxRopePairs];  // rotated query dims: bf16 value
-  __align__(16) uint16_t qrl[kHG][2 * kMaxRopePairs];  // and bf16 remainder
+  __align__(16) uint16_t p[kHB][kTK + 8];
+  __align__(16) f32x4 xs[8][2][kWave];
+  float xmax[4][kHB];
+  float lsum[4][kHB];
+  float qss[2][kHB];                 // query sums of squares over each half of the dims
+  int rescale;                       // a tile's logit exceeded its head's exponent base by more than the slack
+  double rev[kMaxRopePairs];         // RoPE frequencies (revolutions per position), from the host
   int sidx[kMaxSplitKeys];
 };
 
-// One tile's raw rows in registers. Thread t owns row t / TPR of the tile and its 16-byte chunks
-// t % TPR + TPR i (an MX block of 32 dims with its exponent byte for MXFP4), so it looks its row
-// up once and issues its loads from one base address. In a window row, thread j of the row also
-// owns the row's rotated chunk j (d_rope <= 64: at most 8 of them). Entry tiles and window tiles
-// share the registers (the first window tile is requested while the last entry tile is computed).
-template <int KD, int KV>
+// ---------------------------------------------------------------- fp8 entry tiles: direct loads
+// A wave-wide request of 16 (4) bytes per lane from gp into LDS at lds + 16 * lane (4 * lane),
+// the LDS address taken from M0. Nothing is written to registers; the data lands asynchronously
+// and is waited for with s_waitcnt vmcnt, whose count these requests advance in issue order.
+__device__ __forceinline__ void dma16(const void* gp, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gp) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gp, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gp) : "memory", "m0");
+}
+// The wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// s_waitcnt with only the vector-memory count: vmcnt <= n (n < 16)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+// One fp8 tile is D/16 wave-wide chunk requests (lane = key) plus one request for the scales,
+// request i issued by wave i % 8.
+template <int D>
+struct RingGeom {
+  static constexpr int NCH = D / 16;          // chunk requests
+  static constexpr int NREQ = NCH + 1;        // then the scale request
+  static constexpr int reqs(int w) { return w < NREQ ? (NREQ - 1 - w) / 8 + 1 : 0; }
+};
+
+// Requests tile rows [key0, key0 + 64) of the split (entry rows from sidx; a masked key or a key
+// past e_end reads row 0, which the validity mask hides) into ring stage `stage`. Every lane of
+// every wave takes part in each of its wave's requests, so the count per wave is fixed.
+template <int D>
+__device__ __forceinline__ void issue_tile_f8(AttnSmem<D>& sm, int stage, const uint8_t* cbase, const float* sbase,
+                                              int key0, int e_end, int key_begin) {
+  using G = RingGeom<D>;
+  const int lane = threadIdx.x & (kWave - 1), w = wave_id();
+  const uint32_t base = lds_addr(&sm.t.r.k8[stage][0][0][0]);
+  const int key = key0 + lane;
+  const int row = max(key < e_end ? sm.sidx[key - key_begin] : -1, 0);
+  const uint8_t* src = cbase + (int64_t)row * D;
+#pragma unroll
+  for (int j = 0; j < (G::NREQ + 7) / 8; ++j) {
+    const int i = w + 8 * j;
+    if (i < G::NCH)
+      dma16(src + 16 * i, __builtin_amdgcn_readfirstlane(base + 1024u * (uint32_t)i));
+    else if (i == G::NCH)
+      dma4(sbase + row, __builtin_amdgcn_readfirstlane(lds_addr(&sm.t.r.sc[stage][0])));
+  }
+}
+
+// Waits for this wave's requests of the current tile: `later` says whether the next tile's
+// requests were issued after them (they may stay in flight).
+template <int D>
+__device__ __forceinline__ void wait_tile_f8(bool later) {
+  using G = RingGeom<D>;
+  const int w = wave_id();
+  if (!later) {
+    wait_vm<0>();
+    return;
+  }
+  switch (G::reqs(w)) {  // the count is wave-uniform; each case is an immediate
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
+
+// Validity of the tile's 64 keys (key0 + lane < end and its row listed), the same in every wave.
+template <int D>
+__device__ __forceinline__ uint64_t tile_mask(const AttnSmem<D>& sm, int key0, int end, int key_begin) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int key = key0 + lane;
+  const bool ok = key < end && sm.sidx[key - key_begin] >= 0;
+  return __ballot(ok);
+}
+
+// ---------------------------------------------------------------- bf16 tiles: register staging
+// One tile's raw rows in registers. Thread t owns row t / kTPR of the tile and its 16-byte chunks
+// t % kTPR + kTPR i (an MX block of 32 dims with its exponent byte for MXFP4), so it looks its row
+// up once and issues its loads from one base address. bf16 and MXFP4 entry tiles and window tiles
+// (at most two per query) are loaded when they are staged.
+template <int D, int KV>
 struct EntryGeom {
-  static constexpr int TK = KV == kKvFp8 ? kTK8 : kTK16;
-  static constexpr int TPR = kNT / TK;  // threads per row
-  static constexpr int CPR = KV == kKvFp8 ? KD * 2 : (KV == kKvBf16 ? KD * 4 : KD);  // chunks per row
-  static constexpr int NC = (CPR + TPR - 1) / TPR;  // chunks per thread
+  static constexpr int CPR = KV == kKvBf16 ? D / 8 : D / 32;  // chunks per row
+  static constexpr int NC = (CPR + kTPR - 1) / kTPR;          // chunks per thread
 };
-template <int KD>
+template <int D>
 struct WinGeom {
-  static constexpr int TPR = kNT / kTK16;
-  static constexpr int CPR = KD * 4;
-  static constexpr int NC = (CPR + TPR - 1) / TPR;
+  static constexpr int CPR = D / 8;
+  static constexpr int NC = CPR / kTPR;  // D % 64 == 0; the last one holds the last 64 dims
 };
-template <int KD, int KV>
+template <int D, int KV>
 struct TileRegs {
-  static constexpr int NV = EntryGeom<KD, KV>::NC > WinGeom<KD>::NC ? EntryGeom<KD, KV>::NC : WinGeom<KD>::NC;
-  uint4 v[NV];
-  uint4 rot;  // window tiles: this thread's rotated chunk
-  uint32_t bs[KV == kKvMxfp4 ? EntryGeom<KD, KV>::NC : 1];
-  float sc;
+  uint4 v[EntryGeom<D, KV>::NC];
+  uint32_t bs[KV == kKvMxfp4 ? EntryGeom<D, KV>::NC : 1];
   int row;    // -1: masked
+};
+template <int D>
+struct WinRegs {
+  uint4 v[WinGeom<D>::NC];
+  int row;
 };
 
 // Tile loads. The rows of a split's keys were resolved into sm.sidx (entry row in the cache,
 // window row in win, -1 = masked). Loads are unconditional (a masked row reads row 0, a chunk past
 // the row end its last chunk); the store writes zeros for a masked row (a masked key gets p = 0,
 // which must not meet a non-finite value in the MFMA).
-template <int KD, int KV>
+template <int D, int KV>
 __device__ __forceinline__ void entry_load(const uint8_t* cbase, const uint8_t* sbase, int key0, int key_end,
-                                           int key_begin, const AttnSmem<KD>& sm, TileRegs<KD, KV>& R) {
-  using EG = EntryGeom<KD, KV>;
-  constexpr int D = KD * 32;
-  constexpr int RB = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);  // code bytes per row
-  const int r = threadIdx.x / EG::TPR, c0 = threadIdx.x % EG::TPR;
+                                           int key_begin, const AttnSmem<D>& sm, TileRegs<D, KV>& R) {
+  using EG = EntryGeom<D, KV>;
+  constexpr int RB = KV == kKvBf16 ? 2 * D : D / 2;  // code bytes per row
+  const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
   const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
   R.row = row;
   const int64_t rr = max(row, 0);
   const uint8_t* src = cbase + rr * RB;
 #pragma unroll
   for (int i = 0; i < EG::NC; ++i) {
-    const int ch = EG::CPR % EG::TPR == 0 ? c0 + EG::TPR * i : min(c0 + EG::TPR * i, EG::CPR - 1);
+    const int ch = EG::CPR % kTPR == 0 ? c0 + kTPR * i : min(c0 + kTPR * i, EG::CPR - 1);
     R.v[i] = *reinterpret_cast<const uint4*>(src + 16 * ch);
-    if constexpr (KV == kKvMxfp4) R.bs[i] = sbase[rr * KD + ch];
+    if constexpr (KV == kKvMxfp4) R.bs[i] = sbase[rr * (D / 32) + ch];
   }
-  R.sc = KV == kKvFp8 ? reinterpret_cast<const float*>(sbase)[rr] : 1.f;
 }
 
-template <int KD, int KV>
-__device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD>& sm, const TileRegs<KD, KV>& R) {
-  using EG = EntryGeom<KD, KV>;
-  const int r = threadIdx.x / EG::TPR, c0 = threadIdx.x % EG::TPR;
+template <int D, int KV>
+__device__ __forceinline__ void entry_store(AttnSmem<D>& sm, const TileRegs<D, KV>& R) {
+  using EG = EntryGeom<D, KV>;
+  const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
   const bool ok = R.row >= 0;
 #pragma unroll
   for (int i = 0; i < EG::NC; ++i) {
-    const int ch = c0 + EG::TPR * i;
-    if (EG::CPR % EG::TPR != 0 && ch >= EG::CPR) continue;
-    if constexpr (KV == kKvFp8) {
-      *reinterpret_cast<uint4*>(&sm.t.k8[r][16 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
-    } else if constexpr (KV == kKvBf16) {
-      *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
+    const int ch = c0 + kTPR * i;
+    if (EG::CPR % kTPR != 0 && ch >= EG::CPR) continue;
+    if constexpr (KV == kKvBf16) {
+      *reinterpret_cast<uint4*>(&sm.t.b.k[r][8 * ch]) = keep_if(ok, R.v[i]);
     } else {
       // exact e2m1 * 2^E -> bf16, two values (one code byte, low nibble first) per instruction
       const float s = __builtin_amdgcn_ldexpf(1.0f, (int)R.bs[i] - 127);
@@ -272,264 +378,321 @@ __device__ __forceinline__ void entry_store(const AttnArgs& a, AttnSmem<KD>& sm,
         o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 1));
         o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 2));
         o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[q], s, 3));
-        *reinterpret_cast<uint4*>(&sm.t.b.k16[r][32 * ch + 8 * q]) = ok ? o : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sm.t.b.k[r][32 * ch + 8 * q]) = keep_if(ok, o);
       }
     }
   }
-  if (c0 == 0) {
-    sm.kscale[r] = ok ? a.scale_log2 * R.sc : -INFINITY;
-    sm.kvscale[r] = ok ? R.sc : 0.f;
-  }
 }
 
-// Window rows: thread j of a row takes its unrotated chunks j + 8 i and, for j < d_rope/8, the
-// rotated chunk j.
-template <int KD, int KV>
-__device__ __forceinline__ void window_load(const AttnArgs& a, int key0, int key_end, int key_begin, int rope0,
-                                            const AttnSmem<KD>& sm, TileRegs<KD, KV>& R) {
-  using WG = WinGeom<KD>;
-  constexpr int D = KD * 32;
-  const int r = threadIdx.x / WG::TPR, c0 = threadIdx.x % WG::TPR;
+template <int D>
+__device__ __forceinline__ void window_load(const AttnArgs& a, int key0, int key_end, int key_begin,
+                                            const AttnSmem<D>& sm, WinRegs<D>& R) {
+  using WG = WinGeom<D>;
+  const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
   const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
   R.row = row;
   const uint16_t* src = a.win + (int64_t)max(row, 0) * D;
-  const int nu = rope0 >> 3;  // unrotated chunks
 #pragma unroll
-  for (int i = 0; i < WG::NC; ++i) R.v[i] = *reinterpret_cast<const uint4*>(src + 8 * min(c0 + WG::TPR * i, WG::CPR - 1));
-  R.rot = *reinterpret_cast<const uint4*>(src + min(rope0 + 8 * c0, D - 8));
-  (void)nu;
+  for (int i = 0; i < WG::NC; ++i) R.v[i] = *reinterpret_cast<const uint4*>(src + 8 * (c0 + kTPR * i));
 }
 
-// Window rows into the bf16 tile; the rotated chunk is rotated at the token's position here, the
-// remainder going to klo.
-template <int KD, int KV>
-__device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, int rope0,
-                                             AttnSmem<KD>& sm, const TileRegs<KD, KV>& R) {
-  using WG = WinGeom<KD>;
-  constexpr int D = KD * 32;
-  const int r = threadIdx.x / WG::TPR, c0 = threadIdx.x % WG::TPR;
-  const int nu = rope0 >> 3;
+// Window rows into the tile: rotated chunks (all in the last 64 dims, held by each thread's last
+// chunk) are rotated at the token's position, the bf16 remainder going to klo.
+template <int D>
+__device__ __forceinline__ void window_store(const AttnArgs& a, const KeySpace& ks, int key0, AttnSmem<D>& sm,
+                                             const WinRegs<D>& R) {
+  using WG = WinGeom<D>;
+  const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
+  const int rope0 = D - a.d_rope;
   const bool ok = R.row >= 0;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int64_t pos = ks.w0 + (key0 + r - ks.n_c);
 #pragma unroll
   for (int i = 0; i < WG::NC; ++i) {
-    const int ch = c0 + WG::TPR * i;
-    if (ch < nu) *reinterpret_cast<uint4*>(&sm.t.b.k16[r][8 * ch]) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
-  }
-  if (8 * c0 < a.d_rope) {
-    uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
-    if (ok) rope8_hi_lo(R.rot, ks.w0 + (key0 + r - ks.n_c), a.rev_freq, 4 * c0, &hi, &lo);
-    const int d0 = rope0 + 8 * c0;
-    *reinterpret_cast<uint4*>(&sm.t.b.k16[r][d0]) = hi;
-    *reinterpret_cast<uint4*>(&sm.t.b.klo[r][d0 - (D - 64)]) = lo;
-  }
-  if (c0 == 0) {
-    sm.kscale[r] = ok ? a.scale_log2 : -INFINITY;
-    sm.kvscale[r] = ok ? 1.f : 0.f;
+    const int d0 = 8 * (c0 + kTPR * i);
+    uint4 hi = keep_if(ok, R.v[i]);
+    if (i == WG::NC - 1) {
+      uint4 lo = z;
+      if (ok && d0 >= rope0) rope8_hi_lo(R.v[i], pos, sm.rev, (d0 - rope0) >> 1, &hi, &lo);
+      *reinterpret_cast<uint4*>(&sm.t.b.klo[r][d0 - (D - 64)]) = lo;
+    }
+    *reinterpret_cast<uint4*>(&sm.t.b.k[r][d0]) = hi;
   }
 }
 
-// Per-wave online-softmax state for heads 4g..4g+3 of the lane's group. m is the exponent base
-// of the running sums; it may lag the true running maximum by up to kRescaleSlack (p <= 2^8),
-// so O is rescaled only when a logit exceeds it by more than that. l holds this wave's keys only.
-template <int NO>
-struct WaveState {
-  f32x4 o[NO];
-  float m[4], l[4];
+// ---------------------------------------------------------------- the query
+// The QK dims of a block of S^T are shared by two waves (dq = 0, 1): steps [0, NSQ0) and
+// [NSQ0, NS) of 16 dims, split so that both issue the same number of MFMAs (a step in the last 64
+// dims carries a second product for the query remainder).
+template <int D>
+constexpr int qk_split() {
+  constexpr int NS = D / 16, RS0 = (D - 64) / 16;
+  const int total = NS + (NS - RS0);
+  int acc = 0;
+  for (int s = 0; s < NS; ++s) {
+    acc += s >= RS0 ? 2 : 1;
+    if (2 * acc >= total) return s + 1;
+  }
+  return NS;
+}
+template <int D, int DQ>
+struct QkRange {
+  static constexpr int NS = D / 16, RS0 = (D - 64) / 16, NSQ0 = qk_split<D>();
+  static constexpr int S0 = DQ ? NSQ0 : 0, S1 = DQ ? NS : NSQ0;
+  static constexpr int LO0 = S0 > RS0 ? S0 : RS0;        // first step with a query remainder
+  static constexpr int NLO = S1 > LO0 ? S1 - LO0 : 0;    // steps with a query remainder
+  static constexpr int NQ = S1 - S0, NLOA = NLO > 0 ? NLO : 1;
 };
 
-// S for keys [16w, 16w + 16) of the tile staged in LDS. F8: fp8 rows; WIN: window rows (key
-// remainders of the last 64 dims in klo). The rotated dims (d_rope <= 64) lie in the last two
-// 32-dim blocks, whose query remainders (qlo) and window-key remainders are zero outside them.
-template <int KD, bool F8, bool WIN>
-__device__ __forceinline__ f32x4 tile_qk(const AttnSmem<KD>& sm, const uint4* qa, const uint4* qlo) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  const int krow = 16 * w + col;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int BQ = 3;  // operand reads in flight ahead of the MFMAs
-  constexpr int RB0 = KD >= kRB ? KD - kRB : 0;  // first block that may hold rotated dims
+// The query's dims of this wave's steps, lane (head c, half u) holding dims 16 s + 8 u .. + 7 of
+// head c; returns the lane's sum of squares of the raw values (query RMSNorm).
+template <int D, int DQ>
+__device__ __forceinline__ float load_query(const AttnArgs& a, int qi, int hq, uint4* q) {
+  using R = QkRange<D, DQ>;
+  const int ko = 8 * ((threadIdx.x & (kWave - 1)) >> 5);
+  // heads past H (a partial block) compute with head H - 1's dims; their results are not written
+  const uint16_t* src = a.q + ((int64_t)qi * a.H + min(hq, a.H - 1)) * D + ko;
 #pragma unroll
-  for (int s0 = 0; s0 < KD; s0 += BQ) {
-    bf16x8 kb[BQ];
+  for (int s = R::S0; s < R::S1; ++s) q[s - R::S0] = *reinterpret_cast<const uint4*>(src + 16 * s);
+  float ss = 0.f;
+  if (a.q_rms_eps > 0.f) {
 #pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      const int s = s0 + u;
-      if (s < KD) {
-        if constexpr (F8) {
-          const uint2 v = *reinterpret_cast<const uint2*>(&sm.t.k8[krow][32 * s + 8 * g]);
-          kb[u] = fp8x8_to_bf16(v.x, v.y);
-        } else {
-          kb[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.t.b.k16[krow][32 * s + 8 * g]));
-        }
-      }
+    for (int s = R::S0; s < R::S1; ++s) {
+      float f[8];
+      unpack8(q[s - R::S0], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
     }
+  }
+  return ss;
+}
+
+// The rotated dims among this wave's steps (the last d_rope of D): a bf16 value and a bf16
+// remainder (qlo, indexed by step - LO0; zero elsewhere).
+template <int D, int DQ>
+__device__ __forceinline__ void rotate_query(const AttnArgs& a, const double* rev, int64_t t, uint4* q, uint4* qlo) {
+  using R = QkRange<D, DQ>;
+  const int ko = 8 * ((threadIdx.x & (kWave - 1)) >> 5);
+  const int rope0 = D - a.d_rope;
 #pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      const int s = s0 + u;
-      if (s < KD) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[s]), kb[u], acc, 0, 0, 0);
-        if (s >= RB0) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qlo[s - RB0]), kb[u], acc, 0, 0, 0);
-          if constexpr (WIN) {
-            const bf16x8 kl = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4*>(&sm.t.b.klo[krow][32 * (s - RB0) + 8 * g]));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[s]), kl, acc, 0, 0, 0);
-          }
-        }
+  for (int s = R::LO0; s < R::S1; ++s) {
+    uint4 lo = make_uint4(0, 0, 0, 0);
+    const int d0 = 16 * s + ko;
+    if (d0 >= rope0) rope8_hi_lo(q[s - R::S0], t, rev, (d0 - rope0) >> 1, &q[s - R::S0], &lo);
+    qlo[s - R::LO0] = lo;
+  }
+}
+
+// ---------------------------------------------------------------- S^T = K Q^T
+// Partial S^T over this wave's steps for keys [32 kh, 32 kh + 32) of the staged tile and the
+// wave's 32 heads; steps in the last 64 dims add the query remainders and, for window keys, the
+// key remainders in klo. F8: the tile is a ring stage of fp8 codes (widened to bf16 as read).
+template <int D, bool F8, bool WIN, int DQ>
+__device__ __forceinline__ f32x16 tile_qk(const AttnSmem<D>& sm, int stage, const uint4* q, const uint4* qlo,
+                                          int kh) {
+  using R = QkRange<D, DQ>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int key = 32 * kh + (lane & 31), ko = 8 * (lane >> 5);
+  constexpr int NP = 3;  // key operands in flight ahead of the MFMAs
+  auto read = [&](int s) -> uint4 {
+    if constexpr (F8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(&sm.t.r.k8[stage][s][key][ko]);
+      return fp8x8_to_bf16(v.x, v.y);
+    } else {
+      return *reinterpret_cast<const uint4*>(&sm.t.b.k[key][16 * s + ko]);
+    }
+  };
+  uint4 kv[NP];
+#pragma unroll
+  for (int u = 0; u < NP - 1; ++u)
+    if (R::S0 + u < R::S1) kv[u] = read(R::S0 + u);
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = R::S0; s < R::S1; ++s) {
+    const int j = s - R::S0;
+    if (s + NP - 1 < R::S1) kv[(j + NP - 1) % NP] = read(s + NP - 1);
+    acc = mfma32(kv[j % NP], q[j], acc);
+    if (s >= R::LO0) {
+      acc = mfma32(kv[j % NP], qlo[s - R::LO0], acc);
+      if constexpr (WIN) {
+        const uint4 kl = *reinterpret_cast<const uint4*>(&sm.t.b.klo[key][16 * (s - R::RS0) + ko]);
+        acc = mfma32(kl, q[j], acc);
       }
     }
   }
   return acc;
 }
 
-// O += P V over the staged tile (NKS steps of 32 keys) for this wave's value dims. P (A operand):
-// lane (head col, group g) holds keys 8g..8g+7 of a step; V (B operand): lane (dim col, group g)
-// holds the same keys of its dim.
-template <int KD, int NO, bool F8, int NKS, int NVB>
-__device__ __forceinline__ void tile_pv(const AttnSmem<KD>& sm, WaveState<NO>& st) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  constexpr bool kEven = NO * 4 == NVB;  // every wave owns NO value dim blocks
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const int kb0 = 32 * ks + 8 * g;
-    bf16x8 pa;
-    {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.pt[kb0 + (col >> 2)][4 * (col & 3)]));
-      const i16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.pt[kb0 + 4 + (col >> 2)][4 * (col & 3)]));
-      pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    constexpr int BV = 4;
-#pragma unroll
-    for (int n0 = 0; n0 < NO; n0 += BV) {
-      bf16x8 vb[BV];
-#pragma unroll
-      for (int u = 0; u < BV; ++u) {
-        const int n = n0 + u;
-        const int nb = w * NO + n;  // value dim block of this wave
-        if (n < NO && (kEven || nb < NVB)) {
-          if constexpr (F8) {
-            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_i32x2*)(&sm.t.k8[kb0 + (col >> 1)][16 * nb + 8 * (col & 1)]));
-            vb[u] = fp8x8_to_bf16((uint32_t)v.x, (uint32_t)v.y);
-          } else {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(&sm.t.b.k16[kb0 + (col >> 2)][16 * nb + 4 * (col & 3)]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(&sm.t.b.k16[kb0 + 4 + (col >> 2)][16 * nb + 4 * (col & 3)]));
-            vb[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < BV; ++u) {
-        const int n = n0 + u;
-        if (n < NO && (kEven || w * NO + n < NVB))
-          st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[u], st.o[n], 0, 0, 0);
-      }
-    }
-  }
-}
+// ---------------------------------------------------------------- softmax
+// Per-lane online-softmax state of the lane's head. m is the exponent base of the running sums;
+// it may lag the true running maximum by up to kRescaleSlack (p <= 2^8), so O is rescaled only
+// when a logit exceeds it by more than that. l holds the keys this lane wrote P for.
+template <int NO>
+struct HeadState {
+  f32x16 o[NO];  // O^T rows (value dims) of this wave's blocks, column = the lane's head
+  float m, l;
+};
 
-// Softmax of one staged tile of TK keys (wave w owns keys [16w, 16w+16) when 16w < TK): tile maxima
-// through LDS, the exponent base moved when needed (every wave rescales its O), P^T to LDS.
-// Ends with the barrier that makes P^T visible.
-template <int KD, int NO>
-__device__ __forceinline__ void tile_softmax(AttnSmem<KD>& sm, WaveState<NO>& st, const f32x4& s, int TK) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  const int krow = 16 * w + col;
-  const bool active = 16 * w < TK;
-  float x[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  if (active) {
-    const float ck = sm.kscale[krow];
-    const f32x4 qs = *reinterpret_cast<const f32x4*>(&sm.qscale[4 * g]);
+// Softmax of one staged tile. The two waves of a block of S^T (first and second half of the dims)
+// hand each other the half of their partial logits that the other needs through LDS; each then
+// forms the logits of half of the block's keys (valid: the tile's key mask; vsc: per-key scales of
+// fp8 entries, else 1), writes their P^T with the current exponent base and flags the tile if a
+// logit exceeds its head's base by more than the slack. After the barrier that makes P^T visible,
+// a flagged tile (the first one, and rarely another) takes the base from the four waves' maxima:
+// every wave rescales its O and l and forms its P^T again. Ends with P^T visible.
+template <int D, int NO>
+__device__ __forceinline__ void tile_softmax(const AttnArgs& a, AttnSmem<D>& sm, HeadState<NO>& st, const f32x16& s,
+                                             int w, uint64_t valid, const float* vsc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hh = w & 1, kh = (w >> 1) & 1, dq = w >> 2;
+  const int hl = 32 * hh + (lane & 31), kr = 32 * kh + 4 * (lane >> 5);  // keys kr + 8 g + e
+  // the partner's groups of this wave's partial logits
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = ck == -INFINITY ? -INFINITY : s[r] * qs[r] * ck;
-      const float m_ = row16_max(x[r]);
-      if (col == 0) sm.xmax[w][4 * g + r] = m_;
-    }
+  for (int gg = 0; gg < 2; ++gg) {
+    const int g = 2 * (1 - dq) + gg;
+    sm.xs[w][gg][lane] = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
   }
   __syncthreads();
-  const int nk = TK / 16;
-  bool need = false;
-  float mx[4];
+  const float qs = a.q_rms_eps > 0.f ? 1.0f / sqrtf((sm.qss[0][hl] + sm.qss[1][hl]) / (float)D + a.q_rms_eps)
+                                     : 1.0f;  // query RMSNorm factor of the lane's head
+  float lt = 0.f;
+  // logits of this wave's keys (own partial + the partner's, added in dims order), then P^T with
+  // exponent base `base`; returns the head's maximum over this wave's keys
+  auto form_p = [&](float base) {
+    float mloc = -INFINITY;
+    lt = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mx[r] = sm.xmax[0][4 * g + r];
-    for (int j = 1; j < nk; ++j) mx[r] = fmaxf(mx[r], sm.xmax[j][4 * g + r]);
-    need |= mx[r] > st.m[r] + kRescaleSlack;
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = 2 * dq + gg;
+      const f32x4 o = sm.xs[w ^ 4][gg][lane];
+      const f32x4 vk = vsc ? *reinterpret_cast<const f32x4*>(vsc + kr + 8 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kr + 8 * g + e;
+        const float sum = dq == 0 ? s[4 * g + e] + o[e] : o[e] + s[4 * g + e];
+        const bool ok = (valid >> key) & 1;
+        const float x = ok ? sum * (qs * a.scale_log2 * vk[e]) : -INFINITY;
+        mloc = fmaxf(mloc, x);
+        // exponent <= kRescaleSlack once the base is set; below the fp32 range p flushes to 0
+        const float p = __builtin_amdgcn_exp2f(x - base);
+        lt += p;
+        pv[e] = ok ? p * vk[e] : 0.f;  // value-side scale folded into P
+      }
+      uint2 wv;
+      wv.x = cvt_bf16x2(pv[0], pv[1]);
+      wv.y = cvt_bf16x2(pv[2], pv[3]);
+      *reinterpret_cast<uint2*>(&sm.p[hl][kr + 8 * g]) = wv;
+    }
+    return fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+  };
+  {
+    const float mloc = form_p(st.m == -INFINITY ? 0.f : st.m);
+    if (lane < 32) sm.xmax[2 * kh + dq][hl] = mloc;
+    if (__ballot(mloc > st.m + kRescaleSlack) && lane == 0) sm.rescale = 1;
   }
-  if (__ballot(need)) {  // rare after the first tile: move the exponent base up, rescale O and l
-    float alpha[4];
+  __syncthreads();
+  if (sm.rescale) {  // the same in every wave: move the exponent base up, rescale O and l
+    const float tmax = fmaxf(fmaxf(sm.xmax[0][hl], sm.xmax[1][hl]), fmaxf(sm.xmax[2][hl], sm.xmax[3][hl]));
+    if (tmax > st.m + kRescaleSlack) {
+      const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - tmax);
+      st.l *= alpha;
+      st.m = tmax;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mnew = mx[r] > st.m[r] + kRescaleSlack ? mx[r] : st.m[r];
-      alpha[r] = st.m[r] == -INFINITY ? 0.f : exp2f(st.m[r] - mnew);
-      st.l[r] *= alpha[r];
-      st.m[r] = mnew;
+      for (int n = 0; n < NO; ++n) st.o[n] *= alpha;
+    }
+    form_p(st.m);
+    __syncthreads();
+    if (threadIdx.x == 0) sm.rescale = 0;  // read by every wave before the barrier above
+  }
+  st.l += lt;
+}
+
+// ---------------------------------------------------------------- O^T += V^T P^T
+// Over the staged tile (four steps of 16 keys) for this wave's value-dim blocks. V^T (A operand):
+// lane (dim c, half u) holds keys 8u .. 8u+7 of the step for its dim: one transposed byte read of
+// an fp8 ring stage (keys the mask `valid` hides are zeroed: a ring row may hold anything), or two
+// transposed 16-bit reads of 4 keys from a bf16 tile; P^T (B operand): lane (head c, half u) the
+// same keys of its head.
+template <int D, int NO, int NB, bool F8>
+__device__ __forceinline__ void tile_pv(const AttnSmem<D>& sm, HeadState<NO>& st, int hh, int vq, int stage,
+                                        uint64_t valid) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hl = 32 * hh + (lane & 31), u = lane >> 5, L = lane & 15;
+  const bool all = valid == ~0ull;
+#pragma unroll
+  for (int ks = 0; ks < kTK / 16; ++ks) {
+    const uint4 pb = *reinterpret_cast<const uint4*>(&sm.p[hl][16 * ks + 8 * u]);
+    uint32_t m0 = ~0u, m1 = ~0u;  // byte masks of the lane's 8 keys
+    if (F8 && !all) {
+      const uint32_t bits = (uint32_t)(valid >> (16 * ks + 8 * u)) & 0xFFu;
+      m0 = m1 = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m0 |= ((bits >> i) & 1u) ? (0xFFu << (8 * i)) : 0u;
+        m1 |= ((bits >> (4 + i)) & 1u) ? (0xFFu << (8 * i)) : 0u;
+      }
     }
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.o[n][r] *= alpha[r];
+      const int b = vq * NO + n;
+      if (NB % 4 != 0 && b >= NB) continue;
+      uint4 va;
+      if constexpr (F8) {
+        const int key0 = 16 * ks + 8 * u + (L >> 1);
+        const int ch = 2 * b + ((lane >> 4) & 1);  // dims 16 ch .. 16 ch + 15
+        const i32x2 v =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(&sm.t.r.k8[stage][ch][key0][8 * (L & 1)]));
+        va = fp8x8_to_bf16((uint32_t)v.x & m0, (uint32_t)v.y & m1);
+      } else {
+        const int key0 = 16 * ks + 8 * u + (L >> 2);
+        const int dim0 = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.t.b.k[key0][dim0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&sm.t.b.k[key0 + 4][dim0]));
+        va = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      st.o[n] = mfma32(va, pb, st.o[n]);
     }
   }
-  if (active) {
-    const float vk = sm.kvscale[krow];
-    float pv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float base = st.m[r] == -INFINITY ? 0.f : st.m[r];
-      const float p = exp2f(x[r] - base);
-      st.l[r] += row16_sum(p);
-      pv[r] = p * vk;  // value-side scale folded into P
-    }
-    uint2 wv;
-    wv.x = pack_bf16x2(pv[0], pv[1]);
-    wv.y = pack_bf16x2(pv[2], pv[3]);
-    *reinterpret_cast<uint2*>(&sm.pt[krow][4 * g]) = wv;
-  }
-  __syncthreads();
 }
 
-template <int KD, int NVB, int KV>
-__global__ __launch_bounds__(kNT, 2) void attn_kernel(AttnArgs a) {
-  constexpr int D = KD * 32;
-  constexpr int NO = (NVB + 3) / 4;  // value dim blocks per wave
+// ---------------------------------------------------------------- the kernel
+// The work of one wave: DQ is the wave's half of the QK dims (a template parameter, so that only
+// that half's query registers exist).
+template <int D, int DV, int KV, int DQ>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
+  using R = QkRange<D, DQ>;
+  constexpr int NB = DV / 32, NO = (NB + 3) / 4;
   constexpr bool F8 = KV == kKvFp8;
-  constexpr int TKE = F8 ? kTK8 : kTK16;
-  __shared__ AttnSmem<KD> sm;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
-  const int g = lane >> 4, col = lane & 15;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
+  // QK: wave (hh, kh, dq) = head half, key half, half of the dims; PV: (hh, vq) = head half,
+  // quarter of the value dims; w = hh + 2 kh + 4 dq = hh + 2 vq
+  const int hh = w & 1, kh = (w >> 1) & 1, vq = w >> 1;
+  const int hl = 32 * hh + (lane & 31);
+  const int split = (int)(blockIdx.x % (unsigned)a.n_splits);
+  const int qh = (int)(blockIdx.x / (unsigned)a.n_splits);
+  const int qi = qh / a.n_hb;
+  const int hq = (qh % a.n_hb) * kHB + hl;  // this lane's head
 
-  // work item (query, head group, split); with xcd_map the items of a query are contiguous in
-  // the order of one XCD's workgroups (workgroups go round-robin to the 8 XCDs)
-  const int total = a.nq * a.n_hg * a.n_splits;
-  const int item = a.xcd_map ? (int)(blockIdx.x & 7) * (total >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-  const int split = item % a.n_splits;
-  const int qh = item / a.n_splits;
-  const int hg = qh % a.n_hg, qi = qh / a.n_hg;
-  const int h0 = hg * kHG;
-  const int rope0 = D - a.d_rope;
-  constexpr int RB0 = KD >= kRB ? KD - kRB : 0;  // first block that may hold rotated dims
-
-  // the query's raw dims: requested first, they depend on nothing else
-  uint4 qa[KD], qlo[kRB];
-  const int h = h0 + col;
-#pragma unroll
-  for (int s = 0; s < KD; ++s) {
-    const int d0 = 32 * s + 8 * g;
-    qa[s] = h < a.H ? *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + h) * D + d0) : make_uint4(0, 0, 0, 0);
-  }
-  qlo[0] = qlo[1] = make_uint4(0, 0, 0, 0);
+  // the query's dims of this lane's head and wave's steps: requested first (their latency
+  // overlaps the listing of the split's rows)
+  uint4 q[R::NQ], qlo[R::NLOA];
+  float ss = load_query<D, DQ>(a, qi, hq, q);
 
   const KeySpace ks = key_space(a, qi);
-  const int n_keys = ks.n_c + ks.n_w;
-  const int key_begin = split * a.keys_per_split;
-  const int key_end = min(n_keys, key_begin + a.keys_per_split);
+  int key_begin, key_end;
+  if (a.n_esplits < a.n_splits) {  // entry splits, then window splits
+    if (split < a.n_esplits) {
+      key_begin = split * a.keys_per_split;
+      key_end = min(ks.n_c, key_begin + a.keys_per_split);
+    } else {
+      key_begin = ks.n_c + (split - a.n_esplits) * a.win_per_split;
+      key_end = min(ks.n_c + ks.n_w, key_begin + a.win_per_split);
+    }
+  } else {
+    key_begin = split * a.keys_per_split;
+    key_end = min(ks.n_c + ks.n_w, key_begin + a.keys_per_split);
+  }
   const int e_end = min(key_end, ks.n_c);  // entry keys [key_begin, e_end), window keys after
   const int w_begin = max(key_begin, ks.n_c);
   // the rows of this split's keys: entry rows in the sequence's cache (top-k slot or dense
@@ -551,155 +714,131 @@ __global__ __launch_bounds__(kNT, 2) void attn_kernel(AttnArgs a) {
       sm.sidx[i] = row;
     }
   }
-  if (tid < kTK16) {  // window remainders of the last 64 dims below rope0 are zero
-    for (int d = D - 64; d < rope0; ++d)
-      if (d >= 0) sm.t.b.klo[tid][d - (D - 64)] = 0;
-  }
-  __syncthreads();  // sidx ready
+  // the RoPE table in revolutions per position, base^(-2i / d_rope) / (2 pi), in fp64
+  if (w == 0 && 2 * lane < a.d_rope)
+    sm.rev[lane] = exp2(-2.0 * (double)lane / (double)a.d_rope * log2((double)a.rope_base)) *
+                   0.15915494309189533576888376337251;
+  if (tid == 0) sm.rescale = 0;
+  __syncthreads();  // sidx and the RoPE table ready
 
   const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
   constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);
   constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);
   const uint8_t* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
   const uint8_t* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
+  const int n_et = key_begin < e_end ? (e_end - key_begin + kTK - 1) / kTK : 0;  // entry tiles
 
-  // the split's first tile is requested before the query rotation, whose arithmetic then
-  // overlaps the loads
-  const bool has_e = key_begin < e_end;
-  TileRegs<KD, KV> RT;
-  if (has_e)
-    entry_load<KD, KV>(cbase, sbase, key_begin, e_end, key_begin, sm, RT);
-  else if (w_begin < key_end)
-    window_load<KD, KV>(a, w_begin, key_end, key_begin, rope0, sm, RT);
+  // the first fp8 entry tile, then the query's dims of this lane's head and wave's steps
+  if (F8 && n_et > 0)
+    issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin);
+  ss += __shfl_xor(ss, 32, kWave);
+  if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
+  rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
+  // every load so far (the query, the first tile) has landed: the loop then waits on tile loads
+  // only where a tile is used, never because a query register might be pending
+  __builtin_amdgcn_s_waitcnt(0);
+  if (F8 && n_et > 1)
+    issue_tile_f8<D>(sm, 1, cbase, reinterpret_cast<const float*>(sbase), key_begin + kTK, e_end, key_begin);
 
-  // the query's rotated dims: each of the 16 heads x d_rope/8 chunks rotated once at t (a bf16
-  // value and a bf16 remainder) into LDS
-  {
-    const int rc = a.d_rope >> 3;
-    if ((int)tid < kHG * rc) {
-      const int hl = tid / rc, ch = tid - hl * rc;
-      const int hh = h0 + hl;
-      uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
-      if (hh < a.H) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.H + hh) * D + rope0 + 8 * ch);
-        rope8_hi_lo(v, ks.t, a.rev_freq, 4 * ch, &hi, &lo);
-      }
-      *reinterpret_cast<uint4*>(&sm.qrh[hl][8 * ch]) = hi;
-      *reinterpret_cast<uint4*>(&sm.qrl[hl][8 * ch]) = lo;
-    }
-  }
-  float ss = 0.f;  // sum of squares of the raw query over this lane's dims (RMSNorm)
-  if (a.q_rms_eps > 0.f) {
+  HeadState<NO> st;
 #pragma unroll
-    for (int s = 0; s < KD; ++s) {
-      float f[8];
-      unpack8(qa[s], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-    }
-  }
-  // query RMSNorm factor per head (applied to the logits): 1 / sqrt(mean(q^2) + eps)
-  {
-    ss += __shfl_xor(ss, 16, kWave);
-    ss += __shfl_xor(ss, 32, kWave);
-    const float r = a.q_rms_eps > 0.f ? 1.0f / sqrtf(ss / (float)D + a.q_rms_eps) : 1.0f;
-    if (w == 0 && g == 0) sm.qscale[col] = r;
-  }
-  __syncthreads();  // rotated query dims ready
-#pragma unroll
-  for (int s = 0; s < KD; ++s) {
-    const int d0 = 32 * s + 8 * g;
-    if (d0 >= rope0) {
-      qa[s] = *reinterpret_cast<const uint4*>(&sm.qrh[col][d0 - rope0]);
-      const uint4 lo = *reinterpret_cast<const uint4*>(&sm.qrl[col][d0 - rope0]);
-      if (s == RB0)
-        qlo[0] = lo;
-      else
-        qlo[1] = lo;
-    }
-  }
-
-  WaveState<NO> st;
-#pragma unroll
-  for (int n = 0; n < NO; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    st.m[r] = -INFINITY;
-    st.l[r] = 0.f;
-  }
+  for (int n = 0; n < NO; ++n) st.o[n] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
 
   // phase 1: compressed entries
-  if (has_e) {
-    for (int key0 = key_begin; key0 < e_end; key0 += TKE) {
+  for (int t = 0; t < n_et; ++t) {
+    const int key0 = key_begin + kTK * t;
+    int stage = 0;
+    const float* vsc = nullptr;
+    if constexpr (F8) {
+      stage = t % kStages;
+      wait_tile_f8<D>(t + 1 < n_et);  // this wave's requests of tile t have landed
+      __syncthreads();                // everyone's have; the previous tile's reads are done
+      vsc = &sm.t.r.sc[stage][0];
+    } else {
+      TileRegs<D, KV> RT;
+      entry_load<D, KV>(cbase, sbase, key0, e_end, key_begin, sm, RT);
       __syncthreads();  // the previous tile's reads are done
-      entry_store<KD, KV>(a, sm, RT);
+      entry_store<D, KV>(sm, RT);
       __syncthreads();
-      if (key0 + TKE < e_end)
-        entry_load<KD, KV>(cbase, sbase, key0 + TKE, e_end, key_begin, sm, RT);
-      else if (w_begin < key_end)
-        window_load<KD, KV>(a, w_begin, key_end, key_begin, rope0, sm, RT);
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if (16 * w < TKE) s = tile_qk<KD, F8, false>(sm, qa, qlo);
-      tile_softmax<KD, NO>(sm, st, s, TKE);
-      tile_pv<KD, NO, F8, TKE / 32, NVB>(sm, st);
     }
+    const uint64_t valid = tile_mask<D>(sm, key0, e_end, key_begin);
+    const f32x16 s = tile_qk<D, F8, false, DQ>(sm, stage, q, qlo, kh);
+    tile_softmax<D, NO>(a, sm, st, s, w, valid, vsc);
+    if (F8 && t + 2 < n_et)  // ring stage (t + 2) % 3 was last read by tile t - 1, finished by all
+      issue_tile_f8<D>(sm, (t + 2) % kStages, cbase, reinterpret_cast<const float*>(sbase), key0 + 2 * kTK, e_end,
+                       key_begin);
+    tile_pv<D, NO, NB, F8>(sm, st, hh, vq, stage, valid);
   }
-  // phase 2: window tokens
-  for (int key0 = w_begin; key0 < key_end; key0 += kTK16) {
+  // phase 2: window tokens (the bf16 tile overlays the ring: staged after the last entry tile's reads)
+  for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
+    WinRegs<D> RW;
+    window_load<D>(a, key0, key_end, key_begin, sm, RW);
     __syncthreads();
-    window_store<KD, KV>(a, ks, key0, rope0, sm, RT);
+    window_store<D>(a, ks, key0, sm, RW);
     __syncthreads();
-    if (key0 + kTK16 < key_end) window_load<KD, KV>(a, key0 + kTK16, key_end, key_begin, rope0, sm, RT);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if (16 * w < kTK16) s = tile_qk<KD, false, true>(sm, qa, qlo);
-    tile_softmax<KD, NO>(sm, st, s, kTK16);
-    tile_pv<KD, NO, false, 1, NVB>(sm, st);
+    const uint64_t valid = tile_mask<D>(sm, key0, key_end, key_begin);
+    const f32x16 s = tile_qk<D, false, true, DQ>(sm, 0, q, qlo, kh);
+    tile_softmax<D, NO>(a, sm, st, s, w, valid, nullptr);
+    tile_pv<D, NO, NB, false>(sm, st, hh, vq, 0, valid);
   }
 
-  // the key sums of the waves (same exponent base): l = sum over waves
-  if (col == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.lsum[w][4 * g + r] = st.l[r];
+  // the head's key sum: over the lane halves, then over the four waves that wrote its P
+  {
+    const float lw = st.l + __shfl_xor(st.l, 32, kWave);
+    if (lane < 32) sm.lsum[2 * kh + DQ][hl] = lw;
   }
   __syncthreads();
-  float lt[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    lt[r] = sm.lsum[0][4 * g + r] + sm.lsum[1][4 * g + r] + sm.lsum[2][4 * g + r] + sm.lsum[3][4 * g + r];
+  const float lt = sm.lsum[0][hl] + sm.lsum[1][hl] + sm.lsum[2][hl] + sm.lsum[3][hl];
+  const int u4 = 4 * (lane >> 5);  // O^T rows of this lane: 32 b + 8 g + u4 + e
 
   if (a.n_splits == 1) {
+    if (hq >= a.H) return;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* dst = a.out + ((int64_t)qi * a.H + hq) * DV;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hr = h0 + 4 * g + r;
-      if (hr >= a.H) continue;
-      const float inv = lt[r] > 0.f ? 1.f / lt[r] : 0.f;
-      uint16_t* dst = a.out + ((int64_t)qi * a.H + hr) * a.d_v;
+    for (int n = 0; n < NO; ++n) {
+      const int b = vq * NO + n;
+      if (NB % 4 != 0 && b >= NB) continue;
 #pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        const int nb = w * NO + n;
-        if (nb < NVB) dst[16 * nb + col] = (uint16_t)f32_to_bf16_rne(st.o[n][r] * inv);
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = cvt_bf16x2(st.o[n][4 * g] * inv, st.o[n][4 * g + 1] * inv);
+        pk.y = cvt_bf16x2(st.o[n][4 * g + 2] * inv, st.o[n][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g + u4) = pk;
       }
-      if (a.out_lse && col == 0 && w == 0)
-        a.out_lse[(int64_t)qi * a.H + hr] = lt[r] > 0.f ? (st.m[r] + log2f(lt[r])) * kLn2 : -INFINITY;
     }
+    if (a.out_lse && vq == 0 && lane < 32)
+      a.out_lse[(int64_t)qi * a.H + hq] = lt > 0.f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
     return;
   }
 
   // split partial: unnormalised O, exponent base and sum
-  const int64_t pbase = ((int64_t)qh * a.n_splits + split) * kHG;  // first head row of this split
+  const int64_t prow = (((int64_t)qh * a.n_splits + split) * kHB + hl);
+  float* dst = a.part_o + prow * DV;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float* dst = a.part_o + (pbase + 4 * g + r) * a.d_v;
+  for (int n = 0; n < NO; ++n) {
+    const int b = vq * NO + n;
+    if (NB % 4 != 0 && b >= NB) continue;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const int nb = w * NO + n;
-      if (nb < NVB) dst[16 * nb + col] = st.o[n][r];
-    }
-    if (col == 0 && w == 0) {
-      a.part_ml[(pbase + 4 * g + r) * 2 + 0] = st.m[r];
-      a.part_ml[(pbase + 4 * g + r) * 2 + 1] = lt[r];
-    }
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4*>(dst + 32 * b + 8 * g + u4) =
+          f32x4{st.o[n][4 * g], st.o[n][4 * g + 1], st.o[n][4 * g + 2], st.o[n][4 * g + 3]};
   }
+  if (vq == 0 && lane < 32) {
+    a.part_ml[prow * 2 + 0] = st.m;
+    a.part_ml[prow * 2 + 1] = lt;
+  }
+}
+
+template <int D, int DV, int KV>
+__global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem<D> sm;
+  if (wave_id() >> 2)
+    attn_body<D, DV, KV, 1>(a, sm);
+  else
+    attn_body<D, DV, KV, 0>(a, sm);
 }
 
 // One workgroup per (query, head): log-sum-exp merge of the split partials. Thread t owns dims
@@ -713,18 +852,18 @@ __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
   __shared__ float red[2];
   const int qi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int S = a.n_splits;
-  const int64_t row0 = ((int64_t)(qi * a.n_hg + h / kHG) * S) * kHG + h % kHG;  // split s: row0 + s * kHG
+  const int64_t row0 = ((int64_t)(qi * a.n_hb + h / kHB) * S) * kHB + h % kHB;  // split s: row0 + s * kHB
   const int dd = min(4 * tid, a.d_v - 4);  // threads past d_v read the last dims and store nothing
   if (tid < kWave) {
     float mx = -INFINITY;
-    for (int sp = tid; sp < S; sp += kWave) mx = fmaxf(mx, a.part_ml[(row0 + (int64_t)sp * kHG) * 2]);
+    for (int sp = tid; sp < S; sp += kWave) mx = fmaxf(mx, a.part_ml[(row0 + (int64_t)sp * kHB) * 2]);
     mx = wave_max(mx);
     const float Mb = mx == -INFINITY ? 0.f : mx;
     float l = 0.f;
     for (int sp = tid; sp < S + kMergeBatch; sp += kWave) {
       float wt = 0.f;
       if (sp < S) {
-        const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[(row0 + (int64_t)sp * kHG) * 2]);
+        const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[(row0 + (int64_t)sp * kHB) * 2]);
         wt = exp2f(ml.x - Mb);
         l += wt * ml.y;
       }
@@ -743,7 +882,7 @@ __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
   auto fetch = [&](f32x4 (&v)[kMergeBatch], int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(a.part_o + (row0 + (int64_t)min(s0 + u, S - 1) * kHG) * a.d_v + dd);
+      v[u] = *reinterpret_cast<const f32x4*>(a.part_o + (row0 + (int64_t)min(s0 + u, S - 1) * kHB) * a.d_v + dd);
   };
   auto sum = [&](const f32x4 (&v)[kMergeBatch], int s0) {
 #pragma unroll
@@ -776,30 +915,56 @@ __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- host side
 struct AttnPlan {
-  int n_hg, n_splits, keys_per_split;
+  int n_hb, n_splits, n_esplits, keys_per_split, win_per_split;
   size_t ws;  // bytes of the split partials
 };
 
-// Splits of a query's key set: about two workgroups per CU over the whole job, each split a
-// multiple of 64 keys (whole tiles of either kind), at most kMaxSplitKeys keys and kMaxSplits
-// splits.
-static AttnPlan plan_attn(int nq, int H, int d_v, int max_keys) {
-  AttnPlan p;
-  p.n_hg = (H + kHG - 1) / kHG;
-  const int64_t base = (int64_t)nq * p.n_hg;
-  int splits = (int)(kTargetWG / base);
-  if (splits < 1) splits = 1;
-  int per = (max_keys + splits - 1) / splits;
-  per = (per + 63) / 64 * 64;
-  if (per < 64) per = 64;
-  const int min_per = (max_keys + kMaxSplits - 1) / kMaxSplits;
-  if (per < min_per) per = (min_per + 63) / 64 * 64;
-  if (per > kMaxSplitKeys) per = kMaxSplitKeys;
-  splits = (max_keys + per - 1) / per;
-  if (splits < 1) splits = 1;
-  p.n_splits = splits;
-  p.keys_per_split = per;
-  p.ws = splits > 1 ? (size_t)base * splits * kHG * ((size_t)d_v + 2) * sizeof(float) : 0;
+// Splits of a query's key set (at most kMaxSplits, each a whole number of 64-key tiles of at most
+// kMaxSplitKeys keys). Either the keys are cut in order (entries, then window tokens), or the
+// entries are cut into splits and each window tile gets a split of its own. With one workgroup
+// per CU a launch takes ceil(workgroups / kCUs) rounds of its longest split and a workgroup's
+// fixed prologue and epilogue, plus the merge launch when the keys are split; a window tile
+// (loaded and rotated when staged) counts one and a half entry tiles. The cheapest plan wins
+// (ties: the first found, fewer splits).
+static AttnPlan plan_attn(int nq, int H, int d_v, int max_entries, int W) {
+  AttnPlan p{};
+  p.n_hb = (H + kHB - 1) / kHB;
+  const int64_t base = (int64_t)nq * p.n_hb;
+  const int te = (max(max_entries, 0) + kTK - 1) / kTK, tw = (max(W, 0) + kTK - 1) / kTK;
+  const int tiles = max(te + tw, 1);
+  auto rounds = [&](int s) { return (base * s + kCUs - 1) / kCUs; };
+  int64_t best_cost = -1;
+  // keys in order: the split holding the window tiles is the longest
+  for (int s = 1; s <= kMaxSplits && s <= tiles; ++s) {
+    const int per = (tiles + s - 1) / s;
+    if ((tiles + per - 1) / per != s || per * kTK > kMaxSplitKeys) continue;
+    const int64_t cost = rounds(s) * (2 * per + min(tw, per) + 2 * kWgFixedTiles) + (s > 1 ? 2 * kMergeTiles : 0);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      p.n_splits = p.n_esplits = s;
+      p.keys_per_split = per * kTK;
+    }
+  }
+  // entry splits plus one split per window tile
+  if (te > 0 && tw > 0) {
+    for (int se = 1; se + tw <= kMaxSplits && se <= te; ++se) {
+      const int per = (te + se - 1) / se;
+      if ((te + per - 1) / per != se || per * kTK > kMaxSplitKeys) continue;
+      const int64_t cost = rounds(se + tw) * (max(2 * per, 3) + 2 * kWgFixedTiles) + 2 * kMergeTiles;
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        p.n_splits = se + tw;
+        p.n_esplits = se;
+        p.keys_per_split = per * kTK;
+        p.win_per_split = kTK;
+      }
+    }
+  }
+  if (best_cost < 0) {  // refused by launch_attn: more than kMaxSplits splits of kMaxSplitKeys keys
+    p.n_splits = p.n_esplits = kMaxSplits + 1;
+    p.keys_per_split = kMaxSplitKeys;
+  }
+  p.ws = p.n_splits > 1 ? (size_t)base * p.n_splits * kHB * ((size_t)d_v + 2) * sizeof(float) : 0;
   return p;
 }
 
@@ -807,10 +972,10 @@ typedef void (*AttnKernel)(AttnArgs);
 
 template <int KV>
 static AttnKernel pick_dims(int D, int d_v) {
-  if (D == 576 && d_v == 512) return attn_kernel<18, 32, KV>;
-  if (D == 128 && d_v == 128) return attn_kernel<4, 8, KV>;
-  if (D == 64 && d_v == 32) return attn_kernel<2, 2, KV>;
-  if (D == 256 && d_v == 128) return attn_kernel<8, 8, KV>;
+  if (D == 576 && d_v == 512) return attn_kernel<576, 512, KV>;
+  if (D == 128 && d_v == 128) return attn_kernel<128, 128, KV>;
+  if (D == 64 && d_v == 32) return attn_kernel<64, 32, KV>;
+  if (D == 256 && d_v == 128) return attn_kernel<256, 128, KV>;
   return nullptr;
 }
 
@@ -836,24 +1001,23 @@ static int check_common(const char* name, int H, int D, int d_rope, int d_v, int
 }
 
 static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws, size_t ws_bytes, hipStream_t s) {
-  for (int i = 0; i < a.d_rope / 2; ++i)
-    a.rev_freq[i] = pow((double)a.rope_base, -2.0 * (double)i / (double)a.d_rope) / 6.283185307179586476925286766559;
   CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "%s: workspace %zu < %zu bytes", name,
                ws_bytes, p.ws);
-  a.n_hg = p.n_hg;
+  a.n_hb = p.n_hb;
   a.n_splits = p.n_splits;
   a.keys_per_split = p.keys_per_split;
+  a.n_esplits = p.n_esplits;
+  a.win_per_split = p.win_per_split;
   CSKV_REQUIRE(p.n_splits <= kMaxSplits, CSKV_ENOTSUP, "%s: %d key splits > %d (key set too large)", name,
                p.n_splits, kMaxSplits);
   CSKV_REQUIRE(p.n_splits == 1 || a.d_v <= 4 * kMergeNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name,
                a.d_v, 4 * kMergeNT);
   if (p.n_splits > 1) {
     a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = a.part_o + (size_t)a.nq * p.n_hg * p.n_splits * kHG * a.d_v;
+    a.part_ml = a.part_o + (size_t)a.nq * p.n_hb * p.n_splits * kHB * a.d_v;
   }
-  const int64_t total = (int64_t)a.nq * p.n_hg * p.n_splits;
+  const int64_t total = (int64_t)a.nq * p.n_hb * p.n_splits;
   CSKV_REQUIRE(total < (1ll << 31), CSKV_ENOTSUP, "%s: %lld workgroups", name, (long long)total);
-  a.xcd_map = total % 8 == 0 ? 1 : 0;
   AttnKernel kern = pick_kernel(a.D, a.d_v, a.kv_dtype);
   hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(kNT), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
@@ -866,22 +1030,83 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
 
 }  // namespace cskv
 
-using namespace cskv;
-
-extern "C" CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense) {
-  if (B < 1 || H < 1 || d_v < 1) return 0;
-  const int max_keys = (dense ? N_cap : k) + (W > 0 ? W : 0);
-  return plan_attn(B, H, d_v, max_keys > 0 ? max_keys : 1).ws;
-}
-
 namespace cskv {
 
-// Checks the decode arguments and fills the kernel arguments and the split plan.
+static int g_attn_path = 0;  // 0: by the call's shape; 1: the 64-head kernel; 2: the 16-head kernel
+
+// The 16-head kernel takes short key sets of few queries (a few hundred keys: a workgroup's
+// prologue then lasts as long as its tiles, and its two workgroups per CU hide one another's);
+// the 64-head kernel everything else.
+static bool use_g16(int nq, int max_keys) {
+  if (g_attn_path) return g_attn_path == 2;
+  return max_keys <= 512 && nq <= 256;
+}
+
+static size_t attn_ws(int nq, int H, int d_v, int entries, int W) {
+  if (nq < 1 || H < 1 || d_v < 1) return 0;
+  return use_g16(nq, entries + W) ? g16::ws_bytes(nq, H, d_v, entries + W) : plan_attn(nq, H, d_v, entries, W).ws;
+}
+
+// Scratch of hybrid_attn_decode_noalloc, defined below.
+static int scratch_address(const char* name, void** out);
+
+// Runs one call on the kernel its shape selects. noalloc: the split partials go to the static
+// scratch (refused if they need more), ws is ignored.
+static int run_attn(const char* name, const AttnCall& c, bool noalloc, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int entries = c.N_cap > 0 ? (c.topk ? c.k : c.N_cap) : 0;
+  const bool g = use_g16(c.nq, entries + c.W);
+  AttnPlan p{};
+  if (!g) p = plan_attn(c.nq, c.H, c.d_v, entries, c.W);
+  const size_t need = g ? g16::ws_bytes(c.nq, c.H, c.d_v, entries + c.W) : p.ws;
+  if (noalloc) {
+    CSKV_REQUIRE(need <= (size_t)CSKV_NOALLOC_SCRATCH_BYTES, CSKV_EWORKSPACE,
+                 "%s: the key splits need %zu bytes of scratch > the static %zu bytes (use hybrid_attn_decode)",
+                 name, need, (size_t)CSKV_NOALLOC_SCRATCH_BYTES);
+    ws = nullptr;
+    ws_bytes = (size_t)CSKV_NOALLOC_SCRATCH_BYTES;
+    if (need > 0) {
+      const int rc = scratch_address(name, &ws);
+      if (rc) return rc;
+    }
+  }
+  if (g) return g16::launch(name, c, ws, ws_bytes, s);
+  AttnArgs a{};
+  a.q = c.q;
+  a.q_pos = c.q_pos;
+  a.pos0 = c.pos0;
+  a.ckv = c.ckv;
+  a.ckv_scale = c.ckv_scale;
+  a.kv_dtype = c.kv_dtype;
+  a.N_cap = c.N_cap;
+  a.ckv_seq = c.ckv_seq;
+  a.n_entries = c.n_entries;
+  a.m = c.m;
+  a.topk = c.topk;
+  a.k = c.k;
+  a.win = c.win;
+  a.ring = c.ring;
+  a.ring_cap = c.ring_cap;
+  a.q_per_seq = c.q_per_seq;
+  a.W = c.W;
+  a.nq = c.nq;
+  a.H = c.H;
+  a.D = c.D;
+  a.d_rope = c.d_rope;
+  a.d_v = c.d_v;
+  a.rope_base = c.rope_base;
+  a.scale_log2 = c.scale_log2;
+  a.q_rms_eps = c.q_rms_eps;
+  a.out = c.out;
+  a.out_lse = c.out_lse;
+  return launch_attn(name, a, p, ws, ws_bytes, s);
+}
+
+// Checks the decode arguments and fills the call.
 static int decode_setup(const char* name, const uint16_t* q, const int64_t* q_pos, const void* ckv,
                         const void* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
                         const int32_t* topk_idx, int k, const uint16_t* win, int W, int B, int H, int D, int d_rope,
                         int d_v, float rope_base, float softmax_scale, uint16_t* out, float* out_lse,
-                        float q_rms_eps, int T, int R, AttnArgs& a, AttnPlan& p) {
+                        float q_rms_eps, int T, int R, AttnCall& c) {
   CSKV_REQUIRE(B >= 1 && N_cap >= 0, CSKV_EINVAL, "%s: B=%d N_cap=%d", name, B, N_cap);
   if (R == 0) R = W;
   CSKV_REQUIRE(T >= 1 && (int64_t)B * T < (1 << 20), CSKV_EINVAL, "%s: T=%d", name, T);
@@ -895,40 +1120,51 @@ static int decode_setup(const char* name, const uint16_t* q, const int64_t* q_po
   CSKV_REQUIRE(N_cap == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(win), CSKV_EINVAL, "%s: q/ckv/win must be 16-byte aligned",
                name);
-  const int max_keys = (topk_idx ? k : N_cap) + W;
-  p = plan_attn(B * T, H, d_v, max_keys > 0 ? max_keys : 1);
-  a = AttnArgs{};
-  a.q = q;
-  a.q_pos = q_pos;
-  a.pos0 = 0;
-  a.ckv = ckv;
-  a.ckv_scale = ckv_scale;
-  a.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
-  a.N_cap = N_cap;
-  a.ckv_seq = N_cap;
-  a.n_entries = n_entries;
-  a.m = 1;
-  a.topk = topk_idx;
-  a.k = k;
-  a.win = win;
-  a.ring = 1;
-  a.ring_cap = R;
-  a.q_per_seq = T;
-  a.W = W;
-  a.nq = B * T;
-  a.H = H;
-  a.D = D;
-  a.d_rope = d_rope;
-  a.d_v = d_v;
-  a.rope_base = rope_base;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.q_rms_eps = q_rms_eps;
-  a.out = out;
-  a.out_lse = out_lse;
+  c = AttnCall{};
+  c.q = q;
+  c.q_pos = q_pos;
+  c.pos0 = 0;
+  c.ckv = ckv;
+  c.ckv_scale = ckv_scale;
+  c.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.N_cap = N_cap;
+  c.ckv_seq = N_cap;
+  c.n_entries = n_entries;
+  c.m = 1;
+  c.topk = topk_idx;
+  c.k = k;
+  c.win = win;
+  c.ring = 1;
+  c.ring_cap = R;
+  c.q_per_seq = T;
+  c.W = W;
+  c.nq = B * T;
+  c.H = H;
+  c.D = D;
+  c.d_rope = d_rope;
+  c.d_v = d_v;
+  c.rope_base = rope_base;
+  c.scale_log2 = softmax_scale * kLog2e;
+  c.q_rms_eps = q_rms_eps;
+  c.out = out;
+  c.out_lse = out_lse;
   return CSKV_OK;
 }
 
 }  // namespace cskv
+
+using namespace cskv;
+
+extern "C" CSKV_API int cskv_attn_path(int path) {
+  CSKV_REQUIRE(path >= 0 && path <= 2, CSKV_EINVAL, "cskv_attn_path: path=%d outside [0, 2]", path);
+  g_attn_path = path;
+  return CSKV_OK;
+}
+
+extern "C" CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense) {
+  if (B < 1 || H < 1 || d_v < 1) return 0;
+  return attn_ws(B, H, d_v, N_cap > 0 ? (dense ? N_cap : k) : 0, W);
+}
 
 extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const void* ckv,
                                            const void* ckv_scale, int ckv_dtype, int N_cap,
@@ -938,12 +1174,11 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
                                            void* ws, size_t ws_bytes, float q_rms_eps, int T, int R,
                                            void* stream) {
   const char* name = "hybrid_attn_decode";
-  AttnArgs a;
-  AttnPlan p;
+  AttnCall c;
   const int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
-                              D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, a, p);
+                              D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, c);
   if (rc) return rc;
-  return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return run_attn(name, c, false, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
 // Scratch of hybrid_attn_decode_noalloc: the key-split partials, in a device array of fixed size.
@@ -984,20 +1219,11 @@ extern "C" CSKV_API int hybrid_attn_decode_noalloc(const uint16_t* q, const int6
                                                    int d_v, float rope_base, float softmax_scale, uint16_t* out,
                                                    float* out_lse, float q_rms_eps, int T, int R, void* stream) {
   const char* name = "hybrid_attn_decode_noalloc";
-  AttnArgs a;
-  AttnPlan p;
-  int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H, D,
-                        d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, a, p);
+  AttnCall c;
+  const int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
+                              D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, c);
   if (rc) return rc;
-  CSKV_REQUIRE(p.ws <= (size_t)CSKV_NOALLOC_SCRATCH_BYTES, CSKV_EWORKSPACE,
-               "%s: the key splits need %zu bytes of scratch > the static %zu bytes (use hybrid_attn_decode)", name,
-               p.ws, (size_t)CSKV_NOALLOC_SCRATCH_BYTES);
-  void* ws = nullptr;
-  if (p.ws > 0) {
-    rc = scratch_address(name, &ws);
-    if (rc) return rc;
-  }
-  return launch_attn(name, a, p, ws, (size_t)CSKV_NOALLOC_SCRATCH_BYTES, reinterpret_cast<hipStream_t>(stream));
+  return run_attn(name, c, true, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" CSKV_API size_t hybrid_attn_prefill_workspace_size(int T, int H, int d_v, int N, int k, int W, int dense) {
@@ -1021,35 +1247,33 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   CSKV_REQUIRE(N == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(x), CSKV_EINVAL, "%s: q/ckv/x must be 16-byte aligned",
                name);
-  const int max_keys = (topk_idx ? k : N) + W;
-  AttnPlan p = plan_attn(T, H, d_v, max_keys > 0 ? max_keys : 1);
-  AttnArgs a{};
-  a.q = q;
-  a.q_pos = nullptr;
-  a.pos0 = pos0;
-  a.ckv = ckv;
-  a.ckv_scale = ckv_scale;
-  a.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
-  a.N_cap = N;
-  a.ckv_seq = 0;
-  a.n_entries = nullptr;
-  a.m = m;
-  a.topk = topk_idx;
-  a.k = k;
-  a.win = x;
-  a.ring = 0;
-  a.ring_cap = W;
-  a.q_per_seq = 1;
-  a.W = W;
-  a.nq = T;
-  a.H = H;
-  a.D = D;
-  a.d_rope = d_rope;
-  a.d_v = d_v;
-  a.rope_base = rope_base;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.q_rms_eps = q_rms_eps;
-  a.out = out;
-  a.out_lse = out_lse;
-  return launch_attn(name, a, p, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  AttnCall c{};
+  c.q = q;
+  c.q_pos = nullptr;
+  c.pos0 = pos0;
+  c.ckv = ckv;
+  c.ckv_scale = ckv_scale;
+  c.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.N_cap = N;
+  c.ckv_seq = 0;
+  c.n_entries = nullptr;
+  c.m = m;
+  c.topk = topk_idx;
+  c.k = k;
+  c.win = x;
+  c.ring = 0;
+  c.ring_cap = W;
+  c.q_per_seq = 1;
+  c.W = W;
+  c.nq = T;
+  c.H = H;
+  c.D = D;
+  c.d_rope = d_rope;
+  c.d_v = d_v;
+  c.rope_base = rope_base;
+  c.scale_log2 = softmax_scale * kLog2e;
+  c.q_rms_eps = q_rms_eps;
+  c.out = out;
+  c.out_lse = out_lse;
+  return run_attn(name, c, false, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }

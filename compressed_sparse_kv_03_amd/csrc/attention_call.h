@@ -1,0 +1,44 @@
+// One hybrid_attn_decode / hybrid_attn_prefill call, as the two attention kernels take it:
+// the 64-head kernel (attention.hip: long key sets, many queries) and the 16-head kernel
+// (attention_g16.hip: a few hundred keys per query, few queries).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cskv {
+
+enum { kKvBf16 = 0, kKvFp8 = 1, kKvMxfp4 = 2 };
+
+struct AttnCall {
+  const uint16_t* q;         // [nq, H, D]
+  const int64_t* q_pos;      // [nq] (decode) or nullptr (prefill: pos0 + row)
+  int64_t pos0;
+  const void* ckv;           // [B_kv, N_cap, D] bf16 bits, fp8 codes, or MXFP4 codes [.., D/2]
+  const void* ckv_scale;     // fp32 [B_kv, N_cap] (fp8) or E8M0 bytes [B_kv, N_cap, D/32] (MXFP4)
+  int kv_dtype;              // kKvBf16, kKvFp8 or kKvMxfp4
+  int N_cap;
+  int64_t ckv_seq;           // entries between sequences (0: all queries share one cache)
+  const int32_t* n_entries;  // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))
+  int m;
+  const int32_t* topk;       // [nq, k] or nullptr (dense)
+  int k;
+  const uint16_t* win;       // decode: rings [B, R, D]; prefill: x [T, D]
+  int ring;                  // 1: slot = pos mod ring_cap of sequence qi / q_per_seq; 0: row = pos - pos0 of x
+  int ring_cap;
+  int q_per_seq;             // consecutive queries sharing one sequence's ring and cache (decode)
+  int W;
+  int nq, H, D, d_rope, d_v;
+  float rope_base;
+  float scale_log2;          // softmax_scale * log2(e)
+  float q_rms_eps;           // > 0: unit-gain RMSNorm of each query head (folded into its logits)
+  uint16_t* out;             // [nq, H, d_v]
+  float* out_lse;            // [nq, H]
+};
+
+namespace g16 {
+size_t ws_bytes(int nq, int H, int d_v, int max_keys);
+int launch(const char* name, const AttnCall& c, void* ws, size_t ws_bytes, hipStream_t s);
+}  // namespace g16
+
+}  // namespace cskv

@@ -29,6 +29,7 @@ _SIGS = {
     "hybrid_attn_decode": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                             _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "cskv_attn_path": ([_i], _i),
     "hybrid_attn_decode_noalloc": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                                     _p, _p, _f, _i, _i, _p], _i),
     "hybrid_attn_prefill": ([_p, _i64, _i, _p, _p, _i, _i, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
@@ -152,6 +153,12 @@ def hybrid_attn_decode(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, to
 
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024   # CSKV_NOALLOC_SCRATCH_BYTES
+ATTN_AUTO, ATTN_G64, ATTN_G16 = 0, 1, 2     # cskv_attn_path
+
+
+def cskv_attn_path(path):
+    """Which attention kernel the attention calls run (0: by shape, 1: 64-head, 2: 16-head)."""
+    _check(lib().cskv_attn_path(path))
 
 
 def hybrid_attn_decode_noalloc(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,

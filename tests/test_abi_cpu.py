@@ -17,7 +17,7 @@ def declared():
 
 def test_library_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 15
     L = native.lib()
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
@@ -99,7 +99,7 @@ def test_attention_validation():
     assert dec(dt=5) == -1
     assert dec(q=None) == -1
     assert dec(sc=None) == -1
-    assert dec(ws=None, wsb=0) == -3
+    assert dec(ws=None, wsb=0, N=20000) == -3    # 20128 keys are split: partials need a workspace
     assert dec(eps=-1.0) == -1
     assert dec(T=0) == -1
     assert dec(R=100) == -1                  # ring smaller than the window
@@ -120,6 +120,8 @@ def test_attention_validation():
     # refused before any HIP call
     assert L.hybrid_attn_decode_workspace_size(16, 64, 512, 65536, 0, 128, 1) > native.NOALLOC_SCRATCH_BYTES
     assert dec_na(B=16, N=65536) == -3
+    assert L.cskv_attn_path(3) == -1 and L.cskv_attn_path(-1) == -1
+    assert L.cskv_attn_path(0) == 0
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
                                                         k=1, x=16, W=128, H=16, D=128, dr=64, dv=128, m=4,
                                                         base=1e4, scale=0.1, out=16, lse=None, ws=None, wsb=0,

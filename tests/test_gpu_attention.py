@@ -1,4 +1,6 @@
-"""GPU parity of hybrid_attn_decode / hybrid_attn_prefill against the oracle.
+"""GPU parity of hybrid_attn_decode / hybrid_attn_prefill against the oracle. The small cases run
+on both attention kernels (64-head and 16-head); the full-size ones on the kernel the call's shape
+selects.
 
 Tolerances: bf16 outputs with fp32 accumulation, rel-L2 <= 5e-3 and max-abs <= 2e-2;
 lse within 1e-3 (natural log units).
@@ -17,6 +19,14 @@ from tests import parity
 from tests.gpu_util import DEV, down, poisoned, say, up
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=[native.ATTN_G64, native.ATTN_G16], ids=["g64", "g16"])
+def kernel_path(request):
+    """Runs the test on each attention kernel (64-head and 16-head), then restores the default."""
+    native.cskv_attn_path(request.param)
+    yield request.param
+    native.cskv_attn_path(native.ATTN_AUTO)
 
 
 def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, D, d_rope, d_v, scale, q_rms_eps=0.0):
@@ -77,7 +87,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("B,H,D,d_rope,d_v,N,k,W,dtype,dense,std", CASES)
-def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std):
+def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std, kernel_path):
     say("decode small", B, H, D, d_rope, d_v, N, k, W, dtype, dense, std)
     rng = np.random.default_rng(N + H)
     sig = std if std else D ** -0.5
@@ -118,7 +128,7 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std):
     (2, 16, 128, 64, 128, 500, 64, 128, "bf16", False, 1e-6),
     (2, 20, 128, 64, 128, 90, 16, 8, "fp8", True, 4.0),          # eps comparable to the mean square
 ])
-def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps):
+def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps, kernel_path):
     """Unit-gain RMSNorm of every query head folded into its logits (q_rms_eps > 0)."""
     say("decode q-rms", B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps)
     rng = np.random.default_rng(N + 7)
@@ -149,7 +159,7 @@ def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps)
     parity.lse_close(down(lse), l_ref, bnd, "q-rms lse")
 
 
-def test_decode_peaked_key_dominates():
+def test_decode_peaked_key_dominates(kernel_path):
     """One planted key aligned with q: a masking or RoPE error would move the output far."""
     say("decode peaked")
     B, H, D, d_rope, d_v, N, W = 1, 16, 128, 64, 128, 200, 128
@@ -306,7 +316,7 @@ PREFILL = [
 
 
 @pytest.mark.parametrize("T,pos0,m,H,D,d_rope,d_v,k,W,dense,dtype", PREFILL)
-def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype):
+def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype, kernel_path):
     say("prefill small", T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype)
     rng = np.random.default_rng(T + D)
     N = (pos0 + T) // m

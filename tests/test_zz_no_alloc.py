@@ -1,5 +1,6 @@
 """hybrid_attn_decode_noalloc (key-split partials in the library's static per-GPU scratch) against
-hybrid_attn_decode with a caller-allocated workspace, on two calls in a row, the second smaller:
+hybrid_attn_decode with a caller-allocated workspace, on calls in a row, the second smaller (both
+split; a third, CSA top-k over bf16 entries):
 the same kernels and split plan run, so outputs and lse must agree bit for bit. The first call is
 also checked against the oracle on one sequence, and a call whose splits need more than the
 static scratch must be refused before anything runs."""
@@ -17,12 +18,13 @@ pytestmark = pytest.mark.gpu
 DT = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3}
 
 
-def both(q, q_pos, ckv, sc, dtype, nent, topk, k, ring, W, H, D, d_rope, d_v, scale):
+def both(q, q_pos, ckv, sc, dtype, nent, topk, k, ring, W, H, D, d_rope, d_v, scale, split=True):
     """Outputs of the workspace entry point and of the allocation-free one on the same inputs."""
     B, N_cap = q.shape[0], ckv.shape[1]
     wsn = native.hybrid_attn_decode_workspace_size(B, H, d_v, N_cap, k, W, topk is None)
-    assert 0 < wsn <= native.NOALLOC_SCRATCH_BYTES, wsn   # the split path, within the static scratch
-    ws = torch.zeros(wsn, dtype=torch.uint8, device=DEV)
+    if split:
+        assert 0 < wsn <= native.NOALLOC_SCRATCH_BYTES, wsn   # the split path, within the static scratch
+    ws = torch.zeros(max(wsn, 16), dtype=torch.uint8, device=DEV)
     res = []
     for noalloc in (False, True):
         out = poisoned((B, H, d_v), torch.int16)
@@ -56,23 +58,36 @@ def test_noalloc_matches_workspace_entry_point_twice():
     parity.attn_close(o_na[b], o, "noalloc call 1 vs oracle")
     parity.lse_close(l_na[b], l, None, "noalloc call 1 lse vs oracle")
 
-    # call 2, smaller: CSA top-k over 700 bf16 entries, B=3
-    B, H, D, d_rope, d_v, N, k, W = 3, 64, 576, 64, 512, 700, 128, 128
-    say("noalloc call 2: csa", B, N)
-    rng = np.random.default_rng(11)
-    q2 = synth.normal_bf16_bits((B, H, D), D ** -0.5, synth.seed_of(8, 2, 2), DEV)
-    ckv2 = synth.normal_bf16_bits((B, N, D), D ** -0.5, synth.seed_of(8, 2, 3), DEV)
-    ring2 = synth.normal_bf16_bits((B, W, D), D ** -0.5, synth.seed_of(8, 2, 4), DEV)
-    nent2 = np.array([700, 450, 129], np.int32)
-    tpos2 = nent2.astype(np.int64) * 4 + 3
-    topk2 = np.full((B, k), -1, np.int32)
-    for i in range(B):
-        sel = rng.choice(nent2[i], min(k, nent2[i]) - 5, replace=False)
-        topk2[i, :sel.size] = sel
-    (o_ws, l_ws), (o_na, l_na) = both(q2, up(tpos2), ckv2, None, "bf16", up(nent2), up(topk2), k, ring2, W, H, D,
-                                      d_rope, d_v, D ** -0.5)
+    # call 2, smaller: B=3 sequences over 1500 (and fewer) dense fp8 entries, still split
+    B, N = 3, 1500
+    say("noalloc call 2: dense", B, N)
+    nent2 = np.array([1500, 1100, 300], np.int32)
+    q2 = synth.normal_bf16_bits((B, w.H, w.D), w.sigma, synth.seed_of(8, 2, 2), DEV)
+    ckv2, sc2 = synth.fp8_rows_normal((B, N, w.D), w.sigma, synth.seed_of(8, 2, 3), DEV)
+    ring2 = synth.normal_bf16_bits((B, w.W, w.D), w.sigma, synth.seed_of(8, 2, 4), DEV)
+    tpos2 = nent2.astype(np.int64) * 128 + 5
+    (o_ws, l_ws), (o_na, l_na) = both(q2, up(tpos2), ckv2, sc2, "fp8", up(nent2), None, 0, ring2, w.W, w.H, w.D,
+                                      w.d_rope, w.d_v, w.softmax_scale)
     assert np.array_equal(o_na, o_ws), "noalloc output differs from the workspace entry point (call 2)"
     assert np.array_equal(l_na.view(np.uint32), l_ws.view(np.uint32)), "noalloc lse differs (call 2)"
+
+    # call 3: CSA top-k over 700 bf16 entries, B=3 (whatever split the plan picks)
+    B, H, D, d_rope, d_v, N, k, W = 3, 64, 576, 64, 512, 700, 128, 128
+    say("noalloc call 3: csa", B, N)
+    rng = np.random.default_rng(11)
+    q3 = synth.normal_bf16_bits((B, H, D), D ** -0.5, synth.seed_of(9, 2, 2), DEV)
+    ckv3 = synth.normal_bf16_bits((B, N, D), D ** -0.5, synth.seed_of(9, 2, 3), DEV)
+    ring3 = synth.normal_bf16_bits((B, W, D), D ** -0.5, synth.seed_of(9, 2, 4), DEV)
+    nent3 = np.array([700, 450, 129], np.int32)
+    tpos3 = nent3.astype(np.int64) * 4 + 3
+    topk3 = np.full((B, k), -1, np.int32)
+    for i in range(B):
+        sel = rng.choice(nent3[i], min(k, nent3[i]) - 5, replace=False)
+        topk3[i, :sel.size] = sel
+    (o_ws, l_ws), (o_na, l_na) = both(q3, up(tpos3), ckv3, None, "bf16", up(nent3), up(topk3), k, ring3, W, H, D,
+                                      d_rope, d_v, D ** -0.5, split=False)
+    assert np.array_equal(o_na, o_ws), "noalloc output differs from the workspace entry point (call 3)"
+    assert np.array_equal(l_na.view(np.uint32), l_ws.view(np.uint32)), "noalloc lse differs (call 3)"
 
 
 def test_noalloc_refuses_more_than_the_static_scratch():
