@@ -41,6 +41,9 @@ def parse():
                     help="only run a 1 GiB device copy (PMC calibration) and exit")
     ap.add_argument("--index-only", action="store_true",
                     help="only run --steps csa_index_topk calls on the 1M-context indexer inputs (for profilers)")
+    ap.add_argument("--attn-only", choices=["csa", "hca"], default=None,
+                    help="only run --steps hybrid_attn_decode calls of one layer of the 1M-context pair "
+                         "(for profilers; a 512 MB write between calls empties the Infinity Cache)")
     ap.add_argument("--share", choices=["none", "reuse", "reindex"], default="none",
                     help="cross-layer index sharing: the CSA layers of pairs 1.. reuse pair 0's top-k, or "
                          "re-index pair 0's KV and keys with their own queries")
@@ -56,7 +59,22 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
+    ap.add_argument("--workload", choices=["c5", "c2", "c3"], default="c5",
+                    help="c5: the 1M-context hybrid layer pair (the default line); c2: CSA decode, batch 32, 64K "
+                         "context, bf16 entries (indexer + gather attention); c3: HCA decode, batch 16, 1M context, "
+                         "fp8 entries (dense attention)")
     return ap.parse_args()
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
 
 
 def source_sha(files):
@@ -69,18 +87,25 @@ def source_sha(files):
 
 INDEX_SOURCES = ["compressed_sparse_kv_03_amd/csrc/indexer.hip", "compressed_sparse_kv_03_amd/csrc/topk_select.cuh",
                  "compressed_sparse_kv_03_amd/csrc/common.cuh"]
+ATTN_SOURCES = ["compressed_sparse_kv_03_amd/csrc/attention.hip", "compressed_sparse_kv_03_amd/csrc/attention_g16.hip",
+                "compressed_sparse_kv_03_amd/csrc/attention_call.h", "compressed_sparse_kv_03_amd/csrc/common.cuh"]
+PMC_FILES = {"csa_index_topk": ("pmc_csa_index_topk_1m.json", INDEX_SOURCES),
+             "hybrid_attn_decode_hca": ("pmc_hybrid_attn_hca_1m.json", ATTN_SOURCES),
+             "hybrid_attn_decode_csa": ("pmc_hybrid_attn_csa_1m.json", ATTN_SOURCES)}
 
 
-def pmc_traffic(bytes_per_launch_sha):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches the current source."""
-    p = os.path.join(ROOT, "profiles", "pmc_csa_index_topk_1m.json")
+def pmc_traffic(call):
+    """HBM bytes per launch of a call from its committed rocprofv3 PMC summary, if that summary was
+    taken on the current source (else None)."""
+    name, files = PMC_FILES[call]
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     try:
         rec = json.load(open(p))
     except Exception:
         return None
-    if rec.get("source_sha") != bytes_per_launch_sha:
+    if rec.get("source_sha") != source_sha(files):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -115,10 +140,28 @@ def main():
     if args.prefill:
         prefill_bench(args, dev)
         return
+    if args.workload != "c5":
+        attn_workload_bench(args, dev)
+        return
 
     K, W, P = args.steps, args.warmup, args.pairs
     spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0, draft=args.draft,
                    kv_dtype=args.kv)
+    if args.attn_only:
+        pr = hybrid.LayerPair(hybrid.LayerPairSpec(seed=0, **spec_kw), dev)
+        s_, name = pr.s, args.attn_only
+        pr.step(0)  # step 0's top-k (the indexer) and state, which the calls below reuse
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for i in range(W + K):
+            flush.fill_(i & 255)
+            native.hybrid_attn_decode(pr.q[name][0], pr.qpos[0], pr.ckv[name], pr.scl[name], pr.kv_code,
+                                      pr.cap[name], pr.nent[name][0], pr.topk[0] if name == "csa" else None,
+                                      s_.k, pr.ring[name], s_.W, s_.B, s_.H, s_.D, s_.d_rope, s_.d_v, s_.rope_base,
+                                      s_.scale, pr.out[name][0], pr.lse[name][0], pr.ws_att[name],
+                                      q_rms_eps=s_.rms_eps, T=s_.draft, R=pr.R[name])
+        torch.cuda.synchronize()
+        print(json.dumps({"attn_only": name, "calls": W + K}))
+        return
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec_kw), dev) for p in range(P)]
     spec = pairs[0].s
     torch.cuda.synchronize()
@@ -207,10 +250,34 @@ def main():
     t_idx = timed(run_index, reps)
     t_csa = timed(run_attn("csa"), reps)
     t_hca = timed(run_attn("hca"), reps)
-    idx_bytes = sb["csa_index"]
-    achieved = idx_bytes / (t_idx[3] / 1e3) / 1e9
-    idx_sha = source_sha(INDEX_SOURCES)
-    traffic = pmc_traffic(idx_sha) if spec.draft == 1 else None   # counters were taken on one query per sequence
+    calls = {"csa_index_topk": (t_idx, sb["csa_index"], sf["csa_index"],
+                                "csa_index_topk (index_chunk_decode_kernel + index_final_decode_kernel), "
+                                f"{spec.B * spec.draft} queries x {pairs[0].n0['csa']} entries"),
+             "hybrid_attn_decode_csa": (t_csa, sb["csa_attn"], sf["csa_attn"],
+                                        f"hybrid_attn_decode, CSA: {spec.B * spec.draft} queries x ({spec.k} top-k "
+                                        f"entries + {spec.W} window), 64 heads (16-head kernel + merge)"),
+             "hybrid_attn_decode_hca": (t_hca, sb["hca_attn"], sf["hca_attn"],
+                                        f"hybrid_attn_decode, HCA: {spec.B * spec.draft} queries x "
+                                        f"({pairs[0].n0['hca']} entries + {spec.W} window), 64 heads "
+                                        "(64-head kernel + merge)")}
+
+    def roofline(call):
+        t, nbytes, nflops, what = calls[call]
+        gbs = nbytes / (t[3] / 1e3) / 1e9
+        tf = nflops / (t[3] / 1e3) / 1e12
+        # the bound the kernel's own work is nearer to: bytes at 8 TB/s vs bf16 MFMA flops at 2.5 PFLOP/s
+        mfma = call != "csa_index_topk" and tf / 2500.0 > gbs / PEAK_HBM_GBS
+        r = {"kernel": what, "bound": "mfma" if mfma else "hbm",
+             "achieved": round(tf if mfma else gbs, 1), "peak": 2500.0 if mfma else PEAK_HBM_GBS,
+             "unit": "TFLOP/s" if mfma else "GB/s"}
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+        r["traffic"] = pmc_traffic(call) if spec.draft == 1 else None  # counters: one query per sequence
+        r["algorithmic_bytes_per_launch"] = nbytes
+        r["algorithmic_flops_per_launch"] = nflops
+        r["avg_launch_ms"] = round(t[3], 5)
+        return r
+
+    dominant = max(calls, key=lambda c: calls[c][0][3])   # the call with the longest average launch
 
     rec = {
         "metric": "hybrid-attn decode tokens/s & HBM GB/s at 1M ctx; indexer+top-k µs/query",
@@ -245,23 +312,129 @@ def main():
             "hybrid_attn_decode_csa": {"median": t_csa[0], "p10": t_csa[1], "p90": t_csa[2]},
             "hybrid_attn_decode_hca": {"median": t_hca[0], "p10": t_hca[1], "p90": t_hca[2]},
         },
-        "roofline": {
-            "kernel": "csa_index_topk (index_chunk_decode_kernel + index_final_decode_kernel), "
-                      "8 queries x 262144 entries",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": idx_bytes,
-            "avg_launch_ms": round(t_idx[3], 5),
-        },
+        "roofline": roofline(dominant),
+        "roofline_calls": {c: roofline(c) for c in calls if c != dominant},
+        "roofline_step": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+                          "what": "algorithmic bytes of the whole layer-pair step / the step's time"},
         "wall_s_timed": round(t_wall, 4),
     }
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pairs[0])
+    print(json.dumps(rec))
+
+
+def attn_workload_bench(args, dev):
+    """c2 (CSA decode, batch 32, 65536-token context: 16384 bf16 entries per sequence, indexer 8x128
+    MXFP4 top-128 + gather attention over the top-k and a 128-token window) or c3 (HCA decode,
+    batch 16, 2^20-token context: 8192 fp8 entries per sequence, dense attention + window). One
+    step = the layer's calls for the whole batch; P independent caches are cycled so that each step
+    reads its entries from HBM rather than from the Infinity Cache. Inputs are synthetic (the
+    generator's seeded N(0, 1/D) draws) and resident before timing."""
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_03_amd import configs, native, synth
+
+    w = configs.C2 if args.workload == "c2" else configs.C3
+    B, H, D, dv, W, k = w.B, w.H, w.D, w.d_v, w.W, w.k
+    n = w.L // w.m
+    t = w.L - 1
+    P = 4 if args.workload == "c3" else 1   # c2's 604 MB of entries already exceed the cache
+    dense = args.workload == "c3"
+    kv = native.CSKV_FP8_E4M3 if dense else native.CSKV_BF16
+    st = []
+    for p in range(P):
+        d = {"q": synth.normal_bf16_bits((B, H, D), w.sigma, synth.seed_of(p, w.wid, 2), dev),
+             "ring": synth.normal_bf16_bits((B, W, D), w.sigma, synth.seed_of(p, w.wid, 4), dev)}
+        if dense:
+            d["ckv"], d["sc"] = synth.fp8_rows_normal((B, n, D), w.sigma, synth.seed_of(p, w.wid, 3), dev)
+        else:
+            d["ckv"], d["sc"] = synth.normal_bf16_bits((B, n, D), w.sigma, synth.seed_of(p, w.wid, 3), dev), None
+            d["iq"], d["iqs"] = synth.mxfp4_normal((B, 1, w.H_I, w.D_I), synth.seed_of(p, w.wid, 11), dev)
+            d["ik"], d["iks"] = synth.mxfp4_normal((B, n, w.D_I), synth.seed_of(p, w.wid, 10), dev)
+            d["topk"] = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+        st.append(d)
+    qpos = torch.full((B,), t, dtype=torch.int64, device=dev)
+    nent = torch.full((B,), n, dtype=torch.int32, device=dev)
+    nv = torch.full((B, 1), n, dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, dv), dtype=torch.int16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, native.hybrid_attn_decode_workspace_size(B, H, dv, n, k, W, dense)), dtype=torch.uint8,
+                     device=dev)
+    wsi = None if dense else torch.empty(max(16, native.csa_index_topk_workspace_size(B, 1, n, w.H_I, w.D_I, k)),
+                                         dtype=torch.uint8, device=dev)
+
+    def index(d):
+        native.csa_index_topk(d["iq"], d["iqs"], None, d["ik"], d["iks"], nv, B, 1, n, w.H_I, w.D_I, k, d["topk"],
+                              None, wsi)
+
+    def attend(d):
+        native.hybrid_attn_decode(d["q"], qpos, d["ckv"], d["sc"], kv, n, nent, None if dense else d["topk"], k,
+                                  d["ring"], W, B, H, D, w.d_rope, dv, w.rope_base, w.softmax_scale, out, lse, ws)
+
+    def step(i):
+        d = st[i % P]
+        if not dense:
+            index(d)
+        attend(d)
+
+    K = args.steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_step = ms / K
+    eb = D * (1 if dense else 2) + (4 if dense else 0)          # stored entry bytes
+    q_o = B * H * (D + dv) * 2
+    win = B * W * D * 2
+    attn_bytes = (B * n * eb if dense else B * k * eb + B * k * 4) + win + q_o
+    idx_bytes = 0 if dense else B * n * (w.D_I // 2 + w.D_I // 32) + B * w.H_I * (w.D_I // 2 + w.D_I // 32) + B * k * 4
+    attn_flops = 2 * B * H * ((n if dense else k) + W) * (D + dv)
+    # the attention call alone (its own graph): the HBM roofline of the gather / dense attention
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        for i in range(K):
+            attend(st[i % P])
+    g2.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / K
+    gbs = attn_bytes / (ms_attn / 1e3) / 1e9
+    rec = {
+        "metric": "hybrid-attn decode tokens/s & HBM GB/s at 1M ctx; indexer+top-k µs/query",
+        "value": round(B * K / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ("fp8-e4m3" if dense else "bf16") + " KV / bf16 MFMA, fp32 accumulate"
+                 + ("" if dense else " / mxfp4 indexer"),
+        "data": "synthetic (seeded N(0,1/D) draws; no checkpoints)",
+        "config": {"workload": w.name + (": HCA decode, batch 16, context 2^20, 8192 fp8 entries + window 128"
+                                         if dense else ": CSA decode, batch 32, context 65536, 16384 bf16 entries, "
+                                                       "MXFP4 indexer 8x128, top-128 + window 128"),
+                   "batch": B, "context": w.L, "caches_cycled": P},
+        "hbm_gbs_step": round((attn_bytes + idx_bytes) / (ms_step / 1e3) / 1e9, 1),
+        "roofline": {"kernel": "hybrid_attn_decode (attention kernel + merge)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": attn_bytes, "algorithmic_flops_per_launch": attn_flops,
+                     "avg_launch_ms": round(ms_attn, 5),
+                     "mfma_frac_bf16": round(attn_flops / (ms_attn / 1e3) / 1e12 / 2500.0, 4)},
+    }
     print(json.dumps(rec))
 
 
@@ -375,7 +548,7 @@ def prefill_cpu_baseline(p, n_pos=256):
         oatt.prefill_one(qh[r], int(t), 0, oatt.Entries(ent, None, "bf16"), m, idx[0], xh, w.W, w.d_rope, w.d_v,
                          w.rope_base, w.softmax_scale)
     dt = time.perf_counter() - t0
-    return {"value": round(n_pos / dt, 3), "unit": "positions/s", "cores": cores, "kind": "oracle",
+    return {"value": round(n_pos / dt, 3), "unit": "positions/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n_pos} positions of the 128K-token prefill (index + top-k over their visible entries, "
                       f"compression of the entries they select, attention; fp64 numpy oracle, {dt:.1f} s)"}
 
@@ -408,7 +581,7 @@ def cpu_baseline(pair):
     dt = time.perf_counter() - t0
     return {"value": round(spec.B * n_steps / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_steps} decode steps x {spec.B} sequences of one CSA+HCA layer pair at 1M context "
-                      f"(fp64 numpy oracle, {dt:.1f} s, {platform.processor() or platform.machine()})"}
+                      f"(fp64 numpy oracle, {dt:.1f} s)", "cpu": cpu_model()}
 
 
 if __name__ == "__main__":
