@@ -92,8 +92,8 @@ struct AttnArgs {
   int win_per_split;
   uint16_t* out;             // [nq, H, d_v]
   float* out_lse;            // [nq, H]
-  float* part_o;             // [nq, n_hb, n_splits, 64, d_v]
-  float* part_ml;            // [nq, n_hb, n_splits, 64, 2]
+  uint16_t* part_o;          // [nq, n_hb, n_splits, 64, d_v] fp16: the split's O / l
+  float* part_ml;            // [nq, n_hb, n_splits, 64, 2]: exponent base m, sum l
 };
 
 // Per query: entry-key count, window start position and count.
@@ -174,6 +174,13 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats to packed fp16 with round-to-nearest-even.
+__device__ __forceinline__ uint32_t cvt_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -260,12 +267,12 @@ struct RingGeom {
 // every wave takes part in each of its wave's requests, so the count per wave is fixed.
 template <int D>
 __device__ __forceinline__ void issue_tile_f8(AttnSmem<D>& sm, int stage, const uint8_t* cbase, const float* sbase,
-                                              int key0, int e_end, int key_begin) {
+                                              int key0, int e_end, int key_begin, bool dense) {
   using G = RingGeom<D>;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const uint32_t base = lds_addr(&sm.t.r.k8[stage][0][0][0]);
   const int key = key0 + lane;
-  const int row = max(key < e_end ? sm.sidx[key - key_begin] : -1, 0);
+  const int row = max(key < e_end ? (dense ? key : sm.sidx[key - key_begin]) : -1, 0);  // dense: entry = key
   const uint8_t* src = cbase + (int64_t)row * D;
 #pragma unroll
   for (int j = 0; j < (G::NREQ + 7) / 8; ++j) {
@@ -663,7 +670,6 @@ template <int D, int DV, int KV, int DQ>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   using R = QkRange<D, DQ>;
   constexpr int NB = DV / 32, NO = (NB + 3) / 4;
-  constexpr bool F8 = KV == kKvFp8;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
   // QK: wave (hh, kh, dq) = head half, key half, half of the dims; PV: (hh, vq) = head half,
   // quarter of the value dims; w = hh + 2 kh + 4 dq = hh + 2 vq
@@ -680,6 +686,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   float ss = load_query<D, DQ>(a, qi, hq, q);
 
   const KeySpace ks = key_space(a, qi);
+  constexpr bool F8 = KV == kKvFp8;
+  const bool dense = a.topk == nullptr;
   int key_begin, key_end;
   if (a.n_esplits < a.n_splits) {  // entry splits, then window splits
     if (split < a.n_esplits) {
@@ -695,6 +703,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   }
   const int e_end = min(key_end, ks.n_c);  // entry keys [key_begin, e_end), window keys after
   const int w_begin = max(key_begin, ks.n_c);
+  const int n_et = key_begin < e_end ? (e_end - key_begin + kTK - 1) / kTK : 0;  // entry tiles
+  const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
+  constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);
+  constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);
+  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
+  const uint8_t* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
+  // dense fp8 entries: the first tile's rows are known now (entry = key)
+  if (F8 && dense && n_et > 0)
+    issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin, true);
   // the rows of this split's keys: entry rows in the sequence's cache (top-k slot or dense
   // index; out of range = masked), then window rows in win (ring slot or prompt row)
   {
@@ -721,24 +738,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   if (tid == 0) sm.rescale = 0;
   __syncthreads();  // sidx and the RoPE table ready
 
-  const int64_t seq = (int64_t)(a.ckv_seq ? qi / a.q_per_seq : 0) * a.ckv_seq;
-  constexpr int row_bytes = KV == kKvBf16 ? 2 * D : (KV == kKvFp8 ? D : D / 2);
-  constexpr int srow_bytes = KV == kKvFp8 ? 4 : (KV == kKvMxfp4 ? D / 32 : 0);
-  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(a.ckv) + seq * row_bytes;
-  const uint8_t* sbase = a.ckv_scale ? reinterpret_cast<const uint8_t*>(a.ckv_scale) + seq * srow_bytes : nullptr;
-  const int n_et = key_begin < e_end ? (e_end - key_begin + kTK - 1) / kTK : 0;  // entry tiles
-
-  // the first fp8 entry tile, then the query's dims of this lane's head and wave's steps
-  if (F8 && n_et > 0)
-    issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin);
+  // every load so far (the query, the row lists, a dense first tile) has landed: the loop then
+  // waits on tile loads only where a tile is used, never because a query register might be
+  // pending
+  __builtin_amdgcn_s_waitcnt(0);
+  if (F8 && !dense && n_et > 0)
+    issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin, false);
   ss += __shfl_xor(ss, 32, kWave);
   if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
   rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
-  // every load so far (the query, the first tile) has landed: the loop then waits on tile loads
-  // only where a tile is used, never because a query register might be pending
-  __builtin_amdgcn_s_waitcnt(0);
   if (F8 && n_et > 1)
-    issue_tile_f8<D>(sm, 1, cbase, reinterpret_cast<const float*>(sbase), key_begin + kTK, e_end, key_begin);
+    issue_tile_f8<D>(sm, 1, cbase, reinterpret_cast<const float*>(sbase), key_begin + kTK, e_end, key_begin, dense);
 
   HeadState<NO> st;
 #pragma unroll
@@ -768,7 +778,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
     tile_softmax<D, NO>(a, sm, st, s, w, valid, vsc);
     if (F8 && t + 2 < n_et)  // ring stage (t + 2) % 3 was last read by tile t - 1, finished by all
       issue_tile_f8<D>(sm, (t + 2) % kStages, cbase, reinterpret_cast<const float*>(sbase), key0 + 2 * kTK, e_end,
-                       key_begin);
+                       key_begin, dense);
     tile_pv<D, NO, NB, F8>(sm, st, hh, vq, stage, valid);
   }
   // phase 2: window tokens (the bf16 tile overlays the ring: staged after the last entry tile's reads)
@@ -814,17 +824,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
     return;
   }
 
-  // split partial: unnormalised O, exponent base and sum
+  // split partial: O / l in fp16 (a convex combination of value rows, so within their range; the
+  // relative rounding 2^-11 sits well below the output's bf16 rounding), exponent base and sum
   const int64_t prow = (((int64_t)qh * a.n_splits + split) * kHB + hl);
-  float* dst = a.part_o + prow * DV;
+  uint16_t* dst = a.part_o + prow * DV;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
   for (int n = 0; n < NO; ++n) {
     const int b = vq * NO + n;
     if (NB % 4 != 0 && b >= NB) continue;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4*>(dst + 32 * b + 8 * g + u4) =
-          f32x4{st.o[n][4 * g], st.o[n][4 * g + 1], st.o[n][4 * g + 2], st.o[n][4 * g + 3]};
+    for (int g = 0; g < 4; ++g) {
+      uint2 pk;
+      pk.x = cvt_f16x2(st.o[n][4 * g] * inv, st.o[n][4 * g + 1] * inv);
+      pk.y = cvt_f16x2(st.o[n][4 * g + 2] * inv, st.o[n][4 * g + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g + u4) = pk;
+    }
   }
   if (vq == 0 && lane < 32) {
     a.part_ml[prow * 2 + 0] = st.m;
@@ -841,10 +856,10 @@ __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
     attn_body<D, DV, KV, 0>(a, sm);
 }
 
-// One workgroup per (query, head): log-sum-exp merge of the split partials. Thread t owns dims
-// 4t..4t+3 (d_v <= 4 * kMergeNT). Split rows are read kMergeBatch at a time, the batch requested
-// before the previous one is summed; rows past the last split repeat it with weight 0, so every
-// load is unconditional.
+// One workgroup per (query, head): log-sum-exp merge of the split partials, split s weighted by
+// 2^(m_s - M) l_s. Thread t owns dims 4t..4t+3 (d_v <= 4 * kMergeNT). Split rows are read
+// kMergeBatch at a time, the batch requested before the previous one is summed; rows past the
+// last split repeat it with weight 0, so every load is unconditional.
 constexpr int kMergeNT = 128;
 constexpr int kMergeBatch = 8;
 __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
@@ -864,8 +879,8 @@ __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
       float wt = 0.f;
       if (sp < S) {
         const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[(row0 + (int64_t)sp * kHB) * 2]);
-        wt = exp2f(ml.x - Mb);
-        l += wt * ml.y;
+        wt = exp2f(ml.x - Mb) * ml.y;
+        l += wt;
       }
       wsh[sp] = wt;
     }
@@ -879,16 +894,20 @@ __global__ __launch_bounds__(kMergeNT) void attn_merge_kernel(AttnArgs a) {
   const float Mb = red[0], L = red[1];
   const float inv = L > 0.f ? 1.f / L : 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto fetch = [&](f32x4 (&v)[kMergeBatch], int s0) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  auto fetch = [&](uint2 (&v)[kMergeBatch], int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(a.part_o + (row0 + (int64_t)min(s0 + u, S - 1) * kHB) * a.d_v + dd);
+      v[u] = *reinterpret_cast<const uint2*>(a.part_o + (row0 + (int64_t)min(s0 + u, S - 1) * kHB) * a.d_v + dd);
   };
-  auto sum = [&](const f32x4 (&v)[kMergeBatch], int s0) {
+  auto sum = [&](const uint2 (&v)[kMergeBatch], int s0) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) acc += wsh[s0 + u] * v[u];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
+      acc += wsh[s0 + u] * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
   };
-  f32x4 v0[kMergeBatch], v1[kMergeBatch];
+  uint2 v0[kMergeBatch], v1[kMergeBatch];
   fetch(v0, 0);
   for (int s0 = 0;; s0 += 2 * kMergeBatch) {  // v0 holds rows s0.. on entry
     if (s0 + kMergeBatch >= S) {
@@ -964,7 +983,7 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_entries, int W) {
     p.n_splits = p.n_esplits = kMaxSplits + 1;
     p.keys_per_split = kMaxSplitKeys;
   }
-  p.ws = p.n_splits > 1 ? (size_t)base * p.n_splits * kHB * ((size_t)d_v + 2) * sizeof(float) : 0;
+  p.ws = p.n_splits > 1 ? (size_t)base * p.n_splits * kHB * (2 * (size_t)d_v + 2 * sizeof(float)) : 0;
   return p;
 }
 
@@ -1013,8 +1032,8 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   CSKV_REQUIRE(p.n_splits == 1 || a.d_v <= 4 * kMergeNT, CSKV_ENOTSUP, "%s: d_v=%d > %d with split keys", name,
                a.d_v, 4 * kMergeNT);
   if (p.n_splits > 1) {
-    a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = a.part_o + (size_t)a.nq * p.n_hb * p.n_splits * kHB * a.d_v;
+    a.part_o = reinterpret_cast<uint16_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)a.nq * p.n_hb * p.n_splits * kHB * a.d_v);
   }
   const int64_t total = (int64_t)a.nq * p.n_hb * p.n_splits;
   CSKV_REQUIRE(total < (1ll << 31), CSKV_ENOTSUP, "%s: %lld workgroups", name, (long long)total);
