@@ -569,19 +569,25 @@ def cpu_baseline(pair):
                                   h["scl"], "fp8", np.full(spec.B, spec.L // m), h["ring"].copy(), h["ringz"].copy(),
                                   k=spec.k, ik=st["ik"] if name == "csa" else None,
                                   ik_scale=st["iks"] if name == "csa" else None)
-    n_steps = 2
+    n_steps, Td = 2, spec.draft
     t0 = time.perf_counter()
     for i in range(n_steps):
-        t = np.full(spec.B, spec.L + i)
+        t = np.full(spec.B, spec.L + i * Td)
         for name, lay in layers.items():
             h = st[name]
-            iq = st["iq"][i][:, 0] if name == "csa" else None
-            iqs = st["iqs"][i][:, 0] if name == "csa" else None
-            lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs)
+            if Td == 1:
+                iq = st["iq"][i][:, 0] if name == "csa" else None
+                iqs = st["iqs"][i][:, 0] if name == "csa" else None
+                lay.step(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs)
+            else:  # every draft token accepted, as on the GPU
+                iq = st["iq"][i] if name == "csa" else None
+                iqs = st["iqs"][i] if name == "csa" else None
+                lay.step_draft(t, h["xn"][i], h["zn"][i], h["q"][i], iq, iqs)
     dt = time.perf_counter() - t0
-    return {"value": round(spec.B * n_steps / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_steps} decode steps x {spec.B} sequences of one CSA+HCA layer pair at 1M context "
-                      f"(fp64 numpy oracle, {dt:.1f} s)", "cpu": cpu_model()}
+    pos = "positions" if Td > 1 else "steps"
+    return {"value": round(spec.B * Td * n_steps / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} decode steps x {spec.B} sequences{f' x {Td} draft {pos}' if Td > 1 else ''} of one "
+                      f"CSA+HCA layer pair at 1M context (fp64 numpy oracle, {dt:.1f} s)", "cpu": cpu_model()}
 
 
 if __name__ == "__main__":

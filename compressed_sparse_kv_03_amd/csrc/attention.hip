@@ -64,32 +64,34 @@ constexpr float kRescaleSlack = 8.f;  // log2 units the running max may run ahea
 
 
 struct AttnArgs {
+  // the fields a workgroup reads before its first loads, packed at the front of the argument block
   const uint16_t* q;         // [nq, H, D]
   const int64_t* q_pos;      // [nq] (decode) or nullptr (prefill: pos0 + row)
-  int64_t pos0;
+  const int32_t* n_entries;  // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))
+  const int32_t* topk;       // [nq, k] or nullptr (dense)
   const void* ckv;           // [B_kv, N_cap, D] bf16 bits, fp8 codes, or MXFP4 codes [.., D/2]
   const void* ckv_scale;     // fp32 [B_kv, N_cap] (fp8) or E8M0 bytes [B_kv, N_cap, D/32] (MXFP4)
-  int kv_dtype;              // kKvBf16, kKvFp8 or kKvMxfp4
-  int N_cap;
   int64_t ckv_seq;           // entries between sequences (0: all queries share one cache)
-  const int32_t* n_entries;  // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))
-  int m;
-  const int32_t* topk;       // [nq, k] or nullptr (dense)
-  int k;
-  const uint16_t* win;       // decode: rings [B, R, D]; prefill: x [T, D]
-  int ring;                  // 1: slot = pos mod ring_cap of sequence qi / q_per_seq; 0: row = pos - pos0 of x
-  int ring_cap;
+  int64_t pos0;
+  double rope_step;          // base^(-2 / d_rope): ratio of consecutive RoPE frequencies (host fp64)
+  int N_cap;
   int q_per_seq;             // consecutive queries sharing one sequence's ring and cache (decode)
-  int W;
-  int nq, H, D, d_rope, d_v;
-  float rope_base;
-  float scale_log2;          // softmax_scale * log2(e)
-  float q_rms_eps;           // > 0: unit-gain RMSNorm of each query head (folded into its logits)
+  int H;
   int n_hb;                  // head blocks of 64
   int n_splits, keys_per_split;
   int n_esplits;             // n_esplits < n_splits: splits [0, n_esplits) take keys_per_split entry keys
                              // each, the rest win_per_split window keys each; else all keys in order
   int win_per_split;
+  int k, m, W;
+  int ring;                  // 1 (decode, q_pos and n_entries given): slot = pos mod ring_cap of sequence
+                             // qi / q_per_seq; 0 (prefill): row = pos - pos0 of x
+  float q_rms_eps;           // > 0: unit-gain RMSNorm of each query head (folded into its logits)
+  // the rest
+  const uint16_t* win;       // decode: rings [B, R, D]; prefill: x [T, D]
+  int kv_dtype;              // kKvBf16, kKvFp8 or kKvMxfp4
+  int ring_cap;
+  int nq, D, d_rope, d_v;
+  float scale_log2;          // softmax_scale * log2(e)
   uint16_t* out;             // [nq, H, d_v]
   float* out_lse;            // [nq, H]
   uint16_t* part_o;          // [nq, n_hb, n_splits, 64, d_v] fp16: the split's O / l
@@ -106,13 +108,23 @@ struct KeySpace {
 
 __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
   KeySpace ks;
-  ks.t = a.q_pos ? a.q_pos[qi] : a.pos0 + qi;
+  // decode: the query's position and its entry count are requested together, before either is
+  // used (one memory round trip instead of two)
+  const bool by_count = a.ring && a.N_cap != 0 && a.topk == nullptr;
+  int64_t t = a.pos0 + qi;
+  int n = 0;
+  if (by_count) {
+    n = a.n_entries[qi];
+    t = a.q_pos[qi];
+  } else if (a.ring) {
+    t = a.q_pos[qi];
+  }
+  ks.t = t;
   if (a.N_cap == 0) {
     ks.n_c = 0;  // no cache (every top-k slot would be masked)
   } else if (a.topk) {
     ks.n_c = a.k;
-  } else if (a.n_entries) {
-    const int n = a.n_entries[qi];
+  } else if (by_count) {
     ks.n_c = n < 0 ? 0 : (n < a.N_cap ? n : a.N_cap);
   } else {
     const int64_t v = (ks.t + 1) / a.m;
@@ -226,7 +238,7 @@ struct AttnSmem {
   float lsum[4][kHB];
   float qss[2][kHB];                 // query sums of squares over each half of the dims
   int rescale;                       // a tile's logit exceeded its head's exponent base by more than the slack
-  double rev[kMaxRopePairs];         // RoPE frequencies (revolutions per position), from the host
+  double rev[kMaxRopePairs];         // RoPE frequencies (revolutions per position)
   int sidx[kMaxSplitKeys];
 };
 
@@ -454,13 +466,20 @@ struct QkRange {
 // The query's dims of this wave's steps, lane (head c, half u) holding dims 16 s + 8 u .. + 7 of
 // head c; returns the lane's sum of squares of the raw values (query RMSNorm).
 template <int D, int DQ>
-__device__ __forceinline__ float load_query(const AttnArgs& a, int qi, int hq, uint4* q) {
+__device__ __forceinline__ void load_query(const AttnArgs& a, int qi, int hq, uint4* q) {
   using R = QkRange<D, DQ>;
   const int ko = 8 * ((threadIdx.x & (kWave - 1)) >> 5);
   // heads past H (a partial block) compute with head H - 1's dims; their results are not written
   const uint16_t* src = a.q + ((int64_t)qi * a.H + min(hq, a.H - 1)) * D + ko;
 #pragma unroll
   for (int s = R::S0; s < R::S1; ++s) q[s - R::S0] = *reinterpret_cast<const uint4*>(src + 16 * s);
+}
+
+// This lane's part of the query head's sum of squares (0 without the RMSNorm), once the loads
+// have landed.
+template <int D, int DQ>
+__device__ __forceinline__ float query_sumsq(const AttnArgs& a, const uint4* q) {
+  using R = QkRange<D, DQ>;
   float ss = 0.f;
   if (a.q_rms_eps > 0.f) {
 #pragma unroll
@@ -680,14 +699,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   const int qi = qh / a.n_hb;
   const int hq = (qh % a.n_hb) * kHB + hl;  // this lane's head
 
-  // the query's dims of this lane's head and wave's steps: requested first (their latency
-  // overlaps the listing of the split's rows)
-  uint4 q[R::NQ], qlo[R::NLOA];
-  float ss = load_query<D, DQ>(a, qi, hq, q);
-
-  const KeySpace ks = key_space(a, qi);
   constexpr bool F8 = KV == kKvFp8;
   const bool dense = a.topk == nullptr;
+  // the query's dims of this lane's head and wave's steps, then the query's position and entry
+  // count (their latency overlaps the listing of the split's rows)
+  uint4 q[R::NQ], qlo[R::NLOA];
+  load_query<D, DQ>(a, qi, hq, q);
+  const KeySpace ks = key_space(a, qi);
+
   int key_begin, key_end;
   if (a.n_esplits < a.n_splits) {  // entry splits, then window splits
     if (split < a.n_esplits) {
@@ -732,9 +751,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
     }
   }
   // the RoPE table in revolutions per position, base^(-2i / d_rope) / (2 pi), in fp64
-  if (w == 0 && 2 * lane < a.d_rope)
-    sm.rev[lane] = exp2(-2.0 * (double)lane / (double)a.d_rope * log2((double)a.rope_base)) *
-                   0.15915494309189533576888376337251;
+  // (pair i: rope_step^i / (2 pi), the power formed by squaring, a few fp64 roundings)
+  if (w == 0 && 2 * lane < a.d_rope) {
+    double f = 0.15915494309189533576888376337251, r = a.rope_step;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {  // lane < 32
+      if ((lane >> b) & 1) f *= r;
+      r *= r;
+    }
+    sm.rev[lane] = f;
+  }
   if (tid == 0) sm.rescale = 0;
   __syncthreads();  // sidx and the RoPE table ready
 
@@ -744,6 +770,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   __builtin_amdgcn_s_waitcnt(0);
   if (F8 && !dense && n_et > 0)
     issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin, false);
+  float ss = query_sumsq<D, DQ>(a, q);
   ss += __shfl_xor(ss, 32, kWave);
   if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
   rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
@@ -1112,7 +1139,7 @@ static int run_attn(const char* name, const AttnCall& c, bool noalloc, void* ws,
   a.D = c.D;
   a.d_rope = c.d_rope;
   a.d_v = c.d_v;
-  a.rope_base = c.rope_base;
+  a.rope_step = pow((double)c.rope_base, -2.0 / (double)c.d_rope);
   a.scale_log2 = c.scale_log2;
   a.q_rms_eps = c.q_rms_eps;
   a.out = c.out;

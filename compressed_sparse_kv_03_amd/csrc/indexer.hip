@@ -668,7 +668,8 @@ __global__ __launch_bounds__(kDecNT) void index_chunk_decode_kernel(DecodeArgs d
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int i = tid + j * kDecNT;
-        v[j] = i < n ? sm.keys[i] : 0;
+        const uint64_t x = sm.keys[min(i, kMaxSlots + kDecSub - 1)];  // unconditional: all reads in flight
+        v[j] = i < n ? x : 0;
       }
       uint64_t lo, hi;
       key_bounds(sm.ss, &lo, &hi);
@@ -856,6 +857,378 @@ static int launch_decode(const IndexArgs& a, int queries, int ks, void* ws, hipS
   else
     launch_decode_ks<4>(d, queries, s);
   CSKV_LAUNCH_CHECK("csa_index_topk (decode)");
+  return CSKV_OK;
+}
+
+// ---------------------------------------------------------------- decode path, draft queries
+//
+// A decode step that checks T > 1 draft tokens has T queries per sequence, query t seeing the
+// first n_valid[b, t] entries. Kernel M (grid B * ceil(T / TQ) x C, 1024 threads) gives a
+// workgroup TQ consecutive queries of one sequence (H_I <= 8: two queries per MFMA row tile,
+// TQ / 2 row tiles) and streams chunk c of that sequence's keys once for all of them. Each
+// query's scores are kept in LDS by entry position (the entry index is implied by it), then one
+// selection pass serves all TQ queries at once: kernel A's histogram levels with one histogram
+// per query, scanned by a thread group per query, every barrier shared. The slots each query
+// gets for the chunk, and kernel B's merge per query, are kernel A's.
+constexpr int kMqSub = 8448;   // entries of one chunk (LDS holds TQ scores of each)
+constexpr int kMqBins = 1024;  // histogram bins per level and query (10 bits)
+constexpr int kMqU = 6;        // groups of 16 entries per wave and batch
+
+template <int TQ>
+struct MqSmem {
+  uint32_t sc[TQ][kMqSub];  // ordered scores of the chunk's entries (0: not visible)
+  uint32_t hist[TQ][kMqBins];
+  int scratch[TQ][kDecNT / kWave];
+  int thr[TQ], above[TQ];
+  uint32_t mx32[TQ], mn32[TQ];
+};
+
+// Bin b of hist[j] (scanning from the top) whose cumulative count reaches need[j], and the count
+// strictly above it, for every active query j: thread group j (NT / TQ threads) scans hist[j].
+// Every thread calls it after a barrier that follows the histogram's last update and every
+// earlier read of the results; it ends with a barrier.
+// nj, aj: need and activity of this thread's query (tid / (NT / TQ)).
+template <int TQ, int NT>
+__device__ void mq_threshold_bins(MqSmem<TQ>& sm, int nj, bool aj) {
+  constexpr int GT = NT / TQ;             // threads per query
+  constexpr int PB = kMqBins / GT;        // bins per thread
+  constexpr int WPG = GT / kWave;         // waves per query
+  static_assert(PB >= 1 && WPG >= 1, "group shape");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  const int j = tid / GT, lt = tid - j * GT;
+  const int top = kMqBins - PB * lt;  // this thread's bins: [top - PB, top)
+  if (tid < TQ) {  // defaults (bin 0) in case the counts do not reach need
+    sm.thr[tid] = 0;
+    sm.above[tid] = 0;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 1; i <= PB; ++i) sum += (int)sm.hist[j][top - i];
+  const int inc = wave_incl_scan(sum);
+  if (lane == kWave - 1) sm.scratch[0][w] = inc;
+  __syncthreads();
+  int wbase = 0;
+  const int w0 = j * WPG;
+#pragma unroll
+  for (int i = 0; i < WPG; ++i) wbase += w0 + i < w ? sm.scratch[0][w0 + i] : 0;
+  const int incl = inc + wbase, excl = incl - sum;
+  if (aj && excl < nj && incl >= nj) {
+    int c = excl;
+    for (int i = 1; i <= PB; ++i) {
+      const int h = (int)sm.hist[j][top - i];
+      if (c + h >= nj) {
+        sm.thr[j] = top - i;
+        sm.above[j] = c;
+        break;
+      }
+      c += h;
+    }
+  }
+  __syncthreads();
+}
+
+template <int TQ>
+__global__ __launch_bounds__(kDecNT) void index_chunk_multi_kernel(DecodeArgs d, int ngroups) {
+  constexpr int NRT = TQ / 2;                 // row tiles: two queries (8 rows each) per tile
+  constexpr int PER = (kMqSub + kDecNT - 1) / kDecNT;
+  constexpr int U = kMqU, NB = 6;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MqSmem<TQ>& sm = *reinterpret_cast<MqSmem<TQ>*>(smem_raw);
+  const IndexArgs& a = d.a;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 4, col = lane & 15;
+  const int b = blockIdx.x / ngroups, t0 = (blockIdx.x - b * ngroups) * TQ, c = blockIdx.y;
+  // the group's queries: visible entries and the number kept per chunk
+  int nv[TQ], kk[TQ];
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) {
+    const int t = t0 + j;
+    nv[j] = t < a.T ? min(a.n_valid[(int64_t)b * a.T + t], a.N_cap) : 0;
+    kk[j] = min(a.k, nv[j]);
+  }
+  int cmax = 0;
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) cmax = max(cmax, nv[j]);
+  const int c0 = c * d.chunk, c1 = min(c0 + d.chunk, cmax);  // entries [c0, c1) seen by someone
+  const int n_el = max(0, c1 - c0);
+  for (int i = tid; i < TQ * kMqBins; i += kDecNT) (&sm.hist[0][0])[i] = 0;
+  if (tid < TQ) {
+    sm.mx32[tid] = 0;
+    sm.mn32[tid] = ~0u;
+  }
+  // A operand: row tile rt, lane row col = query 2 rt + col / 8, head col % 8
+  uint4 qa[NRT];
+  int qs[NRT];
+  float hw[NRT][4];
+  int nvl[NRT];  // entries visible to the query whose scores this lane writes (G = 0, 2)
+  const int kbytes = a.D_I >> 1, sbytes = a.D_I >> 5;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int ta = t0 + 2 * rt + col / 8, ha = col % 8;
+    const bool oka = ta < a.T && ha < a.H_I && G * 32 < a.D_I;
+    const int64_t qrow = ((int64_t)b * a.T + ta) * a.H_I + ha;
+    qa[rt] = oka ? *reinterpret_cast<const uint4*>(a.iq + qrow * kbytes + G * 16) : make_uint4(0, 0, 0, 0);
+    qs[rt] = oka ? (int)a.iq_scale[qrow * sbytes + G] : 127;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * G + r, tr = t0 + 2 * rt + row / 8, hr = row % 8;
+      hw[rt][r] = (tr < a.T && hr < a.H_I) ? (a.head_w ? a.head_w[((int64_t)b * a.T + tr) * a.H_I + hr] : 1.0f) : 0.0f;
+    }
+    const int jl = 2 * rt + (G >> 1);
+    int v = nv[0];
+#pragma unroll
+    for (int j = 1; j < TQ; ++j) v = jl == j ? nv[j] : v;
+    nvl[rt] = v;
+  }
+
+  // stream the chunk once: every wave keeps two batches of loads in flight; each group of 16
+  // entries takes NRT MFMAs, and lanes of groups 0 / 2 store the scores of the row tile's two
+  // queries
+  const uint8_t* ikb = a.ik + (int64_t)b * a.N_cap * kbytes;
+  const uint32_t* sc32 = reinterpret_cast<const uint32_t*>(a.ik_scale);
+  const int64_t sc_off0 = (int64_t)b * a.N_cap * sbytes;
+  const int groups = (n_el + 15) >> 4;
+  const int stride = (kDecNT / kWave) * U;
+  for (int g0 = wave * U; g0 < groups; g0 += stride * NB) {
+    KBatch<1, U> X[NB];
+    kbatch_load<1, U>(ikb, sc32, sc_off0, kbytes, sbytes, a.D_I, c0, c1, g0, X[0]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int gi = g0 + i * stride;
+      if (gi >= groups) break;
+      if (i + 1 < NB) kbatch_load<1, U>(ikb, sc32, sc_off0, kbytes, sbytes, a.D_I, c0, c1, gi + stride, X[i + 1]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (gi + u >= groups) break;
+        const int el = (gi + u) * 16 + col;
+        const int e = min(c0 + el, c1 - 1);
+        const bool okk = G * 32 < a.D_I;
+        const int sh = 8 * (int)((sc_off0 + (int64_t)e * sbytes + G) & 3);
+        const int byte = okk ? (int)((X[i].sc[u][0] >> sh) & 255u) : 127;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc += mfma_fp4(qa[rt], X[i].kv[u][0], qs[rt], byte);
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part = fmaf(hw[rt][r], fmaxf(acc[r], 0.f), part);
+          part += __shfl_xor(part, 16, kWave);
+          if ((G & 1) == 0 && el < n_el)
+            sm.sc[2 * rt + (G >> 1)][el] = c0 + el < nvl[rt] ? score_to_ordered(part) : 0u;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // keys in registers (thread tid holds entries tid + i * NT), their score range per query;
+  // every read is issued before any is used, and the loop has no branch
+  uint64_t v[TQ][PER];
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) {
+    uint32_t o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = sm.sc[j][min(tid + i * kDecNT, kMqSub - 1)];
+    uint32_t mx = 0, mn = ~0u;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int el = tid + i * kDecNT;
+      const uint32_t x = el < n_el ? o[i] : 0u;
+      v[j][i] = x ? (((uint64_t)x << 32) | (uint64_t)(~(uint32_t)(c0 + el))) : 0ull;
+      mx = max(mx, x);
+      mn = min(mn, x ? x : ~0u);
+    }
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    if (lane == 0) {
+      atomicMax(&sm.mx32[j], mx);
+      atomicMin(&sm.mn32[j], mn);
+    }
+  }
+  __syncthreads();
+  // per query: keys at or above base pass; refine while more than the slots would
+  uint64_t base[TQ];
+  int shift[TQ], need[TQ], above_all[TQ];
+  bool active[TQ];
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) {
+    const uint64_t l = (uint64_t)sm.mn32[j] << 32;
+    const uint64_t lo = l ? l : 1, hi = ((uint64_t)sm.mx32[j] << 32) | 0xffffffffull;
+    const int n_j = max(0, min(c1, nv[j]) - c0);  // visible entries of the chunk
+    base[j] = lo;
+    const uint64_t R = hi - lo;
+    shift[j] = R == 0 ? 0 : max(0, 64 - __builtin_clzll(R) - 10);
+    need[j] = kk[j];
+    above_all[j] = 0;
+    active[j] = n_j > d.slots && kk[j] > 0;
+  }
+  // first level on the threads' largest keys only: the kk-th largest of them is at most the
+  // kk-th largest key (those kk maxima are kk distinct keys), so the lower edge of its bin is a
+  // floor every answer key clears; the levels below then count only the keys above it
+  {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) any = any || active[j];
+    if (any) {
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        if (!active[j]) continue;
+        uint64_t tm = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) tm = v[j][i] > tm ? v[j][i] : tm;
+        if (tm) atomicAdd(&sm.hist[j][(tm - base[j]) >> shift[j]], 1u);
+      }
+      __syncthreads();
+      {
+        const int jt = tid / (kDecNT / TQ);
+        int nj = need[0];
+        bool aj = active[0];
+#pragma unroll
+        for (int j = 1; j < TQ; ++j) {
+          nj = jt == j ? need[j] : nj;
+          aj = jt == j ? active[j] : aj;
+        }
+        mq_threshold_bins<TQ, kDecNT>(sm, nj, aj);
+      }
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        if (!active[j]) continue;
+        base[j] += (uint64_t)sm.thr[j] << shift[j];
+        const uint64_t R = (((uint64_t)sm.mx32[j] << 32) | 0xffffffffull) - base[j];
+        shift[j] = R == 0 ? 0 : max(0, 64 - __builtin_clzll(R) - 10);
+      }
+      __syncthreads();  // result reads done before the histogram is cleared
+      for (int i = tid; i < TQ * kMqBins; i += kDecNT) (&sm.hist[0][0])[i] = 0;
+      __syncthreads();
+    }
+  }
+  for (;;) {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) any = any || active[j];
+    if (!any) break;
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      if (!active[j]) continue;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (v[j][i] >= base[j]) {
+          const uint64_t bin = (v[j][i] - base[j]) >> shift[j];
+          if (bin < (uint64_t)kMqBins) atomicAdd(&sm.hist[j][bin], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int jt = tid / (kDecNT / TQ);  // the query whose histogram this thread scans
+      int nj = need[0];
+      bool aj = active[0];
+#pragma unroll
+      for (int j = 1; j < TQ; ++j) {
+        nj = jt == j ? need[j] : nj;
+        aj = jt == j ? active[j] : aj;
+      }
+      mq_threshold_bins<TQ, kDecNT>(sm, nj, aj);
+    }
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      if (!active[j]) continue;
+      const int thr = sm.thr[j], above = sm.above[j];
+      const int in_bin = (int)sm.hist[j][thr];
+      base[j] += (uint64_t)thr << shift[j];
+      above_all[j] += above;
+      need[j] -= above;
+      if (above_all[j] + in_bin <= d.slots || shift[j] == 0)
+        active[j] = false;
+      else
+        shift[j] = max(0, shift[j] - 10);
+    }
+    __syncthreads();  // histogram and result reads done before they are cleared
+    for (int i = tid; i < TQ * kMqBins; i += kDecNT) (&sm.hist[0][0])[i] = 0;
+    __syncthreads();
+  }
+  // each query's keys at or above its base, to its slots (the rest 0): one scan per query,
+  // all behind one barrier
+  const int w = tid >> 6;
+  int cnt[TQ], inc[TQ];
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) {
+    cnt[j] = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cnt[j] += v[j][i] >= base[j] && v[j][i] != 0;
+    inc[j] = wave_incl_scan(cnt[j]);
+    if (lane == kWave - 1) sm.scratch[j][w] = inc[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < TQ; ++j) {
+    const int t = t0 + j;
+    if (t >= a.T) continue;
+    int off = inc[j] - cnt[j], total = 0;
+#pragma unroll
+    for (int i = 0; i < kDecNT / kWave; ++i) {
+      off += i < w ? sm.scratch[j][i] : 0;
+      total += sm.scratch[j][i];
+    }
+    uint64_t* out = d.cand + (((int64_t)b * a.T + t) * d.n_chunks + c) * d.slots;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (v[j][i] >= base[j] && v[j][i] != 0 && off < d.slots) out[off++] = v[j][i];
+    for (int i = min(total, d.slots) + tid; i < d.slots; i += kDecNT) out[i] = 0;
+  }
+}
+
+// Kernel M's chunking: about one workgroup per CU for the whole job, chunks of at most kMqSub
+// entries (multiples of 16).
+static void multi_chunks(int groups, int N_cap, int* chunk, int* n_chunks) {
+  int n = (256 + groups - 1) / groups;
+  const int by_lds = (N_cap + kMqSub - 1) / kMqSub;
+  if (n < by_lds) n = by_lds;
+  if (n < 1) n = 1;
+  int c = (N_cap + n - 1) / n;
+  c = (c + 15) & ~15;
+  if (c < 16) c = 16;
+  *chunk = c;
+  *n_chunks = (N_cap + c - 1) / c;
+}
+
+// Draft steps take kernel M when a row tile holds two queries and a chunk's scores fit LDS.
+static bool use_multi(int B, int T, int H_I, int D_I, int k) {
+  return T >= 2 && H_I <= 8 && D_I <= 128 && 2 * k <= kMaxSlots / 4 && (int64_t)B * T <= 256;
+}
+static int multi_tq(int T) { return T <= 2 ? 2 : 4; }
+
+static size_t multi_ws_bytes(int B, int T, int N_cap, int k) {
+  const int tq = multi_tq(T), groups = B * ((T + tq - 1) / tq);
+  int chunk, n_chunks;
+  multi_chunks(groups, N_cap, &chunk, &n_chunks);
+  return (size_t)B * T * n_chunks * (2 * k) * sizeof(uint64_t);
+}
+
+template <int TQ>
+static void launch_multi_tq(const DecodeArgs& d, int B, int ngroups, hipStream_t s) {
+  const size_t smem = sizeof(MqSmem<TQ>), smem_b = sizeof(FinalSmem);
+  (void)hipFuncSetAttribute((const void*)index_chunk_multi_kernel<TQ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+  (void)hipFuncSetAttribute((const void*)index_final_decode_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem_b);
+  hipLaunchKernelGGL(index_chunk_multi_kernel<TQ>, dim3(B * ngroups, d.n_chunks), dim3(kDecNT), smem, s, d, ngroups);
+  hipLaunchKernelGGL(index_final_decode_kernel, dim3(B * d.a.T), dim3(kFinNT), smem_b, s, d);
+}
+
+static int launch_multi(const IndexArgs& a, void* ws, hipStream_t s) {
+  DecodeArgs d;
+  d.a = a;
+  const int tq = multi_tq(a.T), ngroups = (a.T + tq - 1) / tq;
+  multi_chunks(a.B * ngroups, a.N_cap > 0 ? a.N_cap : 1, &d.chunk, &d.n_chunks);
+  d.slots = 2 * a.k;
+  d.cand = reinterpret_cast<uint64_t*>(ws);
+  if (tq == 2)
+    launch_multi_tq<2>(d, a.B, ngroups, s);
+  else
+    launch_multi_tq<4>(d, a.B, ngroups, s);
+  CSKV_LAUNCH_CHECK("csa_index_topk (draft queries)");
   return CSKV_OK;
 }
 
@@ -1208,6 +1581,7 @@ struct IndexPlan {
   int chunk, n_chunks, cap;
   size_t ws;
   bool decode;
+  bool multi;    // decode of draft queries (kernel M)
   bool block;    // many-queries path (kernel P)
   int qpt, nqb;  // kernel P: queries per MFMA row tile, query blocks per sequence
 };
@@ -1239,7 +1613,8 @@ static IndexPlan plan_index(int B, int T, int N_cap, int H_I, int D_I, int k) {
   p.ws = (size_t)queries * n_chunks * k * sizeof(uint64_t);
   // decode path: few queries (at most one chunk workgroup per CU when they are alone)
   p.decode = k <= 1024 && queries <= 256;
-  if (p.decode) p.ws = decode_ws_bytes((int)queries, N_cap, k);
+  p.multi = p.decode && use_multi(B, T, H_I, D_I, k);
+  if (p.decode) p.ws = p.multi ? multi_ws_bytes(B, T, N_cap, k) : decode_ws_bytes((int)queries, N_cap, k);
   // many queries: blocks of consecutive queries share the entry stream (kernel P); chunks of
   // the entries only when the query blocks alone leave the GPU idle (then the merge kernel)
   if (!p.decode && k <= kPfKMax) {
@@ -1354,7 +1729,8 @@ extern "C" CSKV_API int csa_index_topk(const uint8_t* iq, const uint8_t* iq_scal
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int queries = B * T;
   const int ks = (D_I + 127) / 128;
-  int rc = p.decode  ? launch_decode(a, queries, ks, ws, s)
+  int rc = p.multi   ? launch_multi(a, ws, s)
+           : p.decode ? launch_decode(a, queries, ks, ws, s)
            : p.block ? launch_block(a, p, ks, s)
                      : (p.cap == 512 ? launch_index<512>(a, queries, ks, s) : launch_index<2048>(a, queries, ks, s));
   if (rc != CSKV_OK) return rc;

@@ -17,7 +17,7 @@ def run_index(iq, iqs, ik, iks, n_valid, k, head_w=None):
     N_cap = ik.shape[1]
     D_I = half * 2
     ws_n = native.csa_index_topk_workspace_size(B, T, N_cap, H_I, D_I, k)
-    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device=DEV)
     oi = poisoned((B, T, k), torch.int32)
     os_ = poisoned((B, T, k), torch.float32)
     native.csa_index_topk(iq, iqs, head_w, ik, iks, n_valid, B, T, N_cap, H_I, D_I, k, oi, os_, ws)
@@ -202,3 +202,70 @@ def test_index_topk_query_blocks_many_rows_single_chunk():
         r, _ = run_index(iq[:, t0:t0 + 256], iqs[:, t0:t0 + 256], ik, iks, nv[:, t0:t0 + 256], k)
         bad += int((r[0] != oi[0, t0:t0 + 256]).any(dim=1).sum().item())
     assert bad == 0, f"{bad} rows differ from the decode kernels"
+
+
+def test_index_topk_workspace_reuse():
+    """Decode-path calls in a row on one workspace, which carries nothing from one call to the
+    next: different inputs and visible counts per call (one sequence seeing a single entry), every
+    call checked."""
+    say("index workspace reuse")
+    B, T, H_I, D_I, N, k = 8, 1, 8, 128, 40000, 128
+    ws = torch.empty(max(16, native.csa_index_topk_workspace_size(B, T, N, H_I, D_I, k)), dtype=torch.uint8,
+                     device=DEV)
+    for call, (seed, n_lo) in enumerate(((121, 30000), (122, 1), (123, 39000))):
+        iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), seed, DEV)
+        ik, iks = synth.mxfp4_normal((B, N, D_I), seed + 10, DEV)
+        nv = up(np.linspace(n_lo, N, B).astype(np.int32).reshape(B, T))
+        oi, os_ = poisoned((B, T, k), torch.int32), poisoned((B, T, k), torch.float32)
+        native.csa_index_topk(iq, iqs, None, ik, iks, nv, B, T, N, H_I, D_I, k, oi, os_, ws)
+        check_against_oracle(iq, iqs, ik, iks, nv, k, oi, os_, rows=[0])
+
+
+@pytest.mark.parametrize("B,T,k,N,ties", [
+    (3, 5, 128, 20000, False),   # query groups of 4 and 1 (three padding queries), several chunks
+    (2, 2, 256, 9000, True),     # groups of 2, massive score ties
+    (4, 3, 16, 3000, False),     # one padding query per group, chunks of a few hundred entries
+    (1, 6, 1, 70000, True),      # k = 1, ties, chunks of 280 entries
+])
+def test_index_topk_draft_queries(B, T, k, N, ties):
+    """Draft steps (T queries per sequence, each with its own visible count): one key stream per
+    group of queries (kernel M). Every row bit-exact against the oracle, scores included."""
+    say("index draft queries", B, T, k, N, ties)
+    rng = np.random.default_rng(7 * T + k)
+    H_I, D_I = 8, 128
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 171 + T, DEV)
+    if ties:
+        base, bsc = synth.mxfp4_normal((4, D_I), 172, DEV)
+        pick = torch.from_numpy(rng.integers(0, 4, (B, N))).to(DEV)
+        ik, iks = base[pick].contiguous(), bsc[pick].contiguous()
+    else:
+        ik, iks = synth.mxfp4_normal((B, N, D_I), 173 + T, DEV)
+    # causal visibility inside the draft: nondecreasing along t, one sequence short of k
+    nvh = np.sort(rng.integers(N // 2, N + 1, (B, T)), axis=1).astype(np.int32)
+    nvh[0] = np.minimum(nvh[0], np.arange(T) * max(1, k // 3))
+    hw = up(rng.choice(np.array([1.0, -1.0, 0.5, 2.0], np.float32), (B, T, H_I))) if ties else None
+    oi, os_ = run_index(iq, iqs, ik, iks, up(nvh), k, hw)
+    check_against_oracle(iq, iqs, ik, iks, up(nvh), k, oi, os_, head_w=hw)
+
+
+def test_index_topk_draft_queries_1m_shape():
+    """Four draft queries per sequence at the 1M-context decode shape (8 x 262144 entries): every
+    row equal to the single-query path's (one call per draft position), two rows against the
+    oracle."""
+    say("index draft 1m")
+    B, T, H_I, D_I, N, k = 8, 4, 8, 128, 262144, 128
+    iq, iqs = synth.mxfp4_normal((B, T, H_I, D_I), 181, DEV)
+    ik, iks = synth.mxfp4_normal((B, N, D_I), 182, DEV)
+    nvh = (N - 64 + np.arange(T)[None, :] * 16 + np.zeros((B, 1), np.int64)).astype(np.int32)
+    nv = up(nvh)
+    oi, os_ = run_index(iq, iqs, ik, iks, nv, k)
+    for t in range(T):
+        oi1, os1 = run_index(iq[:, t:t + 1].contiguous(), iqs[:, t:t + 1].contiguous(), ik, iks,
+                             nv[:, t:t + 1].contiguous(), k)
+        assert torch.equal(oi[:, t], oi1[:, 0]), f"draft position {t}: indices differ from the single-query path"
+        assert torch.equal(os_[:, t].view(torch.int32), os1[:, 0].view(torch.int32)), f"draft position {t}: scores differ"
+    torch.cuda.synchronize()
+    iqh, iqsh, ikh, iksh, oih = down(iq), down(iqs), down(ik), down(iks), down(oi)
+    for b, t in ((0, 0), (7, 3)):
+        sc = oidx.scores(iqh[b, t][None], iqsh[b, t][None], ikh[b], iksh[b], nvh[b, t][None])
+        parity.topk_exact(oih[b, t], otopk.topk(sc, k)[0][0], f"draft 1m b={b} t={t}")
