@@ -9,30 +9,34 @@
 // 100만 토큰 컨텍스트를 저비용에 구현한 방법", section "쉽게 이해하기": the window
 // holds the latest 128 tokens. Entries and window tokens share one softmax.
 //
-// Design. A workgroup of four waves takes one query, a block of 64 heads and one
+// Design. A workgroup of eight waves takes one query, a block of 64 heads and one
 // contiguous split of the query's key set (compressed entries, then window
-// tokens); one workgroup runs per CU. Keys are staged through LDS 64 at a time
-// as bf16 rows: fp8 and MXFP4 entries are widened exactly as they are stored
-// (once per key, not once per head group), window tokens are rotated at their
-// own position. The next tile's rows travel in registers while the current one
-// is computed. Every product is a v_mfma_f32_32x32x16_bf16 with the keys or the
+// tokens); one workgroup runs per CU. Keys go through LDS 64 at a time: fp8
+// entries as their raw codes in a three-tile ring filled by direct global-to-LDS
+// loads two tiles ahead, bf16 and MXFP4 entries and window tokens as bf16 rows
+// staged through registers (MXFP4 widened exactly, window tokens rotated at their
+// own position). Every product is a v_mfma_f32_32x32x16_bf16 with the keys or the
 // value dims as rows and 32 heads as columns, so each K and V element read from
 // LDS serves 32 heads and each lane owns one head:
-//   S^T = K Q^T: wave (h, k) takes heads [32h, 32h+32) and keys [32k, 32k+32);
-//     the query's dims stay in registers for the whole split (B operand);
-//   softmax in the log2 domain per head, the two key halves meeting in LDS;
+//   S^T = K Q^T: wave (hh, kh, dq) takes heads [32hh, 32hh+32), keys
+//     [32kh, 32kh+32) and one half of the dims (the halves balance the MFMA
+//     count); the query's dims stay in registers for the whole split (B operand);
+//   softmax in the log2 domain per head: the two dim halves of a block hand each
+//     other half of their partial logits through LDS, the key halves meet in LDS;
 //     P^T goes to LDS as [head][key];
-//   O^T += V^T P^T: wave (h, v) takes heads [32h, 32h+32) and value dims
-//     [v d_v/2, (v+1) d_v/2); V^T is read with the transposed LDS read
-//     ds_read_b64_tr_b16.
+//   O^T += V^T P^T: wave (hh, vq) takes heads [32hh, 32hh+32) and a quarter of
+//     the value dims; V^T is read with the transposed LDS reads ds_read_b64_tr_b8
+//     (fp8 codes, widened in registers) or ds_read_b64_tr_b16 (bf16 rows).
 // The rotated dims of the query and of window keys carry 16 significant bits:
 // they are split into a bf16 value and a bf16 remainder and both go through the
 // MFMA (for entry keys, stored exactly, the query remainder only), so the
 // rotation adds no bf16 rounding to the logits.
-// A query's splits write unnormalised partial outputs with their (max, sum) in
-// fp32 and a second launch merges them (log-sum-exp merge; merging in the last
-// split to finish needs an agent-scope release per workgroup, an L2 write-back
-// that costs more than the launch). One split writes the output directly.
+// A query's splits write their normalised partial outputs O / l in fp16 with
+// (max, sum) in fp32, and a second launch merges them (log-sum-exp merge; merging
+// in the last split to finish needs a device-scope release per workgroup, an L2
+// write-back that costs about what the launch does). One split writes the output
+// directly. Short key sets of few queries go to the 16-head kernel instead
+// (attention_g16.hip).
 #include <math.h>
 
 #include <mutex>
@@ -138,7 +142,7 @@ __device__ __forceinline__ KeySpace key_space(const AttnArgs& a, int qi) {
   return ks;
 }
 
-// cos / sin of the RoPE angle pos * inv_freq, with rev = inv_freq / (2 pi) (host fp64): the angle
+// cos / sin of the RoPE angle pos * inv_freq, with rev = inv_freq / (2 pi) (fp64): the angle
 // in revolutions is formed and reduced to [-1/2, 1/2] in fp64 (positions reach 2^20), then
 // evaluated with the hardware sine and cosine, which take revolutions (error of order 2^-22).
 __device__ __forceinline__ void rope_cs(double rev, int64_t pos, float* c, float* s) {
