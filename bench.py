@@ -56,6 +56,9 @@ def parse():
                          "every draft token accepted, value counts positions)")
     ap.add_argument("--kv", choices=["fp8", "mxfp4"], default="fp8",
                     help="storage of the compressed entries (mxfp4: OCP MX e2m1 codes + E8M0 per 32 dims)")
+    ap.add_argument("--qk-fp4", action="store_true",
+                    help="with --kv mxfp4: entry logits on the scaled FP4 x FP8 MFMA from the stored codes "
+                         "(CSKV_QK_FP4) instead of widening the entries to bf16")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -145,8 +148,10 @@ def main():
         return
 
     K, W, P = args.steps, args.warmup, args.pairs
+    if args.qk_fp4 and args.kv != "mxfp4":
+        sys.exit("--qk-fp4 needs --kv mxfp4")
     spec_kw = dict(steps=K, derive_keys=args.derive_keys, rms_eps=1e-6 if args.rms_norm else 0.0, draft=args.draft,
-                   kv_dtype=args.kv)
+                   kv_dtype=args.kv, qk_fp4=args.qk_fp4)
     if args.attn_only:
         pr = hybrid.LayerPair(hybrid.LayerPairSpec(seed=0, **spec_kw), dev)
         s_, name = pr.s, args.attn_only
@@ -290,7 +295,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{'mxfp4' if args.kv == 'mxfp4' else 'fp8-e4m3'} KV / mxfp4 indexer / bf16 MFMA, fp32 accumulate",
+        "dtype": f"{'mxfp4' if args.kv == 'mxfp4' else 'fp8-e4m3'} KV / mxfp4 indexer / "
+                 f"{'fp4xfp8 MFMA for entry logits, ' if args.qk_fp4 else ''}bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) draws; no checkpoints)",
         "config": {
             "workload": "c5_hybrid_1m: CSA(m=4,k=128,FP4 indexer 8x128)+HCA(m=128) layer pair, decode batch 8, "

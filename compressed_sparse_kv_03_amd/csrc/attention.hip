@@ -51,6 +51,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNT = 512;             // threads per workgroup (8 waves)
 constexpr int kHB = 64;              // heads per workgroup
@@ -234,6 +235,8 @@ struct AttnSmem {
     struct {
       __align__(16) uint16_t k[kTK][D + 8];
       __align__(16) uint16_t klo[kTK][64 + 8];
+      __align__(16) uint8_t k4[D / 32][kTK][16];  // MXFP4 entries: e2m1 codes, 32-dim block major
+      uint8_t s4[kTK][D / 32];                    // and their E8M0 block exponents
     } b;
   } t;
   __align__(16) uint16_t p[kHB][kTK + 8];
@@ -379,8 +382,11 @@ __device__ __forceinline__ void entry_load(const uint8_t* cbase, const uint8_t* 
   }
 }
 
-template <int D, int KV>
-__device__ __forceinline__ void entry_store(AttnSmem<D>& sm, const TileRegs<D, KV>& R) {
+// F4: MXFP4 entries whose keys go through the scaled FP4 MFMA: the codes and block exponents are
+// stored as they are (a masked row as code 0, exponent 1.0) and only the value dims (d_v) are
+// widened to bf16 rows.
+template <int D, int KV, bool F4 = false>
+__device__ __forceinline__ void entry_store(AttnSmem<D>& sm, const TileRegs<D, KV>& R, int d_v = D) {
   using EG = EntryGeom<D, KV>;
   const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
   const bool ok = R.row >= 0;
@@ -388,6 +394,11 @@ __device__ __forceinline__ void entry_store(AttnSmem<D>& sm, const TileRegs<D, K
   for (int i = 0; i < EG::NC; ++i) {
     const int ch = c0 + kTPR * i;
     if (EG::CPR % kTPR != 0 && ch >= EG::CPR) continue;
+    if constexpr (F4) {
+      *reinterpret_cast<uint4*>(&sm.t.b.k4[ch][r][0]) = keep_if(ok, R.v[i]);
+      sm.t.b.s4[r][ch] = ok ? (uint8_t)R.bs[i] : (uint8_t)127;
+      if (32 * ch >= d_v) continue;
+    }
     if constexpr (KV == kKvBf16) {
       *reinterpret_cast<uint4*>(&sm.t.b.k[r][8 * ch]) = keep_if(ok, R.v[i]);
     } else {
@@ -553,6 +564,218 @@ __device__ __forceinline__ f32x16 tile_qk(const AttnSmem<D>& sm, int stage, cons
   return acc;
 }
 
+// ---------------------------------------------------------------- S^T = K Q^T on the scaled FP4 MFMA
+// MXFP4 entries (D a multiple of 64): v_mfma_scale_f32_32x32x64_f8f6f4 takes the stored e2m1 codes
+// and E8M0 block exponents as they are. A operand: lane (key, g) holds the 32 dims of block 2s + g
+// of its key (one 16-byte chunk of the row) with that block's exponent. B operand: lane (head, g)
+// holds the query's dims 64s + 16g .. +15 in bytes 0-15 and 64s + 32 + 16g .. +15 in bytes 16-31
+// as e4m3 codes, with one exponent per head and 64-dim step (the layout was checked on the GPU
+// against a host product). The query enters as a sum of e4m3 parts, each scaled by 2^-4 of the
+// previous one: two parts hold a bf16 value exactly (4 + 4 significant bits) unless it is below
+// 2^-14 of its step's maximum; the last step (the rotated dims, d_rope <= 64, rotated in fp32)
+// takes four parts, 16 significant bits, as many as the bf16 value plus remainder of the other
+// path. Steps are split between the two dim halves so both issue the same number of MFMAs.
+template <int D, int DQ>
+struct F4Range {
+  static constexpr int NK = D / 64;
+  static constexpr int parts(int s) { return s == NK - 1 ? 4 : 2; }
+  static constexpr int cut() {
+    int total = 0, acc = 0;
+    for (int s = 0; s < NK; ++s) total += parts(s);
+    for (int s = 0; s < NK; ++s) {
+      acc += parts(s);
+      if (2 * acc >= total) return s + 1;
+    }
+    return NK;
+  }
+  static constexpr int S0 = DQ ? cut() : 0, S1 = DQ ? NK : cut();
+  static constexpr int NKW = S1 > S0 ? S1 - S0 : 1;  // this wave's steps (1 when none, unused)
+  static constexpr int count() {
+    int n = 0;
+    for (int s = S0; s < S1; ++s) n += parts(s);
+    return n > 0 ? n : 1;
+  }
+  static constexpr int NP = count();  // this wave's query parts
+};
+
+// The query's dims of this wave's steps in the B layout above: 4 chunks of 8 bf16 per step.
+template <int D, int DQ>
+__device__ __forceinline__ void load_query_f4(const AttnArgs& a, int qi, int hq, uint4* qr) {
+  using FR = F4Range<D, DQ>;
+  const int g = (threadIdx.x & (kWave - 1)) >> 5;
+  const uint16_t* src = a.q + ((int64_t)qi * a.H + min(hq, a.H - 1)) * D;
+#pragma unroll
+  for (int s = FR::S0; s < FR::S1; ++s) {
+    const int j = 4 * (s - FR::S0);
+    qr[j + 0] = *reinterpret_cast<const uint4*>(src + 64 * s + 16 * g);
+    qr[j + 1] = *reinterpret_cast<const uint4*>(src + 64 * s + 16 * g + 8);
+    qr[j + 2] = *reinterpret_cast<const uint4*>(src + 64 * s + 32 + 16 * g);
+    qr[j + 3] = *reinterpret_cast<const uint4*>(src + 64 * s + 32 + 16 * g + 8);
+  }
+}
+
+// Eight consecutive dims (RoPE pairs pair0 .. pair0 + 3) rotated to position pos, in fp32.
+__device__ __forceinline__ void rope8_f32(float* f, int64_t pos, const double* rev, int pair0) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float cs, sn;
+    rope_cs(rev[pair0 + p], pos, &cs, &sn);
+    const float u0 = f[2 * p], u1 = f[2 * p + 1];
+    f[2 * p] = u0 * cs - u1 * sn;
+    f[2 * p + 1] = u0 * sn + u1 * cs;
+  }
+}
+
+// LDS exchange of the query parts between the two waves of a (head half, dim half) pair, in the
+// tile region (free until the first tile is staged).
+template <int D>
+struct F4Xchg {
+  static constexpr int NPMAX = F4Range<D, 0>::NP > F4Range<D, 1>::NP ? F4Range<D, 0>::NP : F4Range<D, 1>::NP;
+  int part[2][2][NPMAX][kWave][8];  // [dq][hh][part][lane]
+  int exp[2][2][D / 64][kWave];     // [dq][hh][step][lane]
+  float ss[2][2][2][32];            // [dq][hh][kh][head]: sums of squares of each wave's steps
+};
+
+// The query as e4m3 parts (qf, B operands in step order) with one exponent per step (qe: part p
+// of step s is scaled by 2^(qe - 4p)). The two waves of a (head half, dim half) pair share the
+// work: wave kh converts the steps j = s - S0 with j % 2 == kh and the two swap results through
+// LDS (one barrier). Two-part steps (raw bf16 dims) split each value by truncation: the top 4
+// significant bits and the exact remainder; the last step's rotated dims (fp32) take four parts,
+// each the rounding of the previous remainder. Every rotated or normal-range value is held
+// exactly (to 16 significant bits when rotated); a raw value below 2^-13 of its step's maximum
+// may round in the e4m3 subnormal range, an error under 2^-17 of that maximum. Writes the query's
+// sums of squares per dim half (RMSNorm) to qss. Where the exchange does not fit the tile region
+// (small D), each wave converts all of its steps.
+template <int D, int DQ>
+__device__ __forceinline__ void quantize_query_f4(const AttnArgs& a, AttnSmem<D>& sm, int64_t t, const uint4* qr,
+                                                  int hh, int kh, i32x8* qf, int* qe) {
+  using FR = F4Range<D, DQ>;
+  constexpr bool SHARE = sizeof(F4Xchg<D>) <= sizeof(sm.t);
+  F4Xchg<D>& X = *reinterpret_cast<F4Xchg<D>*>(&sm.t);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 5;
+  const int rope0 = D - a.d_rope;
+  const bool rms = a.q_rms_eps > 0.f;
+  float ss = 0.f;
+  int pb = 0;  // first part of step s
+#pragma unroll
+  for (int s = FR::S0; s < FR::S1; ++s) {
+    const int j = s - FR::S0;
+    if (!SHARE || (j & 1) == kh) {
+      float x[32];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) unpack8(qr[4 * j + c], x + 8 * c);
+      if (rms) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ss += x[e] * x[e];
+      }
+      if (s == FR::NK - 1) {  // the rotated dims (d_rope <= 64) all lie in the last step
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = 64 * s + (c < 2 ? 16 * g + 8 * c : 32 + 16 * g + 8 * (c - 2));
+          if (d0 >= rope0) rope8_f32(x + 8 * c, t, sm.rev, (d0 - rope0) >> 1);
+        }
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));  // the head's 64 dims of the step
+      const int E = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;  // amax * 2^-E in [128, 256)
+      qe[j] = E;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = __builtin_amdgcn_ldexpf(x[e], -E);
+      if (FR::parts(s) == 2) {
+        i32x8 hi, lo;
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) {
+          float h[4], l[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = __uint_as_float(__float_as_uint(x[4 * wd + e]) & 0xFFF00000u);  // 4 significant bits
+            l[e] = (x[4 * wd + e] - h[e]) * 16.f;                                  // the exact rest
+          }
+          int wh = __builtin_amdgcn_cvt_pk_fp8_f32(h[0], h[1], 0, false);
+          hi[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(h[2], h[3], wh, true);
+          int wl = __builtin_amdgcn_cvt_pk_fp8_f32(l[0], l[1], 0, false);
+          lo[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(l[2], l[3], wl, true);
+        }
+        qf[pb] = hi;
+        qf[pb + 1] = lo;
+      } else {
+#pragma unroll
+        for (int p = 0; p < FR::parts(s); ++p) {
+          i32x8 v;
+#pragma unroll
+          for (int wd = 0; wd < 8; ++wd) {
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * wd], x[4 * wd + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * wd + 2], x[4 * wd + 3], word, true);
+            v[wd] = word;
+            if (p + 1 < FR::parts(s)) {  // the remainder (exact: within 2^-4 of the value), scaled up
+              const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+              const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+              x[4 * wd] = (x[4 * wd] - lo2[0]) * 16.f;
+              x[4 * wd + 1] = (x[4 * wd + 1] - lo2[1]) * 16.f;
+              x[4 * wd + 2] = (x[4 * wd + 2] - hi2[0]) * 16.f;
+              x[4 * wd + 3] = (x[4 * wd + 3] - hi2[1]) * 16.f;
+            }
+          }
+          qf[pb + p] = v;
+        }
+      }
+      if constexpr (SHARE) {
+#pragma unroll
+        for (int p = 0; p < FR::parts(s); ++p)
+#pragma unroll
+          for (int wd = 0; wd < 8; ++wd) X.part[DQ][hh][pb + p][lane][wd] = qf[pb + p][wd];
+        X.exp[DQ][hh][s][lane] = E;
+      }
+    }
+    pb += FR::parts(s);
+  }
+  ss += __shfl_xor(ss, 32, kWave);
+  if constexpr (!SHARE) {
+    if (kh == 0 && lane < 32) sm.qss[DQ][32 * hh + lane] = ss;
+    return;
+  }
+  if (lane < 32) X.ss[DQ][hh][kh][lane] = ss;
+  __syncthreads();
+  pb = 0;
+#pragma unroll
+  for (int s = FR::S0; s < FR::S1; ++s) {
+    const int j = s - FR::S0;
+    if ((j & 1) != kh) {
+#pragma unroll
+      for (int p = 0; p < FR::parts(s); ++p)
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) qf[pb + p][wd] = X.part[DQ][hh][pb + p][lane][wd];
+      qe[j] = X.exp[DQ][hh][s][lane];
+    }
+    pb += FR::parts(s);
+  }
+  if (kh == 0 && lane < 32) sm.qss[DQ][32 * hh + lane] = X.ss[DQ][hh][0][lane] + X.ss[DQ][hh][1][lane];
+}
+
+// Partial S^T over this wave's steps for keys [32 kh, 32 kh + 32) of the staged MXFP4 tile.
+template <int D, int DQ>
+__device__ __forceinline__ f32x16 tile_qk_f4(const AttnSmem<D>& sm, const i32x8* qf, const int* qe, int kh) {
+  using FR = F4Range<D, DQ>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int key = 32 * kh + (lane & 31), g = lane >> 5;
+  f32x16 acc = {};
+  int pi = 0;
+#pragma unroll
+  for (int s = FR::S0; s < FR::S1; ++s) {
+    const uint4 kc = *reinterpret_cast<const uint4*>(&sm.t.b.k4[2 * s + g][key][0]);
+    const int ka = sm.t.b.s4[key][2 * s + g];
+    const i32x8 av = {(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < FR::parts(s); ++p)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[pi++], acc, 4, 0, 0, ka, 0,
+                                                            qe[s - FR::S0] - 4 * p + 127);
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------- softmax
 // Per-lane online-softmax state of the lane's head. m is the exponent base of the running sums;
 // it may lag the true running maximum by up to kRescaleSlack (p <= 2^8), so O is rescaled only
@@ -688,9 +911,12 @@ __device__ __forceinline__ void tile_pv(const AttnSmem<D>& sm, HeadState<NO>& st
 
 // ---------------------------------------------------------------- the kernel
 // The work of one wave: DQ is the wave's half of the QK dims (a template parameter, so that only
-// that half's query registers exist).
-template <int D, int DV, int KV, int DQ>
+// that half's query registers exist). F4 (MXFP4 entries, D a multiple of 64): the entry keys go
+// through the scaled FP4 MFMA with the query as e4m3 parts; the bf16 query (window keys) is then
+// loaded after the entries, so the two register sets are never live together.
+template <int D, int DV, int KV, int DQ, bool F4>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
+  static_assert(!F4 || (KV == kKvMxfp4 && D % 64 == 0), "FP4 QK needs MXFP4 entries and D % 64 == 0");
   using R = QkRange<D, DQ>;
   constexpr int NB = DV / 32, NO = (NB + 3) / 4;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
@@ -704,11 +930,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   const int hq = (qh % a.n_hb) * kHB + hl;  // this lane's head
 
   constexpr bool F8 = KV == kKvFp8;
+  using FR = F4Range<D, DQ>;
   const bool dense = a.topk == nullptr;
   // the query's dims of this lane's head and wave's steps, then the query's position and entry
   // count (their latency overlaps the listing of the split's rows)
   uint4 q[R::NQ], qlo[R::NLOA];
-  load_query<D, DQ>(a, qi, hq, q);
+  uint4 qr[F4 ? 4 * FR::NKW : 1];
+  if constexpr (F4)
+    load_query_f4<D, DQ>(a, qi, hq, qr);
+  else
+    load_query<D, DQ>(a, qi, hq, q);
   const KeySpace ks = key_space(a, qi);
 
   int key_begin, key_end;
@@ -774,10 +1005,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   __builtin_amdgcn_s_waitcnt(0);
   if (F8 && !dense && n_et > 0)
     issue_tile_f8<D>(sm, 0, cbase, reinterpret_cast<const float*>(sbase), key_begin, e_end, key_begin, false);
-  float ss = query_sumsq<D, DQ>(a, q);
-  ss += __shfl_xor(ss, 32, kWave);
-  if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
-  rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
+  i32x8 qf[F4 ? FR::NP : 1];
+  int qe[F4 ? FR::NKW : 1];
+  if constexpr (F4) {
+    quantize_query_f4<D, DQ>(a, sm, ks.t, qr, hh, kh, qf, qe);  // qss too; one barrier
+  } else {
+    float ss = query_sumsq<D, DQ>(a, q);
+    rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
+    ss += __shfl_xor(ss, 32, kWave);
+    if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
+  }
   if (F8 && n_et > 1)
     issue_tile_f8<D>(sm, 1, cbase, reinterpret_cast<const float*>(sbase), key_begin + kTK, e_end, key_begin, dense);
 
@@ -801,11 +1038,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
       TileRegs<D, KV> RT;
       entry_load<D, KV>(cbase, sbase, key0, e_end, key_begin, sm, RT);
       __syncthreads();  // the previous tile's reads are done
-      entry_store<D, KV>(sm, RT);
+      entry_store<D, KV, F4>(sm, RT, DV);
       __syncthreads();
     }
     const uint64_t valid = tile_mask<D>(sm, key0, e_end, key_begin);
-    const f32x16 s = tile_qk<D, F8, false, DQ>(sm, stage, q, qlo, kh);
+    f32x16 s;
+    if constexpr (F4)
+      s = tile_qk_f4<D, DQ>(sm, qf, qe, kh);
+    else
+      s = tile_qk<D, F8, false, DQ>(sm, stage, q, qlo, kh);
     tile_softmax<D, NO>(a, sm, st, s, w, valid, vsc);
     if (F8 && t + 2 < n_et)  // ring stage (t + 2) % 3 was last read by tile t - 1, finished by all
       issue_tile_f8<D>(sm, (t + 2) % kStages, cbase, reinterpret_cast<const float*>(sbase), key0 + 2 * kTK, e_end,
@@ -813,6 +1054,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
     tile_pv<D, NO, NB, F8>(sm, st, hh, vq, stage, valid);
   }
   // phase 2: window tokens (the bf16 tile overlays the ring: staged after the last entry tile's reads)
+  if constexpr (F4) {
+    if (w_begin < key_end) {  // the bf16 query for the window keys
+      load_query<D, DQ>(a, qi, hq, q);
+      rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
+    }
+  }
   for (int key0 = w_begin; key0 < key_end; key0 += kTK) {
     WinRegs<D> RW;
     window_load<D>(a, key0, key_end, key_begin, sm, RW);
@@ -878,13 +1125,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   }
 }
 
-template <int D, int DV, int KV>
+template <int D, int DV, int KV, bool F4>
 __global__ __launch_bounds__(kNT, 1) void attn_kernel(AttnArgs a) {
   __shared__ AttnSmem<D> sm;
   if (wave_id() >> 2)
-    attn_body<D, DV, KV, 1>(a, sm);
+    attn_body<D, DV, KV, 1, F4>(a, sm);
   else
-    attn_body<D, DV, KV, 0>(a, sm);
+    attn_body<D, DV, KV, 0, F4>(a, sm);
 }
 
 // One workgroup per (query, head): log-sum-exp merge of the split partials, split s weighted by
@@ -1020,19 +1267,19 @@ static AttnPlan plan_attn(int nq, int H, int d_v, int max_entries, int W) {
 
 typedef void (*AttnKernel)(AttnArgs);
 
-template <int KV>
+template <int KV, bool F4 = false>
 static AttnKernel pick_dims(int D, int d_v) {
-  if (D == 576 && d_v == 512) return attn_kernel<576, 512, KV>;
-  if (D == 128 && d_v == 128) return attn_kernel<128, 128, KV>;
-  if (D == 64 && d_v == 32) return attn_kernel<64, 32, KV>;
-  if (D == 256 && d_v == 128) return attn_kernel<256, 128, KV>;
+  if (D == 576 && d_v == 512) return attn_kernel<576, 512, KV, F4>;
+  if (D == 128 && d_v == 128) return attn_kernel<128, 128, KV, F4>;
+  if (D == 64 && d_v == 32) return attn_kernel<64, 32, KV, F4>;
+  if (D == 256 && d_v == 128) return attn_kernel<256, 128, KV, F4>;
   return nullptr;
 }
 
-// Compiled (D, d_v) pairs.
-static AttnKernel pick_kernel(int D, int d_v, int kv) {
-  return kv == kKvFp8 ? pick_dims<kKvFp8>(D, d_v)
-                      : (kv == kKvMxfp4 ? pick_dims<kKvMxfp4>(D, d_v) : pick_dims<kKvBf16>(D, d_v));
+// Compiled (D, d_v) pairs (every D a multiple of 64, so each has the FP4-QK variant).
+static AttnKernel pick_kernel(int D, int d_v, int kv, bool qk_fp4 = false) {
+  if (kv == kKvMxfp4) return qk_fp4 ? pick_dims<kKvMxfp4, true>(D, d_v) : pick_dims<kKvMxfp4>(D, d_v);
+  return kv == kKvFp8 ? pick_dims<kKvFp8>(D, d_v) : pick_dims<kKvBf16>(D, d_v);
 }
 
 static int check_common(const char* name, int H, int D, int d_rope, int d_v, int W, int ckv_dtype, float q_rms_eps) {
@@ -1043,14 +1290,18 @@ static int check_common(const char* name, int H, int D, int d_rope, int d_v, int
   CSKV_REQUIRE(W >= 0, CSKV_EINVAL, "%s: W=%d", name, W);
   CSKV_REQUIRE(q_rms_eps >= 0.f && q_rms_eps < INFINITY, CSKV_EINVAL, "%s: q_rms_eps=%g", name, (double)q_rms_eps);
   CSKV_REQUIRE(d_rope <= 2 * kMaxRopePairs, CSKV_ENOTSUP, "%s: d_rope=%d > %d", name, d_rope, 2 * kMaxRopePairs);
-  CSKV_REQUIRE(ckv_dtype == CSKV_BF16 || ckv_dtype == CSKV_FP8_E4M3 || ckv_dtype == CSKV_MXFP4, CSKV_EINVAL,
-               "%s: ckv_dtype=%d", name, ckv_dtype);
+  const int kv = ckv_dtype & ~CSKV_QK_FP4;
+  CSKV_REQUIRE(kv == CSKV_BF16 || kv == CSKV_FP8_E4M3 || kv == CSKV_MXFP4, CSKV_EINVAL, "%s: ckv_dtype=%d", name,
+               ckv_dtype);
+  CSKV_REQUIRE(!(ckv_dtype & CSKV_QK_FP4) || (kv == CSKV_MXFP4 && D % 64 == 0), CSKV_EINVAL,
+               "%s: CSKV_QK_FP4 needs CSKV_MXFP4 entries and D %% 64 == 0 (D=%d)", name, D);
   CSKV_REQUIRE(pick_kernel(D, d_v, kKvBf16) != nullptr, CSKV_ENOTSUP,
                "%s: (D, d_v) = (%d, %d) not compiled (576/512, 128/128, 256/128, 64/32)", name, D, d_v);
   return CSKV_OK;
 }
 
-static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws, size_t ws_bytes, hipStream_t s) {
+static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, bool qk_fp4, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
   CSKV_REQUIRE(p.ws == 0 || (ws && ws_bytes >= p.ws), CSKV_EWORKSPACE, "%s: workspace %zu < %zu bytes", name,
                ws_bytes, p.ws);
   a.n_hb = p.n_hb;
@@ -1068,7 +1319,7 @@ static int launch_attn(const char* name, AttnArgs a, const AttnPlan& p, void* ws
   }
   const int64_t total = (int64_t)a.nq * p.n_hb * p.n_splits;
   CSKV_REQUIRE(total < (1ll << 31), CSKV_ENOTSUP, "%s: %lld workgroups", name, (long long)total);
-  AttnKernel kern = pick_kernel(a.D, a.d_v, a.kv_dtype);
+  AttnKernel kern = pick_kernel(a.D, a.d_v, a.kv_dtype, qk_fp4);
   hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(kNT), 0, s, a);
   CSKV_LAUNCH_CHECK(name);
   if (p.n_splits > 1) {
@@ -1148,7 +1399,7 @@ static int run_attn(const char* name, const AttnCall& c, bool noalloc, void* ws,
   a.q_rms_eps = c.q_rms_eps;
   a.out = c.out;
   a.out_lse = c.out_lse;
-  return launch_attn(name, a, p, ws, ws_bytes, s);
+  return launch_attn(name, a, p, c.qk_fp4, ws, ws_bytes, s);
 }
 
 // Checks the decode arguments and fills the call.
@@ -1167,7 +1418,8 @@ static int decode_setup(const char* name, const uint16_t* q, const int64_t* q_po
   CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
   CSKV_REQUIRE(q && q_pos && out && n_entries, CSKV_EINVAL, "%s: null pointer", name);
   CSKV_REQUIRE(W == 0 || win, CSKV_EINVAL, "%s: null window", name);
-  CSKV_REQUIRE(N_cap == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
+  const int kv = ckv_dtype & ~CSKV_QK_FP4;
+  CSKV_REQUIRE(N_cap == 0 || (ckv && (kv == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(win), CSKV_EINVAL, "%s: q/ckv/win must be 16-byte aligned",
                name);
   c = AttnCall{};
@@ -1176,7 +1428,8 @@ static int decode_setup(const char* name, const uint16_t* q, const int64_t* q_po
   c.pos0 = 0;
   c.ckv = ckv;
   c.ckv_scale = ckv_scale;
-  c.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.kv_dtype = kv == CSKV_FP8_E4M3 ? kKvFp8 : (kv == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.qk_fp4 = (ckv_dtype & CSKV_QK_FP4) != 0;
   c.N_cap = N_cap;
   c.ckv_seq = N_cap;
   c.n_entries = n_entries;
@@ -1294,7 +1547,8 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   if (T == 0) return CSKV_OK;
   CSKV_REQUIRE(!topk_idx || k >= 1, CSKV_EINVAL, "%s: k=%d", name, k);
   CSKV_REQUIRE(q && out && (W == 0 || x), CSKV_EINVAL, "%s: null pointer", name);
-  CSKV_REQUIRE(N == 0 || (ckv && (ckv_dtype == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
+  const int kv = ckv_dtype & ~CSKV_QK_FP4;
+  CSKV_REQUIRE(N == 0 || (ckv && (kv == CSKV_BF16 || ckv_scale)), CSKV_EINVAL, "%s: null cache", name);
   CSKV_REQUIRE(aligned16(q) && aligned16(ckv) && aligned16(x), CSKV_EINVAL, "%s: q/ckv/x must be 16-byte aligned",
                name);
   AttnCall c{};
@@ -1303,7 +1557,8 @@ extern "C" CSKV_API int hybrid_attn_prefill(const uint16_t* q, int64_t pos0, int
   c.pos0 = pos0;
   c.ckv = ckv;
   c.ckv_scale = ckv_scale;
-  c.kv_dtype = ckv_dtype == CSKV_FP8_E4M3 ? kKvFp8 : (ckv_dtype == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.kv_dtype = kv == CSKV_FP8_E4M3 ? kKvFp8 : (kv == CSKV_MXFP4 ? kKvMxfp4 : kKvBf16);
+  c.qk_fp4 = (ckv_dtype & CSKV_QK_FP4) != 0;
   c.N_cap = N;
   c.ckv_seq = 0;
   c.n_entries = nullptr;

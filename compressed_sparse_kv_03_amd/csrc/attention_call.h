@@ -17,6 +17,7 @@ struct AttnCall {
   const void* ckv;           // [B_kv, N_cap, D] bf16 bits, fp8 codes, or MXFP4 codes [.., D/2]
   const void* ckv_scale;     // fp32 [B_kv, N_cap] (fp8) or E8M0 bytes [B_kv, N_cap, D/32] (MXFP4)
   int kv_dtype;              // kKvBf16, kKvFp8 or kKvMxfp4
+  bool qk_fp4;               // MXFP4: QK^T on the scaled FP4 MFMA (64-head kernel; the 16-head one widens)
   int N_cap;
   int64_t ckv_seq;           // entries between sequences (0: all queries share one cache)
   const int32_t* n_entries;  // [nq] (decode) or nullptr (prefill: min(N, (t+1)/m))

@@ -67,6 +67,8 @@ class LayerPairSpec:
     accept_seed: int = -1
     # storage of the compressed entries: "fp8" (e4m3fn + fp32 scale per entry) or "mxfp4"
     kv_dtype: str = "fp8"
+    # mxfp4 entries: attention logits on the scaled FP4 MFMA from the stored codes (CSKV_QK_FP4)
+    qk_fp4: bool = False
 
     @property
     def sigma(self):
@@ -86,7 +88,9 @@ class LayerPair:
         self.dev = device
         assert s.W % s.m_csa == 0 and s.W % s.m_hca == 0 and s.L % s.m_hca == 0 and s.L % s.m_csa == 0
         assert s.L >= s.W and s.draft >= 1 and s.kv_dtype in ("fp8", "mxfp4")
+        assert not s.qk_fp4 or s.kv_dtype == "mxfp4"
         self.kv_code = native.CSKV_MXFP4 if s.kv_dtype == "mxfp4" else native.CSKV_FP8_E4M3
+        self.attn_code = self.kv_code | (native.CSKV_QK_FP4 if s.qk_fp4 else 0)
         sd = lambda t: synth.seed_of(s.seed, s.wid, t)  # noqa: E731
         B, D, T, Td = s.B, s.D, s.steps, s.draft
         self.m = {"csa": s.m_csa, "hca": s.m_hca}
@@ -252,7 +256,7 @@ class LayerPair:
         for name in ("csa", "hca"):
             c = kv[name]
             native.hybrid_attn_decode(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
-                                      self.kv_code, self.cap[name], self.nent[name][i],
+                                      self.attn_code, self.cap[name], self.nent[name][i],
                                       topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
                                       self.ws_att[name], None, stream, q_rms_eps=s.rms_eps, T=Td, R=c.R[name])

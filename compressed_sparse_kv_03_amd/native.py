@@ -15,6 +15,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcskv.so
 CSKV_BF16 = 0
 CSKV_FP8_E4M3 = 1
 CSKV_MXFP4 = 2
+CSKV_QK_FP4 = 0x100   # OR-ed into CSKV_MXFP4 for the attention calls: QK^T on the scaled FP4 MFMA
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 

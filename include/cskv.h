@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSKV_ABI_VERSION 2
+#define CSKV_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define CSKV_API __attribute__((visibility("default")))
@@ -56,6 +56,16 @@ extern "C" {
 #define CSKV_BF16 0
 #define CSKV_FP8_E4M3 1
 #define CSKV_MXFP4 2   /* OCP MXFP4: e2m1 codes [.., D/2] (element 2i in the low nibble) + E8M0 [.., D/32] */
+/* Flag OR-ed into the ckv_dtype CSKV_MXFP4 of hybrid_attn_decode(_noalloc) and
+ * hybrid_attn_prefill (D % 64 == 0): the 64-head kernel takes the entry logits q . key on the
+ * scaled FP4 x FP8 MFMA straight from the stored e2m1 codes and E8M0 exponents, the rotated
+ * query held as a sum of e4m3 parts with one power-of-two scale per 64 dims (the mixed-precision
+ * matrix cores of CDNA4, for the FP4 main KV of the "SWA Bounded Replay" global attention state;
+ * without the flag the entries are widened exactly to bf16 first). Parts: two per raw dim (its
+ * top 4 significant bits, then the exact rest), four per rotated dim (16 significant bits); a
+ * raw dim below 2^-13 of its 64-dim block's largest magnitude may lose bits below 2^-17 of that
+ * magnitude. The 16-head kernel (short key sets) widens either way. */
+#define CSKV_QK_FP4 0x100
 
 CSKV_API int cskv_abi_version(void);
 CSKV_API const char* cskv_strerror(int code);

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
     assert set(names) == set(native.exported_symbols())
-    assert L.cskv_abi_version() == 2
+    assert L.cskv_abi_version() == 3
 
 
 @pytest.mark.parametrize("code,text", [(0, "ok"), (-1, "invalid argument"), (-2, "shape not supported"),
@@ -106,6 +106,9 @@ def test_attention_validation():
     assert dec(T=2) == -1                    # a 2-token draft needs R >= W + 1 (R = 0 means R = W)
     assert dec(T=3, R=129) == -1             # ... and a 3-token one R >= W + 2
     assert dec(eps=float("nan")) == -1
+    assert dec(dt=native.CSKV_FP8_E4M3 | native.CSKV_QK_FP4) == -1    # FP4 logits need MXFP4 entries
+    assert dec(dt=native.CSKV_MXFP4 | native.CSKV_QK_FP4, D=160, dv=128) == -1  # ... and D % 64 == 0
+    assert dec(dt=native.CSKV_MXFP4 | 0x200) == -1                     # an unknown flag
     assert L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) > 0
 
     def dec_na(**kw):     # the allocation-free variant: same arguments without ws / ws_bytes

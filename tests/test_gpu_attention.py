@@ -29,6 +29,17 @@ def kernel_path(request):
     native.cskv_attn_path(native.ATTN_AUTO)
 
 
+# Entry dtypes of the calls: "mxfp4q" stores MXFP4 entries like "mxfp4" and sets CSKV_QK_FP4 (the
+# 64-head kernel's entry logits on the scaled FP4 MFMA; the 16-head kernel widens either way).
+DT = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4,
+      "mxfp4q": native.CSKV_MXFP4 | native.CSKV_QK_FP4}
+
+
+def store(dtype):
+    """The storage format of an entry dtype (what the generator and the oracle take)."""
+    return "mxfp4" if dtype == "mxfp4q" else dtype
+
+
 def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, D, d_rope, d_v, scale, q_rms_eps=0.0):
     B = q.shape[0]
     N_cap = ckv.shape[1]
@@ -36,8 +47,7 @@ def run_decode(q, q_pos, ckv, ckv_scale, dtype, n_entries, topk, k, ring, W, H, 
     ws = torch.zeros(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((B, H, d_v), torch.int16)
     lse = poisoned((B, H), torch.float32)
-    dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
-    native.hybrid_attn_decode(q, q_pos, ckv, ckv_scale, dt, N_cap, n_entries, topk, k, ring, W, B, H, D, d_rope,
+    native.hybrid_attn_decode(q, q_pos, ckv, ckv_scale, DT[dtype], N_cap, n_entries, topk, k, ring, W, B, H, D, d_rope,
                               d_v, 10000.0, scale, out, lse, ws, q_rms_eps=q_rms_eps)
     return out, lse
 
@@ -83,6 +93,11 @@ CASES = [
     (3, 64, 576, 64, 512, 700, 128, 128, "mxfp4", False, None),    # MXFP4 entries (gather)
     (3, 64, 576, 64, 512, 300, 128, 128, "mxfp4", True, None),     # MXFP4 entries (dense)
     (2, 20, 128, 64, 128, 90, 16, 8, "mxfp4", True, 1.0),
+    (3, 64, 576, 64, 512, 700, 128, 128, "mxfp4q", False, None),   # MXFP4, logits on the FP4 MFMA
+    (3, 64, 576, 64, 512, 300, 128, 128, "mxfp4q", True, None),
+    (2, 20, 128, 64, 128, 90, 16, 8, "mxfp4q", True, 1.0),
+    (2, 4, 64, 16, 32, 50, 40, 0, "mxfp4q", False, 1.0),           # one 64-dim step, no window
+    (2, 48, 256, 0, 128, 333, 64, 128, "mxfp4q", True, 0.5),       # no RoPE
 ]
 
 
@@ -96,7 +111,7 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std, kernel_p
     if dtype == "bf16":
         ckv = synth.normal_bf16_bits((B, N, D), sig, 2, DEV)
         sc = None
-    elif dtype == "mxfp4":
+    elif store(dtype) == "mxfp4":
         ckv, sc = synth.mxfp4_rows_normal((B, N, D), sig, 2, DEV)
     else:
         ckv, sc = synth.fp8_rows_normal((B, N, D), sig, 2, DEV)
@@ -116,7 +131,7 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std, kernel_p
     out, lse = run_decode(q, up(tpos), ckv, sc, dtype, up(nent), topk, k, ring, W, H, D, d_rope, d_v, scale)
     o_ref, l_ref, bnd = oracle_decode(down(q).view(np.uint16), tpos,
                                       down(ckv).view(np.uint16) if dtype == "bf16" else down(ckv),
-                                      None if sc is None else down(sc), dtype, nent,
+                                      None if sc is None else down(sc), store(dtype), nent,
                                       None if topk is None else down(topk), down(ring).view(np.uint16), W, d_rope,
                                       d_v, scale)
     parity.attn_close(down(out), o_ref)
@@ -127,6 +142,7 @@ def test_decode_small(B, H, D, d_rope, d_v, N, k, W, dtype, dense, std, kernel_p
     (3, 64, 576, 64, 512, 300, 128, 128, "fp8", True, 1e-6),
     (2, 16, 128, 64, 128, 500, 64, 128, "bf16", False, 1e-6),
     (2, 20, 128, 64, 128, 90, 16, 8, "fp8", True, 4.0),          # eps comparable to the mean square
+    (3, 64, 576, 64, 512, 300, 128, 128, "mxfp4q", True, 1e-6),
 ])
 def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps, kernel_path):
     """Unit-gain RMSNorm of every query head folded into its logits (q_rms_eps > 0)."""
@@ -136,6 +152,8 @@ def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps,
     q = synth.normal_bf16_bits((B, H, D), 1.0, 41, DEV)
     if dtype == "bf16":
         ckv, sc = synth.normal_bf16_bits((B, N, D), 1.0, 42, DEV), None
+    elif store(dtype) == "mxfp4":
+        ckv, sc = synth.mxfp4_rows_normal((B, N, D), 1.0, 42, DEV)
     else:
         ckv, sc = synth.fp8_rows_normal((B, N, D), 1.0, 42, DEV)
     ring = synth.normal_bf16_bits((B, W, D), 1.0, 43, DEV)
@@ -152,7 +170,7 @@ def test_decode_query_rms_norm(B, H, D, d_rope, d_v, N, k, W, dtype, dense, eps,
                           q_rms_eps=eps)
     o_ref, l_ref, bnd = oracle_decode(down(q).view(np.uint16), tpos,
                                       down(ckv).view(np.uint16) if dtype == "bf16" else down(ckv),
-                                      None if sc is None else down(sc), dtype, nent,
+                                      None if sc is None else down(sc), store(dtype), nent,
                                       None if topk is None else down(topk), down(ring).view(np.uint16), W, d_rope,
                                       d_v, scale, q_rms_eps=eps)
     parity.attn_close(down(out), o_ref, "q-rms attention")
@@ -312,6 +330,8 @@ PREFILL = [
     (400, 0, 128, 20, 128, 64, 128, 0, 64, True, "fp8"),
     (130, 5, 4, 4, 64, 16, 32, 0, 8, True, "bf16"),
     (260, 37, 4, 64, 576, 64, 512, 16, 16, False, "mxfp4"),
+    (260, 37, 4, 64, 576, 64, 512, 16, 16, False, "mxfp4q"),
+    (400, 0, 128, 20, 128, 64, 128, 0, 64, True, "mxfp4q"),
 ]
 
 
@@ -326,7 +346,7 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype, kernel
     if dtype == "bf16":
         ckv = synth.normal_bf16_bits((N, D), sig, 43, DEV)
         sc = None
-    elif dtype == "mxfp4":
+    elif store(dtype) == "mxfp4":
         ckv, sc = synth.mxfp4_rows_normal((N, D), sig, 43, DEV)
     else:
         ckv, sc = synth.fp8_rows_normal((N, D), sig, 43, DEV)
@@ -343,12 +363,11 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype, kernel
     ws = torch.zeros(max(wsn, 16), dtype=torch.uint8, device=DEV)
     out = poisoned((T, H, d_v), torch.int16)
     lse = poisoned((T, H), torch.float32)
-    dt = {"bf16": native.CSKV_BF16, "fp8": native.CSKV_FP8_E4M3, "mxfp4": native.CSKV_MXFP4}[dtype]
-    native.hybrid_attn_prefill(q, pos0, T, ckv, sc, dt, N, topk, max(k, 1), x, W, H, D, d_rope, d_v, m, 10000.0,
+    native.hybrid_attn_prefill(q, pos0, T, ckv, sc, DT[dtype], N, topk, max(k, 1), x, W, H, D, d_rope, d_v, m, 10000.0,
                                D ** -0.5, out, lse, ws)
     qh, xh = down(q).view(np.uint16), down(x).view(np.uint16)
     ent = oatt.Entries(down(ckv).view(np.uint16) if dtype == "bf16" else down(ckv), None if sc is None else down(sc),
-                       dtype)
+                       store(dtype))
     rows = sorted(set(range(0, T, 7)) | {0, 1, 2, m - 1, m, T - 1})
     rows = [r for r in rows if r < T]
     outs, lses, bnds = [], [], []
@@ -364,3 +383,26 @@ def test_prefill_small(T, pos0, m, H, D, d_rope, d_v, k, W, dense, dtype, kernel
     oh, lh = down(out), down(lse)
     parity.attn_close(oh[rows], np.stack(outs))
     parity.lse_close(lh[rows], np.stack(lses), np.stack(bnds))
+
+
+@pytest.mark.parametrize("dtype", ["mxfp4", "mxfp4q"])
+def test_decode_mxfp4_hca_1m_shape(dtype):
+    """HCA decode over MXFP4 entries at the 1M-context layer shape (B=8, 8192 entries each, window
+    128, 64 heads, D=512+64), widened to bf16 (mxfp4) or with the entry logits on the scaled FP4
+    MFMA from the stored codes and block exponents, the query as e4m3 parts (mxfp4q). Every
+    sequence against the oracle."""
+    B, H, D, d_rope, d_v, W = 8, 64, 576, 64, 512, 128
+    n = (1 << 20) // 128
+    t = (1 << 20) - 1
+    sig = D ** -0.5
+    say("decode mxfp4 hca 1m", dtype)
+    q = synth.normal_bf16_bits((B, H, D), sig, 61, DEV)
+    ckv, sc = synth.mxfp4_rows_normal((B, n, D), sig, 62, DEV)
+    ring = synth.normal_bf16_bits((B, W, D), sig, 63, DEV)
+    nent = np.full(B, n, np.int32)
+    out, lse = run_decode(q, up(np.full(B, t, np.int64)), ckv, sc, dtype, up(nent), None, 0, ring, W, H, D, d_rope,
+                          d_v, D ** -0.5)
+    o_ref, l_ref, bnd = oracle_decode(down(q).view(np.uint16), np.full(B, t), down(ckv), down(sc), "mxfp4", nent,
+                                      None, down(ring).view(np.uint16), W, d_rope, d_v, D ** -0.5)
+    parity.attn_close(down(out), o_ref, "mxfp4 hca 1m")
+    parity.lse_close(down(lse), l_ref, bnd, "mxfp4 hca 1m lse")

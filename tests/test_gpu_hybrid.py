@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from compressed_sparse_kv_03_amd import hybrid
+from compressed_sparse_kv_03_amd import hybrid, native
 from oracle import attention as oatt
 from oracle import hybrid as ohyb
 from tests import parity
@@ -146,15 +146,23 @@ def test_hybrid_loop_rms_norm_every_step(eps):
     assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
 
 
-def test_hybrid_loop_mxfp4_entries_every_step():
+@pytest.mark.parametrize("qk_fp4", [False, True], ids=["widened", "qk_fp4"])
+def test_hybrid_loop_mxfp4_entries_every_step(qk_fp4):
     """MXFP4 compressed KV (OCP MX: e2m1 codes, per-32 E8M0 exponents) written by the loop and read
-    by both attention layers; every step against the oracle loop storing its own MXFP4 entries."""
+    by both attention layers; every step against the oracle loop storing its own MXFP4 entries.
+    qk_fp4: the entry logits on the scaled FP4 MFMA (CSKV_QK_FP4), on the 64-head kernel (forced:
+    these key sets are short enough for the 16-head kernel, which widens either way)."""
     spec = hybrid.LayerPairSpec(B=2, L=2048, steps=260, H=16, D=128, d_rope=64, d_v=128, k=32, H_I=4, D_I=64,
-                                wid=60, kv_dtype="mxfp4")
+                                wid=60, kv_dtype="mxfp4", qk_fp4=qk_fp4)
     say("hybrid mxfp4", spec)
-    pair = hybrid.LayerPair(spec)
-    pair.run(0, spec.steps)
-    torch.cuda.synchronize()
+    if qk_fp4:
+        native.cskv_attn_path(native.ATTN_G64)  # before the workspaces are sized
+    try:
+        pair = hybrid.LayerPair(spec)
+        pair.run(0, spec.steps)
+        torch.cuda.synchronize()
+    finally:
+        native.cskv_attn_path(native.ATTN_AUTO)
     assert check_loop(pair, set(range(spec.steps))) == 2 * spec.steps
 
 
