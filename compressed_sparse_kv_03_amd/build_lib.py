@@ -1,6 +1,11 @@
 """Build libcskv.so for gfx950 with hipcc (in-tree; run on a machine with or without a GPU).
 
-    python -m compressed_sparse_kv_03_amd.build_lib
+    python -m compressed_sparse_kv_03_amd.build_lib            # the library
+    python -m compressed_sparse_kv_03_amd.build_lib --sanitize # _build/asan/libcskv_asan.so
+
+The sanitized build instruments the host code only (argument checks, planning, launch setup)
+with AddressSanitizer and UndefinedBehaviorSanitizer; its device code is the ordinary build's.
+It is for CPU tests of the host paths, loaded into a process that preloads the ASan runtime.
 """
 import concurrent.futures as cf
 import os
@@ -26,9 +31,28 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libcskv_asan.so")
+# host-side sanitizers only: each -fsanitize= follows -Xarch_host
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+SAN_FLAGS = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer"] + SAN
+
+
+def asan_runtime():
+    """Path of clang's shared ASan runtime (which a process must preload to load ASAN_LIB), or None."""
+    d = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+    if not os.path.isdir(d):
+        return None
+    for ver in sorted(os.listdir(d), reverse=True):
+        p = os.path.join(d, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return None
+
+
+def _compile(src, flags=FLAGS, out_dir=BUILD):
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC] + flags + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops' is not a recognized feature" not in l)
@@ -37,24 +61,32 @@ def _compile(src):
     return obj, msgs
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
+def _build(lib, flags, out_dir, link_extra, verbose):
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda src: _compile(src, flags, out_dir), srcs))
     for obj, msgs in results:
         if msgs.strip() and verbose:
             print(msgs, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + link_extra + ["-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build(verbose=True):
+    return _build(LIB, FLAGS, BUILD, [], verbose)
+
+
+def build_sanitized(verbose=True):
+    return _build(ASAN_LIB, SAN_FLAGS, ASAN_DIR, ["-shared-libsan"] + SAN, verbose)
 
 
 if __name__ == "__main__":
-    build()
+    build_sanitized() if "--sanitize" in sys.argv[1:] else build()

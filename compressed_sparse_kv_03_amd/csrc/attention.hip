@@ -253,6 +253,9 @@ struct AttnSmem {
 // A wave-wide request of 16 (4) bytes per lane from gp into LDS at lds + 16 * lane (4 * lane),
 // the LDS address taken from M0. Nothing is written to registers; the data lands asynchronously
 // and is waited for with s_waitcnt vmcnt, whose count these requests advance in issue order.
+// m0 is named as clobbered; the compiler warns that, being reserved, it may not be preserved
+// around the statement. No compiler-generated code in these kernels uses m0 (it appears in the
+// generated assembly only in these statements), so nothing of the compiler's is live in it.
 __device__ __forceinline__ void dma16(const void* gp, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gp) : "memory", "m0");
 }

@@ -10,7 +10,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcskv.so")
+# CSKV_LIB_PATH selects another build of the library (the host-sanitized one in CPU tests)
+_LIB_PATH = os.environ.get("CSKV_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcskv.so")
 
 CSKV_BF16 = 0
 CSKV_FP8_E4M3 = 1
