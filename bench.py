@@ -56,6 +56,8 @@ def parse():
                          "every draft token accepted, value counts positions)")
     ap.add_argument("--kv", choices=["fp8", "mxfp4"], default="fp8",
                     help="storage of the compressed entries (mxfp4: OCP MX e2m1 codes + E8M0 per 32 dims)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured HBM / MFMA ceilings (libcskv_peaks.so) reported beside the spec peaks")
     ap.add_argument("--qk-fp4", action="store_true",
                     help="with --kv mxfp4: entry logits on the scaled FP4 x FP8 MFMA from the stored codes "
                          "(CSKV_QK_FP4) instead of widening the entries to bf16")
@@ -111,6 +113,70 @@ def pmc_traffic(call):
     if rec.get("source_sha") != source_sha(files):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def measured_peaks(dev):
+    """Measured ceilings on this GPU, from libcskv_peaks.so (include/cskv_peaks.h): an 8 GiB
+    streaming read (best of 4096/8192 workgroups, median of 7 launches) and independent MFMA
+    chains (1024 workgroups of 4 waves, median of 5 launches) for bf16, fp4 and fp8."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from compressed_sparse_kv_03_amd import build_lib
+    L = ctypes.CDLL(build_lib.PEAKS_LIB)
+    L.cskv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.cskv_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def time_ms(launch, reps):
+        launch()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    nbytes = 8 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(65536, dtype=torch.float32, device=dev)
+    best = 0.0
+    for blocks in (4096, 8192):
+        def rd():
+            rc = L.cskv_peak_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                      blocks, stream)
+            assert rc == 0, rc
+        best = max(best, nbytes / (time_ms(rd, 7) / 1e3) / 1e9)
+    del buf
+    out = {"hbm_read_GBs": round(best, 1)}
+    iters, blocks = 4096, 1024
+    for kind, name, fl in ((0, "mfma_bf16_TFLOPs", 32768), (1, "mfma_fp4_TFLOPs", 131072),
+                           (2, "mfma_fp8_TFLOPs", 131072)):
+        def mm():
+            rc = L.cskv_peak_mfma(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()), stream)
+            assert rc == 0, rc
+        out[name] = round(blocks * 4 * iters * 4 * fl / (time_ms(mm, 5) / 1e3) / 1e12, 1)
+    out["method"] = ("8 GiB non-temporal streaming read; 4 independent 32x32 MFMA chains per wave (bf16 32x32x16, "
+                     "scaled e2m1 and e4m3 32x32x64)")
+    return out
+
+
+def with_measured(r, peaks):
+    """Adds the fraction of the measured ceiling matching a roofline record's bound and unit."""
+    if peaks is None:
+        return r
+    if r["unit"] == "GB/s":
+        pm = peaks["hbm_read_GBs"]
+    else:
+        pm = peaks.get(r.get("mfma_type", "mfma_bf16_TFLOPs"))
+    r["peak_measured"] = pm
+    r["frac_measured"] = round(r["achieved"] / pm, 4) if pm else None
+    return r
 
 
 def main():
@@ -266,6 +332,8 @@ def main():
                                         f"({pairs[0].n0['hca']} entries + {spec.W} window), 64 heads "
                                         "(64-head kernel + merge)")}
 
+    peaks = None if args.no_peaks else measured_peaks(dev)   # after the timed runs
+
     def roofline(call):
         t, nbytes, nflops, what = calls[call]
         gbs = nbytes / (t[3] / 1e3) / 1e9
@@ -318,11 +386,13 @@ def main():
             "hybrid_attn_decode_csa": {"median": t_csa[0], "p10": t_csa[1], "p90": t_csa[2]},
             "hybrid_attn_decode_hca": {"median": t_hca[0], "p10": t_hca[1], "p90": t_hca[2]},
         },
-        "roofline": roofline(dominant),
-        "roofline_calls": {c: roofline(c) for c in calls if c != dominant},
-        "roofline_step": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
-                          "what": "algorithmic bytes of the whole layer-pair step / the step's time"},
+        "roofline": with_measured(roofline(dominant), peaks),
+        "roofline_calls": {c: with_measured(roofline(c), peaks) for c in calls if c != dominant},
+        "roofline_step": with_measured({"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s", "frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+                                        "what": "algorithmic bytes of the whole layer-pair step / the step's time"},
+                                       peaks),
+        "measured_peaks": peaks,
         "wall_s_timed": round(t_wall, 4),
     }
 
@@ -441,6 +511,9 @@ def attn_workload_bench(args, dev):
                      "avg_launch_ms": round(ms_attn, 5),
                      "mfma_frac_bf16": round(attn_flops / (ms_attn / 1e3) / 1e12 / 2500.0, 4)},
     }
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    with_measured(rec["roofline"], peaks)
+    rec["measured_peaks"] = peaks
     print(json.dumps(rec))
 
 
@@ -492,8 +565,8 @@ def prefill_bench(args, dev):
         f()
     torch.cuda.synchronize()
     work = p.work()
-    peaks = {"compress": ("hbm", PEAK_HBM_GBS, "GB/s"), "index": ("mfma", 10100.0, "TFLOP/s"),
-             "attend": ("mfma", 2500.0, "TFLOP/s")}
+    bounds = {"compress": ("hbm", PEAK_HBM_GBS, "GB/s", None), "index": ("mfma", 10100.0, "TFLOP/s", "mfma_fp4_TFLOPs"),
+              "attend": ("mfma", 2500.0, "TFLOP/s", "mfma_bf16_TFLOPs")}
     res = {}
     for name, f in calls.items():
         ts = []
@@ -505,18 +578,21 @@ def prefill_bench(args, dev):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         ms = sorted(ts)[len(ts) // 2]
-        bound, peak, unit = peaks[name]
+        bound, peak, unit, mtype = bounds[name]
         r = {"ms": round(ms, 4), "bytes": work[name]["bytes"], "GB/s": round(work[name]["bytes"] / ms / 1e6, 1)}
         if "flops" in work[name]:
             r["flops"] = work[name]["flops"]
             r["TFLOP/s"] = round(work[name]["flops"] / ms / 1e9, 1)
         achieved = r["GB/s"] if bound == "hbm" else r["TFLOP/s"]
         r["roofline"] = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                         "frac": round(achieved / peak, 4)}
+                         "frac": round(achieved / peak, 4), **({"mfma_type": mtype} if mtype else {})}
         res[name] = r
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    for r in res.values():
+        with_measured(r["roofline"], peaks)
     total_ms = sum(r["ms"] for r in res.values())
     rec = {"prefill": w.name, "runs": max(1, args.steps), "calls": res, "total_ms": round(total_ms, 4),
-           "positions_per_s": round(w.L / (total_ms / 1e3), 1)}
+           "positions_per_s": round(w.L / (total_ms / 1e3), 1), "measured_peaks": peaks}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = prefill_cpu_baseline(p)
     print(json.dumps(rec))

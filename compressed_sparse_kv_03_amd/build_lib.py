@@ -1,6 +1,6 @@
 """Build libcskv.so for gfx950 with hipcc (in-tree; run on a machine with or without a GPU).
 
-    python -m compressed_sparse_kv_03_amd.build_lib            # the library
+    python -m compressed_sparse_kv_03_amd.build_lib            # libcskv.so and libcskv_peaks.so
     python -m compressed_sparse_kv_03_amd.build_lib --sanitize # _build/asan/libcskv_asan.so
 
 The sanitized build instruments the host code only (argument checks, planning, launch setup)
@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcskv.so")
+# measurement helpers (include/cskv_peaks.h): the measured HBM and MFMA ceilings bench.py reports
+PEAKS_SRC = os.path.join(PKG, "peaks")
+PEAKS_LIB = os.path.join(PKG, "libcskv_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -27,8 +30,8 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 ASAN_DIR = os.path.join(BUILD, "asan")
@@ -61,9 +64,9 @@ def _compile(src, flags=FLAGS, out_dir=BUILD):
     return obj, msgs
 
 
-def _build(lib, flags, out_dir, link_extra, verbose):
+def _build(lib, flags, out_dir, link_extra, verbose, src_dir=CSRC):
     os.makedirs(out_dir, exist_ok=True)
-    srcs = sources()
+    srcs = sources(src_dir)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(lambda src: _compile(src, flags, out_dir), srcs))
     for obj, msgs in results:
@@ -81,6 +84,7 @@ def _build(lib, flags, out_dir, link_extra, verbose):
 
 
 def build(verbose=True):
+    _build(PEAKS_LIB, FLAGS, os.path.join(BUILD, "peaks"), [], verbose, PEAKS_SRC)
     return _build(LIB, FLAGS, BUILD, [], verbose)
 
 

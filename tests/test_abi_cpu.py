@@ -142,3 +142,25 @@ def test_ring_append_validation():
     assert L.cskv_ring_append(16, None, 16, 16, None, 1, 2, 60, 8, None) == -1     # D % 8
     assert L.cskv_ring_append(16, 16, 16, 16, None, 1, 2, 64, 8, None) == -1       # z_new without ring_z
     assert L.cskv_ring_append(None, None, 16, 16, None, 1, 2, 64, 8, None) == -1   # null
+
+
+def test_peaks_library_exports_and_validation():
+    """The measurement helpers (include/cskv_peaks.h): every declared symbol exported, bad
+    arguments refused before any launch."""
+    import ctypes
+
+    from compressed_sparse_kv_03_amd import build_lib
+    hdr = os.path.join(os.path.dirname(HDR), "cskv_peaks.h")
+    names = re.findall(r"CSKV_PEAKS_API\s+(?:const\s+char\*|int)\s+([a-z_]+)\(", open(hdr).read())
+    assert sorted(names) == ["cskv_peak_hbm_read", "cskv_peak_mfma", "cskv_peaks_last_error"]
+    L = ctypes.CDLL(build_lib.PEAKS_LIB)
+    for n in names:
+        assert getattr(L, n, None) is not None, f"{n} not exported"
+    L.cskv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.cskv_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.cskv_peak_hbm_read(None, 1 << 20, 16, 1024, None) == -1
+    assert L.cskv_peak_hbm_read(16, 100, 16, 1024, None) == -1          # size not a multiple of 16
+    assert L.cskv_peak_hbm_read(16, 1 << 20, 16, 0, None) == -1
+    assert L.cskv_peak_mfma(3, 1, 1, 16, None) == -1
+    assert L.cskv_peak_mfma(0, 0, 1, 16, None) == -1
+    assert L.cskv_peak_mfma(0, 1, 1, None, None) == -1
