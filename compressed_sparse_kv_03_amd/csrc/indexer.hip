@@ -1252,7 +1252,8 @@ constexpr int kPfRT = 2;          // MFMA row tiles per wave
 constexpr int kPfCap = 512;       // candidate slots per query
 constexpr int kPfKMax = 128;      // k on this path
 constexpr int kPfPL = kPfCap / kWave;
-constexpr int kPfU = 4;           // entry groups (of 16) per scoring step
+constexpr int kPfU = 8;           // entry groups (of 16) per scoring step
+constexpr int kPfHB = 256;        // bins of a wave's threshold histogram
 constexpr int kPfMargin = 64;     // a reduction leaves between k and k + kPfMargin keys
 constexpr int kPfRankPL = (kPfKMax + kPfMargin + kWave - 1) / kWave;  // survivors ranked per lane
 constexpr int kPfTileBytes = 10240;  // key codes of one tile (KT x pitch)
@@ -1270,8 +1271,8 @@ struct PfSmem {
   __align__(16) uint8_t kt[2][kPfTileBytes + 256];  // codes, row pitch = kbytes + 16 (+ read slack)
   __align__(16) uint8_t st[2][512];                 // E8M0 scales, KT x sbytes
   uint64_t cand[QB][kPfCap];
-  int cnt[QB];
   int nv[QB];
+  __align__(16) uint32_t hist[kPfWaves][kPfHB];  // one threshold histogram per wave
 };
 
 // A threshold th with kk <= #{key >= th} <= kk + margin among the n distinct keys buf[0..n)
@@ -1314,6 +1315,56 @@ __device__ uint64_t wave_threshold(const uint64_t* buf, int n, int kk, int margi
   return lo;
 }
 
+// The same threshold as wave_threshold, usually in one pass: a 256-bin histogram (LDS, this
+// wave's own bins) of the keys' scores over equal-width bins of [smin, smax], the highest bin B
+// whose suffix count reaches kk, and th = the lowest key of the lowest score in bins >= B (that
+// score in the high word, 0 in the low one). The bin of a score is monotone in the score, so
+// #{key >= th} is that suffix count: at least kk, and at most kk + margin when bin B holds few
+// enough keys; otherwise (and when every score is equal) the pivot search decides.
+__device__ __forceinline__ uint64_t wave_threshold_hist(const uint64_t* buf, int n, int kk, int margin, uint32_t* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t v[kPfPL];
+  bool ok[kPfPL];
+  uint32_t omx = 0, omn = ~0u;
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) {
+    ok[i] = lane + kWave * i < n;
+    v[i] = buf[min(lane + kWave * i, kPfCap - 1)];
+    const uint32_t o = (uint32_t)(v[i] >> 32);
+    omx = ok[i] ? max(omx, o) : omx;
+    omn = ok[i] ? min(omn, o) : omn;
+  }
+  omx = wave_max_u32(omx);
+  omn = wave_min_u32(omn);
+  const float s0 = ordered_to_score(omn);
+  const float scale = (float)kPfHB / (ordered_to_score(omx) - s0);
+  if (omx == omn || !(scale > 0.f && scale < INFINITY)) return wave_threshold(buf, n, kk, margin);
+  *reinterpret_cast<uint4*>(&hist[4 * lane]) = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_wave_barrier();
+  int bin[kPfPL];
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) {
+    bin[i] = min(kPfHB - 1, (int)((ordered_to_score((uint32_t)(v[i] >> 32)) - s0) * scale));
+    if (ok[i]) atomicAdd(&hist[bin[i]], 1u);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint4 c = *reinterpret_cast<const uint4*>(&hist[4 * lane]);  // bins 4 lane .. 4 lane + 3
+  const int tot = (int)(c.x + c.y + c.z + c.w);
+  const int above = n - wave_incl_scan(tot);  // keys in the bins of higher lanes
+  // suffix counts of the lane's bins, then the highest bin whose suffix count reaches kk
+  const int g3 = above + (int)c.w, g2 = g3 + (int)c.z, g1 = g2 + (int)c.y, g0 = g1 + (int)c.x;
+  const int jb = g3 >= kk ? 3 : (g2 >= kk ? 2 : (g1 >= kk ? 1 : (g0 >= kk ? 0 : -1)));
+  const int mine = jb >= 0 ? 4 * lane + jb : -1;
+  const int B = wave_reduce_i32(mine, [](int x, int y) { return max(x, y); });  // g0 of lane 0 is n >= kk
+  const int gB = __builtin_amdgcn_readlane(jb == 3 ? g3 : (jb == 2 ? g2 : (jb == 1 ? g1 : g0)), B >> 2);
+  __builtin_amdgcn_wave_barrier();
+  if (gB > kk + margin) return wave_threshold(buf, n, kk, margin);
+  uint32_t ts = ~0u;
+#pragma unroll
+  for (int i = 0; i < kPfPL; ++i) ts = ok[i] && bin[i] >= B ? min(ts, (uint32_t)(v[i] >> 32)) : ts;
+  return (uint64_t)wave_min_u32(ts) << 32;
+}
+
 // Keeps the keys >= th of buf[0..n) at the front of buf (order not kept); returns their count.
 __device__ int wave_compact_ge(uint64_t* buf, int n, uint64_t th) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1346,11 +1397,25 @@ __device__ __forceinline__ float head_sum(const f32x4& acc, const float* hw) {
   return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
-// Appends key (score, e) to query q's candidates when it is at or above the query's threshold.
-__device__ __forceinline__ void pf_append(uint64_t (*cand)[kPfCap], int* cnt, int q, float score, int e,
-                                          uint64_t th) {
+// Appends the keys (score, e) of the lanes with `sel` that reach their query's threshold th to
+// the candidate buffer of their query jq (of the QPT queries at buf[0..QPT)), which only this
+// wave writes: slots by ballot rank after the wave-uniform count n[jq], which grows by the
+// number appended. A wave whose lanes all miss the score floor thf skips the rest.
+template <int QPT>
+__device__ __forceinline__ void pf_append(uint64_t (*buf)[kPfCap], int (&n)[QPT], bool sel, int jq, float score,
+                                          int e, float thf, uint64_t th) {
+  const bool near = sel && score >= thf;
+  if (__ballot(near) == 0) return;  // wave-uniform
   const uint64_t key = make_key(score, (uint32_t)e);
-  if (key >= th) cand[q][atomicAdd(&cnt[q], 1)] = key;
+  const bool in = near && key >= th;
+  const uint64_t below = (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const bool mine = in && jq == j;
+    const uint64_t m = __ballot(mine);
+    if (mine) buf[j][n[j] + __popcll(m & below)] = key;
+    n[j] += __popcll(m);
+  }
 }
 
 template <int KS, int QPT, bool HW>
@@ -1377,7 +1442,6 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
   if (tid < QB) {
     const int t = t0 + tid;
     sm.nv[tid] = t < a.T ? min(a.n_valid[(int64_t)b * a.T + t], a.N_cap) : 0;
-    sm.cnt[tid] = 0;
   }
   // A operand: lane row `col` is query col / RPQ of the row tile, head col % RPQ
   uint4 qa[kPfRT][KS];
@@ -1407,6 +1471,7 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
   // groups 2, 3 -> query 1; QPT = 1: one query)
   const int jq = QPT == 2 ? (G >> 1) : 0;
   int nvq[kPfRT];
+  int ncand[kPfRT][QPT] = {};  // candidates held by each of the wave's queries (wave-uniform)
   uint64_t th[kPfRT];
   float thf[kPfRT];  // the score of th (a key >= th has a score >= thf)
 #pragma unroll
@@ -1458,25 +1523,35 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
     // U groups of 16 entries per step: their MFMAs issue back to back, then the scores
 #pragma unroll 1
     for (int g = 0; g < KT / 16; g += U) {
-      f32x4 acc[U][kPfRT];
+      // every operand read (unconditional: a piece past D_I reads the row's first one, its scale
+      // replaced by 1), then every product, then the scores: the MFMAs issue back to back and
+      // the first results are ready when the score epilogue starts
+      uint4 kv[U][KS];
+      int ks[U][KS];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kl = 16 * (g + u) + col;
-        uint4 kv[KS];
-        int ks[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const bool okk = (s * 128 + G * 32) < a.D_I;
-          kv[s] = *reinterpret_cast<const uint4*>(kt + kl * pitch + (okk ? s * 64 + G * 16 : 0));
-          ks[s] = okk ? (int)st[kl * sbytes + s * 4 + G] : 127;
-        }
-#pragma unroll
-        for (int rt = 0; rt < kPfRT; ++rt) {
-          acc[u][rt] = mfma_fp4(qa[rt][0], kv[0], qs[rt][0], ks[0]);
-#pragma unroll
-          for (int s = 1; s < KS; ++s) acc[u][rt] = mfma_fp4_acc(qa[rt][s], kv[s], qs[rt][s], ks[s], acc[u][rt]);
+          const int off = okk ? s * 64 + G * 16 : 0, soff = okk ? s * 4 + G : 0;
+          kv[u][s] = *reinterpret_cast<const uint4*>(kt + kl * pitch + off);
+          const int sv = st[kl * sbytes + soff];
+          ks[u][s] = okk ? sv : 127;
         }
       }
+      f32x4 acc[U][kPfRT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int rt = 0; rt < kPfRT; ++rt) {
+          acc[u][rt] = mfma_fp4(qa[rt][0], kv[u][0], qs[rt][0], ks[u][0]);
+#pragma unroll
+          for (int s = 1; s < KS; ++s)
+            acc[u][rt] = mfma_fp4_acc(qa[rt][s], kv[u][s], qs[rt][s], ks[u][s], acc[u][rt]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (QPT == 2) {
         // lane group G holds rows 4G..4G+3: heads 0-3 / 4-7 of query 0 (G = 0, 1) and of query 1
         // (G = 2, 3). One permlane16 swap of the two groups' partial sums and one add leave
@@ -1490,7 +1565,7 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
             const float p0 = head_sum<HW>(acc[u][rt], hw[rt]), p1 = head_sum<HW>(acc[u + 1][rt], hw[rt]);
             const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
             const float part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (e < nvq[rt] && part >= thf[rt]) pf_append(sm.cand, sm.cnt, wave * QW + rt * QPT + jq, part, e, th[rt]);
+            pf_append<QPT>(&sm.cand[wave * QW + rt * QPT], ncand[rt], e < nvq[rt], jq, part, e, thf[rt], th[rt]);
           }
         }
       } else {
@@ -1502,7 +1577,7 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
             float part = head_sum<HW>(acc[u][rt], hw[rt]);
             part += __shfl_xor(part, 16, kWave);
             part += __shfl_xor(part, 32, kWave);
-            if (G == 0 && e < nvq[rt] && part >= thf[rt]) pf_append(sm.cand, sm.cnt, wave * QW + rt, part, e, th[rt]);
+            pf_append<QPT>(&sm.cand[wave * QW + rt * QPT], ncand[rt], G == 0 && e < nvq[rt], 0, part, e, thf[rt], th[rt]);
           }
         }
       }
@@ -1513,11 +1588,11 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
         const int q = wave * QW + rt * QPT + j;
-        const int n = __builtin_amdgcn_readfirstlane(sm.cnt[q]);
+        const int n = ncand[rt][j];
         if (n > kPfCap - KT) {
-          const uint64_t kth = wave_threshold(sm.cand[q], n, a.k, kPfMargin);
+          const uint64_t kth = wave_threshold_hist(sm.cand[q], n, a.k, kPfMargin, sm.hist[wave]);
           const int m = wave_compact_ge(sm.cand[q], n, kth);
-          if (lane == 0) sm.cnt[q] = m;
+          ncand[rt][j] = m;
           if (jq == j) {
             th[rt] = kth;
             thf[rt] = ordered_to_score((uint32_t)(kth >> 32));
@@ -1529,6 +1604,14 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
     __syncthreads();
   }
 
+  // the candidate counts go to nv (no longer read by any wave), each wave's own queries' slots,
+  // read back below by the same wave (LDS requests of one wave complete in order)
+  if (lane == 0) {
+#pragma unroll
+    for (int rt = 0; rt < kPfRT; ++rt)
+#pragma unroll
+      for (int j = 0; j < QPT; ++j) sm.nv[wave * QW + rt * QPT + j] = ncand[rt][j];
+  }
   // final: each query's top min(k, candidates), ranked (one chunk) or as chunk winners
 #pragma unroll 1
   for (int j = 0; j < QW; ++j) {
@@ -1537,9 +1620,9 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
     if (t >= a.T) continue;
     const int64_t bq = (int64_t)b * a.T + t;
     uint64_t* buf = sm.cand[q];
-    int n = __builtin_amdgcn_readfirstlane(sm.cnt[q]);
+    int n = __builtin_amdgcn_readfirstlane(sm.nv[q]);
     const int kk = min(a.k, n);
-    if (n > kk + kPfMargin) n = wave_compact_ge(buf, n, wave_threshold(buf, n, kk, kPfMargin));
+    if (n > kk + kPfMargin) n = wave_compact_ge(buf, n, wave_threshold_hist(buf, n, kk, kPfMargin, sm.hist[wave]));
     // rank the n (<= kk + margin) survivors; those ranked below kk are the answer
     uint64_t key[kPfRankPL];
     int rank[kPfRankPL];
