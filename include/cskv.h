@@ -260,7 +260,11 @@ CSKV_API int hybrid_attn_decode_noalloc(const uint16_t* q, const int64_t* q_pos,
                        uint16_t* out, float* out_lse, float q_rms_eps, int T, int R, void* stream);
 
 /*
- * hybrid_attn_prefill - the same attention for every row of one prompt.
+ * hybrid_attn_prefill - the same attention for every row of one prompt. (Page
+ * "DeepSeek-V4가 ... 달성하는 방법", section "두 가지 압축 전략: CSA 및 HCA", as for
+ * hybrid_attn_decode: every prompt position is a query of CSA's top-k entries plus its
+ * window, or of all HCA entries; causally it sees only entries of blocks already complete
+ * and tokens up to itself.)
  * Row r is position t = pos0 + r. It sees entries j < min(N, floor((t+1)/m))
  * (CSA: those listed in topk_idx[r]; HCA: all of them when topk_idx == NULL)
  * and the raw tokens x at positions [max(pos0, t-W+1), t], rotated at their
