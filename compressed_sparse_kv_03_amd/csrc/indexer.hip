@@ -35,6 +35,18 @@ constexpr int kIdxNT = 256;          // threads per workgroup
 constexpr int kSub = 4096;           // entries scored per LDS pass
 constexpr int kMaxMergeKeys = 8192;  // chunk winners merged per query in stage 2
 
+// x plus the x of the lane 16 (32) apart, on the VALU: a permlane swap of two copies of x
+// exchanges the halves of every 32-lane (64-lane) group, and the two results sum to
+// x[l] + x[l ^ 16] (x[l] + x[l ^ 32]) in every lane; no LDS round trip as for a shuffle.
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 __device__ __forceinline__ f32x4 mfma_fp4_acc(uint4 a, uint4 b, int sa, int sb, f32x4 acc) {
   i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
@@ -135,8 +147,7 @@ __device__ __forceinline__ void score_range_to(const IndexArgs& a, int b, int e_
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
+      part = add_xor32(add_xor16(part));
       const int el = (g0 + u) * 16 + col;
       sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
     }
@@ -197,8 +208,7 @@ __device__ __forceinline__ void kbatch_score(const KBatch<KS, U>& B, int64_t sc_
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
-    part += __shfl_xor(part, 16, kWave);
-    part += __shfl_xor(part, 32, kWave);
+    part = add_xor32(add_xor16(part));
     const int el = (g + u) * 16 + col;
     sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
   }
@@ -1013,7 +1023,7 @@ __global__ __launch_bounds__(kDecNT) void index_chunk_multi_kernel(DecodeArgs d,
           float part = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) part = fmaf(hw[rt][r], fmaxf(acc[r], 0.f), part);
-          part += __shfl_xor(part, 16, kWave);
+          part = add_xor16(part);
           if ((G & 1) == 0 && el < n_el)
             sm.sc[2 * rt + (G >> 1)][el] = c0 + el < nvl[rt] ? score_to_ordered(part) : 0u;
         }
@@ -1575,8 +1585,7 @@ __global__ __launch_bounds__(kPfNT) void index_block_kernel(IndexArgs a, int nqb
 #pragma unroll
           for (int rt = 0; rt < kPfRT; ++rt) {
             float part = head_sum<HW>(acc[u][rt], hw[rt]);
-            part += __shfl_xor(part, 16, kWave);
-            part += __shfl_xor(part, 32, kWave);
+            part = add_xor32(add_xor16(part));
             pf_append<QPT>(&sm.cand[wave * QW + rt * QPT], ncand[rt], G == 0 && e < nvq[rt], 0, part, e, thf[rt], th[rt]);
           }
         }
