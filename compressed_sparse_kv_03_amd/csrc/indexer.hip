@@ -35,6 +35,10 @@ constexpr int kIdxNT = 256;          // threads per workgroup
 constexpr int kSub = 4096;           // entries scored per LDS pass
 constexpr int kMaxMergeKeys = 8192;  // chunk winners merged per query in stage 2
 
+// max(x, 0) as an integer max on the bit pattern (a negative float, -0 included, has a negative
+// pattern): one instruction, no canonicalisation; scores are finite.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // x plus the x of the lane 16 (32) apart, on the VALU: a permlane swap of two copies of x
 // exchanges the halves of every 32-lane (64-lane) group, and the two results sum to
 // x[l] + x[l ^ 16] (x[l] + x[l ^ 32]) in every lane; no LDS round trip as for a shuffle.
@@ -141,12 +145,12 @@ __device__ __forceinline__ void score_range_to(const IndexArgs& a, int b, int e_
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int sc = (s * 128 + kb * 32) < a.D_I ? wsc[(u * 16 + col) * sbytes + s * 4 + kb] : 127;
-        acc += mfma_fp4(qa[s], kv[u][s], qs[s], sc);
+        acc = mfma_fp4_acc(qa[s], kv[u][s], qs[s], sc, acc);
       }
       // rows 4*kb + r are heads; ReLU, head weight, then sum over the 4 lane groups
       float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
+      for (int r = 0; r < 4; ++r) part = fmaf(hw[r], relu_bits(acc[r]), part);
       part = add_xor32(add_xor16(part));
       const int el = (g0 + u) * 16 + col;
       sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
@@ -203,11 +207,11 @@ __device__ __forceinline__ void kbatch_score(const KBatch<KS, U>& B, int64_t sc_
       // no masking; only the scale is replaced (an E8M0 byte of 255 would be NaN)
       const int sh = 8 * (int)((sc_off0 + (int64_t)e * sbytes + s * 4 + kb) & 3);
       const int byte = (int)((B.sc[u][s] >> sh) & 255u);
-      acc += mfma_fp4(qa[s], B.kv[u][s], qs[s], okk ? byte : 127);
+      acc = mfma_fp4_acc(qa[s], B.kv[u][s], qs[s], okk ? byte : 127, acc);
     }
     float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part = fmaf(hw[r], fmaxf(acc[r], 0.f), part);
+    for (int r = 0; r < 4; ++r) part = fmaf(hw[r], relu_bits(acc[r]), part);
     part = add_xor32(add_xor16(part));
     const int el = (g + u) * 16 + col;
     sink(kb == 0 && el < n, el, make_key(part, (uint32_t)(e_begin + el)));
@@ -1018,11 +1022,10 @@ __global__ __launch_bounds__(kDecNT) void index_chunk_multi_kernel(DecodeArgs d,
         const int byte = okk ? (int)((X[i].sc[u][0] >> sh) & 255u) : 127;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc += mfma_fp4(qa[rt], X[i].kv[u][0], qs[rt], byte);
+          const f32x4 acc = mfma_fp4(qa[rt], X[i].kv[u][0], qs[rt], byte);
           float part = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) part = fmaf(hw[rt][r], fmaxf(acc[r], 0.f), part);
+          for (int r = 0; r < 4; ++r) part = fmaf(hw[rt][r], relu_bits(acc[r]), part);
           part = add_xor16(part);
           if ((G & 1) == 0 && el < n_el)
             sm.sc[2 * rt + (G >> 1)][el] = c0 + el < nvl[rt] ? score_to_ordered(part) : 0u;
