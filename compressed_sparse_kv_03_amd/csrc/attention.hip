@@ -1338,12 +1338,15 @@ namespace cskv {
 
 static int g_attn_path = 0;  // 0: by the call's shape; 1: the 64-head kernel; 2: the 16-head kernel
 
-// The 16-head kernel takes short key sets of few queries (a few hundred keys: a workgroup's
-// prologue then lasts as long as its tiles, and its two workgroups per CU hide one another's);
-// the 64-head kernel everything else.
+// The 16-head kernel takes short key sets of few queries: a workgroup's prologue then lasts as
+// long as its tiles, and its two workgroups per CU hide one another's. The 64-head kernel takes
+// everything else. Measured crossover (cold calls, 64 heads, D = 512+64, fp8 and bf16 entries):
+// the 16-head kernel is faster up to about 4096 (query, key) pairs per call — 16 queries of
+// 192 or 256 keys, 8 of 512 — and slower beyond (at 32 queries of 256 keys, 31.5 µs against
+// 26.6 µs).
 static bool use_g16(int nq, int max_keys) {
   if (g_attn_path) return g_attn_path == 2;
-  return max_keys <= 512 && nq <= 256;
+  return max_keys <= 512 && (int64_t)nq * max_keys <= 4096;
 }
 
 static size_t attn_ws(int nq, int H, int d_v, int entries, int W) {

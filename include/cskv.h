@@ -228,8 +228,9 @@ CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_c
 /*
  * cskv_attn_path - which attention kernel hybrid_attn_decode, _noalloc and _prefill run (and
  * their *_workspace_size functions plan for): 0 (the default) chooses by the call's shape, the
- * 16-head kernel for short key sets of few queries (at most 512 keys per query and at most 256
- * queries) and the 64-head kernel otherwise; 1 forces the 64-head kernel, 2 the 16-head kernel.
+ * 16-head kernel for short key sets of few queries (at most 512 keys per query and at most 4096
+ * (query, key) pairs in the call) and the 64-head kernel otherwise; 1 forces the 64-head kernel,
+ * 2 the 16-head kernel.
  * Both compute the same attention (parity-tested each); the choice moves only time and
  * workspace size. A process-wide setting, read at each call: set it before sizing a workspace
  * and keep it until the calls that use that workspace have been issued; not for concurrent use
