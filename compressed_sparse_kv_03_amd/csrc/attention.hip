@@ -262,6 +262,17 @@ __device__ __forceinline__ void dma16(const void* gp, uint32_t lds) {
 __device__ __forceinline__ void dma4(const void* gp, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gp) : "memory", "m0");
 }
+// x combined with the x of the lane 32 apart, on the VALU: a permlane32 swap of two copies of x
+// leaves x[l] in one result and x[l ^ 32] in the other, in every lane (no LDS round trip as for
+// a shuffle).
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
 // The wave's index in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
@@ -682,7 +693,7 @@ __device__ __forceinline__ void quantize_query_f4(const AttnArgs& a, AttnSmem<D>
       float amax = 0.f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));  // the head's 64 dims of the step
+      amax = max_xor32(amax);  // the head's 64 dims of the step
       const int E = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;  // amax * 2^-E in [128, 256)
       qe[j] = E;
 #pragma unroll
@@ -735,7 +746,7 @@ __device__ __forceinline__ void quantize_query_f4(const AttnArgs& a, AttnSmem<D>
     }
     pb += FR::parts(s);
   }
-  ss += __shfl_xor(ss, 32, kWave);
+  ss = add_xor32(ss);
   if constexpr (!SHARE) {
     if (kh == 0 && lane < 32) sm.qss[DQ][32 * hh + lane] = ss;
     return;
@@ -840,7 +851,7 @@ __device__ __forceinline__ void tile_softmax(const AttnArgs& a, AttnSmem<D>& sm,
       wv.y = cvt_bf16x2(pv[2], pv[3]);
       *reinterpret_cast<uint2*>(&sm.p[hl][kr + 8 * g]) = wv;
     }
-    return fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    return max_xor32(mloc);
   };
   {
     const float mloc = form_p(st.m == -INFINITY ? 0.f : st.m);
@@ -1015,7 +1026,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   } else {
     float ss = query_sumsq<D, DQ>(a, q);
     rotate_query<D, DQ>(a, sm.rev, ks.t, q, qlo);
-    ss += __shfl_xor(ss, 32, kWave);
+    ss = add_xor32(ss);
     if (kh == 0 && lane < 32) sm.qss[DQ][hl] = ss;  // read after the first tile's barriers
   }
   if (F8 && n_et > 1)
@@ -1077,7 +1088,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
 
   // the head's key sum: over the lane halves, then over the four waves that wrote its P
   {
-    const float lw = st.l + __shfl_xor(st.l, 32, kWave);
+    const float lw = add_xor32(st.l);
     if (lane < 32) sm.lsum[2 * kh + DQ][hl] = lw;
   }
   __syncthreads();
