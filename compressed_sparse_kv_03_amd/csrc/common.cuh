@@ -60,27 +60,23 @@ __device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, floa
 }
 
 // ---------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // Reductions over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane gets the
 // result. quad_perm [1,0,3,2] and [2,3,0,1] combine within quads, row_ror 4 and 8 across them.
-__device__ __forceinline__ float dpp_f(float v, int ctrl) {
-  const int x = __builtin_bit_cast(int, v);
+__device__ __forceinline__ int dpp_i(int x, int ctrl) {
   switch (ctrl) {
-    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
-    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
-    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
-    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+    case 0: return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+    case 1: return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);
   }
+}
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  return __builtin_bit_cast(float, dpp_i(__builtin_bit_cast(int, v), ctrl));
+}
+__device__ __forceinline__ double dpp_d(double v, int ctrl) {
+  const uint64_t x = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)dpp_i((int)(uint32_t)x, ctrl), hi = (uint32_t)dpp_i((int)(uint32_t)(x >> 32), ctrl);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f(v, 0));
@@ -93,6 +89,35 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f(v, 1);
   v += dpp_f(v, 2);
   return v + dpp_f(v, 3);
+}
+// Whole-wave reductions: the four row results read with readlane (every lane gets the result;
+// no LDS round trip as for shuffles).
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const uint64_t x = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v = fmax(v, dpp_d(v, c));
+  return fmax(fmax(lane_d(v, 0), lane_d(v, 16)), fmax(lane_d(v, 32), lane_d(v, 48)));
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v += dpp_d(v, c);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
 }
 
 // ---------------------------------------------------------------- RoPE

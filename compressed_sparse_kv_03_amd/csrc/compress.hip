@@ -35,17 +35,6 @@ struct RopeTable {
   double inv_freq[kRopeTab];
 };
 
-__device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // floor(log2 |v|) of a finite nonzero double (exact: from the binary exponent).
 __device__ __forceinline__ int floor_log2_d(double v) {
   int ex;
