@@ -11,7 +11,11 @@ in HBM before timing starts.
 So that every step reads its caches from HBM rather than from the 256 MB
 Infinity Cache (one pair's per-step working set, ~186 MB, would fit in it), the
 timed loop runs a stack of P independent layer pairs per step, as consecutive
-layers of a model do; throughput is reported per layer pair.
+layers of a model do; throughput is reported per layer pair. The pairs are
+independent (each has its own synthetic queries and tokens), so by default a
+step issues the HCA layers on a second stream beside the CSA layers (in a model,
+where a layer's inputs come from the layer before it, the same overlap needs two
+micro-batches in flight); --serial issues every call on one stream.
 
 Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -61,6 +65,9 @@ def parse():
     ap.add_argument("--qk-fp4", action="store_true",
                     help="with --kv mxfp4: entry logits on the scaled FP4 x FP8 MFMA from the stored codes "
                          "(CSKV_QK_FP4) instead of widening the entries to bf16")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue every call of a step on one stream (default: the HCA layers on a second stream "
+                         "beside the CSA layers)")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -239,12 +246,11 @@ def main():
 
     share = None if args.share == "none" else args.share
 
+    # the HCA layers on a second stream beside the CSA layers (default priority, like the first)
+    side = None if args.serial else torch.cuda.Stream()
+
     def step_all(i):
-        for p_, pr_ in enumerate(pairs):
-            if p_ == 0 or share is None:
-                pr_.step(i)
-            else:
-                pr_.step(i, share=share, src=pairs[0])
+        hybrid.step_stack(pairs, i, share=share, side=side)
 
     # ---- warmup: W eager steps of every pair, then restore the windows
     for i in range(min(W, K)):
@@ -370,6 +376,7 @@ def main():
             "workload": "c5_hybrid_1m: CSA(m=4,k=128,FP4 indexer 8x128)+HCA(m=128) layer pair, decode batch 8, "
                         f"context 2^20, H=64, D=512+64, {args.kv} entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
+            "streams": 1 if args.serial else 2,
             "tokens_per_step_per_pair": spec.B * spec.draft,
             **({"draft_tokens_per_step": spec.draft} if spec.draft > 1 else {}),
             **({"index_keys": "derived in the loop (per-token keys pooled, MXFP4)"} if args.derive_keys else {}),

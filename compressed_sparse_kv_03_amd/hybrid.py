@@ -215,8 +215,11 @@ class LayerPair:
         return st
 
     # ------------------------------------------------------------------ one step
-    def step(self, i, stream=None, share=None, src=None):
+    def step(self, i, stream=None, share=None, src=None, layers=("csa", "hca")):
         """Decode step i of both layers (draft tokens t0 .. t0 + draft - 1).
+
+        layers: the layers whose calls are issued (both by default). The two layers of a pair
+        share no buffer, so their calls may be issued on different streams.
 
         share (cross-layer index sharing of the CSA layer, with `src` another LayerPair of the
         same shapes that has already run step i):
@@ -228,8 +231,9 @@ class LayerPair:
         s = self.s
         B, D, W, Td = s.B, s.D, s.W, s.draft
         assert share in (None, "reuse", "reindex") and (share is None or src is not None)
+        assert set(layers) <= {"csa", "hca"}
         kv = {"csa": src if share == "reindex" else self, "hca": self}
-        for name in ("csa", "hca"):
+        for name in layers:
             if kv[name] is not self:
                 continue
             R, m = self.R[name], self.m[name]
@@ -246,14 +250,16 @@ class LayerPair:
                 if keys:
                     native.csa_index_key_pool(self.ring_xk[:, slot0:], R * s.D_I, self.ringz[name][:, slot0:], R, B, m,
                                               s.D_I, m, self.ik, self.iks, self.cap[name], e0, stream)
-        if share == "reuse":
+        if "csa" not in layers:
+            topk = None
+        elif share == "reuse":
             topk = src.topk[i]
         else:
             ik = kv["csa"]
             native.csa_index_topk(self.iq[i], self.iqs[i], None, ik.ik, ik.iks, self.nvalid[i], B, Td,
                                   self.cap["csa"], s.H_I, s.D_I, s.k, self.topk[i], None, self.ws_idx, None, stream)
             topk = self.topk[i]
-        for name in ("csa", "hca"):
+        for name in layers:
             c = kv[name]
             native.hybrid_attn_decode(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
                                       self.attn_code, self.cap[name], self.nent[name][i],
@@ -293,3 +299,27 @@ class LayerPair:
         idx = 2 * s.B * Td * n_c * s.H_I * s.D_I
         att = lambda nk: 2 * s.B * Td * s.H * nk * (s.D + s.d_v)  # noqa: E731
         return {"csa_index": idx, "csa_attn": att(s.k + s.W), "hca_attn": att(n_h + s.W)}
+
+
+def step_stack(pairs, i, share=None, side=None):
+    """Decode step i of a stack of independent layer pairs on the current stream.
+
+    share: as in LayerPair.step, for pairs 1.. (pair 0 always indexes its own keys).
+    side: None issues every call on the current stream, pair after pair. Given a second stream,
+    the HCA layers of all pairs go to it, forked from the current stream at the start of the
+    step and joined at its end, so that they run beside the CSA layers' calls (the HCA layer of
+    a pair reads nothing the CSA layers write). Under graph capture this records two parallel
+    branches per step.
+    """
+    if side is None:
+        for p, pr in enumerate(pairs):
+            pr.step(i, share=None if p == 0 else share, src=pairs[0])
+        return
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        for pr in pairs:
+            pr.step(i, layers=("hca",))
+    for p, pr in enumerate(pairs):
+        pr.step(i, share=None if p == 0 else share, src=pairs[0], layers=("csa",))
+    main.wait_stream(side)

@@ -192,6 +192,44 @@ def test_hybrid_loop_graph_replays_match_eager():
         assert torch.equal(pair.topk, ref_tk), f"replay {rep}: top-k differs from eager"
 
 
+@pytest.mark.parametrize("share", [None, "reuse"])
+def test_hybrid_stack_two_streams_graph_matches_serial(share):
+    """A stack of three pairs with the HCA layers on a second stream, captured in one graph (two
+    parallel branches per step) and replayed three times: every replay equals the serial eager
+    run bit for bit (outputs, lse and top-k of every step)."""
+    spec = dict(B=2, L=4096, steps=132, H=64, D=576, d_rope=64, d_v=512, wid=57)
+    say("hybrid stack two streams", spec, share)
+    pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec)) for p in range(3)]
+    for i in range(spec["steps"]):
+        hybrid.step_stack(pairs, i, share=share)
+    torch.cuda.synchronize()
+    ref = [({n: (pr.out[n].clone(), pr.lse[n].clone()) for n in ("csa", "hca")}, pr.topk.clone()) for pr in pairs]
+    side = torch.cuda.Stream()
+    for pr in pairs:
+        pr.restore()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(spec["steps"]):
+            hybrid.step_stack(pairs, i, share=share, side=side)
+    for rep in range(3):
+        for pr in pairs:
+            pr.restore()
+            for n in ("csa", "hca"):
+                pr.out[n].zero_()
+                pr.lse[n].zero_()
+            pr.topk.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device="cuda").sum().item()    # eager work between replays
+        for p, pr in enumerate(pairs):
+            for n in ("csa", "hca"):
+                assert torch.equal(pr.out[n], ref[p][0][n][0]), f"replay {rep}: pair {p} {n} output"
+                assert torch.equal(pr.lse[n], ref[p][0][n][1]), f"replay {rep}: pair {p} {n} lse"
+            if share is None or p == 0:
+                assert torch.equal(pr.topk, ref[p][1]), f"replay {rep}: pair {p} top-k"
+
+
 def test_hybrid_loop_1m():
     """The 1M-context pair (B=8, 256 steps): the top-k of every step and sequence bit-exact against
     the oracle's indexer over the same keys, and both layers' attention on sampled steps (block
