@@ -13,9 +13,10 @@ Infinity Cache (one pair's per-step working set, ~186 MB, would fit in it), the
 timed loop runs a stack of P independent layer pairs per step, as consecutive
 layers of a model do; throughput is reported per layer pair. The pairs are
 independent (each has its own synthetic queries and tokens), so by default a
-step issues the HCA layers on a second stream beside the CSA layers (in a model,
-where a layer's inputs come from the layer before it, the same overlap needs two
-micro-batches in flight); --serial issues every call on one stream.
+step runs them as two micro-batches: pairs 0-1 on one stream and pairs 2-3 on a
+second, each stream stepping its pairs in layer order (CSA, HCA, CSA, HCA), the
+two streams forked and joined once per step. --streams 1 issues every call on
+one stream.
 
 Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -65,9 +66,12 @@ def parse():
     ap.add_argument("--qk-fp4", action="store_true",
                     help="with --kv mxfp4: entry logits on the scaled FP4 x FP8 MFMA from the stored codes "
                          "(CSKV_QK_FP4) instead of widening the entries to bf16")
-    ap.add_argument("--serial", action="store_true",
-                    help="issue every call of a step on one stream (default: the HCA layers on a second stream "
-                         "beside the CSA layers)")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="streams a step's calls are issued on (1: every call on one stream)")
+    ap.add_argument("--split", choices=["chains", "layers"], default="chains",
+                    help="with --streams > 1: chains = the pairs cut into one contiguous group per stream, each "
+                         "stepped in layer order (independent micro-batches); layers = (2 streams) the HCA layers "
+                         "of all pairs beside the CSA layers")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the 128K-token CSA prefill (compress, causal index + top-k, attention); "
                          "--steps timed runs of each call after one warm-up")
@@ -246,11 +250,13 @@ def main():
 
     share = None if args.share == "none" else args.share
 
-    # the HCA layers on a second stream beside the CSA layers (default priority, like the first)
-    side = None if args.serial else torch.cuda.Stream()
+    # further streams (default priority, like the first) for the parallel branches of a step
+    if args.streams < 1 or args.streams > P or (args.split == "layers" and args.streams != 2):
+        sys.exit("--streams: 1 .. pairs (exactly 2 with --split layers)")
+    side = [torch.cuda.Stream() for _ in range(args.streams - 1)]
 
     def step_all(i):
-        hybrid.step_stack(pairs, i, share=share, side=side)
+        hybrid.step_stack(pairs, i, share=share, side=side, split=args.split)
 
     # ---- warmup: W eager steps of every pair, then restore the windows
     for i in range(min(W, K)):
@@ -376,7 +382,11 @@ def main():
             "workload": "c5_hybrid_1m: CSA(m=4,k=128,FP4 indexer 8x128)+HCA(m=128) layer pair, decode batch 8, "
                         f"context 2^20, H=64, D=512+64, {args.kv} entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
-            "streams": 1 if args.serial else 2,
+            "streams": args.streams,
+            **({"stream_split": ("pairs in one contiguous group per stream, each stepped in layer order "
+                                 "(independent micro-batches)") if args.split == "chains" else
+                "the HCA layers of all pairs on the second stream beside the CSA layers"}
+               if args.streams > 1 else {}),
             "tokens_per_step_per_pair": spec.B * spec.draft,
             **({"draft_tokens_per_step": spec.draft} if spec.draft > 1 else {}),
             **({"index_keys": "derived in the loop (per-token keys pooled, MXFP4)"} if args.derive_keys else {}),

@@ -301,25 +301,50 @@ class LayerPair:
         return {"csa_index": idx, "csa_attn": att(s.k + s.W), "hca_attn": att(n_h + s.W)}
 
 
-def step_stack(pairs, i, share=None, side=None):
-    """Decode step i of a stack of independent layer pairs on the current stream.
+
+def step_stack(pairs, i, share=None, side=None, split="chains"):
+    """Decode step i of a stack of independent layer pairs, forked from the current stream.
 
     share: as in LayerPair.step, for pairs 1.. (pair 0 always indexes its own keys).
-    side: None issues every call on the current stream, pair after pair. Given a second stream,
-    the HCA layers of all pairs go to it, forked from the current stream at the start of the
-    step and joined at its end, so that they run beside the CSA layers' calls (the HCA layer of
-    a pair reads nothing the CSA layers write). Under graph capture this records two parallel
-    branches per step.
+    side: None issues every call on the current stream, pair after pair. Otherwise a list of
+    further streams, forked from the current stream at the start of the step and joined at its
+    end. Under graph capture this records parallel branches per step.
+    split: how the calls go to the streams --
+      "chains": the pairs are cut into len(side) + 1 contiguous groups, one per stream, each
+                group stepped pair after pair (CSA layer, then HCA layer), so every stream keeps
+                the layer order of a model and the streams are independent micro-batches;
+      "layers": (one side stream) the HCA layers of all pairs go to the side stream, beside the
+                CSA layers (the HCA layer of a pair reads nothing its CSA layer writes).
+    With share, pairs 1.. wait for pair 0's step before theirs.
     """
-    if side is None:
+    shr = lambda p: None if p == 0 else share  # noqa: E731
+    if not side:
         for p, pr in enumerate(pairs):
-            pr.step(i, share=None if p == 0 else share, src=pairs[0])
+            pr.step(i, share=shr(p), src=pairs[0])
         return
     main = torch.cuda.current_stream()
-    side.wait_stream(main)
-    with torch.cuda.stream(side):
+    for st in side:
+        st.wait_stream(main)
+    if split == "layers":
+        assert len(side) == 1 and share is None
+        with torch.cuda.stream(side[0]):
+            for pr in pairs:
+                pr.step(i, layers=("hca",))
         for pr in pairs:
-            pr.step(i, layers=("hca",))
-    for p, pr in enumerate(pairs):
-        pr.step(i, share=None if p == 0 else share, src=pairs[0], layers=("csa",))
-    main.wait_stream(side)
+            pr.step(i, layers=("csa",))
+    else:
+        assert split == "chains"
+        streams = [main] + list(side)
+        n = len(streams)
+        groups = [[p for p in range(len(pairs)) if p * n // len(pairs) == g] for g in range(n)]
+        done0 = torch.cuda.Event() if share is not None else None
+        for g, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                for p in groups[g]:
+                    if share is not None and p > 0 and g > 0:
+                        st.wait_event(done0)
+                    pairs[p].step(i, share=shr(p), src=pairs[0])
+                    if p == 0 and done0 is not None:
+                        done0.record(st)
+    for st in side:
+        main.wait_stream(st)

@@ -192,25 +192,26 @@ def test_hybrid_loop_graph_replays_match_eager():
         assert torch.equal(pair.topk, ref_tk), f"replay {rep}: top-k differs from eager"
 
 
-@pytest.mark.parametrize("share", [None, "reuse"])
-def test_hybrid_stack_two_streams_graph_matches_serial(share):
-    """A stack of three pairs with the HCA layers on a second stream, captured in one graph (two
-    parallel branches per step) and replayed three times: every replay equals the serial eager
-    run bit for bit (outputs, lse and top-k of every step)."""
+@pytest.mark.parametrize("split,nside,share", [("layers", 1, None), ("chains", 1, None), ("chains", 2, "reuse"),
+                                               ("chains", 1, "reindex")])
+def test_hybrid_stack_streams_graph_matches_serial(split, nside, share):
+    """A stack of three pairs stepped on several streams (parallel branches per step), captured in
+    one graph and replayed three times: every replay equals the serial eager run bit for bit
+    (outputs, lse and top-k of every step)."""
     spec = dict(B=2, L=4096, steps=132, H=64, D=576, d_rope=64, d_v=512, wid=57)
-    say("hybrid stack two streams", spec, share)
+    say("hybrid stack streams", spec, split, nside, share)
     pairs = [hybrid.LayerPair(hybrid.LayerPairSpec(seed=p, **spec)) for p in range(3)]
     for i in range(spec["steps"]):
         hybrid.step_stack(pairs, i, share=share)
     torch.cuda.synchronize()
     ref = [({n: (pr.out[n].clone(), pr.lse[n].clone()) for n in ("csa", "hca")}, pr.topk.clone()) for pr in pairs]
-    side = torch.cuda.Stream()
+    side = [torch.cuda.Stream() for _ in range(nside)]
     for pr in pairs:
         pr.restore()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(spec["steps"]):
-            hybrid.step_stack(pairs, i, share=share, side=side)
+            hybrid.step_stack(pairs, i, share=share, side=side, split=split)
     for rep in range(3):
         for pr in pairs:
             pr.restore()
