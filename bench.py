@@ -68,6 +68,10 @@ def parse():
                          "(CSKV_QK_FP4) instead of widening the entries to bf16")
     ap.add_argument("--streams", type=int, default=2,
                     help="streams a step's calls are issued on (1: every call on one stream)")
+    ap.add_argument("--attn-cus", type=int, default=-1,
+                    help="CUs the 64-head attention's split plan counts on in the timed loop (cskv_attn_cu_budget; "
+                         "-1: 256 / streams, i.e. the whole GPU on one stream); the cold per-call timings plan "
+                         "for the whole GPU")
     ap.add_argument("--split", choices=["chains", "layers"], default="chains",
                     help="with --streams > 1: chains = the pairs cut into one contiguous group per stream, each "
                          "stepped in layer order (independent micro-batches); layers = (2 streams) the HCA layers "
@@ -254,6 +258,9 @@ def main():
     if args.streams < 1 or args.streams > P or (args.split == "layers" and args.streams != 2):
         sys.exit("--streams: 1 .. pairs (exactly 2 with --split layers)")
     side = [torch.cuda.Stream() for _ in range(args.streams - 1)]
+    # the workspaces were sized for the whole-GPU plan, which needs the most splits
+    attn_cus = 256 // args.streams if args.attn_cus < 0 else args.attn_cus
+    native.cskv_attn_cu_budget(attn_cus)
 
     def step_all(i):
         hybrid.step_stack(pairs, i, share=share, side=side, split=args.split)
@@ -295,7 +302,9 @@ def main():
     stack_bytes = step_bytes * P - (sb["csa_index"] * (P - 1) if share == "reuse" else 0)
     hbm_gbs = stack_bytes / (ms_per_step / 1e3) / 1e9
 
-    # ---- per-call timings with a cold Infinity Cache (512 MB write before each launch)
+    # ---- per-call timings with a cold Infinity Cache (512 MB write before each launch), each call
+    # alone on the GPU and planned for all of it
+    native.cskv_attn_cu_budget(0)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     pr = pairs[0]
     pr.restore()
@@ -383,6 +392,7 @@ def main():
                         f"context 2^20, H=64, D=512+64, {args.kv} entries, bf16 window 128",
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "streams": args.streams,
+            "attn_cu_budget": attn_cus,
             **({"stream_split": ("pairs in one contiguous group per stream, each stepped in layer order "
                                  "(independent micro-batches)") if args.split == "chains" else
                 "the HCA layers of all pairs on the second stream beside the CSA layers"}

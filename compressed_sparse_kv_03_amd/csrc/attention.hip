@@ -60,7 +60,7 @@ constexpr int kTPR = kNT / kTK;      // staging threads per key row
 constexpr int kMaxRopePairs = 32;
 constexpr int kMaxSplitKeys = 2048;  // key rows listed per split
 constexpr int kMaxSplits = 64;
-constexpr int kCUs = 256;            // one workgroup per CU
+constexpr int kCUs = 256;            // one workgroup per CU (the default CU budget of a split plan)
 constexpr int kMergeTiles = 2;       // the merge launch, in tile times (split planning)
 constexpr int kWgFixedTiles = 2;     // a workgroup's prologue and epilogue, in tile times
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1234,16 +1234,21 @@ struct AttnPlan {
 // kMaxSplitKeys keys). Either the keys are cut in order (entries, then window tokens), or the
 // entries are cut into splits and each window tile gets a split of its own. With one workgroup
 // per CU a launch takes ceil(workgroups / kCUs) rounds of its longest split and a workgroup's
-// fixed prologue and epilogue, plus the merge launch when the keys are split; a window tile
+// fixed prologue and epilogue, plus the merge launch when the keys are split (with a CU budget
+// below the GPU's 256, for calls that share the GPU with kernels of another stream, the rounds
+// are counted over that many CUs, so fewer, longer splits win); a window tile
 // (loaded and rotated when staged) counts one and a half entry tiles. The cheapest plan wins
 // (ties: the first found, fewer splits).
+static int g_attn_cus = kCUs;  // CUs a split plan of the 64-head kernel counts on
+
 static AttnPlan plan_attn(int nq, int H, int d_v, int max_entries, int W) {
   AttnPlan p{};
+  const int cus = g_attn_cus;
   p.n_hb = (H + kHB - 1) / kHB;
   const int64_t base = (int64_t)nq * p.n_hb;
   const int te = (max(max_entries, 0) + kTK - 1) / kTK, tw = (max(W, 0) + kTK - 1) / kTK;
   const int tiles = max(te + tw, 1);
-  auto rounds = [&](int s) { return (base * s + kCUs - 1) / kCUs; };
+  auto rounds = [&](int s) { return (base * s + cus - 1) / cus; };
   int64_t best_cost = -1;
   // keys in order: the split holding the window tiles is the longest
   for (int s = 1; s <= kMaxSplits && s <= tiles; ++s) {
@@ -1478,6 +1483,12 @@ using namespace cskv;
 extern "C" CSKV_API int cskv_attn_path(int path) {
   CSKV_REQUIRE(path >= 0 && path <= 2, CSKV_EINVAL, "cskv_attn_path: path=%d outside [0, 2]", path);
   g_attn_path = path;
+  return CSKV_OK;
+}
+
+extern "C" CSKV_API int cskv_attn_cu_budget(int cus) {
+  CSKV_REQUIRE(cus >= 0 && cus <= 4096, CSKV_EINVAL, "cskv_attn_cu_budget: cus=%d outside [0, 4096]", cus);
+  g_attn_cus = cus ? cus : kCUs;
   return CSKV_OK;
 }
 

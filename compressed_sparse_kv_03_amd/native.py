@@ -32,6 +32,7 @@ _SIGS = {
                             _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "cskv_attn_path": ([_i], _i),
+    "cskv_attn_cu_budget": ([_i], _i),
     "hybrid_attn_decode_noalloc": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                                     _p, _p, _f, _i, _i, _p], _i),
     "hybrid_attn_prefill": ([_p, _i64, _i, _p, _p, _i, _i, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
@@ -161,6 +162,11 @@ ATTN_AUTO, ATTN_G64, ATTN_G16 = 0, 1, 2     # cskv_attn_path
 def cskv_attn_path(path):
     """Which attention kernel the attention calls run (0: by shape, 1: 64-head, 2: 16-head)."""
     _check(lib().cskv_attn_path(path))
+
+
+def cskv_attn_cu_budget(cus):
+    """CUs the 64-head attention kernel's split plan counts on (0: the whole GPU)."""
+    _check(lib().cskv_attn_cu_budget(cus))
 
 
 def hybrid_attn_decode_noalloc(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,

@@ -239,6 +239,20 @@ CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_c
 CSKV_API int cskv_attn_path(int path);
 
 /*
+ * cskv_attn_cu_budget - the number of compute units the 64-head kernel's key-split plan counts
+ * on (hybrid_attn_decode, _noalloc, _prefill and their *_workspace_size functions). The plan
+ * weighs each workgroup's fixed prologue and epilogue against the rounds of workgroups the CUs
+ * take; 0 (the default) counts the whole GPU (256 CUs). A caller that runs other kernels beside
+ * the attention calls on another stream passes the share it expects them to leave, so that the
+ * plan takes fewer, longer splits. Results are the same for every budget (the split count only
+ * reorders the fp32 sums of a head's partials); time and workspace size change. Process-wide,
+ * with the same rules as cskv_attn_path (set before sizing a workspace, keep while the calls
+ * using it are issued, not for concurrent use from several host threads).
+ * Errors: CSKV_EINVAL (cus outside [0, 4096]).
+ */
+CSKV_API int cskv_attn_cu_budget(int cus);
+
+/*
  * hybrid_attn_decode_noalloc - hybrid_attn_decode without a workspace argument, for callers
  * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. It computes the same result with the same kernels; the

@@ -17,7 +17,7 @@ def declared():
 
 def test_library_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 16
     L = native.lib()
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
@@ -125,6 +125,13 @@ def test_attention_validation():
     assert dec_na(B=16, N=65536) == -3
     assert L.cskv_attn_path(3) == -1 and L.cskv_attn_path(-1) == -1
     assert L.cskv_attn_path(0) == 0
+    # a smaller CU budget plans fewer, longer splits of the 1M HCA key set (smaller workspace)
+    assert L.cskv_attn_cu_budget(-1) == -1 and L.cskv_attn_cu_budget(4097) == -1
+    full = L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1)
+    assert L.cskv_attn_cu_budget(128) == 0
+    half = L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1)
+    assert L.cskv_attn_cu_budget(0) == 0
+    assert 0 < half < full and L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) == full
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
                                                         k=1, x=16, W=128, H=16, D=128, dr=64, dv=128, m=4,
                                                         base=1e4, scale=0.1, out=16, lse=None, ws=None, wsb=0,

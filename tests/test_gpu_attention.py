@@ -304,11 +304,21 @@ def test_decode_c3_gpu_compressed_sequences():
     del x
 
 
-def test_decode_c3_all_sequences():
+@pytest.mark.parametrize("cus", [0, 64], ids=["whole_gpu_plan", "cu_budget_64"])
+def test_decode_c3_all_sequences(cus):
     """HCA decode at the full 1M-context shape (B=16, 8192 fp8 entries each, window 128, 64 heads):
-    the whole output tensor against the oracle, on caches drawn directly from the generator."""
+    the whole output tensor against the oracle, on caches drawn directly from the generator; with
+    the split plan for the whole GPU and for a 64-CU budget (fewer, longer key splits)."""
     w = configs.C3
-    say("decode", w.name, "generated caches")
+    say("decode", w.name, "generated caches, cu budget", cus)
+    native.cskv_attn_cu_budget(cus)
+    try:
+        _c3_all_sequences(w)
+    finally:
+        native.cskv_attn_cu_budget(0)
+
+
+def _c3_all_sequences(w):
     n = w.L // w.m
     t = w.L - 1
     q = synth.normal_bf16_bits((w.B, w.H, w.D), w.sigma, synth.seed_of(1, w.wid, 2), DEV)
