@@ -38,6 +38,7 @@
 // directly. Short key sets of few queries go to the 16-head kernel instead
 // (attention_g16.hip).
 #include <math.h>
+#include <stdint.h>
 
 #include <mutex>
 
@@ -101,6 +102,10 @@ struct AttnArgs {
   float* out_lse;            // [nq, H]
   uint16_t* part_o;          // [nq, n_hb, n_splits, 64, d_v] fp16: the split's O / l
   float* part_ml;            // [nq, n_hb, n_splits, 64, 2]: exponent base m, sum l
+  const uint16_t* x_new;     // append mode: [B, T, D] new tokens (rows >= kNewRow), else nullptr
+  const float* z_new;        // [B, T] or nullptr
+  uint16_t* ring_w;          // the rings (win), written in append mode
+  float* ring_z;             // [B, R] (with z_new)
 };
 
 // Per query: entry-key count, window start position and count.
@@ -439,7 +444,7 @@ __device__ __forceinline__ void window_load(const AttnArgs& a, int key0, int key
   const int r = threadIdx.x / kTPR, c0 = threadIdx.x % kTPR;
   const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
   R.row = row;
-  const uint16_t* src = a.win + (int64_t)max(row, 0) * D;
+  const uint16_t* src = row >= kNewRow ? a.x_new + (int64_t)(row - kNewRow) * D : a.win + (int64_t)max(row, 0) * D;
 #pragma unroll
   for (int i = 0; i < WG::NC; ++i) R.v[i] = *reinterpret_cast<const uint4*>(src + 8 * (c0 + kTPR * i));
 }
@@ -985,12 +990,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
   {
     const int64_t wseq = a.ring ? (int64_t)(qi / a.q_per_seq) * a.ring_cap : -a.pos0;
     const int64_t wbase = a.ring ? ks.w0 % a.ring_cap : ks.w0;  // row of window key 0 before wrapping
+    // append mode: positions from the sequence's first query on are the step's new tokens
+    const int j = qi % a.q_per_seq;
+    const int64_t t_new = a.x_new ? ks.t - j : INT64_MAX;
     for (int i = tid; i < key_end - key_begin; i += kNT) {
       const int key = key_begin + i;
       int row;
       if (key < ks.n_c) {
         row = a.topk ? a.topk[(int64_t)qi * a.k + key] : key;
         if (row >= a.N_cap) row = -1;
+      } else if (ks.w0 + (key - ks.n_c) >= t_new) {
+        row = kNewRow + (qi - j) + (int)(ks.w0 + (key - ks.n_c) - t_new);
       } else {
         int64_t slot = wbase + (key - ks.n_c);
         if (a.ring && slot >= a.ring_cap) slot -= a.ring_cap;  // n_w <= W <= ring_cap
@@ -998,6 +1008,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, AttnSmem<D>& sm) {
       }
       sm.sidx[i] = row;
     }
+    // one workgroup per sequence writes the new tokens to the ring
+    if (a.x_new && j == 0 && split == 0 && qh % a.n_hb == 0)
+      append_new_tokens(a.x_new, a.z_new, a.ring_w, a.ring_z, qi, a.q_per_seq, ks.t, a.ring_cap, a.D, tid, kNT);
   }
   // the RoPE table in revolutions per position, base^(-2i / d_rope) / (2 pi), in fp64
   // (pair i: rope_step^i / (2 pi), the power formed by squaring, a few fp64 roundings)
@@ -1407,6 +1420,10 @@ static int run_attn(const char* name, const AttnCall& c, bool noalloc, void* ws,
   a.topk = c.topk;
   a.k = c.k;
   a.win = c.win;
+  a.x_new = c.x_new;
+  a.z_new = c.z_new;
+  a.ring_w = const_cast<uint16_t*>(c.win);  // written only in append mode, whose caller passes a writable ring
+  a.ring_z = c.ring_z;
   a.ring = c.ring;
   a.ring_cap = c.ring_cap;
   a.q_per_seq = c.q_per_seq;
@@ -1509,6 +1526,31 @@ extern "C" CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_p
   const int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, win, W, B, H,
                               D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, c);
   if (rc) return rc;
+  return run_attn(name, c, false, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" CSKV_API int hybrid_attn_decode_append(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                                                  const void* ckv_scale, int ckv_dtype, int N_cap,
+                                                  const int32_t* n_entries, const int32_t* topk_idx, int k,
+                                                  uint16_t* ring_x, float* ring_z, const uint16_t* x_new,
+                                                  const float* z_new, int W, int B, int H, int D, int d_rope,
+                                                  int d_v, float rope_base, float softmax_scale, uint16_t* out,
+                                                  float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps, int T,
+                                                  int R, void* stream) {
+  const char* name = "hybrid_attn_decode_append";
+  if (R == 0) R = W;
+  CSKV_REQUIRE(ring_x && x_new, CSKV_EINVAL, "%s: null ring or new tokens", name);
+  CSKV_REQUIRE(!z_new || ring_z, CSKV_EINVAL, "%s: z_new needs ring_z", name);
+  CSKV_REQUIRE(R >= 1 && R >= T, CSKV_EINVAL, "%s: ring of %d slots for %d new tokens", name, R, T);
+  CSKV_REQUIRE(B >= 1 && (int64_t)B * R < kNewRow, CSKV_EINVAL, "%s: B=%d rings of %d slots", name, B, R);
+  CSKV_REQUIRE(aligned16(x_new), CSKV_EINVAL, "%s: x_new must be 16-byte aligned", name);
+  AttnCall c;
+  const int rc = decode_setup(name, q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, ring_x, W, B,
+                              H, D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, q_rms_eps, T, R, c);
+  if (rc) return rc;
+  c.x_new = x_new;
+  c.z_new = z_new;
+  c.ring_z = ring_z;
   return run_attn(name, c, false, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 

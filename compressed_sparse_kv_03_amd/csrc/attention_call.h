@@ -35,7 +35,35 @@ struct AttnCall {
   float q_rms_eps;           // > 0: unit-gain RMSNorm of each query head (folded into its logits)
   uint16_t* out;             // [nq, H, d_v]
   float* out_lse;            // [nq, H]
+  // decode with the state update: the step's new tokens are read from x_new (window positions
+  // from the sequence's first query position on) and written to their ring slots by the call
+  const uint16_t* x_new;     // [B, T, D] or nullptr (no append)
+  const float* z_new;        // [B, T] or nullptr
+  float* ring_z;             // [B, R] (with z_new)
 };
+
+// Window rows at or above kNewRow name row kNewRow + i of x_new (append mode); ring rows stay
+// below it (B * R < kNewRow is checked by the call).
+constexpr int kNewRow = 1 << 30;
+
+// Append mode: the T new tokens of the sequence whose first query is qi (at position t0) go to
+// ring slots (t0 + i) mod R, rows and pooling logits, with 16-byte vector stores by the nt
+// threads of one workgroup. No workgroup of the call reads those slots: a query's window
+// positions at or above t0 come from x_new, and the positions below t0 it sees
+// (t0 + j - W + 1 .. t0 - 1) take other slots because R >= W + T - 1.
+__device__ __forceinline__ void append_new_tokens(const uint16_t* __restrict__ x_new, const float* __restrict__ z_new,
+                                                  uint16_t* __restrict__ ring_x, float* __restrict__ ring_z,
+                                                  int qi, int T, int64_t t0, int R, int D, int tid, int nt) {
+  const int b = qi / T;
+  const int cpr = D >> 3;  // 16-byte chunks per row
+  for (int c = tid; c < T * cpr; c += nt) {
+    const int i = c / cpr, ch = c - i * cpr;
+    const int64_t slot = (int64_t)b * R + (t0 + i) % R;
+    const uint4 v = *reinterpret_cast<const uint4*>(x_new + (int64_t)(qi + i) * D + 8 * ch);
+    *reinterpret_cast<uint4*>(ring_x + slot * D + 8 * ch) = v;
+  }
+  if (z_new && tid < T) ring_z[(int64_t)b * R + (t0 + tid) % R] = z_new[qi + tid];
+}
 
 namespace g16 {
 size_t ws_bytes(int nq, int H, int d_v, int max_keys);

@@ -20,6 +20,7 @@
 // rotated dims of the query and of window keys go through the MFMA as a bf16 value plus a bf16
 // remainder. A query's splits write unnormalised partials merged by a second launch.
 #include <math.h>
+#include <stdint.h>
 
 #include <mutex>
 
@@ -78,6 +79,10 @@ struct AttnArgs {
   float* out_lse;            // [nq, H]
   float* part_o;             // [nq, n_hg, n_splits, 16, d_v]
   float* part_ml;            // [nq, n_hg, n_splits, 16, 2]
+  const uint16_t* x_new;     // append mode: [B, T, D] new tokens (rows >= kNewRow), else nullptr
+  const float* z_new;        // [B, T] or nullptr
+  uint16_t* ring_w;          // the rings (win), written in append mode
+  float* ring_z;             // [B, R] (with z_new)
   double rev_freq[kMaxRopePairs];  // RoPE frequencies base^(-2i/d_rope) / (2 pi), formed on the host in fp64
 };
 
@@ -277,7 +282,7 @@ __device__ __forceinline__ void window_load(const AttnArgs& a, int key0, int key
   const int r = threadIdx.x / WG::TPR, c0 = threadIdx.x % WG::TPR;
   const int row = key0 + r < key_end ? sm.sidx[key0 - key_begin + r] : -1;
   R.row = row;
-  const uint16_t* src = a.win + (int64_t)max(row, 0) * D;
+  const uint16_t* src = row >= kNewRow ? a.x_new + (int64_t)(row - kNewRow) * D : a.win + (int64_t)max(row, 0) * D;
   const int nu = rope0 >> 3;  // unrotated chunks
 #pragma unroll
   for (int i = 0; i < WG::NC; ++i) R.v[i] = *reinterpret_cast<const uint4*>(src + 8 * min(c0 + WG::TPR * i, WG::CPR - 1));
@@ -522,12 +527,17 @@ __global__ __launch_bounds__(kNT, 2) void attn_kernel(AttnArgs a) {
   {
     const int64_t wseq = a.ring ? (int64_t)(qi / a.q_per_seq) * a.ring_cap : -a.pos0;
     const int64_t wbase = a.ring ? ks.w0 % a.ring_cap : ks.w0;  // row of window key 0 before wrapping
+    // append mode: positions from the sequence's first query on are the step's new tokens
+    const int j = qi % a.q_per_seq;
+    const int64_t t_new = a.x_new ? ks.t - j : INT64_MAX;
     for (int i = tid; i < key_end - key_begin; i += kNT) {
       const int key = key_begin + i;
       int row;
       if (key < ks.n_c) {
         row = a.topk ? a.topk[(int64_t)qi * a.k + key] : key;
         if (row >= a.N_cap) row = -1;
+      } else if (ks.w0 + (key - ks.n_c) >= t_new) {
+        row = kNewRow + (qi - j) + (int)(ks.w0 + (key - ks.n_c) - t_new);
       } else {
         int64_t slot = wbase + (key - ks.n_c);
         if (a.ring && slot >= a.ring_cap) slot -= a.ring_cap;  // n_w <= W <= ring_cap
@@ -535,6 +545,9 @@ __global__ __launch_bounds__(kNT, 2) void attn_kernel(AttnArgs a) {
       }
       sm.sidx[i] = row;
     }
+    // one workgroup per sequence writes the new tokens to the ring
+    if (a.x_new && j == 0 && split == 0 && hg == 0)
+      append_new_tokens(a.x_new, a.z_new, a.ring_w, a.ring_z, qi, a.q_per_seq, ks.t, a.ring_cap, a.D, tid, kNT);
   }
   if (tid < kTK16) {  // window remainders of the last 64 dims below rope0 are zero
     for (int d = D - 64; d < rope0; ++d)
@@ -852,6 +865,10 @@ int launch(const char* name, const AttnCall& c, void* ws, size_t ws_bytes, hipSt
   a.topk = c.topk;
   a.k = c.k;
   a.win = c.win;
+  a.x_new = c.x_new;
+  a.z_new = c.z_new;
+  a.ring_w = const_cast<uint16_t*>(c.win);  // written only in append mode, whose caller passes a writable ring
+  a.ring_z = c.ring_z;
   a.ring = c.ring;
   a.ring_cap = c.ring_cap;
   a.q_per_seq = c.q_per_seq;

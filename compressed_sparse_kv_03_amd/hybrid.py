@@ -8,7 +8,8 @@ CSA 및 HCA": CSA pools 4 tokens per entry and selects top-k with the FP4 indexe
 HCA pools 128 per entry and attends densely.
 
 One decode step at position t (the same t for every sequence of the batch):
-  1. each layer writes its new raw token and pooling logit to ring slot t mod R;
+  1. each layer writes its new raw token and pooling logit to ring slot t mod R (inside the
+     layer's attention call when step 2 has nothing to compress, hybrid_attn_decode_append);
   2. if (t+1) % m == 0 the layer compresses ring slots of positions [t-m+1, t]
      (contiguous because m divides R) into entry (t+1)/m - 1;
   3. CSA: csa_index_topk over the visible entries, then hybrid_attn_decode on
@@ -69,6 +70,9 @@ class LayerPairSpec:
     kv_dtype: str = "fp8"
     # mxfp4 entries: attention logits on the scaled FP4 MFMA from the stored codes (CSKV_QK_FP4)
     qk_fp4: bool = False
+    # a step that completes no block of a layer appends that layer's new tokens inside its attention
+    # call (hybrid_attn_decode_append) instead of a cskv_ring_append launch of its own
+    fuse_append: bool = True
 
     @property
     def sigma(self):
@@ -233,12 +237,16 @@ class LayerPair:
         assert share in (None, "reuse", "reindex") and (share is None or src is not None)
         assert set(layers) <= {"csa", "hca"}
         kv = {"csa": src if share == "reindex" else self, "hca": self}
+        fused = {}
         for name in layers:
             if kv[name] is not self:
                 continue
             R, m = self.R[name], self.m[name]
-            native.cskv_ring_append(self.xn[name][i], self.zn[name][i], self.pos[i], self.ring[name],
-                                    self.ringz[name], B, D, R, stream, T=Td)
+            # the compression of a completed block reads the new tokens from the ring
+            fused[name] = s.fuse_append and not self.blocks[name][i]
+            if not fused[name]:
+                native.cskv_ring_append(self.xn[name][i], self.zn[name][i], self.pos[i], self.ring[name],
+                                        self.ringz[name], B, D, R, stream, T=Td)
             keys = name == "csa" and s.derive_keys
             if keys:
                 native.cskv_ring_append(self.xkn[i], None, self.pos[i], self.ring_xk, None, B, s.D_I, R, stream, T=Td)
@@ -261,9 +269,18 @@ class LayerPair:
             topk = self.topk[i]
         for name in layers:
             c = kv[name]
+            tk = topk if name == "csa" else None
+            if fused.get(name):
+                native.hybrid_attn_decode_append(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
+                                                 self.attn_code, self.cap[name], self.nent[name][i], tk, s.k,
+                                                 c.ring[name], c.ringz[name], self.xn[name][i], self.zn[name][i], W,
+                                                 B, s.H, D, s.d_rope, s.d_v, s.rope_base, s.scale,
+                                                 self.out[name][i], self.lse[name][i], self.ws_att[name], None,
+                                                 stream, q_rms_eps=s.rms_eps, T=Td, R=c.R[name])
+                continue
             native.hybrid_attn_decode(self.q[name][i], self.qpos[i], c.ckv[name], c.scl[name],
                                       self.attn_code, self.cap[name], self.nent[name][i],
-                                      topk if name == "csa" else None, s.k, c.ring[name], W, B, s.H, D,
+                                      tk, s.k, c.ring[name], W, B, s.H, D,
                                       s.d_rope, s.d_v, s.rope_base, s.scale, self.out[name][i], self.lse[name][i],
                                       self.ws_att[name], None, stream, q_rms_eps=s.rms_eps, T=Td, R=c.R[name])
 

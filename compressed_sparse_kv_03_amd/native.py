@@ -31,6 +31,8 @@ _SIGS = {
     "hybrid_attn_decode": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
                             _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "hybrid_attn_decode_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "hybrid_attn_decode_append": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                   _f, _f, _p, _p, _p, _sz, _f, _i, _i, _p], _i),
     "cskv_attn_path": ([_i], _i),
     "cskv_attn_cu_budget": ([_i], _i),
     "hybrid_attn_decode_noalloc": ([_p, _p, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _f,
@@ -153,6 +155,20 @@ def hybrid_attn_decode(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, to
                                     _ptr(n_entries), _ptr(topk_idx), k, _ptr(win), W, B, H, D, d_rope, d_v,
                                     rope_base, softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes,
                                     q_rms_eps, T, R, _stream(stream)))
+
+
+def hybrid_attn_decode_append(q, q_pos, ckv, ckv_scale, ckv_dtype, N_cap, n_entries, topk_idx, k, ring_x, ring_z,
+                              x_new, z_new, W, B, H, D, d_rope, d_v, rope_base, softmax_scale, out, out_lse, ws,
+                              ws_bytes=None, stream=None, *, q_rms_eps=0.0, T=1, R=0):
+    """cskv_ring_append of the step's T new tokens per sequence (x_new [B, T, D], z_new [B, T] or
+    None) into ring_x / ring_z, then hybrid_attn_decode over ring_x, in one call."""
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hybrid_attn_decode_append(_ptr(q), _ptr(q_pos), _ptr(ckv), _ptr(ckv_scale), ckv_dtype, N_cap,
+                                           _ptr(n_entries), _ptr(topk_idx), k, _ptr(ring_x), _ptr(ring_z),
+                                           _ptr(x_new), _ptr(z_new), W, B, H, D, d_rope, d_v, rope_base,
+                                           softmax_scale, _ptr(out), _ptr(out_lse), _ptr(ws), ws_bytes, q_rms_eps,
+                                           T, R, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024   # CSKV_NOALLOC_SCRATCH_BYTES

@@ -226,6 +226,33 @@ CSKV_API int hybrid_attn_decode(const uint16_t* q, const int64_t* q_pos, const v
 CSKV_API size_t hybrid_attn_decode_workspace_size(int B, int H, int d_v, int N_cap, int k, int W, int dense);
 
 /*
+ * hybrid_attn_decode_append - the decode state update of a layer and its attention in one call:
+ * the same result as cskv_ring_append(x_new, z_new, pos, ring_x, ring_z, B, T, D, R) with
+ * pos[b] = q_pos[b*T], followed by hybrid_attn_decode(..., win = ring_x, ...) on the same
+ * stream. (Page "딥시크 V4 분석 ...", section "쉽게 이해하기": every layer keeps the latest 128
+ * tokens raw beside its compressed entries; each decode step adds its token to that window and
+ * attends over it.) The attention takes the step's new tokens from x_new and writes them to
+ * their ring slots in the same launch, one workgroup per sequence (no reader of the call needs
+ * those slots: R >= W + T - 1). Where a block of m tokens completes at this step, the caller
+ * runs cskv_ring_append, the compression and then hybrid_attn_decode instead, since the
+ * compression reads the new token from the ring.
+ *
+ * Arguments as in hybrid_attn_decode, with win replaced by ring_x [B, R, D] bf16 (written:
+ * slots (q_pos[b*T] + i) mod R, i < T), and x_new [B, T, D] bf16 (16-byte aligned), z_new
+ * [B, T] fp32 pooling logits or NULL, ring_z [B, R] fp32 (written with z_new). Queries of a
+ * sequence must sit at consecutive positions: q_pos[b*T + j] = q_pos[b*T] + j. Workspace:
+ * hybrid_attn_decode_workspace_size(B*T, ...). Requirements as in hybrid_attn_decode, and
+ * R >= T, B * R < 2^30, ring_x and x_new non-NULL (CSKV_EINVAL otherwise).
+ */
+CSKV_API int hybrid_attn_decode_append(const uint16_t* q, const int64_t* q_pos, const void* ckv,
+                       const void* ckv_scale, int ckv_dtype, int N_cap, const int32_t* n_entries,
+                       const int32_t* topk_idx, int k, uint16_t* ring_x, float* ring_z,
+                       const uint16_t* x_new, const float* z_new, int W, int B, int H, int D,
+                       int d_rope, int d_v, float rope_base, float softmax_scale, uint16_t* out,
+                       float* out_lse, void* ws, size_t ws_bytes, float q_rms_eps, int T, int R,
+                       void* stream);
+
+/*
  * cskv_attn_path - which attention kernel hybrid_attn_decode, _noalloc and _prefill run (and
  * their *_workspace_size functions plan for): 0 (the default) chooses by the call's shape, the
  * 16-head kernel for short key sets of few queries (at most 512 keys per query and at most 4096

@@ -17,7 +17,7 @@ def declared():
 
 def test_library_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 17
     L = native.lib()
     for n in names:
         assert getattr(L, n, None) is not None, f"{n} not exported"
@@ -132,6 +132,21 @@ def test_attention_validation():
     half = L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1)
     assert L.cskv_attn_cu_budget(0) == 0
     assert 0 < half < full and L.hybrid_attn_decode_workspace_size(8, 64, 512, 8194, 128, 128, 1) == full
+    def dec_ap(**kw):     # the call with the state update: rings and new tokens instead of win
+        a = dict(q=16, qp=16, ckv=16, sc=16, dt=1, N=100, ne=16, tk=None, k=128, ring=16, rz=None, x=16, z=None,
+                 W=128, B=1, H=64, D=576, dr=64, dv=512, base=1e4, scale=0.04, out=16, lse=None, ws=None, wsb=0,
+                 eps=0.0, T=1, R=0, s=None)
+        a.update(kw)
+        return L.hybrid_attn_decode_append(*a.values())
+    assert dec_ap(ring=None) == -1                      # no ring to write
+    assert dec_ap(x=None) == -1                         # no new tokens
+    assert dec_ap(z=16) == -1                           # z_new without ring_z
+    assert dec_ap(W=0, R=0) == -1                       # no ring slots at all
+    assert dec_ap(W=0, R=2, T=3) == -1                  # fewer slots than new tokens
+    assert dec_ap(T=2, R=128) == -1                     # R < W + T - 1
+    assert dec_ap(B=1 << 16, R=1 << 14) == -1           # B * R >= 2^30 (row encoding)
+    assert dec_ap(x=24) == -1                           # x_new not 16-byte aligned
+    assert dec_ap(D=100) == -1                          # the decode requirements hold as well
     pre = lambda **kw: L.hybrid_attn_prefill(*dict(dict(q=16, p0=0, T=10, ckv=16, sc=None, dt=0, N=2, tk=None,  # noqa
                                                         k=1, x=16, W=128, H=16, D=128, dr=64, dv=128, m=4,
                                                         base=1e4, scale=0.1, out=16, lse=None, ws=None, wsb=0,

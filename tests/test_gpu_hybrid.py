@@ -192,6 +192,30 @@ def test_hybrid_loop_graph_replays_match_eager():
         assert torch.equal(pair.topk, ref_tk), f"replay {rep}: top-k differs from eager"
 
 
+@pytest.mark.parametrize("draft,accept_seed,H,D,d_v,k", [(1, -1, 64, 576, 512, 128), (4, 3, 64, 576, 512, 128),
+                                                         (1, -1, 16, 128, 128, 32)])
+def test_hybrid_loop_fused_append_matches_separate(draft, accept_seed, H, D, d_v, k):
+    """The loop with each layer's state update inside its attention call (hybrid_attn_decode_append,
+    on steps that complete no block) equals the loop with separate cskv_ring_append launches bit
+    for bit: outputs, lse and top-k of every step, and the final rings."""
+    spec = dict(B=2, L=4096, steps=140, H=H, D=D, d_rope=64, d_v=d_v, k=k, wid=58, draft=draft,
+                accept_seed=accept_seed)
+    say("hybrid fused append", spec)
+    res = []
+    for fuse in (False, True):
+        pair = hybrid.LayerPair(hybrid.LayerPairSpec(fuse_append=fuse, **spec))
+        pair.run(0, spec["steps"])
+        torch.cuda.synchronize()
+        res.append(pair)
+    a, b = res
+    for n in ("csa", "hca"):
+        assert torch.equal(a.out[n], b.out[n]), f"{n} outputs differ"
+        assert torch.equal(a.lse[n], b.lse[n]), f"{n} lse differs"
+        assert torch.equal(a.ring[n], b.ring[n]) and torch.equal(a.ringz[n], b.ringz[n]), f"{n} rings differ"
+        assert torch.equal(a.ckv[n], b.ckv[n]), f"{n} compressed entries differ"
+    assert torch.equal(a.topk, b.topk), "top-k differs"
+
+
 @pytest.mark.parametrize("split,nside,share", [("layers", 1, None), ("chains", 1, None), ("chains", 2, "reuse"),
                                                ("chains", 1, "reindex")])
 def test_hybrid_stack_streams_graph_matches_serial(split, nside, share):
