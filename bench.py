@@ -72,6 +72,9 @@ def parse():
                     help="CUs the 64-head attention's split plan counts on in the timed loop (cskv_attn_cu_budget; "
                          "-1: 256 / streams, i.e. the whole GPU on one stream); the cold per-call timings plan "
                          "for the whole GPU")
+    ap.add_argument("--attn-path", type=int, choices=[0, 1, 2], default=0,
+                    help="attention kernel of the timed loop (cskv_attn_path: 0 by shape, 1 the 64-head kernel, "
+                         "2 the 16-head kernel); the cold per-call timings choose by shape")
     ap.add_argument("--split", choices=["chains", "layers"], default="chains",
                     help="with --streams > 1: chains = the pairs cut into one contiguous group per stream, each "
                          "stepped in layer order (independent micro-batches); layers = (2 streams) the HCA layers "
@@ -261,6 +264,7 @@ def main():
     # the workspaces were sized for the whole-GPU plan, which needs the most splits
     attn_cus = 256 // args.streams if args.attn_cus < 0 else args.attn_cus
     native.cskv_attn_cu_budget(attn_cus)
+    native.cskv_attn_path(args.attn_path)
 
     def step_all(i):
         hybrid.step_stack(pairs, i, share=share, side=side, split=args.split)
@@ -305,6 +309,7 @@ def main():
     # ---- per-call timings with a cold Infinity Cache (512 MB write before each launch), each call
     # alone on the GPU and planned for all of it
     native.cskv_attn_cu_budget(0)
+    native.cskv_attn_path(0)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     pr = pairs[0]
     pr.restore()
@@ -395,6 +400,7 @@ def main():
             "batch": spec.B, "context": spec.L, "layer_pairs_per_step": P,
             "streams": args.streams,
             "attn_cu_budget": attn_cus,
+            **({"attn_path": {1: "64-head kernel", 2: "16-head kernel"}[args.attn_path]} if args.attn_path else {}),
             **({"stream_split": ("pairs in one contiguous group per stream, each stepped in layer order "
                                  "(independent micro-batches)") if args.split == "chains" else
                 "the HCA layers of all pairs on the second stream beside the CSA layers"}
