@@ -260,6 +260,8 @@ def main():
     # further streams (default priority, like the first) for the parallel branches of a step
     if args.streams < 1 or args.streams > P or (args.split == "layers" and args.streams != 2):
         sys.exit("--streams: 1 .. pairs (exactly 2 with --split layers)")
+    if args.split == "layers" and share is not None:
+        sys.exit("--split layers takes no --share (the sharing layers wait for pair 0's step)")
     side = [torch.cuda.Stream() for _ in range(args.streams - 1)]
     # the workspaces were sized for the whole-GPU plan, which needs the most splits
     attn_cus = 256 // args.streams if args.attn_cus < 0 else args.attn_cus
